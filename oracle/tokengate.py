@@ -1,0 +1,252 @@
+"""Plain CPU oracle of the TokenGate gated prefill (test infrastructure).
+
+What the method computes, in the order the coverage pages give it ([KO] "작동
+방식"; [FR] lede; [IT] "Come funziona"; source tags are defined in
+``oracle/__init__.py``):
+
+  1. layers below the gate layer run over all N tokens (not modelled here: the
+     post-attention residual of the gate layer is an input);
+  2. at the gate layer a small MLP gives every token a score computed from its
+     post-attention residual;
+  3. a top-K selector keeps the best-scoring tokens of the *document* part of
+     the prompt; the question is never pruned;
+  4. only the kept rows go up: the layers above the gate see K tokens and build
+     no KV entries for the dropped ones;
+  5. above the gate, attention is *token-gated*: each kept key's score is added
+     to the attention logits as a bias, with a learned gain and temperature per
+     head ([KO] "작동 방식"; [PT] "TokenGate “ensina”…"; [ABS]).
+
+Everything here is numpy in float64, written for a reader to check by eye; no
+blocking or fusion beyond splitting query rows into blocks to bound memory,
+which does not change any value.
+
+Readings of points the pages leave open (each is also listed in the design
+notes of the repository):
+
+  * logit form: q.k / (sqrt(d) * tau_h) + g_h * s_j, with s_j the raw gate
+    output of key j (the pages only say "score as a bias, per-head gain and
+    temperature");
+  * gate MLP: z = W1 h + b1, a = GELU(z) with the exact erf form, s = w2.a + b2,
+    no normalisation inside the gate; every row is scored (question rows too,
+    since their scores are their own key bias above the gate);
+  * selection total order: scores are compared as float32 through a monotone
+    32-bit key; -0.0 equals +0.0; NaN ranks below -inf; ties go to the lower
+    token index; the kept set is therefore unique;
+  * kept rows stay in ascending original order, so causality in compacted
+    order equals causality in original positions; kept tokens keep their
+    original RoPE positions (applied to q/k before attention);
+  * the bias applies only to layers above the gate (the pages place it there).
+
+Pins (tests in ``tests/test_oracle_pins.py``):
+  gelu_erf         -- torch's erf GELU and x*Phi(x) from scipy.stats; limits.
+  gate_scores      -- H_g = 1 detector special case vs torch GELU; linear
+                      regime closed form; pure-Python loop brute force.
+  score_keys       -- order agreement with Python float comparison on a
+                      hand-built list incl. +-inf, +-0, NaN, denormals.
+  topk_select      -- brute force over all k-subsets on tiny inputs (the unique
+                      dominating subset); invariants; golden fixture.
+  compact_rows     -- bytewise definition on random bytes.
+  gated_attention  -- torch SDPA (fp64) with K=N, g=0, tau=1; masking identity
+                      vs torch SDPA with an additive float mask on the full-N
+                      problem; two-key closed form; first-row identity; shift
+                      invariance; temperature equivalence; golden fixture.
+  full_attention   -- torch SDPA (fp64, causal, GQA by repetition).
+No function is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+__all__ = [
+    "gelu_erf",
+    "gate_scores",
+    "score_keys",
+    "kept_count",
+    "topk_select",
+    "compact_rows",
+    "gated_attention",
+    "full_attention",
+    "gated_prefill",
+]
+
+
+# ---------------------------------------------------------------------------
+# Gate: a small MLP scores every token from its post-attention residual
+# ([KO] "작동 방식"; [FR] lede; [IT] "Come funziona").
+# ---------------------------------------------------------------------------
+
+def gelu_erf(x):
+    """Exact GELU, x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def gate_scores(h, w1, b1, w2, b2, row_block: int = 4096):
+    """Score s_i = w2 . GELU(W1 h_i + b1) + b2 for every row i.
+
+    h  [N, H]     post-attention residual at the gate layer
+    w1 [Hg, H]    first layer (out x in, as a linear layer stores it)
+    b1 [Hg], w2 [Hg], b2 scalar
+    Returns float64 [N].  Rows are processed in blocks only to bound memory.
+    """
+    h = np.asarray(h)
+    w1 = np.asarray(w1, dtype=np.float64)
+    b1 = np.asarray(b1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    n = h.shape[0]
+    out = np.empty(n, dtype=np.float64)
+    for r0 in range(0, n, row_block):
+        hb = h[r0:r0 + row_block].astype(np.float64)
+        z = hb @ w1.T + b1
+        out[r0:r0 + row_block] = gelu_erf(z) @ w2 + float(b2)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Selection: top-K over the document part only; the question is always kept
+# ([KO] "작동 방식"; [PT] "TokenGate “ensina”…"; [IT] "Come funziona").
+# ---------------------------------------------------------------------------
+
+def score_keys(scores_f32):
+    """Map float32 scores to uint32 keys whose unsigned order is the total order.
+
+    Non-negative floats get their sign bit set; negative floats are bit-flipped
+    (so a larger magnitude sorts lower); -0.0 is first turned into +0.0 and any
+    NaN maps to key 0, below -inf.
+    """
+    s = np.ascontiguousarray(np.asarray(scores_f32, dtype=np.float32))
+    bits = s.view(np.uint32).copy()
+    bits[bits == np.uint32(0x80000000)] = 0
+    neg = (bits >> np.uint32(31)) == 1
+    keys = np.where(neg, ~bits, bits | np.uint32(0x80000000)).astype(np.uint32)
+    keys[np.isnan(s)] = 0
+    return keys
+
+
+def kept_count(n: int, doc_begin: int, doc_end: int, k_doc: int) -> int:
+    """Rows that survive: min(K, N_doc) document rows plus every other row."""
+    n_doc = doc_end - doc_begin
+    return min(k_doc, n_doc) + (n - n_doc)
+
+
+def topk_select(scores_f32, doc_begin: int, doc_end: int, k_doc: int):
+    """Kept row indices, ascending, as int32.
+
+    Document rows [doc_begin, doc_end) are ranked by (score key descending,
+    index ascending) and the first min(K, N_doc) are kept; every row outside
+    the document is kept.  The selection is decided in float32, the precision
+    the scores are handed over in.
+    """
+    keys = score_keys(scores_f32)
+    n = keys.shape[0]
+    assert 0 <= doc_begin <= doc_end <= n and k_doc >= 0
+    doc = np.arange(doc_begin, doc_end, dtype=np.int64)
+    # np.lexsort: last key is primary.  Primary = key descending, i.e. the
+    # complement ascending; secondary = index ascending.
+    order = np.lexsort((doc, np.uint32(0xFFFFFFFF) - keys[doc_begin:doc_end]))
+    k = min(k_doc, doc.size)
+    chosen = doc[order[:k]]
+    others = np.concatenate([np.arange(0, doc_begin), np.arange(doc_end, n)])
+    return np.sort(np.concatenate([chosen, others])).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Compaction: only kept rows go up; no KV rows exist for the dropped tokens
+# ([KO] "작동 방식"; [FR] lede).
+# ---------------------------------------------------------------------------
+
+def compact_rows(idx, src):
+    """dst[i] = src[idx[i]] (a copy of whole rows)."""
+    return np.array(np.asarray(src)[np.asarray(idx, dtype=np.int64)], copy=True)
+
+
+# ---------------------------------------------------------------------------
+# Token-gated attention above the gate ([KO] "작동 방식"; [PT] "TokenGate
+# “ensina”…"; [ABS]; [IT] "Come funziona").
+# ---------------------------------------------------------------------------
+
+def gated_attention(q, k, v, key_score, gain, tau, rows=None, return_lse=False,
+                    row_block: int = 256):
+    """Causal GQA attention with a per-key score bias.
+
+    q [M, Hq, d]; k, v [M, Hkv, d]; key_score [M]; gain, tau [Hq].
+    For query head h (KV head h // (Hq/Hkv)) and query row i:
+        logit_ij = q_i.k_j / (sqrt(d) tau_h) + gain_h * key_score_j,  j <= i
+        out_i    = sum_j softmax_j(logit_i.) v_j
+    ``rows``: optional subset of query rows (each row depends only on keys
+    0..i, so a subset is exact).  Returns float64 out [R, Hq, d] and, if asked,
+    the natural-log log-sum-exp [Hq, R].
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    assert k.shape == (m, hkv, d) and v.shape == (m, hkv, d) and hq % hkv == 0
+    group = hq // hkv
+    s = np.asarray(key_score, dtype=np.float64).reshape(m)
+    gain = np.asarray(gain, dtype=np.float64).reshape(hq)
+    tau = np.asarray(tau, dtype=np.float64).reshape(hq)
+    rows = np.arange(m, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    r = rows.size
+    out = np.zeros((r, hq, d), dtype=np.float64)
+    lse = np.zeros((hq, r), dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        kh = k[:, g, :].astype(np.float64)
+        vh = v[:, g, :].astype(np.float64)
+        scale = 1.0 / (math.sqrt(d) * tau[h])
+        for b0 in range(0, r, row_block):
+            rb = rows[b0:b0 + row_block]
+            kend = int(rb.max()) + 1
+            qb = q[rb, h, :].astype(np.float64)
+            logits = (qb @ kh[:kend].T) * scale + gain[h] * s[None, :kend]
+            j = np.arange(kend)[None, :]
+            logits = np.where(j <= rb[:, None], logits, -np.inf)
+            mx = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - mx)
+            l = p.sum(axis=1, keepdims=True)
+            out[b0:b0 + row_block, h, :] = (p @ vh[:kend]) / l
+            lse[h, b0:b0 + row_block] = (mx + np.log(l))[:, 0]
+    return (out, lse) if return_lse else out
+
+
+def full_attention(q, k, v, rows=None, return_lse=False):
+    """Unpruned causal GQA attention over all N rows: the gated form with
+    gain 0 and temperature 1, i.e. softmax(q.k / sqrt(d)) v."""
+    n, hq, _ = np.asarray(q).shape
+    return gated_attention(q, k, v, np.zeros(n), np.zeros(hq), np.ones(hq),
+                           rows=rows, return_lse=return_lse)
+
+
+# ---------------------------------------------------------------------------
+# The three-stage forward ([KO] "작동 방식"; [FR] lede).
+# ---------------------------------------------------------------------------
+
+def gated_prefill(h, w1, b1, w2, b2, doc_begin, doc_end, k_doc, layers,
+                  scores_f32=None, layer_ids=None, rows=None):
+    """Score -> select -> compact -> token-gated attention for each upper layer.
+
+    ``layers``: list of (q, k, v, gain, tau) where q/k/v are full-N rows of the
+    upper layer (positions already encoded at the original ids); the kept rows
+    are taken with the selected indices.  ``scores_f32``: optional float32
+    scores to select on (the precision the selection is decided in); by default
+    the oracle's own scores rounded to float32.
+    Returns dict(scores, idx, h_kept, s_kept, outs={layer: out}).
+    """
+    s64 = gate_scores(h, w1, b1, w2, b2)
+    s32 = s64.astype(np.float32) if scores_f32 is None else np.asarray(scores_f32, np.float32)
+    idx = topk_select(s32, doc_begin, doc_end, k_doc)
+    h_kept = compact_rows(idx, h)
+    s_kept = compact_rows(idx, s32).astype(np.float64)
+    outs = {}
+    ids = range(len(layers)) if layer_ids is None else layer_ids
+    for li in ids:
+        q, k, v, gain, tau = layers[li]
+        outs[li] = gated_attention(compact_rows(idx, q), compact_rows(idx, k),
+                                   compact_rows(idx, v), s_kept, gain, tau, rows=rows)
+    return dict(scores=s64, idx=idx, h_kept=h_kept, s_kept=s_kept, outs=outs)
