@@ -1,0 +1,276 @@
+"""Gated-prefill benchmark on one MI355X.
+
+One step = one pass of the whole gated path over one synthetic prompt:
+    gate scores (all N rows) -> top-K over the document -> compaction of the
+    residual and scores -> token-gated attention in each of the 27 upper layers.
+The unpruned baseline (causal attention over all N rows in the same 27 layers)
+is timed beside it.  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line (rank 0).  Usage:
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def _parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="qwen3-1.7b-16k")
+    p.add_argument("--k-doc", type=int, default=None, help="override the document budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-full-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def attn_flops(m: int, hq: int, d: int) -> float:
+    """Algorithmic flops of causal attention over m rows: 4 d flops (q.k and
+    p.v) per visible (i >= j) pair per query head."""
+    return 2.0 * hq * d * m * (m + 1)
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is a design, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from learned_token_pruning_tg_amd import inputs, tg
+
+    w = inputs.WORKLOADS[args.workload]
+    if args.k_doc is not None:
+        w = w.with_budget(args.k_doc)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tg.lib()  # fail loudly before any work if the library is missing
+
+    def bf16_dev(x):
+        bits = inputs.bf16_bits(inputs.round_bf16(x))
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def f32_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+    # ---------------------------------------------------------------- inputs (untimed)
+    g = inputs.gate_inputs(w)
+    gain, tau = inputs.layer_params(w)
+    h = bf16_dev(g["h"])
+    w1, b1, w2 = bf16_dev(g["w1"]), f32_dev(g["b1"]), f32_dev(g["w2"])
+    gain_d = [f32_dev(gain[l]) for l in range(w.n_layers)]
+    tau_d = [f32_dev(tau[l]) for l in range(w.n_layers)]
+    n_t = min(w.n_templates, w.n_layers)
+    full_qkv = []
+    for t in range(n_t):
+        full_qkv.append(tuple(bf16_dev(x) for x in inputs.qkv_template(w, t)))
+    m = w.kept
+    scores = torch.empty(w.n, dtype=torch.float32, device=dev)
+    idx = torch.empty(m, dtype=torch.int32, device=dev)
+    h_kept = torch.empty((m, w.hidden), dtype=torch.bfloat16, device=dev)
+    s_kept = torch.empty(m, dtype=torch.float32, device=dev)
+    outs = [torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+            for _ in range(2)]
+    # The upper layers' q/k/v of the kept rows stand for what the layers'
+    # projections would produce from the kept residual; they are gathered
+    # once from the full-N templates with the selection of this very input.
+    tg.gate_score(h, w1, b1, w2, g["b2"], out=scores)
+    tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx)
+    kept_qkv = [tuple(tg.compact(idx, x) for x in full_qkv[t]) for t in range(n_t)]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    n_ev = 5
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tg.gate_score(h, w1, b1, w2, g["b2"], out=scores)
+        if ev is not None:
+            ev[1].record(stream)
+        tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx)
+        if ev is not None:
+            ev[2].record(stream)
+        tg.compact(idx, h, out=h_kept)
+        tg.compact(idx, scores, out=s_kept)
+        if ev is not None:
+            ev[3].record(stream)
+        for l in range(w.n_layers):
+            q, k, v = kept_qkv[inputs.template_of_layer(w, l)]
+            tg.gated_attn_fwd(q, k, v, s_kept, gain_d[l], tau_d[l], out=outs[l & 1])
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    stage = np.zeros(4)
+    for e in evs:
+        stage += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
+    stage /= args.steps
+    attn_ms_launch = stage[3] / w.n_layers
+
+    # ---------------------------------------------------------------- full-N baseline
+    full = None
+    if not args.no_full_baseline:
+        fout = torch.empty((w.n, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+
+        def full_step():
+            for l in range(w.n_layers):
+                q, k, v = full_qkv[inputs.template_of_layer(w, l)]
+                tg.full_attn_fwd(q, k, v, out=fout)
+
+        fsteps = max(1, min(args.steps, 5))
+        for _ in range(min(args.warmup, 1)):
+            full_step()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(fsteps):
+            full_step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        f_ms = a.elapsed_time(b) / fsteps
+        f_launch = f_ms / w.n_layers
+        f_fl = attn_flops(w.n, w.n_q_heads, w.head_dim)
+        full = {
+            "ms_per_step": round(f_ms, 4),
+            "tokens_per_s": round(w.n / (f_ms / 1e3), 1),
+            "attn_ms_per_layer": round(f_launch, 5),
+            "attn_tflops": round(f_fl / (f_launch / 1e3) / 1e12, 2),
+            "attn_frac_bf16_peak": round(f_fl / (f_launch / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "speedup_gated_vs_full": round(f_ms / ms_step, 2),
+            "steps": fsteps,
+        }
+        del fout
+
+    # ---------------------------------------------------------------- rooflines
+    fl = attn_flops(m, w.n_q_heads, w.head_dim)
+    achieved = fl / (attn_ms_launch / 1e3) / 1e12
+    gate_bytes = 2.0 * w.n * w.hidden + 2.0 * w.gate_hidden * w.hidden + 4.0 * w.n
+    gate_flops = 2.0 * w.n * w.hidden * w.gate_hidden
+    compact_bytes = 2.0 * m * (2 * w.hidden + 4)
+    stages = {
+        "gate": {"ms": round(stage[0], 5),
+                 "gb_s": round(gate_bytes / (stage[0] / 1e3) / 1e9, 1),
+                 "tflops": round(gate_flops / (stage[0] / 1e3) / 1e12, 1)},
+        "topk": {"ms": round(stage[1], 5)},
+        "compact": {"ms": round(stage[2], 5),
+                    "gb_s": round(compact_bytes / (stage[2] / 1e3) / 1e9, 1)},
+        "gated_attn": {"ms_total": round(stage[3], 4), "ms_per_layer": round(attn_ms_launch, 5),
+                       "tflops": round(achieved, 2)},
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, g, gain, tau, args.cpu_seconds)
+
+    line = {
+        "metric": "gated-prefill tokens/s + attn TFLOP/s (% bf16 MFMA peak) vs full-N prefill",
+        "value": round(w.n / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; planted-span document + question; random-init gate)",
+        "config": {"workload": w.name, "n_tokens": w.n, "n_doc": w.n_doc, "k_doc": w.k_doc,
+                   "kept_rows": m, "upper_layers": w.n_layers, "hidden": w.hidden,
+                   "gate_hidden": w.gate_hidden, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "parallelism": "single-gpu"},
+        "roofline": {"kernel": "tg_gated_attn_fwd", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "flops_per_launch": fl, "avg_launch_ms": round(attn_ms_launch, 5)},
+        "stages": stages,
+        "full_prefill_baseline": full,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, g, gain, tau, budget_s):
+    """The CPU oracle on a bounded sample of the same workload: the gate on all
+    N rows, the top-K, the compaction, and as many upper layers of gated
+    attention as fit the time budget; the per-step time is the measured stages
+    plus the mean measured layer time times the number of layers."""
+    from learned_token_pruning_tg_amd import inputs
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import tokengate as O
+
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()),
+                      default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    s64 = O.gate_scores(g["h"], g["w1"], g["b1"], g["w2"], g["b2"])
+    t1 = time.perf_counter()
+    s32 = s64.astype(np.float32)
+    idx = O.topk_select(s32, w.doc_begin, w.doc_end, w.k_doc)
+    t2 = time.perf_counter()
+    _ = O.compact_rows(idx, g["h"])
+    s_kept = O.compact_rows(idx, s32)
+    t3 = time.perf_counter()
+    q, k, v = inputs.qkv_template(w, 0)
+    qk, kk, vk = q[idx], k[idx], v[idx]
+    layer_t = []
+    while True:
+        a = time.perf_counter()
+        O.gated_attention(qk, kk, vk, s_kept, gain[len(layer_t)], tau[len(layer_t)])
+        layer_t.append(time.perf_counter() - a)
+        if (time.perf_counter() - t0) + np.mean(layer_t) > budget_s or len(layer_t) >= w.n_layers:
+            break
+    step_s = (t1 - t0) + (t2 - t1) + (t3 - t2) + w.n_layers * float(np.mean(layer_t))
+    return {
+        "value": round(w.n / step_s, 2),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"numpy float64 oracle on {w.name}: gate over all {w.n} rows "
+                   f"({t1 - t0:.2f} s), top-K ({t2 - t1:.3f} s), compaction ({t3 - t2:.3f} s), "
+                   f"{len(layer_t)} of {w.n_layers} gated-attention layers measured "
+                   f"(mean {np.mean(layer_t):.2f} s/layer, scaled to {w.n_layers})"),
+        "seconds_measured": round(time.perf_counter() - t0, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

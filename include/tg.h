@@ -1,0 +1,164 @@
+/*
+ * tg.h -- C ABI of the TokenGate gated-prefill kernels for MI355X (gfx950).
+ *
+ * The path these calls implement (coverage pages of the method, cited by
+ * title and section):
+ *   - lucasainews.com, Korean TokenGate article, section "작동 방식" (how it
+ *     works): below the gate layer every token is processed; at the gate
+ *     layer a small MLP scores each token from its post-attention residual and
+ *     a top-K selector keeps only the best-scoring ones; the layers above see
+ *     only the kept tokens and build no KV entries for the dropped ones; only
+ *     the document part of the prompt is pruned, the question stays whole.
+ *     The same section says the kept tokens' scores enter the attention
+ *     logits above the gate as a bias, with a learned gain and temperature per
+ *     head.  Section "사용법과 비용" (usage and cost): the document is marked
+ *     in the prompt and the caller passes a budget of kept prefill tokens.
+ *   - fugumt.com, "論文の概要: TokenGate: Adapting LLMs for Fast and
+ *     Memory-Efficient Prefill with Learned Token Pruning", English abstract:
+ *     token-gated attention re-weights attention logits with token
+ *     importance scores.
+ *
+ * Readings fixed here where the pages are silent:
+ *   - logit_ij = q_i.k_j / (sqrt(d) * tau_h) + gain_h * s_j (s_j raw score);
+ *   - selection compares float32 scores in a total order: -0.0 == +0.0,
+ *     NaN below -inf, ties to the lower index;
+ *   - kept rows stay in ascending original order and keep their original
+ *     rotary positions (applied to q/k by the caller).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless stated; the caller allocates and
+ *     frees them.  The library never allocates, never synchronises the stream
+ *     and keeps no global mutable state besides a thread-local error text.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; 0 = the
+ *     null stream).  Inputs must stay valid until the work completes.
+ *   - Arguments are validated on the host before any launch.  On a non-OK
+ *     return nothing was launched (except TG_E_HIP, reported by the launch
+ *     itself) and outputs are undefined; tg_last_error() gives the detail.
+ *   - bf16 tensors are passed as tg_bf16 (the raw 16-bit pattern).
+ *   - Row-major tensors must be 16-byte aligned where stated.
+ */
+#ifndef TG_H_
+#define TG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same underlying type as hipStream_t, so a hipStream_t can be passed as is. */
+typedef struct ihipStream_t* tg_stream_t;
+
+/* bfloat16 bit pattern. */
+typedef uint16_t tg_bf16;
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_E_INVALID = 1,     /* bad pointer, size, range or alignment            */
+  TG_E_UNSUPPORTED = 2, /* valid request outside the shapes the kernels take */
+  TG_E_WORKSPACE = 3,   /* reserved: no call takes a workspace at present    */
+  TG_E_HIP = 4          /* the HIP runtime reported an error at launch       */
+} tg_status;
+
+/* Static description of a status code. */
+const char* tg_status_str(tg_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* tg_last_error(void);
+
+/*
+ * Number of rows that survive selection: min(k_doc, N_doc) + (n - N_doc),
+ * N_doc = doc_end - doc_begin.  Host-only arithmetic (lucasainews.com
+ * article, "작동 방식": document tokens are pruned to the budget, the rest is
+ * kept).  Returns -1 if 0 <= doc_begin <= doc_end <= n and k_doc >= 0 do not
+ * hold.
+ */
+int64_t tg_kept_count(int64_t n, int64_t doc_begin, int64_t doc_end, int64_t k_doc);
+
+/*
+ * Gate MLP score of every row (lucasainews.com article, "작동 방식"; a small
+ * MLP scores each token from its post-attention residual):
+ *     scores[i] = sum_u w2[u] * GELU(sum_c w1[u, c] * h[i, c] + b1[u]) + b2
+ * with the exact (erf) GELU, bf16 products accumulated in fp32.
+ *   h        [n, hidden] bf16, row stride ld_h elements (ld_h >= hidden,
+ *            ld_h % 8 == 0, 16-byte aligned)
+ *   w1       [gate_hidden, hidden] bf16, contiguous, 16-byte aligned
+ *   b1, w2   [gate_hidden] fp32
+ *   scores   [n] fp32 (output)
+ * Supported: hidden % 32 == 0, gate_hidden % 32 == 0, gate_hidden <= 512.
+ * n == 0 is a no-op.  Deterministic: identical inputs give identical bits.
+ */
+tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidden,
+                        const tg_bf16* w1, const float* b1, const float* w2, float b2,
+                        int32_t gate_hidden, float* scores, tg_stream_t stream);
+
+/*
+ * Top-K selection over the document rows [doc_begin, doc_end) with every
+ * other row kept (lucasainews.com article, "작동 방식": only the document is
+ * pruned, the question stays; "사용법과 비용": the budget is a token count).
+ * Document rows are ranked by score (total order above, ties to the lower
+ * index) and the first min(k_doc, N_doc) are kept.
+ *   scores    [n] fp32
+ *   kept_idx  [tg_kept_count(n, doc_begin, doc_end, k_doc)] int32 (output),
+ *             strictly ascending original row indices (they double as the
+ *             rows' position ids)
+ * Exact: the result is unique and reproduced bit for bit.  n < 2^31.
+ */
+tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
+                         int64_t k_doc, int32_t* kept_idx, tg_stream_t stream);
+
+/*
+ * Row compaction (lucasainews.com article, "작동 방식": only kept rows go
+ * up; nothing is built for the dropped ones):
+ *     dst[i, :] = src[kept_idx[i], :]   for i < n_kept, bytewise
+ *   kept_idx  [n_kept] int32; entries outside [0, src_rows) are skipped (that
+ *             dst row is left unwritten)
+ *   src       src_rows rows of row_bytes, stride src_stride_bytes
+ *   dst       n_kept rows of row_bytes, stride dst_stride_bytes
+ * Strides must be >= row_bytes; src and dst must not overlap.  Rows whose
+ * bytes, strides and base pointers are multiples of 16 (else 4) move with
+ * 16-byte (else 4-byte, else 1-byte) accesses.
+ */
+tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, int64_t src_rows,
+                     int64_t src_stride_bytes, int64_t row_bytes, void* dst,
+                     int64_t dst_stride_bytes, tg_stream_t stream);
+
+/*
+ * Token-gated causal GQA attention over the n kept rows (lucasainews.com
+ * article, "작동 방식": each kept token's score is added to the attention
+ * logits above the gate, scaled by a per-head learned gain, with a per-head
+ * temperature; fugumt.com abstract: attention logits re-weighted by token
+ * importance scores):
+ *     logit_ij = q_i,h . k_j,g / (sqrt(head_dim) * tau[h]) + gain[h] * key_score[j]
+ *     out_i,h  = sum_{j <= i} softmax_j(logit_i,h) v_j,g,   g = h / (n_q_heads / n_kv_heads)
+ * Causality is by row order (kept rows are in original order).
+ *   q    [n, n_q_heads, head_dim] bf16, contiguous, 16-byte aligned
+ *   k, v [n, n_kv_heads, head_dim] bf16, contiguous, 16-byte aligned
+ *   key_score [n] fp32; gain, tau [n_q_heads] fp32 (tau > 0)
+ *   out  [n, n_q_heads, head_dim] bf16 (output, round-to-nearest-even)
+ *   lse  [n_q_heads, n] fp32 natural-log log-sum-exp of the logits
+ *        (output; may be NULL)
+ * Supported: head_dim in {64, 128}, n_q_heads % n_kv_heads == 0, n < 2^31.
+ * bf16 products, fp32 softmax and accumulation.  n == 0 is a no-op.
+ */
+tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            const float* key_score, const float* gain, const float* tau,
+                            tg_bf16* out, float* lse, tg_stream_t stream);
+
+/*
+ * Unpruned causal GQA attention over all n rows, softmax(q.k / sqrt(d)) v:
+ * the full prefill that the pages' speed-ups are measured against
+ * (lucasainews.com article, lede and "성능 결과").  Same layouts, limits and
+ * numerics as tg_gated_attn_fwd with gain = 0 and tau = 1.
+ */
+tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           tg_bf16* out, float* lse, tg_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_H_ */

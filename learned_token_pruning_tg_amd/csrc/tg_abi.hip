@@ -1,0 +1,145 @@
+// C ABI of libtg: host-side argument validation, error reporting and dispatch
+// to the HIP launchers.  Every check runs before any HIP call, so a rejected
+// call touches neither the device nor the stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/tg.h"
+#include "tg_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tg_status fail(tg_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tg_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TG_OK;
+  return fail(TG_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipStream_t as_hip(tg_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+tg_status check_attn(const char* fn, const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
+                     int64_t n, int32_t hq, int32_t hkv, int32_t d, const tg_bf16* out) {
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(TG_E_INVALID, "%s: n=%lld out of range", fn, (long long)n);
+  if (hq <= 0 || hkv <= 0) return fail(TG_E_INVALID, "%s: head counts must be positive", fn);
+  if (hq % hkv != 0)
+    return fail(TG_E_INVALID, "%s: n_q_heads=%d not a multiple of n_kv_heads=%d", fn, hq, hkv);
+  if (d != 64 && d != 128) return fail(TG_E_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", fn, d);
+  if (n == 0) return TG_OK;
+  if (!q || !k || !v || !out) return fail(TG_E_INVALID, "%s: null tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(TG_E_INVALID, "%s: q/k/v/out must be 16-byte aligned", fn);
+  return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_str(tg_status s) {
+  switch (s) {
+    case TG_OK: return "ok";
+    case TG_E_INVALID: return "invalid argument";
+    case TG_E_UNSUPPORTED: return "unsupported shape";
+    case TG_E_WORKSPACE: return "workspace too small";
+    case TG_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tg_last_error(void) { return g_err; }
+
+int64_t tg_kept_count(int64_t n, int64_t doc_begin, int64_t doc_end, int64_t k_doc) {
+  if (!(0 <= doc_begin && doc_begin <= doc_end && doc_end <= n) || k_doc < 0) return -1;
+  const int64_t n_doc = doc_end - doc_begin;
+  return (k_doc < n_doc ? k_doc : n_doc) + (n - n_doc);
+}
+
+tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidden,
+                        const tg_bf16* w1, const float* b1, const float* w2, float b2,
+                        int32_t gate_hidden, float* scores, tg_stream_t stream) {
+  if (n < 0) return fail(TG_E_INVALID, "tg_gate_score: n=%lld < 0", (long long)n);
+  if (hidden <= 0 || gate_hidden <= 0)
+    return fail(TG_E_INVALID, "tg_gate_score: hidden=%d gate_hidden=%d must be positive", hidden,
+                gate_hidden);
+  if (ld_h < hidden) return fail(TG_E_INVALID, "tg_gate_score: ld_h=%lld < hidden=%d", (long long)ld_h, hidden);
+  if (hidden % 32 != 0 || gate_hidden % 32 != 0 || gate_hidden > 512)
+    return fail(TG_E_UNSUPPORTED,
+                "tg_gate_score: hidden=%d gate_hidden=%d (need multiples of 32, gate_hidden <= 512)",
+                hidden, gate_hidden);
+  if (ld_h % 8 != 0) return fail(TG_E_INVALID, "tg_gate_score: ld_h=%lld not a multiple of 8", (long long)ld_h);
+  if (n == 0) return TG_OK;
+  if (!h || !w1 || !b1 || !w2 || !scores) return fail(TG_E_INVALID, "tg_gate_score: null pointer");
+  if (!aligned16(h) || !aligned16(w1)) return fail(TG_E_INVALID, "tg_gate_score: h/w1 must be 16-byte aligned");
+  return hip_status(tg::launch_gate_score(h, n, ld_h, hidden, w1, b1, w2, b2, gate_hidden, scores,
+                                          as_hip(stream)),
+                    "tg_gate_score launch");
+}
+
+tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
+                         int64_t k_doc, int32_t* kept_idx, tg_stream_t stream) {
+  if (n < 0 || n >= (int64_t(1) << 31))
+    return fail(TG_E_INVALID, "tg_topk_select: n=%lld out of range", (long long)n);
+  if (tg_kept_count(n, doc_begin, doc_end, k_doc) < 0)
+    return fail(TG_E_INVALID, "tg_topk_select: need 0 <= doc_begin=%lld <= doc_end=%lld <= n=%lld, k_doc=%lld >= 0",
+                (long long)doc_begin, (long long)doc_end, (long long)n, (long long)k_doc);
+  if (n == 0) return TG_OK;
+  if (!scores || !kept_idx) return fail(TG_E_INVALID, "tg_topk_select: null pointer");
+  return hip_status(tg::launch_topk_select(scores, n, doc_begin, doc_end, k_doc, kept_idx, as_hip(stream)),
+                    "tg_topk_select launch");
+}
+
+tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, int64_t src_rows,
+                     int64_t src_stride_bytes, int64_t row_bytes, void* dst,
+                     int64_t dst_stride_bytes, tg_stream_t stream) {
+  if (n_kept < 0 || src_rows < 0 || row_bytes < 0)
+    return fail(TG_E_INVALID, "tg_compact: negative size");
+  if (src_stride_bytes < row_bytes || dst_stride_bytes < row_bytes)
+    return fail(TG_E_INVALID, "tg_compact: strides (%lld, %lld) smaller than row_bytes=%lld",
+                (long long)src_stride_bytes, (long long)dst_stride_bytes, (long long)row_bytes);
+  if (n_kept == 0 || row_bytes == 0) return TG_OK;
+  if (!kept_idx || !src || !dst) return fail(TG_E_INVALID, "tg_compact: null pointer");
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  const char* s1 = s0 + (src_rows > 0 ? (src_rows - 1) * src_stride_bytes + row_bytes : 0);
+  const char* d1 = d0 + (n_kept - 1) * dst_stride_bytes + row_bytes;
+  if (s0 < d1 && d0 < s1) return fail(TG_E_INVALID, "tg_compact: src and dst overlap");
+  return hip_status(tg::launch_compact(kept_idx, n_kept, src, src_rows, src_stride_bytes, row_bytes,
+                                       dst, dst_stride_bytes, as_hip(stream)),
+                    "tg_compact launch");
+}
+
+tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            const float* key_score, const float* gain, const float* tau,
+                            tg_bf16* out, float* lse, tg_stream_t stream) {
+  const tg_status st = check_attn("tg_gated_attn_fwd", q, k, v, n, n_q_heads, n_kv_heads, head_dim, out);
+  if (st != TG_OK || n == 0) return st;
+  if (!key_score || !gain || !tau)
+    return fail(TG_E_INVALID, "tg_gated_attn_fwd: null key_score/gain/tau");
+  return hip_status(tg::launch_attn_fwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, key_score,
+                                        gain, tau, out, lse, as_hip(stream)),
+                    "tg_gated_attn_fwd launch");
+}
+
+tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           tg_bf16* out, float* lse, tg_stream_t stream) {
+  const tg_status st = check_attn("tg_full_attn_fwd", q, k, v, n, n_q_heads, n_kv_heads, head_dim, out);
+  if (st != TG_OK || n == 0) return st;
+  return hip_status(tg::launch_attn_fwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, nullptr,
+                                        nullptr, nullptr, out, lse, as_hip(stream)),
+                    "tg_full_attn_fwd launch");
+}
+
+}  // extern "C"

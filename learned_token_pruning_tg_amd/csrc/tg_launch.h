@@ -1,0 +1,27 @@
+// Internal launchers (host side).  Arguments arrive here already validated by
+// the C ABI layer; each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+hipError_t launch_gate_score(const uint16_t* h, int64_t n, int64_t ld_h, int hidden,
+                             const uint16_t* w1, const float* b1, const float* w2, float b2,
+                             int gate_hidden, float* scores, hipStream_t stream);
+
+hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
+                              int64_t k_doc, int32_t* kept_idx, hipStream_t stream);
+
+hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, const void* src,
+                          int64_t src_rows, int64_t src_stride, int64_t row_bytes, void* dst,
+                          int64_t dst_stride, hipStream_t stream);
+
+// gain == nullptr selects the unbiased (full-prefill) kernel with tau = 1.
+hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
+                           int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
+                           const float* gain, const float* tau, uint16_t* out, float* lse,
+                           hipStream_t stream);
+
+}  // namespace tg

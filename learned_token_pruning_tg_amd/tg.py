@@ -1,0 +1,212 @@
+"""Thin Python binding of libtg (the C ABI declared in include/tg.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (torch is used for device
+memory and the current stream); outputs are allocated with torch when not
+given.  A missing library raises at first use -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtg.so")
+_lib = None
+
+TG_OK = 0
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+_SIGNATURES = {
+    "tg_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "tg_last_error": (ctypes.c_char_p, []),
+    "tg_kept_count": (_I64, [_I64, _I64, _I64, _I64]),
+    "tg_gate_score": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, ctypes.c_float, _I32, _P, _P]),
+    "tg_topk_select": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
+    "tg_compact": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+}
+
+
+class TGError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_str(status)} ({status}): {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtg.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m learned_token_pruning_tg_amd.build`")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def status_str(status: int) -> str:
+    return lib().tg_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().tg_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != TG_OK:
+        raise TGError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, contiguous: bool = True) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+
+def kept_count(n: int, doc_begin: int, doc_end: int, k_doc: int) -> int:
+    m = lib().tg_kept_count(n, doc_begin, doc_end, k_doc)
+    if m < 0:
+        raise ValueError(f"invalid segment/budget: n={n} doc=[{doc_begin},{doc_end}) k={k_doc}")
+    return m
+
+
+def gate_score(h: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """scores[i] = w2 . GELU(W1 h[i] + b1) + b2.  h [n, H] bf16 (row stride may
+    exceed H), w1 [Hg, H] bf16, b1/w2 [Hg] fp32 -> [n] fp32."""
+    _need(h, "h", torch.bfloat16, contiguous=False)
+    if h.dim() != 2 or h.stride(1) != 1:
+        raise ValueError("h must be [n, H] with unit column stride")
+    _need(w1, "w1", torch.bfloat16); _need(b1, "b1", torch.float32); _need(w2, "w2", torch.float32)
+    n, hidden = h.shape
+    hg = w1.shape[0]
+    if w1.shape != (hg, hidden) or b1.shape != (hg,) or w2.shape != (hg,):
+        raise ValueError("gate weight shapes do not match h")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=h.device)
+    _need(out, "out", torch.float32)
+    _check(lib().tg_gate_score(_ptr(h), n, h.stride(0), hidden, _ptr(w1), _ptr(b1), _ptr(w2),
+                               float(b2), hg, _ptr(out), _stream(stream)))
+    return out
+
+
+def topk_select(scores: torch.Tensor, doc_begin: int, doc_end: int, k_doc: int,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Kept row indices (ascending int32) of a top-K over the document rows
+    [doc_begin, doc_end) with every other row kept."""
+    _need(scores, "scores", torch.float32)
+    n = scores.numel()
+    m = kept_count(n, doc_begin, doc_end, k_doc)
+    if out is None:
+        out = torch.empty(m, dtype=torch.int32, device=scores.device)
+    _need(out, "out", torch.int32)
+    if out.numel() < m:
+        raise ValueError(f"out holds {out.numel()} < {m} indices")
+    _check(lib().tg_topk_select(_ptr(scores), n, doc_begin, doc_end, k_doc, _ptr(out),
+                                _stream(stream)))
+    return out
+
+
+def compact(idx: torch.Tensor, src: torch.Tensor, out: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """out[i] = src[idx[i]] over the leading dimension (rows of any dtype)."""
+    _need(idx, "idx", torch.int32)
+    if not src.is_cuda:
+        raise ValueError("src must be a GPU tensor")
+    rows = src.shape[0]
+    row_shape = tuple(src.shape[1:])
+    row_elems = 1
+    for s in row_shape:
+        row_elems *= s
+    es = src.element_size()
+    if src.dim() > 1 and not src[0].is_contiguous():
+        raise ValueError("src rows must be contiguous")
+    n_kept = idx.numel()
+    if out is None:
+        out = torch.empty((n_kept,) + row_shape, dtype=src.dtype, device=src.device)
+    if out.dtype != src.dtype or tuple(out.shape[1:]) != row_shape or out.shape[0] < n_kept:
+        raise ValueError("out does not match src rows")
+    src_stride = src.stride(0) * es if src.dim() > 0 and rows > 0 else row_elems * es
+    dst_stride = out.stride(0) * es if n_kept > 0 else row_elems * es
+    _check(lib().tg_compact(_ptr(idx), n_kept, _ptr(src), rows, src_stride, row_elems * es,
+                            _ptr(out), dst_stride, _stream(stream)))
+    return out
+
+
+def _attn_out(q, out, lse, want_lse):
+    n, hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16)
+    if want_lse and lse is None:
+        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    return out, lse
+
+
+def gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
+                   gain: torch.Tensor, tau: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None):
+    """Token-gated causal GQA attention over the kept rows.
+    q [M, Hq, d], k/v [M, Hkv, d] bf16; key_score [M], gain/tau [Hq] fp32.
+    Returns out (and lse [Hq, M] if requested or given)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    _need(key_score, "key_score", torch.float32); _need(gain, "gain", torch.float32)
+    _need(tau, "tau", torch.float32)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (n, hkv, d) or v.shape != k.shape or key_score.shape != (n,) \
+            or gain.shape != (hq,) or tau.shape != (hq,):
+        raise ValueError("attention operand shapes do not match")
+    out, lse = _attn_out(q, out, lse, want_lse)
+    _check(lib().tg_gated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(key_score),
+                                   _ptr(gain), _ptr(tau), _ptr(out), _ptr(lse), _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def full_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  want_lse: bool = False, stream=None):
+    """Unpruned causal GQA attention softmax(q.k / sqrt(d)) v over all rows."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (n, hkv, d) or v.shape != k.shape:
+        raise ValueError("attention operand shapes do not match")
+    out, lse = _attn_out(q, out, lse, want_lse)
+    _check(lib().tg_full_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(out), _ptr(lse),
+                                  _stream(stream)))
+    return (out, lse) if lse is not None else out

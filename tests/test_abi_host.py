@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every entry point that include/tg.h declares, and
+rejects invalid arguments on the host before any HIP call.  No call here
+reaches a kernel launch.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from learned_token_pruning_tg_amd import tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tg.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+A = 4096  # a fake, 16-byte-aligned "device" address: never dereferenced by these calls
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tg.lib_path()):
+        pytest.skip("libtg.so not built")
+    return tg.lib()
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for fn in ("tg_gate_score", "tg_topk_select", "tg_compact", "tg_gated_attn_fwd",
+               "tg_full_attn_fwd", "tg_kept_count", "tg_status_str", "tg_last_error"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", tg.lib_path()], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (tg_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_status_strings(L):
+    assert tg.status_str(OK) == "ok"
+    assert "invalid" in tg.status_str(INVALID)
+    assert "unsupported" in tg.status_str(UNSUPPORTED)
+    assert tg.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((512, 0, 448, 128), 192), ((512, 0, 448, 0), 64), ((512, 0, 448, 10**6), 512),
+    ((16384, 0, 16128, 2048), 2304), ((131072, 0, 130816, 8192), 8448),
+    ((10, 3, 3, 5), 10), ((10, 2, 8, 4), 8), ((0, 0, 0, 0), 0),
+    ((10, 5, 4, 1), -1), ((10, 0, 11, 1), -1), ((10, -1, 5, 1), -1), ((10, 0, 5, -1), -1),
+])
+def test_kept_count(L, args, expect):
+    assert L.tg_kept_count(*args) == expect
+
+
+def test_gate_validation(L):
+    s = 0
+    f = L.tg_gate_score
+    assert f(A, -1, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID
+    assert f(A, 10, 200, 256, A, A, A, 0.0, 64, A, s) == INVALID         # ld_h < hidden
+    assert f(A, 10, 260, 256, A, A, A, 0.0, 64, A, s) == INVALID         # ld_h % 8
+    assert f(A, 10, 256, 250, A, A, A, 0.0, 64, A, s) == UNSUPPORTED     # hidden % 32
+    assert f(A, 10, 256, 256, A, A, A, 0.0, 544, A, s) == UNSUPPORTED    # gate_hidden > 512
+    assert f(A, 10, 256, 256, A, A, A, 0.0, 48, A, s) == UNSUPPORTED     # gate_hidden % 32
+    assert f(None, 10, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID
+    assert f(A + 2, 10, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID     # alignment
+    assert "aligned" in tg.last_error()
+    assert f(None, 0, 256, 256, None, None, None, 0.0, 64, None, s) == OK  # n == 0: no-op
+
+
+def test_topk_validation(L):
+    f = L.tg_topk_select
+    assert f(A, 10, 0, 11, 3, A, 0) == INVALID
+    assert f(A, 10, 6, 5, 3, A, 0) == INVALID
+    assert f(A, 10, 0, 5, -1, A, 0) == INVALID
+    assert f(None, 10, 0, 5, 3, A, 0) == INVALID
+    assert f(A, 1 << 31, 0, 5, 3, A, 0) == INVALID
+    assert f(None, 0, 0, 0, 3, None, 0) == OK
+
+
+def test_compact_validation(L):
+    f = L.tg_compact
+    assert f(A, -1, A, 10, 16, 16, A * 4, 16, 0) == INVALID
+    assert f(A, 4, A, 10, 8, 16, A * 4, 16, 0) == INVALID               # src stride < row
+    assert f(A, 4, A, 10, 16, 16, A + 64, 16, 0) == INVALID             # overlap
+    assert "overlap" in tg.last_error()
+    assert f(None, 4, A, 10, 16, 16, A * 4, 16, 0) == INVALID
+    assert f(None, 0, None, 0, 16, 16, None, 16, 0) == OK
+
+
+def test_attention_validation(L):
+    g = L.tg_gated_attn_fwd
+    full = L.tg_full_attn_fwd
+    assert g(A, A, A, 10, 16, 8, 96, A, A, A, A, None, 0) == UNSUPPORTED
+    assert "head_dim" in tg.last_error()
+    assert g(A, A, A, 10, 16, 6, 128, A, A, A, A, None, 0) == INVALID
+    assert g(A, A, A, 10, 0, 8, 128, A, A, A, A, None, 0) == INVALID
+    assert g(A, A, A, -3, 16, 8, 128, A, A, A, A, None, 0) == INVALID
+    assert g(A, A, A, 10, 16, 8, 128, None, A, A, A, None, 0) == INVALID  # key_score
+    assert g(A + 8, A, A, 10, 16, 8, 128, A, A, A, A, None, 0) == INVALID
+    assert full(A, A, None, 10, 16, 8, 128, A, None, 0) == INVALID
+    assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, 0) == UNSUPPORTED
+    assert g(None, None, None, 0, 16, 8, 128, None, None, None, None, None, 0) == OK
+    assert full(None, None, None, 0, 16, 8, 128, None, None, 0) == OK
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(tg, "_lib", None)
+    monkeypatch.setattr(tg, "_LIB_PATH", "/nonexistent/libtg.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        tg.lib()
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "learned_token_pruning_tg_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), fn
+                assert "oracle/" not in text, fn

@@ -1,0 +1,316 @@
+"""GPU parity: every HIP entry point against the CPU oracle, through the C ABI.
+
+Bars: top-K indices and compacted bytes bit-exact (top-K is fed the GPU's own
+float32 scores, so both sides decide on identical values); scores within 1e-3
+relative; attention outputs within max-abs 1e-2 and relative-L2 5e-3 of the
+float64 oracle.  The fp32 tiny workload runs on bf16-rounded copies, and the
+oracle is given the same rounded values.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from learned_token_pruning_tg_amd import inputs, tg
+from oracle import tokengate as O
+
+from gpu_util import (check_attn, check_scores, dev_bf16, dev_f32, host_bf16, say)
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+
+
+def _sample_rows(m, rng, extra=(), n_random=40):
+    base = {0, 1, 2, m // 2, m - 2, m - 1, 63, 64, 127, 128, 129, 255, 256}
+    base |= set(int(x) for x in extra)
+    base |= set(int(x) for x in rng.integers(0, m, size=n_random))
+    return np.array(sorted(r for r in base if 0 <= r < m), dtype=np.int64)
+
+
+# --------------------------------------------------------------------------- gate
+
+@pytest.mark.parametrize("random_bias", [False, True])
+def test_gate_tiny(random_bias):
+    w = W["tiny"]
+    g = inputs.gate_inputs(w, random_bias=random_bias)
+    h = inputs.round_bf16(g["h"]); w1 = inputs.round_bf16(g["w1"])
+    say(f"gate tiny random_bias={random_bias}")
+    s = tg.gate_score(dev_bf16(h), dev_bf16(w1), dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
+    torch.cuda.synchronize()
+    check_scores(s.cpu().numpy(), O.gate_scores(h, w1, g["b1"], g["w2"], g["b2"]), "gate tiny")
+
+
+@pytest.mark.parametrize("n,hidden,hg,ld", [(1000, 256, 96, 264), (1, 64, 32, 64),
+                                           (130, 512, 512, 520), (64, 128, 64, 128)])
+def test_gate_ragged_strided(n, hidden, hg, ld):
+    rng = np.random.default_rng(n + hg)
+    base = inputs.round_bf16(rng.standard_normal((n, ld)).astype(np.float32))
+    w1 = inputs.round_bf16((rng.standard_normal((hg, hidden)) * 0.08).astype(np.float32))
+    b1 = (rng.standard_normal(hg) * 0.5).astype(np.float32)
+    w2 = rng.standard_normal(hg).astype(np.float32)
+    say(f"gate ragged n={n} hidden={hidden} hg={hg} ld={ld}")
+    hd = dev_bf16(base)[:, :hidden]
+    s = tg.gate_score(hd, dev_bf16(w1), dev_f32(b1), dev_f32(w2), -0.25)
+    torch.cuda.synchronize()
+    check_scores(s.cpu().numpy(), O.gate_scores(base[:, :hidden], w1, b1, w2, -0.25), "gate ragged")
+
+
+@pytest.mark.parametrize("n", [16384, 65536 + 37])
+def test_gate_qwen_shapes_and_determinism(n):
+    w = W["qwen3-1.7b-16k"]
+    wk = w.with_n(n, n - 256, 2048)
+    g = inputs.gate_inputs(wk, random_bias=True)
+    say(f"gate qwen n={n}")
+    hd = dev_bf16(g["h"]); w1d = dev_bf16(g["w1"])
+    s1 = tg.gate_score(hd, w1d, dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
+    s2 = tg.gate_score(hd, w1d, dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
+    torch.cuda.synchronize()
+    a, b = s1.cpu().numpy(), s2.cpu().numpy()
+    assert a.tobytes() == b.tobytes()                     # deterministic
+    rows = _sample_rows(n, np.random.default_rng(n), n_random=2000)
+    ref = O.gate_scores(g["h"][rows], g["w1"], g["b1"], g["w2"], g["b2"])
+    check_scores(a[rows], ref, f"gate qwen n={n}")
+
+
+# --------------------------------------------------------------------------- top-K
+
+def _topk_gpu(s32, db, de, k):
+    say(f"topk n={s32.size} doc=[{db},{de}) k={k}")
+    out = tg.topk_select(dev_f32(s32), db, de, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_topk_tiny_on_gpu_scores():
+    w = W["tiny"]
+    g = inputs.gate_inputs(w)
+    s = tg.gate_score(dev_bf16(g["h"]), dev_bf16(g["w1"]), dev_f32(g["b1"]), dev_f32(g["w2"]),
+                      g["b2"])
+    s32 = s.cpu().numpy()
+    for k in (0, 1, 17, 128, 447, 448, 1000):
+        assert np.array_equal(_topk_gpu(s32, 0, w.n_doc, k), O.topk_select(s32, 0, w.n_doc, k))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_topk_special_values_and_ties(seed):
+    rng = np.random.default_rng(seed)
+    pool = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, 1e-45, -1e-45, 0.5, -2.0, 3.0],
+                    dtype=np.float32)
+    s32 = rng.choice(pool, size=5000).astype(np.float32)
+    for db, de in ((100, 4900), (0, 5000), (2500, 2500), (0, 1)):
+        for k in (0, 1, 2, 999, 1000, de - db - 1, de - db, 6000):
+            if k < 0:
+                continue
+            assert np.array_equal(_topk_gpu(s32, db, de, k), O.topk_select(s32, db, de, k)), \
+                (seed, db, de, k)
+
+
+@pytest.mark.parametrize("n,db,de,k", [(131072, 0, 130816, 8192), (131072, 1000, 130000, 8192),
+                                       (65536, 0, 65280, 1024), (65536, 0, 65280, 16384),
+                                       (16384, 0, 16128, 2048), (70001, 3, 69999, 33333)])
+def test_topk_large_quantised(n, db, de, k):
+    rng = np.random.default_rng(n + k)
+    s32 = (np.round(rng.standard_normal(n) * 64) / 64).astype(np.float32)   # many exact ties
+    a = _topk_gpu(s32, db, de, k)
+    assert np.array_equal(a, O.topk_select(s32, db, de, k))
+    assert np.array_equal(a, _topk_gpu(s32, db, de, k))                     # deterministic
+
+
+def test_topk_all_equal():
+    s32 = np.full(9000, 1.25, dtype=np.float32)
+    assert np.array_equal(_topk_gpu(s32, 10, 8990, 4000), O.topk_select(s32, 10, 8990, 4000))
+
+
+# --------------------------------------------------------------------------- compaction
+
+@pytest.mark.parametrize("row_shape,dtype", [((2048,), torch.bfloat16), ((), torch.float32),
+                                             ((3,), torch.int16), ((3,), torch.float32),
+                                             ((8, 128), torch.bfloat16), ((5,), torch.uint8)])
+def test_compact_bytewise(row_shape, dtype):
+    rng = np.random.default_rng(len(row_shape))
+    rows = 3000
+    src = torch.from_numpy(rng.integers(0, 255, size=(rows,) + row_shape).astype(np.uint8))
+    if dtype != torch.uint8:
+        nbytes = int(np.prod(row_shape or (1,))) * torch.empty((), dtype=dtype).element_size()
+        raw = rng.integers(0, 256, size=(rows, nbytes), dtype=np.uint8)
+        src = torch.from_numpy(raw).view(dtype).reshape((rows,) + row_shape)
+    idx = np.sort(rng.choice(rows, size=777, replace=False)).astype(np.int32)
+    say(f"compact row_shape={row_shape} dtype={dtype}")
+    out = tg.compact(torch.from_numpy(idx).cuda(), src.cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().contiguous().view(torch.uint8).numpy().reshape(777, -1)
+    ref = src[torch.from_numpy(idx).long()].contiguous().view(torch.uint8).numpy().reshape(777, -1)
+    assert got.tobytes() == ref.tobytes()
+
+
+def test_compact_strided_and_out_of_range_indices():
+    rng = np.random.default_rng(9)
+    big = torch.from_numpy(rng.standard_normal((500, 40)).astype(np.float32)).cuda()
+    src = big[:, 4:36]                       # row stride 160 B, rows of 128 B
+    assert not src.is_contiguous() and src[0].is_contiguous()
+    idx = torch.tensor([5, -1, 499, 500, 0, 7], dtype=torch.int32).cuda()
+    out = torch.full((6, 32), -7.0, device="cuda")
+    say("compact strided + invalid idx")
+    tg.compact(idx, src, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy(); s = src.cpu().numpy()
+    for r, i in enumerate([5, -1, 499, 500, 0, 7]):
+        if 0 <= i < 500:
+            assert np.array_equal(o[r], s[i])
+        else:
+            assert np.all(o[r] == -7.0)      # skipped row left unwritten
+
+
+# --------------------------------------------------------------------------- attention
+
+def _rand_attn(rng, m, hq, hkv, d):
+    q = inputs.round_bf16(np.clip(rng.standard_normal((m, hq, d)), -3.5, 3.5).astype(np.float32))
+    k = inputs.round_bf16(np.clip(rng.standard_normal((m, hkv, d)), -3.5, 3.5).astype(np.float32))
+    v = inputs.round_bf16(np.clip(rng.standard_normal((m, hkv, d)), -3.5, 3.5).astype(np.float32))
+    s = (rng.standard_normal(m) * 1.5).astype(np.float32)
+    gain = rng.uniform(0.5, 1.5, hq).astype(np.float32)
+    tau = rng.uniform(0.8, 1.2, hq).astype(np.float32)
+    return q, k, v, s, gain, tau
+
+
+@pytest.mark.parametrize("m,hq,hkv,d", [(1, 4, 2, 64), (2, 4, 2, 128), (63, 4, 2, 64),
+                                        (64, 4, 4, 128), (65, 8, 1, 128), (127, 4, 2, 64),
+                                        (129, 16, 8, 128), (200, 4, 2, 64), (515, 16, 8, 128),
+                                        (1000, 2, 1, 128)])
+def test_gated_attention_ragged(m, hq, hkv, d):
+    rng = np.random.default_rng(m * 7 + d)
+    q, k, v, s, gain, tau = _rand_attn(rng, m, hq, hkv, d)
+    say(f"gated attn m={m} hq={hq} hkv={hkv} d={d}")
+    out, lse = tg.gated_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s), dev_f32(gain),
+                                 dev_f32(tau), want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.gated_attention(q, k, v, s, gain, tau, return_lse=True)
+    check_attn(host_bf16(out), ref, f"gated m={m} d={d}")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) < 2e-3
+    # first row sees only key 0: output is v_0 of its KV group, exactly
+    g = hq // hkv
+    got0 = host_bf16(out)[0]
+    for h in range(hq):
+        assert np.array_equal(got0[h], v[0, h // g])
+
+
+@pytest.mark.parametrize("m,d", [(300, 128), (777, 64)])
+def test_no_gain_unit_temperature_equals_full(m, d):
+    rng = np.random.default_rng(m)
+    q, k, v, s, _, _ = _rand_attn(rng, m, 4, 2, d)
+    say(f"gated(g=0,tau=1) vs full m={m} d={d}")
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    a = tg.gated_attn_fwd(qd, kd, vd, dev_f32(s), dev_f32(np.zeros(4)), dev_f32(np.ones(4)))
+    b, lse = tg.full_attn_fwd(qd, kd, vd, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref, ref_lse = O.full_attention(q, k, v, return_lse=True)
+    check_attn(host_bf16(b), ref, "full")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) < 2e-3
+
+
+def test_tiny_workload_chain_all_layers():
+    w = W["tiny"]
+    g = inputs.gate_inputs(w, random_bias=True)
+    h = inputs.round_bf16(g["h"]); w1 = inputs.round_bf16(g["w1"])
+    gain, tau = inputs.layer_params(w)
+    say("tiny chain")
+    hd = dev_bf16(h)
+    s_d = tg.gate_score(hd, dev_bf16(w1), dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
+    idx_d = tg.topk_select(s_d, w.doc_begin, w.doc_end, w.k_doc)
+    h_kept = tg.compact(idx_d, hd)
+    s_kept = tg.compact(idx_d, s_d)
+    torch.cuda.synchronize()
+    s32 = s_d.cpu().numpy(); idx = idx_d.cpu().numpy()
+    check_scores(s32, O.gate_scores(h, w1, g["b1"], g["w2"], g["b2"]), "tiny scores")
+    assert np.array_equal(idx, O.topk_select(s32, w.doc_begin, w.doc_end, w.k_doc))
+    assert np.array_equal(host_bf16(h_kept), h[idx])
+    assert np.array_equal(s_kept.cpu().numpy(), s32[idx])
+    for li in range(w.n_layers):
+        q, k, v = (inputs.round_bf16(x) for x in inputs.qkv_template(w, inputs.template_of_layer(w, li)))
+        qk, kk, vk = (tg.compact(idx_d, dev_bf16(x)) for x in (q, k, v))
+        out = tg.gated_attn_fwd(qk, kk, vk, s_kept, dev_f32(gain[li]), dev_f32(tau[li]))
+        torch.cuda.synchronize()
+        ref = O.gated_attention(q[idx], k[idx], v[idx], s32[idx], gain[li], tau[li])
+        check_attn(host_bf16(out), ref, f"tiny layer {li}")
+
+
+# --------------------------------------------------------------------------- full-size chains
+
+def _chain(w, layers, n_rows=48, full_rows=32):
+    """Gate -> top-K -> compaction -> gated attention at full size, checked on
+    sampled rows (gate, attention) and in full (indices, compacted bytes)."""
+    rng = np.random.default_rng(w.seed)
+    g = inputs.gate_inputs(w)
+    gain, tau = inputs.layer_params(w)
+    say(f"chain {w.name}: gate/top-K/compact")
+    hd = dev_bf16(g["h"])
+    s_d = tg.gate_score(hd, dev_bf16(g["w1"]), dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
+    idx_d = tg.topk_select(s_d, w.doc_begin, w.doc_end, w.k_doc)
+    h_kept = tg.compact(idx_d, hd)
+    s_kept = tg.compact(idx_d, s_d)
+    torch.cuda.synchronize()
+    s32 = s_d.cpu().numpy(); idx = idx_d.cpu().numpy()
+    rows = _sample_rows(w.n, rng, n_random=1000)
+    check_scores(s32[rows], O.gate_scores(g["h"][rows], g["w1"], g["b1"], g["w2"], g["b2"]),
+                 f"{w.name} scores")
+    assert idx.size == w.kept
+    assert np.array_equal(idx, O.topk_select(s32, w.doc_begin, w.doc_end, w.k_doc))
+    assert host_bf16(h_kept).tobytes() == g["h"][idx].tobytes()
+    assert np.array_equal(s_kept.cpu().numpy(), s32[idx])
+    del hd, h_kept
+    kept_doc = min(w.k_doc, w.n_doc)
+    for li in layers:
+        t = inputs.template_of_layer(w, li)
+        q, k, v = inputs.qkv_template(w, t)
+        qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+        say(f"chain {w.name}: gated attention layer {li} (M={w.kept})")
+        qk, kk, vk = (tg.compact(idx_d, x) for x in (qd, kd, vd))
+        out, lse = tg.gated_attn_fwd(qk, kk, vk, s_kept, dev_f32(gain[li]), dev_f32(tau[li]),
+                                     want_lse=True)
+        torch.cuda.synchronize()
+        r = _sample_rows(w.kept, rng, extra=(kept_doc - 1, kept_doc, kept_doc + 1), n_random=n_rows)
+        ref, ref_lse = O.gated_attention(q[idx], k[idx], v[idx], s32[idx], gain[li], tau[li],
+                                         rows=r, return_lse=True)
+        check_attn(host_bf16(out)[r], ref, f"{w.name} layer {li}")
+        assert np.max(np.abs(lse.cpu().numpy()[:, r] - ref_lse)) < 2e-3
+        if li == layers[0] and full_rows:
+            say(f"chain {w.name}: full attention (N={w.n})")
+            fo = tg.full_attn_fwd(qd, kd, vd)
+            torch.cuda.synchronize()
+            fr = _sample_rows(w.n, rng, extra=(w.n_doc - 1, w.n_doc), n_random=full_rows)
+            check_attn(host_bf16(fo)[fr], O.full_attention(q, k, v, rows=fr), f"{w.name} full")
+            del fo
+        del qd, kd, vd, qk, kk, vk, out
+
+
+def test_chain_qwen_16k():
+    _chain(W["qwen3-1.7b-16k"], layers=[0, 26])
+
+
+def test_chain_qwen_32k():
+    _chain(W["qwen3-1.7b-32k"], layers=[1])
+
+
+def test_chain_qwen_128k():
+    _chain(W["qwen3-1.7b-128k"], layers=[2], n_rows=32, full_rows=16)
+
+
+@pytest.mark.parametrize("k_doc", inputs.SWEEP_BUDGETS)
+def test_chain_qwen_64k_budget_sweep(k_doc):
+    w = W["qwen3-1.7b-64k-sweep"].with_budget(k_doc)
+    _chain(w, layers=[0], n_rows=24, full_rows=0)
+
+
+def test_budget_n_with_no_gain_is_full_prefill_64k():
+    """K = N, gain 0, temperature 1: the gated path is the plain full prefill."""
+    w = W["qwen3-1.7b-64k-sweep"]
+    q, k, v = inputs.qkv_template(w, 0)
+    say("64k K=N equivalence")
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    s = dev_f32(np.random.default_rng(3).standard_normal(w.n))
+    a = tg.gated_attn_fwd(qd, kd, vd, s, dev_f32(np.zeros(16)), dev_f32(np.ones(16)))
+    b = tg.full_attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
