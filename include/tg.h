@@ -86,7 +86,7 @@ int64_t tg_kept_count(int64_t n, int64_t doc_begin, int64_t doc_end, int64_t k_d
  *   w1       [gate_hidden, hidden] bf16, contiguous, 16-byte aligned
  *   b1, w2   [gate_hidden] fp32
  *   scores   [n] fp32 (output)
- * Supported: hidden % 32 == 0, gate_hidden % 32 == 0, gate_hidden <= 512.
+ * Supported: hidden % 32 == 0, gate_hidden <= 512.
  * n == 0 is a no-op.  Deterministic: identical inputs give identical bits.
  */
 tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidden,
@@ -102,7 +102,7 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
  *   scores    [n] fp32
  *   kept_idx  [tg_kept_count(n, doc_begin, doc_end, k_doc)] int32 (output),
  *             strictly ascending original row indices (they double as the
- *             rows' position ids)
+ *             rows' position ids); may be NULL when that count is 0
  * Exact: the result is unique and reproduced bit for bit.  n < 2^31.
  */
 tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
@@ -139,8 +139,11 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
  *   out  [n, n_q_heads, head_dim] bf16 (output, round-to-nearest-even)
  *   lse  [n_q_heads, n] fp32 natural-log log-sum-exp of the logits
  *        (output; may be NULL)
- * Supported: head_dim in {64, 128}, n_q_heads % n_kv_heads == 0, n < 2^31.
- * bf16 products, fp32 softmax and accumulation.  n == 0 is a no-op.
+ * Supported: head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
+ * n * n_q_heads * head_dim * 2 < 2^31 (byte offsets fit 31 bits).
+ * Numerics: q.k as bf16 products with fp32 accumulation; softmax in fp32;
+ * probabilities and v rounded to fp16 for the p.v product (v magnitudes above
+ * 65504 saturate), fp32 accumulation.  n == 0 is a no-op.
  */
 tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

@@ -35,6 +35,9 @@ tg_status check_attn(const char* fn, const tg_bf16* q, const tg_bf16* k, const t
   if (hq % hkv != 0)
     return fail(TG_E_INVALID, "%s: n_q_heads=%d not a multiple of n_kv_heads=%d", fn, hq, hkv);
   if (d != 64 && d != 128) return fail(TG_E_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", fn, d);
+  if (n * hq * d * 2 >= (int64_t(1) << 31))
+    return fail(TG_E_UNSUPPORTED, "%s: n=%lld rows of %d heads x %d exceed 2^31 bytes", fn,
+                (long long)n, hq, d);
   if (n == 0) return TG_OK;
   if (!q || !k || !v || !out) return fail(TG_E_INVALID, "%s: null tensor pointer", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -73,9 +76,9 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
     return fail(TG_E_INVALID, "tg_gate_score: hidden=%d gate_hidden=%d must be positive", hidden,
                 gate_hidden);
   if (ld_h < hidden) return fail(TG_E_INVALID, "tg_gate_score: ld_h=%lld < hidden=%d", (long long)ld_h, hidden);
-  if (hidden % 32 != 0 || gate_hidden % 32 != 0 || gate_hidden > 512)
+  if (hidden % 32 != 0 || gate_hidden > 512)
     return fail(TG_E_UNSUPPORTED,
-                "tg_gate_score: hidden=%d gate_hidden=%d (need multiples of 32, gate_hidden <= 512)",
+                "tg_gate_score: hidden=%d gate_hidden=%d (need hidden %% 32 == 0, gate_hidden <= 512)",
                 hidden, gate_hidden);
   if (ld_h % 8 != 0) return fail(TG_E_INVALID, "tg_gate_score: ld_h=%lld not a multiple of 8", (long long)ld_h);
   if (n == 0) return TG_OK;
@@ -93,7 +96,7 @@ tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int6
   if (tg_kept_count(n, doc_begin, doc_end, k_doc) < 0)
     return fail(TG_E_INVALID, "tg_topk_select: need 0 <= doc_begin=%lld <= doc_end=%lld <= n=%lld, k_doc=%lld >= 0",
                 (long long)doc_begin, (long long)doc_end, (long long)n, (long long)k_doc);
-  if (n == 0) return TG_OK;
+  if (n == 0 || tg_kept_count(n, doc_begin, doc_end, k_doc) == 0) return TG_OK;  // nothing kept
   if (!scores || !kept_idx) return fail(TG_E_INVALID, "tg_topk_select: null pointer");
   return hip_status(tg::launch_topk_select(scores, n, doc_begin, doc_end, k_doc, kept_idx, as_hip(stream)),
                     "tg_topk_select launch");

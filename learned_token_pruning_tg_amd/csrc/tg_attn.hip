@@ -8,21 +8,36 @@
 // With gain = 0 and tau = 1 the same kernel is plain causal attention, the
 // unpruned baseline.
 //
-// Design (flash-style, one work-group = 128 query rows of one query head):
-//  * 4 waves, each owning 32 query rows.  S^T = K Q^T is formed with
-//    v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = Q kept in registers),
-//    so every lane owns one query column and 16 keys of each 32-key block:
-//    the online-softmax row statistics are lane-local plus one exchange with
-//    the other lane half.
-//  * O^T = V^T P^T reuses the softmax output straight from registers as the B
-//    operand; V is stored transposed in LDS (key order permuted within each
-//    16-key group so that each lane's eight keys are one 16-byte read).
+// Design (flash-style; one work-group = 128 query rows of one query head,
+// four waves of 32 rows each):
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = Q held
+//    in registers): each lane owns one query column and 16 keys of each
+//    32-key block, so the online-softmax statistics are lane-local plus one
+//    exchange between lane halves.
+//  * O^T = V^T P^T on v_mfma_f32_32x32x16_f16 takes the probabilities straight
+//    from registers as the B operand.  P and V are fp16 for this product:
+//    bf16 P (8-bit mantissa) costs up to ~3e-3 of output error on peaked
+//    rows, on top of the bf16 output rounding; fp16 P is 4x finer.  V is
+//    converted bf16 -> fp16 (exact in fp16's normal range) while it is
+//    transposed into LDS; the key order inside each 16-key group is permuted
+//    so each lane's eight keys are one 16-byte LDS read.
 //  * Scores are pre-multiplied by gain_h * log2(e) when staged into LDS; the
-//    temperature and 1/sqrt(d) are folded with log2(e) into one scale, so each
-//    logit costs one FMA before the exp2-based online softmax.
-//  * The next K/V tile is loaded into registers while the current one is
-//    consumed; fully masked causal tiles are skipped per wave; work-groups
-//    are issued longest-first (last query tile first).
+//    temperature and 1/sqrt(d) are folded with log2(e) into one scale, so a
+//    logit costs one FMA before the exp2-based online softmax.  The running
+//    max is only moved when a tile raises it by more than 2^8 (lazy
+//    rescaling): probabilities stay <= 256, exact in fp16's range.
+//  * Software pipeline, one barrier per 64-key tile: while tile j's softmax
+//    and P.V run, S for tile j+1 is issued from the other LDS buffer and the
+//    global loads of tile j+2 are in flight.  Loads are raw buffer loads whose
+//    hardware range check returns zeros past the last row, so the loop has no
+//    per-row guards.
+//  * Causal masking is applied only on the (at most two) diagonal tiles of a
+//    wave, and tiles entirely above a wave's rows are skipped.
+//  * Work-groups: heads of one KV group are pinned to one XCD (work-groups are
+//    dealt round-robin over the 8 XCDs) so that group's K/V stays in that
+//    XCD's L2; within an XCD the longest (last) query tiles go first.
+#include <type_traits>
+
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -32,6 +47,30 @@ namespace {
 constexpr int kBM = 128;     // query rows per work-group
 constexpr int kBN = 64;      // keys per tile
 constexpr int kThreads = 256;
+constexpr float kRescaleThreshold = 8.f;  // log2 units
+
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+__device__ __forceinline__ floatx16 mfma_f16(f16x8 a, f16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Two bf16 (one dword) -> two fp16 (one dword), round toward zero.  Exact for
+// bf16 values in fp16's normal range; larger magnitudes saturate at 65504.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  const float lo = __uint_as_float(x << 16);
+  const float hi = __uint_as_float(x & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
 
 template <int D, bool kBias>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
@@ -40,22 +79,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const float* __restrict__ tau, bf16* __restrict__ out, float* __restrict__ lse) {
   constexpr int KSTEPS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;            // 32-row tiles of O^T
-  constexpr int K_LD = D + 8;           // K row in LDS, padded by 16 B
-  constexpr int VT_LD = kBN + 8;        // V^T row in LDS, padded by 16 B
+  constexpr int K_LD = D + 8;           // K row in LDS (bf16), padded by 16 B
+  constexpr int VT_LD = kBN + 8;        // V^T row in LDS (fp16), padded by 16 B
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-  constexpr int K_TASKS = kBN * CPR;    // 16-byte K chunks per tile
-  constexpr int K_PER_T = K_TASKS / kThreads;
-  constexpr int V_TASKS = (kBN / 4) * CPR;  // (4 keys x 8 dims) V blocks per tile
-  static_assert(K_TASKS % kThreads == 0, "K tile split");
+  constexpr int K_PER_T = kBN * CPR / kThreads;
+  constexpr int V_TASKS = (kBN / 4) * CPR;  // blocks of 4 keys x 8 dims
+  static_assert((kBN * CPR) % kThreads == 0, "K tile split");
   static_assert(V_TASKS <= kThreads, "V tile split");
 
-  __shared__ __align__(16) bf16 k_lds[kBN * K_LD];
-  __shared__ __align__(16) bf16 vt_lds[D * VT_LD];
-  __shared__ __align__(16) float b_lds[kBN];
+  __shared__ __align__(16) bf16 k_lds[2][kBN * K_LD];
+  __shared__ __align__(16) _Float16 vt_lds[2][D * VT_LD];
+  __shared__ __align__(16) float b_lds[2][kBN];
 
+  // ---- work-group -> (query tile, head)
   const int n_qt = (M + kBM - 1) / kBM;
-  const int head = blockIdx.x % Hq;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x / Hq);
+  int head, qt;
+  {
+    const int b = blockIdx.x;
+    if ((Hq & 7) == 0) {
+      const int hpx = Hq >> 3;            // heads per XCD
+      const int xcd = b & 7, slot = b >> 3;
+      head = xcd * hpx + slot % hpx;
+      qt = n_qt - 1 - slot / hpx;
+    } else {
+      head = b % Hq;
+      qt = n_qt - 1 - b / Hq;
+    }
+  }
   const int kvh = head / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -69,17 +119,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const float alpha = kLog2e / (sqrtf(static_cast<float>(D)) * t_h);
   const float beta = kBias ? gain[head] * kLog2e : 0.f;
 
-  const size_t q_stride = static_cast<size_t>(Hq) * D;
-  const size_t kv_stride = static_cast<size_t>(Hkv) * D;
+  const uint32_t q_row_bytes = static_cast<uint32_t>(Hq) * D * 2;
+  const uint32_t kv_row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
+  const uint32_t kv_tile_bytes = kv_row_bytes * kBN;
+  const uint32_t kv_bytes = kv_row_bytes * static_cast<uint32_t>(M);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(head) * D, q_row_bytes * M);
+  const char* k_base = reinterpret_cast<const char*>(k + static_cast<size_t>(kvh) * D);
+  const char* v_base = reinterpret_cast<const char*>(v + static_cast<size_t>(kvh) * D);
+  // Per-tile descriptors: base moved to the tile's first row (scalar work
+  // only), so the per-thread offsets below are loop-invariant and the range
+  // check still zero-fills rows >= M.
+  auto tile_rsrc = [&](const char* base, int kt) __attribute__((always_inline)) {
+    const uint32_t off = static_cast<uint32_t>(kt) * kv_tile_bytes;
+    return make_rsrc(base + off, off < kv_bytes ? kv_bytes - off : 0u);
+  };
+  auto score_rsrc = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t off = static_cast<uint32_t>(kt) * kBN;
+    return make_rsrc(key_score + off, off < static_cast<uint32_t>(M) ? 4u * (M - off) : 0u);
+  };
 
-  // Q fragments: lane holds Q[my_q][16 s + 8 hh .. + 7].
+  // Q fragments (B operand): lane holds Q[my_q][16 s + 8 hh .. + 7].
   bf16x8 qf[KSTEPS];
-  {
-    const bf16* qrow = q + static_cast<size_t>(my_q) * q_stride + static_cast<size_t>(head) * D;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      qf[s] = as_bf16x8(my_q < M ? ld16(qrow + 16 * s + 8 * hh) : zero_u32x4());
-  }
+  for (int s = 0; s < KSTEPS; ++s)
+    qf[s] = as_bf16x8(bload16(rq, static_cast<uint32_t>(my_q) * q_row_bytes + (16 * s + 8 * hh) * 2));
 
   floatx16 o[DT];
 #pragma unroll
@@ -89,47 +152,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
   const int q_last = min(qt * kBM + kBM, M) - 1;
   const int n_kt = q_last / kBN + 1;
+  const int w_last = min(q0 + 31, q_last);          // last row this wave owns
+  const int n_vis = q0 <= q_last ? w_last / kBN + 1 : 0;  // tiles this wave sees
 
-  // ---- register staging of one K/V tile
+  // ---- register staging
   u32x4 kreg[K_PER_T];
   u32x4 vreg[4];
   float breg = 0.f;
   const int v_kg = tid % 16;  // group of 4 consecutive keys
   const int v_dc = tid / 16;  // 8-dim chunk
 
-  auto load_tile = [&](int kt) {
-    const int kb = kt * kBN;
+  uint32_t k_off[K_PER_T];
+#pragma unroll
+  for (int p = 0; p < K_PER_T; ++p) {
+    const int f = tid + p * kThreads;
+    k_off[p] = static_cast<uint32_t>(f / CPR) * kv_row_bytes + 16 * (f % CPR);
+  }
+  const uint32_t v_off = static_cast<uint32_t>(4 * v_kg) * kv_row_bytes + 16 * v_dc;
+
+  auto load_k = [&](int kt) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc(k_base, kt);
+#pragma unroll
+    for (int p = 0; p < K_PER_T; ++p) kreg[p] = bload16(r, k_off[p]);
+  };
+  auto load_v = [&](int kt) __attribute__((always_inline)) {
+    if (tid < V_TASKS) {
+      const __amdgpu_buffer_rsrc_t r = tile_rsrc(v_base, kt);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vreg[i] = bload16(r, v_off + i * kv_row_bytes);
+    }
+    if (kBias && tid < kBN)
+      breg = beta * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  score_rsrc(kt), 4 * tid, 0, 0));
+  };
+  auto store_k = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < K_PER_T; ++p) {
       const int f = tid + p * kThreads;
-      const int row = f / CPR, c = f % CPR;
-      const int key = kb + row;
-      kreg[p] = key < M ? ld16(k + static_cast<size_t>(key) * kv_stride +
-                               static_cast<size_t>(kvh) * D + 8 * c)
-                        : zero_u32x4();
-    }
-    if (tid < V_TASKS) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * v_kg + r;
-        vreg[r] = key < M ? ld16(v + static_cast<size_t>(key) * kv_stride +
-                                 static_cast<size_t>(kvh) * D + 8 * v_dc)
-                          : zero_u32x4();
-      }
-    }
-    if (kBias && tid < kBN) {
-      const int key = kb + tid;
-      breg = key < M ? beta * key_score[key] : 0.f;
+      st16(&k_lds[buf][(f / CPR) * K_LD + 8 * (f % CPR)], kreg[p]);
     }
   };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int p = 0; p < K_PER_T; ++p) {
-      const int f = tid + p * kThreads;
-      const int row = f / CPR, c = f % CPR;
-      st16(&k_lds[row * K_LD + 8 * c], kreg[p]);
-    }
+  auto store_v = [&](int buf) __attribute__((always_inline)) {
     if (tid < V_TASKS) {
       // keys 4 kg + r sit at positions 16 s + 8 h' + 4 b + r, with
       // s = kg / 4, h' = (kg % 4) & 1, b = (kg % 4) >> 1.
@@ -137,95 +200,139 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       const int phys = 16 * s + 8 * (j & 1) + 4 * (j >> 1);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = vreg[0][w], x1 = vreg[1][w], x2 = vreg[2][w], x3 = vreg[3][w];
-        // dim 2w: low halves; dim 2w+1: high halves
-        uint2 lo, hi;
+        const uint32_t x0 = bf16x2_to_f16x2(vreg[0][w]), x1 = bf16x2_to_f16x2(vreg[1][w]);
+        const uint32_t x2 = bf16x2_to_f16x2(vreg[2][w]), x3 = bf16x2_to_f16x2(vreg[3][w]);
+        uint2 lo, hi;  // dim 2w: low halves; dim 2w+1: high halves
         lo.x = (x0 & 0xFFFFu) | (x1 << 16);
         lo.y = (x2 & 0xFFFFu) | (x3 << 16);
         hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
         hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
         const int d0 = 8 * v_dc + 2 * w;
-        *reinterpret_cast<uint2*>(&vt_lds[d0 * VT_LD + phys]) = lo;
-        *reinterpret_cast<uint2*>(&vt_lds[(d0 + 1) * VT_LD + phys]) = hi;
+        *reinterpret_cast<uint2*>(&vt_lds[buf][d0 * VT_LD + phys]) = lo;
+        *reinterpret_cast<uint2*>(&vt_lds[buf][(d0 + 1) * VT_LD + phys]) = hi;
       }
     }
-    if (kBias && tid < kBN) b_lds[tid] = breg;
+    if (kBias && tid < kBN) b_lds[buf][tid] = breg;
   };
 
-  load_tile(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-
-    const int kb = kt * kBN;
-    if (kb <= q0 + 31) {  // some key of this tile is visible to this wave
-      floatx16 s[2];
-      s[0] = zero16();
-      s[1] = zero16();
+  auto qk = [&](int buf, floatx16* s) __attribute__((always_inline)) {
+    s[0] = zero16();
+    s[1] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 a = lds_bf16x8(&k_lds[(32 * t + l32) * K_LD + 16 * ks + 8 * hh]);
-          s[t] = mfma_32x32x16(a, qf[ks], s[t]);
-        }
-      }
-      const bool diag = kb + kBN - 1 > q0;
-      float mx = -INFINITY;
+    for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        const bf16x8 a = lds_bf16x8(&k_lds[buf][(32 * t + l32) * K_LD + 16 * ks + 8 * hh]);
+        s[t] = mfma_32x32x16(a, qf[ks], s[t]);
+      }
+    }
+  };
+
+  // softmax of tile kt held in s (in place -> probabilities), then O += P V
+  auto soft_pv = [&](int buf, int kb, floatx16* s, bool mask) __attribute__((always_inline)) {
+    float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kl = 32 * t + 8 * (j >> 2) + 4 * hh + (j & 3);
-          float x = kBias ? fmaf(s[t][j], alpha, b_lds[kl]) : s[t][j] * alpha;
-          if (diag && kb + kl > my_q) x = -INFINITY;
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        float bias[4] = {0.f, 0.f, 0.f, 0.f};
+        if (kBias) {
+          const float4 b4 = *reinterpret_cast<const float4*>(&b_lds[buf][32 * t + 8 * j4 + 4 * hh]);
+          bias[0] = b4.x; bias[1] = b4.y; bias[2] = b4.z; bias[3] = b4.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 4 * j4 + r;
+          float x = kBias ? fmaf(s[t][j], alpha, bias[r]) : s[t][j] * alpha;
+          if (mask && kb + 32 * t + 8 * j4 + 4 * hh + r > my_q) x = -INFINITY;
           s[t][j] = x;
           mx = fmaxf(mx, x);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Wave-uniform and rare after the first tiles: a real branch, not a select.
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane(__any(mx > m_run + kRescaleThreshold)), 0)) {
       const float m_new = fmaxf(m_run, mx);
       const float corr = fast_exp2(m_run - m_new);
       m_run = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = fast_exp2(s[t][j] - m_new);
-          s[t][j] = p;
-          rs += p;
-        }
-      }
-      l_run = l_run * corr + rs;
+      l_run *= corr;
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[i][j] *= corr;
       }
-      bf16x8 pf[4];
+    }
+    float rs = 0.f;
+    uint32_t pk[2][8];
 #pragma unroll
-      for (int ps = 0; ps < 4; ++ps) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pf[ps][i] = static_cast<bf16>(s[ps >> 1][8 * (ps & 1) + i]);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int ps = 0; ps < 4; ++ps) {
-          const bf16x8 a = lds_bf16x8(&vt_lds[(32 * dt + l32) * VT_LD + 16 * ps + 8 * hh]);
-          o[dt] = mfma_32x32x16(a, pf[ps], o[dt]);
-        }
+      for (int j = 0; j < 16; j += 2) {
+        const float p0 = fast_exp2(s[t][j] - m_run);
+        const float p1 = fast_exp2(s[t][j + 1] - m_run);
+        rs += p0 + p1;
+        pk[t][j >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
       }
     }
+    l_run += rs;
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+      const uint32_t* src = &pk[ps >> 1][4 * (ps & 1)];
+      const u32x4 pv = {src[0], src[1], src[2], src[3]};
+      const f16x8 b = __builtin_bit_cast(f16x8, pv);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(
+            &vt_lds[buf][(32 * dt + l32) * VT_LD + 16 * ps + 8 * hh]);
+        o[dt] = mfma_f16(a, b, o[dt]);
+      }
+    }
+  };
+
+  // ---- prologue: K_0 in LDS, S_0 computed; K_1, V_0 in registers
+  load_k(0);
+  store_k(0);
+  load_k(1);
+  load_v(0);
+  __syncthreads();
+  floatx16 s_cur[2];
+  if (n_vis > 0) qk(0, s_cur);
+
+  // One pipeline stage; `cur` is a compile-time buffer index (the loop is
+  // unrolled by two so that no register or LDS index is loop-carried).
+  auto stage = [&](auto cur_c, int kt) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
+    store_k(nxt);   // K_{kt+1}
+    store_v(cur);   // V_kt and its scores
     __syncthreads();
+    load_k(kt + 2);
+    load_v(kt + 1);
+    if (kt < n_vis) {
+      const int kb = kt * kBN;
+      const bool diag = kb + kBN - 1 > q0;
+      if (kt + 1 < n_vis) {
+        floatx16 s_nxt[2];
+        qk(nxt, s_nxt);
+        if (diag) soft_pv(cur, kb, s_cur, true);
+        else soft_pv(cur, kb, s_cur, false);
+        s_cur[0] = s_nxt[0];
+        s_cur[1] = s_nxt[1];
+      } else {
+        if (diag) soft_pv(cur, kb, s_cur, true);
+        else soft_pv(cur, kb, s_cur, false);
+      }
+    }
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    stage(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < n_kt) stage(std::integral_constant<int, 1>{}, kt + 1);
   }
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (my_q < M) {
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.f / l_tot;
-    bf16* orow = out + static_cast<size_t>(my_q) * q_stride + static_cast<size_t>(head) * D;
+    bf16* orow = out + static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -233,14 +340,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         bf16 pk[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) pk[r] = static_cast<bf16>(o[dt][4 * jj + r] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * jj + 4 * hh) =
-            __builtin_bit_cast(uint2, pk);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * jj + 4 * hh) = __builtin_bit_cast(uint2, pk);
       }
     }
     if (lse != nullptr && hh == 0)
       lse[static_cast<size_t>(head) * M + my_q] = (m_run + __log2f(l_tot)) * kLn2;
-  } else {
-    (void)__shfl_xor(l_run, 32);
   }
 }
 

@@ -2,18 +2,29 @@
 //
 // Method (lucasainews.com TokenGate article, section "작동 방식"): at the gate
 // layer a small MLP scores every token from its post-attention residual.
-// Read here as s_i = w2 . GELU(W1 h_i + b1) + b2 with the exact erf GELU.
+// Read here as s_i = w2 . GELU(W1 h_i + b1) + b2 with the exact (erf) GELU.
 //
-// Design: the first layer is a dense contraction [n x H] . [H x Hg], run on
-// bf16 MFMA as Z^T = W1 . h^T so that each lane owns one token column and 16
-// gate units per 32x32 tile: GELU, the w2 weighting and the reduction over
-// gate units then stay lane-local, plus one exchange between lane halves and
-// a fixed-order sum over the four column waves in LDS (deterministic, no
-// atomics, no workspace).  One work-group takes BM tokens and all Hg <= 512
-// gate units, so h is read from HBM exactly once and W1 (2 MiB at Qwen3
-// shapes, L2-resident) is re-read once per BM tokens.  K is streamed in
-// 32-wide chunks through padded LDS tiles with the next chunk held in
-// registers while the current one is consumed.
+// Design: the first layer is a dense contraction [n x H] . [H x Hg] on bf16
+// MFMA, computed as Z^T = W1 . h^T so that each lane owns one token column and
+// 16 gate units per 32x32 tile: GELU, the w2 weighting and the reduction over
+// gate units stay lane-local, plus one exchange between lane halves and a
+// fixed-order sum over the four column waves in LDS (deterministic, no
+// atomics, no workspace).
+//  * One work-group takes BM tokens and all gate units (padded to 128 * CT;
+//    padding units read as zeros and contribute nothing), so h streams from
+//    HBM exactly once while W1 (2 MiB at Qwen3 shapes) is re-read from L2
+//    once per BM tokens.
+//  * K is streamed in 32-wide chunks through double-buffered, padded LDS tiles
+//    with one barrier per chunk; the next chunk's raw buffer loads are in
+//    flight while the current chunk is multiplied.  Per-chunk descriptors put
+//    the hardware range check on the row boundary, so rows past n read as
+//    zeros without per-row guards.
+//  * Work-groups start their K loop at staggered chunks so the CUs of one XCD
+//    do not all hit the same W1 lines of L2 at the same time.
+//  * erf uses Abramowitz & Stegun formula 7.1.26 (|error| <= 1.5e-7),
+//    branch-free, with the hardware exp2.
+#include <type_traits>
+
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -22,122 +33,192 @@ namespace {
 
 constexpr int kKC = 32;          // K chunk
 constexpr int kLD = kKC + 8;     // padded LDS row (80 B): conflict-free 16-byte reads
-constexpr int kMaxHg = 512;
 
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
 }
 
-// BM tokens per work-group; BM / 64 row groups x 4 column waves.
-template <int BM>
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+
+// erf(x) by Abramowitz & Stegun 7.1.26: for x >= 0,
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x);  odd symmetry for x < 0.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * kLog2e);
+  const float r = fmaf(-poly, e, 1.f);
+  return copysignf(r, x);
+}
+
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.f + erf_as(z * 0.70710678118654752f));
+}
+
+// BM tokens per work-group (BM / 64 row groups x 4 column waves); each wave
+// owns CT gate-unit tiles of 32, so the work-group covers 128 * CT units.
+template <int BM, int CT>
 __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
     const bf16* __restrict__ h, int64_t n, int64_t ld_h, int H, const bf16* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2, int Hg,
     float* __restrict__ scores) {
   constexpr int NT = BM / 64 * 256;
-  constexpr int W_TASKS = kMaxHg * (kKC / 8);       // 16-byte chunks of a W1 K-chunk
-  constexpr int W_PER_T = W_TASKS / NT;
-  constexpr int H_TASKS = BM * (kKC / 8);
-  constexpr int H_PER_T = (H_TASKS + NT - 1) / NT;
-  static_assert(W_TASKS % NT == 0, "W1 chunk split");
+  constexpr int HGP = 128 * CT;                 // padded gate units
+  constexpr int W_PER_T = HGP * (kKC / 8) / NT;
+  constexpr int H_PER_T = BM * (kKC / 8) / NT;
+  static_assert(HGP * (kKC / 8) % NT == 0 && BM * (kKC / 8) % NT == 0, "chunk split");
 
-  __shared__ __align__(16) bf16 w_lds[kMaxHg * kLD];
-  __shared__ __align__(16) bf16 h_lds[BM * kLD];
+  __shared__ __align__(16) bf16 w_lds[2][HGP * kLD];
+  __shared__ __align__(16) bf16 h_lds[2][BM * kLD];
   __shared__ float red[4][BM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int rw = wave >> 2;   // 64-token group
-  const int cw = wave & 3;    // column wave: gate-unit tiles cw, cw+4, cw+8, cw+12
-  const int n_ct = Hg / 32;
+  const int cw = wave & 3;    // column wave: gate-unit tiles cw + 4 i
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t rows_left = n - row0;
+  const uint32_t rows_valid = static_cast<uint32_t>(rows_left < BM ? rows_left : BM);
+  const uint32_t h_row_bytes = static_cast<uint32_t>(ld_h) * 2;
+  const uint32_t h_bytes = rows_valid * h_row_bytes;
+  const uint32_t w_row_bytes = static_cast<uint32_t>(H) * 2;
+  const uint32_t w_bytes = static_cast<uint32_t>(Hg) * w_row_bytes;
+  const char* h_base = reinterpret_cast<const char*>(h + row0 * ld_h);
+  const char* w_base = reinterpret_cast<const char*>(w1);
 
-  floatx16 acc[4][2];
+  uint32_t w_off[W_PER_T], h_off[H_PER_T];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int p = 0; p < W_PER_T; ++p) {
+    const int f = tid + p * NT;
+    w_off[p] = static_cast<uint32_t>(f >> 2) * w_row_bytes + 16 * (f & 3);
+  }
+#pragma unroll
+  for (int p = 0; p < H_PER_T; ++p) {
+    const int f = tid + p * NT;
+    h_off[p] = static_cast<uint32_t>(f >> 2) * h_row_bytes + 16 * (f & 3);
+  }
+
+  floatx16 acc[CT][2];
+#pragma unroll
+  for (int i = 0; i < CT; ++i) {
     acc[i][0] = zero16();
     acc[i][1] = zero16();
   }
 
   u32x4 wreg[W_PER_T];
   u32x4 hreg[H_PER_T];
-  const int w_tasks = Hg * (kKC / 8);
+  const int n_chunks = H / kKC;
+  const int start = static_cast<int>(blockIdx.x >> 3) % n_chunks;
 
-  auto load_chunk = [&](int k0) {
+  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+    const int k0 = ((start + c) % n_chunks) * kKC;
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2;
+    const __amdgpu_buffer_rsrc_t rw_ = make_rsrc(w_base + kb, w_bytes > kb ? w_bytes - kb : 0u);
+    const __amdgpu_buffer_rsrc_t rh_ = make_rsrc(h_base + kb, h_bytes > kb ? h_bytes - kb : 0u);
+#pragma unroll
+    for (int p = 0; p < W_PER_T; ++p) wreg[p] = bload16(rw_, w_off[p]);
+#pragma unroll
+    for (int p = 0; p < H_PER_T; ++p) hreg[p] = bload16(rh_, h_off[p]);
+  };
+  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < W_PER_T; ++p) {
       const int f = tid + p * NT;
-      const int r = f >> 2, c = f & 3;
-      wreg[p] = f < w_tasks ? ld16(w1 + static_cast<size_t>(r) * H + k0 + 8 * c) : zero_u32x4();
+      st16(&w_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], wreg[p]);
     }
 #pragma unroll
     for (int p = 0; p < H_PER_T; ++p) {
       const int f = tid + p * NT;
-      const int r = f >> 2, c = f & 3;
-      const int64_t row = row0 + r;
-      hreg[p] = (f < H_TASKS && row < n) ? ld16(h + row * ld_h + k0 + 8 * c) : zero_u32x4();
+      st16(&h_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], hreg[p]);
     }
   };
-  auto store_chunk = [&]() {
-#pragma unroll
-    for (int p = 0; p < W_PER_T; ++p) {
-      const int f = tid + p * NT;
-      if (f < w_tasks) st16(&w_lds[(f >> 2) * kLD + 8 * (f & 3)], wreg[p]);
-    }
-#pragma unroll
-    for (int p = 0; p < H_PER_T; ++p) {
-      const int f = tid + p * NT;
-      if (f < H_TASKS) st16(&h_lds[(f >> 2) * kLD + 8 * (f & 3)], hreg[p]);
-    }
-  };
-
-  load_chunk(0);
-  for (int k0 = 0; k0 < H; k0 += kKC) {
-    store_chunk();
-    __syncthreads();
-    if (k0 + kKC < H) load_chunk(k0 + kKC);
+  auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < kKC / 16; ++ks) {
       bf16x8 hb[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        hb[tt] = lds_bf16x8(&h_lds[(64 * rw + 32 * tt + l32) * kLD + 16 * ks + 8 * hh]);
+        hb[tt] = lds_bf16x8(&h_lds[buf][(64 * rw + 32 * tt + l32) * kLD + 16 * ks + 8 * hh]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ct = cw + 4 * i;
-        if (ct < n_ct) {
-          const bf16x8 a = lds_bf16x8(&w_lds[(32 * ct + l32) * kLD + 16 * ks + 8 * hh]);
-          acc[i][0] = mfma_32x32x16(a, hb[0], acc[i][0]);
-          acc[i][1] = mfma_32x32x16(a, hb[1], acc[i][1]);
-        }
+      for (int i = 0; i < CT; ++i) {
+        const bf16x8 a = lds_bf16x8(&w_lds[buf][(32 * (cw + 4 * i) + l32) * kLD + 16 * ks + 8 * hh]);
+        acc[i][0] = mfma_32x32x16(a, hb[0], acc[i][0]);
+        acc[i][1] = mfma_32x32x16(a, hb[1], acc[i][1]);
       }
     }
+  };
+  // One barrier per chunk: the buffer written at chunk c was last read at
+  // chunk c - 2, which every wave finished before passing barrier c - 1.
+  auto stage = [&](auto buf_c, int c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+    store_chunk(buf);
     __syncthreads();
+    if (c + 1 < n_chunks) load_chunk(c + 1);
+    compute(buf);
+  };
+
+  load_chunk(0);
+  for (int c = 0; c < n_chunks; c += 2) {
+    stage(std::integral_constant<int, 0>{}, c);
+    if (c + 1 < n_chunks) stage(std::integral_constant<int, 1>{}, c + 1);
   }
 
-  // Epilogue: GELU, weight by w2, reduce over gate units.
+  // Epilogue: GELU, weight by w2, reduce over gate units (padding units have
+  // b1 = w2 = 0 through the range-checked loads).
+  const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(b1, 4u * Hg);
+  const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(w2, 4u * Hg);
+  float part[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < CT; ++i) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t u = 32 * (cw + 4 * i) + 8 * (j >> 2) + 4 * hh + (j & 3);
+      const float bu = bload4f(rb1, 4 * u), wu = bload4f(rw2, 4 * u);
+      part[0] = fmaf(wu, gelu_erf(acc[i][0][j] + bu), part[0]);
+      part[1] = fmaf(wu, gelu_erf(acc[i][1][j] + bu), part[1]);
+    }
+  }
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ct = cw + 4 * i;
-      if (ct < n_ct) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int u = 32 * ct + 8 * (j >> 2) + 4 * hh + (j & 3);
-          part = fmaf(w2[u], gelu_erf(acc[i][tt][j] + b1[u]), part);
-        }
-      }
-    }
-    part += __shfl_xor(part, 32);
-    if (hh == 0) red[cw][64 * rw + 32 * tt + l32] = part;
+    const float p = part[tt] + __shfl_xor(part[tt], 32);
+    if (hh == 0) red[cw][64 * rw + 32 * tt + l32] = p;
   }
   __syncthreads();
   for (int r = tid; r < BM; r += NT) {
-    const int64_t row = row0 + r;
-    if (row < n) scores[row] = (((red[0][r] + red[1][r]) + red[2][r]) + red[3][r]) + b2;
+    if (r < static_cast<int>(rows_valid))
+      scores[row0 + r] = (((red[0][r] + red[1][r]) + red[2][r]) + red[3][r]) + b2;
+  }
+}
+
+template <int BM, int CT>
+void launch_bm_ct(const bf16* h, int64_t n, int64_t ld_h, int H, const bf16* w1, const float* b1,
+                  const float* w2, float b2, int Hg, float* scores, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((n + BM - 1) / BM));
+  hipLaunchKernelGGL((gate_score_kernel<BM, CT>), grid, dim3(BM / 64 * 256), 0, stream, h, n,
+                     ld_h, H, w1, b1, w2, b2, Hg, scores);
+}
+
+template <int BM>
+void launch_bm(const bf16* h, int64_t n, int64_t ld_h, int H, const bf16* w1, const float* b1,
+               const float* w2, float b2, int Hg, float* scores, hipStream_t stream) {
+  switch ((Hg + 127) / 128) {
+    case 1: launch_bm_ct<BM, 1>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    case 2: launch_bm_ct<BM, 2>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    case 3: launch_bm_ct<BM, 3>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    default: launch_bm_ct<BM, 4>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
   }
 }
 
@@ -149,17 +230,12 @@ hipError_t launch_gate_score(const uint16_t* h, int64_t n, int64_t ld_h, int hid
   if (n == 0) return hipSuccess;
   const bf16* hp = reinterpret_cast<const bf16*>(h);
   const bf16* wp = reinterpret_cast<const bf16*>(w1);
-  // Prefer 128-token tiles (half the W1 re-reads) once they still give at
+  // 128-token tiles halve the W1 re-reads; use them once they still give at
   // least two work-groups per compute unit.
-  if (n >= 128 * 512) {
-    const dim3 grid(static_cast<unsigned>((n + 127) / 128));
-    hipLaunchKernelGGL(gate_score_kernel<128>, grid, dim3(512), 0, stream, hp, n, ld_h, hidden,
-                       wp, b1, w2, b2, gate_hidden, scores);
-  } else {
-    const dim3 grid(static_cast<unsigned>((n + 63) / 64));
-    hipLaunchKernelGGL(gate_score_kernel<64>, grid, dim3(256), 0, stream, hp, n, ld_h, hidden,
-                       wp, b1, w2, b2, gate_hidden, scores);
-  }
+  if (n >= 128 * 512)
+    launch_bm<128>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
+  else
+    launch_bm<64>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
   return hipGetLastError();
 }
 

@@ -75,7 +75,6 @@ def test_gate_validation(L):
     assert f(A, 10, 260, 256, A, A, A, 0.0, 64, A, s) == INVALID         # ld_h % 8
     assert f(A, 10, 256, 250, A, A, A, 0.0, 64, A, s) == UNSUPPORTED     # hidden % 32
     assert f(A, 10, 256, 256, A, A, A, 0.0, 544, A, s) == UNSUPPORTED    # gate_hidden > 512
-    assert f(A, 10, 256, 256, A, A, A, 0.0, 48, A, s) == UNSUPPORTED     # gate_hidden % 32
     assert f(None, 10, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID
     assert f(A + 2, 10, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID     # alignment
     assert "aligned" in tg.last_error()
@@ -90,6 +89,7 @@ def test_topk_validation(L):
     assert f(None, 10, 0, 5, 3, A, 0) == INVALID
     assert f(A, 1 << 31, 0, 5, 3, A, 0) == INVALID
     assert f(None, 0, 0, 0, 3, None, 0) == OK
+    assert f(A, 10, 0, 10, 0, None, 0) == OK                             # nothing kept
 
 
 def test_compact_validation(L):
@@ -114,6 +114,7 @@ def test_attention_validation(L):
     assert g(A + 8, A, A, 10, 16, 8, 128, A, A, A, A, None, 0) == INVALID
     assert full(A, A, None, 10, 16, 8, 128, A, None, 0) == INVALID
     assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, 0) == UNSUPPORTED
+    assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, 0) == UNSUPPORTED  # 2^31-byte offsets
     assert g(None, None, None, 0, 16, 8, 128, None, None, None, None, None, 0) == OK
     assert full(None, None, None, 0, 16, 8, 128, None, None, 0) == OK
 
