@@ -46,7 +46,7 @@ namespace {
 
 constexpr int kBM = 128;     // query rows per work-group
 constexpr int kBN = 64;      // keys per tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;    // two groups of four waves
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
@@ -73,7 +73,7 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 template <int D, bool kBias>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, int M,
     int Hq, int Hkv, const float* __restrict__ key_score, const float* __restrict__ gain,
     const float* __restrict__ tau, bf16* __restrict__ out, float* __restrict__ lse) {
@@ -82,14 +82,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   constexpr int K_LD = D + 8;           // K row in LDS (bf16), padded by 16 B
   constexpr int VT_LD = kBN + 8;        // V^T row in LDS (fp16), padded by 16 B
   constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-  constexpr int K_PER_T = kBN * CPR / kThreads;
-  constexpr int V_TASKS = (kBN / 4) * CPR;  // blocks of 4 keys x 8 dims
-  static_assert((kBN * CPR) % kThreads == 0, "K tile split");
-  static_assert(V_TASKS <= kThreads, "V tile split");
+  constexpr int K_PER_T = 2 * kBN * CPR / kThreads;   // K chunks per thread per tile pair
+  constexpr int V_TASKS = (kBN / 4) * CPR;             // (4 keys x 8 dims) blocks per tile
+  static_assert((2 * kBN * CPR) % kThreads == 0, "K tile split");
+  static_assert(2 * V_TASKS <= kThreads, "V tile split");
 
-  __shared__ __align__(16) bf16 k_lds[2][kBN * K_LD];
-  __shared__ __align__(16) _Float16 vt_lds[2][D * VT_LD];
-  __shared__ __align__(16) float b_lds[2][kBN];
+  // [step parity][wave group] tiles; the group-1 half of k_lds is reused for
+  // the final merge of the two groups' partial results.
+  __shared__ __align__(16) bf16 k_lds[2][2][kBN * K_LD];
+  __shared__ __align__(16) _Float16 vt_lds[2][2][D * VT_LD];
+  __shared__ __align__(16) float b_lds[2][2][kBN];
 
   // ---- work-group -> (query tile, head)
   const int n_qt = (M + kBM - 1) / kBM;
@@ -109,10 +111,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int kvh = head / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int grp = wave >> 2;            // 0: even key tiles, 1: odd key tiles
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int q0 = qt * kBM + wave * 32;
+  const int q0 = qt * kBM + (wave & 3) * 32;
   const int my_q = q0 + l32;
 
   const float t_h = kBias ? tau[head] : 1.f;
@@ -126,15 +129,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(head) * D, q_row_bytes * M);
   const char* k_base = reinterpret_cast<const char*>(k + static_cast<size_t>(kvh) * D);
   const char* v_base = reinterpret_cast<const char*>(v + static_cast<size_t>(kvh) * D);
-  // Per-tile descriptors: base moved to the tile's first row (scalar work
-  // only), so the per-thread offsets below are loop-invariant and the range
+  // Per-tile-pair descriptors: base moved to the pair's first row (scalar
+  // work only), so the per-thread offsets are loop-invariant and the range
   // check still zero-fills rows >= M.
-  auto tile_rsrc = [&](const char* base, int kt) __attribute__((always_inline)) {
-    const uint32_t off = static_cast<uint32_t>(kt) * kv_tile_bytes;
+  auto pair_rsrc = [&](const char* base, int t0) __attribute__((always_inline)) {
+    const uint32_t off = static_cast<uint32_t>(t0) * kv_tile_bytes;
     return make_rsrc(base + off, off < kv_bytes ? kv_bytes - off : 0u);
   };
-  auto score_rsrc = [&](int kt) __attribute__((always_inline)) {
-    const uint32_t off = static_cast<uint32_t>(kt) * kBN;
+  auto score_rsrc = [&](int t0) __attribute__((always_inline)) {
+    const uint32_t off = static_cast<uint32_t>(t0) * kBN;
     return make_rsrc(key_score + off, off < static_cast<uint32_t>(M) ? 4u * (M - off) : 0u);
   };
 
@@ -151,53 +154,60 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   float l_run = 0.f;
 
   const int q_last = min(qt * kBM + kBM, M) - 1;
-  const int n_kt = q_last / kBN + 1;
-  const int w_last = min(q0 + 31, q_last);          // last row this wave owns
+  const int n_kt = q_last / kBN + 1;                  // key tiles of the work-group
+  const int n_steps = (n_kt + 1) / 2;                 // tile pairs
+  const int w_last = min(q0 + 31, q_last);            // last row this wave owns
   const int n_vis = q0 <= q_last ? w_last / kBN + 1 : 0;  // tiles this wave sees
 
-  // ---- register staging
+  // ---- register staging of one tile pair
   u32x4 kreg[K_PER_T];
   u32x4 vreg[4];
   float breg = 0.f;
-  const int v_kg = tid % 16;  // group of 4 consecutive keys
-  const int v_dc = tid / 16;  // 8-dim chunk
+  const int v_tp = tid / V_TASKS;       // tile of the pair this thread's V block is in
+  const int v_task = tid % V_TASKS;
+  const int v_kg = v_task % 16;         // group of 4 consecutive keys
+  const int v_dc = v_task / 16;         // 8-dim chunk
+  const bool v_active = tid < 2 * V_TASKS;
 
   uint32_t k_off[K_PER_T];
 #pragma unroll
   for (int p = 0; p < K_PER_T; ++p) {
-    const int f = tid + p * kThreads;
+    const int f = tid + p * kThreads;   // chunk index within the pair
     k_off[p] = static_cast<uint32_t>(f / CPR) * kv_row_bytes + 16 * (f % CPR);
   }
-  const uint32_t v_off = static_cast<uint32_t>(4 * v_kg) * kv_row_bytes + 16 * v_dc;
+  const uint32_t v_off =
+      static_cast<uint32_t>(v_tp * kBN + 4 * v_kg) * kv_row_bytes + 16 * v_dc;
 
-  auto load_k = [&](int kt) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc(k_base, kt);
+  auto load_k = [&](int t0) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = pair_rsrc(k_base, t0);
 #pragma unroll
     for (int p = 0; p < K_PER_T; ++p) kreg[p] = bload16(r, k_off[p]);
   };
-  auto load_v = [&](int kt) __attribute__((always_inline)) {
-    if (tid < V_TASKS) {
-      const __amdgpu_buffer_rsrc_t r = tile_rsrc(v_base, kt);
+  auto load_v = [&](int t0) __attribute__((always_inline)) {
+    if (v_active) {
+      const __amdgpu_buffer_rsrc_t r = pair_rsrc(v_base, t0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) vreg[i] = bload16(r, v_off + i * kv_row_bytes);
     }
-    if (kBias && tid < kBN)
+    if (kBias && tid < 2 * kBN)
       breg = beta * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  score_rsrc(kt), 4 * tid, 0, 0));
+                                                  score_rsrc(t0), 4 * tid, 0, 0));
   };
-  auto store_k = [&](int buf) __attribute__((always_inline)) {
+  auto store_k = [&](int par) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < K_PER_T; ++p) {
       const int f = tid + p * kThreads;
-      st16(&k_lds[buf][(f / CPR) * K_LD + 8 * (f % CPR)], kreg[p]);
+      const int row = f / CPR;          // 0 .. 2 kBN - 1
+      st16(&k_lds[par][row / kBN][(row % kBN) * K_LD + 8 * (f % CPR)], kreg[p]);
     }
   };
-  auto store_v = [&](int buf) __attribute__((always_inline)) {
-    if (tid < V_TASKS) {
+  auto store_v = [&](int par) __attribute__((always_inline)) {
+    if (v_active) {
       // keys 4 kg + r sit at positions 16 s + 8 h' + 4 b + r, with
       // s = kg / 4, h' = (kg % 4) & 1, b = (kg % 4) >> 1.
       const int s = v_kg >> 2, j = v_kg & 3;
       const int phys = 16 * s + 8 * (j & 1) + 4 * (j >> 1);
+      _Float16* dst = vt_lds[par][v_tp];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t x0 = bf16x2_to_f16x2(vreg[0][w]), x1 = bf16x2_to_f16x2(vreg[1][w]);
@@ -208,28 +218,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
         hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
         const int d0 = 8 * v_dc + 2 * w;
-        *reinterpret_cast<uint2*>(&vt_lds[buf][d0 * VT_LD + phys]) = lo;
-        *reinterpret_cast<uint2*>(&vt_lds[buf][(d0 + 1) * VT_LD + phys]) = hi;
+        *reinterpret_cast<uint2*>(&dst[d0 * VT_LD + phys]) = lo;
+        *reinterpret_cast<uint2*>(&dst[(d0 + 1) * VT_LD + phys]) = hi;
       }
     }
-    if (kBias && tid < kBN) b_lds[buf][tid] = breg;
+    if (kBias && tid < 2 * kBN) b_lds[par][tid / kBN][tid % kBN] = breg;
   };
 
-  auto qk = [&](int buf, floatx16* s) __attribute__((always_inline)) {
+  auto qk = [&](const bf16* kt_lds, floatx16* s) __attribute__((always_inline)) {
     s[0] = zero16();
     s[1] = zero16();
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = lds_bf16x8(&k_lds[buf][(32 * t + l32) * K_LD + 16 * ks + 8 * hh]);
+        const bf16x8 a = lds_bf16x8(&kt_lds[(32 * t + l32) * K_LD + 16 * ks + 8 * hh]);
         s[t] = mfma_32x32x16(a, qf[ks], s[t]);
       }
     }
   };
 
-  // softmax of tile kt held in s (in place -> probabilities), then O += P V
-  auto soft_pv = [&](int buf, int kb, floatx16* s, bool mask) __attribute__((always_inline)) {
+  // softmax of the tile held in s (in place -> probabilities), then O += P V
+  auto soft_pv = [&](const _Float16* vt, const float* bt, int kb, floatx16* s, bool mask)
+      __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       for (int j4 = 0; j4 < 4; ++j4) {
         float bias[4] = {0.f, 0.f, 0.f, 0.f};
         if (kBias) {
-          const float4 b4 = *reinterpret_cast<const float4*>(&b_lds[buf][32 * t + 8 * j4 + 4 * hh]);
+          const float4 b4 = *reinterpret_cast<const float4*>(&bt[32 * t + 8 * j4 + 4 * hh]);
           bias[0] = b4.x; bias[1] = b4.y; bias[2] = b4.z; bias[3] = b4.w;
         }
 #pragma unroll
@@ -283,50 +294,82 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
       const f16x8 b = __builtin_bit_cast(f16x8, pv);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(
-            &vt_lds[buf][(32 * dt + l32) * VT_LD + 16 * ps + 8 * hh]);
+        const f16x8 a = *reinterpret_cast<const f16x8*>(&vt[(32 * dt + l32) * VT_LD + 16 * ps + 8 * hh]);
         o[dt] = mfma_f16(a, b, o[dt]);
       }
     }
   };
 
-  // ---- prologue: K_0 in LDS, S_0 computed; K_1, V_0 in registers
+  // ---- prologue: K of tiles 0, 1 in LDS and S of this group's first tile;
+  // K of tiles 2, 3 and V of tiles 0, 1 in registers.
   load_k(0);
   store_k(0);
-  load_k(1);
+  load_k(2);
   load_v(0);
   __syncthreads();
   floatx16 s_cur[2];
-  if (n_vis > 0) qk(0, s_cur);
+  if (grp < n_vis) qk(k_lds[0][grp], s_cur);
 
-  // One pipeline stage; `cur` is a compile-time buffer index (the loop is
-  // unrolled by two so that no register or LDS index is loop-carried).
-  auto stage = [&](auto cur_c, int kt) __attribute__((always_inline)) {
-    constexpr int cur = decltype(cur_c)::value, nxt = cur ^ 1;
-    store_k(nxt);   // K_{kt+1}
-    store_v(cur);   // V_kt and its scores
+  // One pipeline stage per tile pair: group g consumes tile 2 st + g while
+  // S of tile 2 st + 2 + g is formed from the other LDS buffer and the loads
+  // of the following pair are in flight.  One barrier per stage: a buffer
+  // written at stage st was last read at stage st - 1.
+  auto stage = [&](auto par_c, int st) __attribute__((always_inline)) {
+    constexpr int par = decltype(par_c)::value, npar = par ^ 1;
+    store_k(npar);   // K of tiles 2 st + 2, 2 st + 3
+    store_v(par);    // V (and scores) of tiles 2 st, 2 st + 1
     __syncthreads();
-    load_k(kt + 2);
-    load_v(kt + 1);
-    if (kt < n_vis) {
-      const int kb = kt * kBN;
+    load_k(2 * st + 4);
+    load_v(2 * st + 2);
+    const int t = 2 * st + grp;
+    if (t < n_vis) {
+      const int kb = t * kBN;
       const bool diag = kb + kBN - 1 > q0;
-      if (kt + 1 < n_vis) {
+      const _Float16* vt = vt_lds[par][grp];
+      const float* bt = b_lds[par][grp];
+      if (t + 2 < n_vis) {
         floatx16 s_nxt[2];
-        qk(nxt, s_nxt);
-        if (diag) soft_pv(cur, kb, s_cur, true);
-        else soft_pv(cur, kb, s_cur, false);
+        qk(k_lds[npar][grp], s_nxt);
+        if (diag) soft_pv(vt, bt, kb, s_cur, true);
+        else soft_pv(vt, bt, kb, s_cur, false);
         s_cur[0] = s_nxt[0];
         s_cur[1] = s_nxt[1];
       } else {
-        if (diag) soft_pv(cur, kb, s_cur, true);
-        else soft_pv(cur, kb, s_cur, false);
+        if (diag) soft_pv(vt, bt, kb, s_cur, true);
+        else soft_pv(vt, bt, kb, s_cur, false);
       }
     }
   };
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    stage(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < n_kt) stage(std::integral_constant<int, 1>{}, kt + 1);
+  for (int st = 0; st < n_steps; st += 2) {
+    stage(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < n_steps) stage(std::integral_constant<int, 1>{}, st + 1);
+  }
+
+  // ---- merge the two groups' partial softmax states (same query rows)
+  __syncthreads();
+  float* xch = reinterpret_cast<float*>(&k_lds[0][0][0]) + ((wave & 3) * 64 + lane) * (16 * DT + 2);
+  if (grp == 1) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xch[16 * i + j] = o[i][j];
+    }
+    xch[16 * DT] = m_run;
+    xch[16 * DT + 1] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const float m1 = xch[16 * DT], l1 = xch[16 * DT + 1];
+    const float m = fmaxf(m_run, m1);
+    const float c0 = fast_exp2(m_run - m), c1 = fast_exp2(m1 - m);
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[i][j] = o[i][j] * c0 + xch[16 * i + j] * c1;
+    }
+    l_run = l_run * c0 + l1 * c1;
+    m_run = m;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

@@ -15,8 +15,8 @@
 //    HBM exactly once while W1 (2 MiB at Qwen3 shapes) is re-read from L2
 //    once per BM tokens.
 //  * K is streamed in 32-wide chunks through double-buffered, padded LDS tiles
-//    with one barrier per chunk; the next chunk's raw buffer loads are in
-//    flight while the current chunk is multiplied.  Per-chunk descriptors put
+//    with one barrier per chunk; raw buffer loads run two chunks ahead of the
+//    MFMAs (two register stage sets).  Per-chunk descriptors put
 //    the hardware range check on the row boundary, so rows past n read as
 //    zeros without per-row guards.
 //  * Work-groups start their K loop at staggered chunks so the CUs of one XCD
@@ -118,31 +118,33 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
     acc[i][1] = zero16();
   }
 
-  u32x4 wreg[W_PER_T];
-  u32x4 hreg[H_PER_T];
+  // Two register stage sets: chunk c is loaded at stage c - 2 into set c & 1,
+  // so each load has two chunks of MFMA work to arrive.
+  u32x4 wreg[2][W_PER_T];
+  u32x4 hreg[2][H_PER_T];
   const int n_chunks = H / kKC;
   const int start = static_cast<int>(blockIdx.x >> 3) % n_chunks;
 
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+  auto load_chunk = [&](int set, int c) __attribute__((always_inline)) {
     const int k0 = ((start + c) % n_chunks) * kKC;
     const uint32_t kb = static_cast<uint32_t>(k0) * 2;
     const __amdgpu_buffer_rsrc_t rw_ = make_rsrc(w_base + kb, w_bytes > kb ? w_bytes - kb : 0u);
     const __amdgpu_buffer_rsrc_t rh_ = make_rsrc(h_base + kb, h_bytes > kb ? h_bytes - kb : 0u);
 #pragma unroll
-    for (int p = 0; p < W_PER_T; ++p) wreg[p] = bload16(rw_, w_off[p]);
+    for (int p = 0; p < W_PER_T; ++p) wreg[set][p] = bload16(rw_, w_off[p]);
 #pragma unroll
-    for (int p = 0; p < H_PER_T; ++p) hreg[p] = bload16(rh_, h_off[p]);
+    for (int p = 0; p < H_PER_T; ++p) hreg[set][p] = bload16(rh_, h_off[p]);
   };
   auto store_chunk = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < W_PER_T; ++p) {
       const int f = tid + p * NT;
-      st16(&w_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], wreg[p]);
+      st16(&w_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], wreg[buf][p]);
     }
 #pragma unroll
     for (int p = 0; p < H_PER_T; ++p) {
       const int f = tid + p * NT;
-      st16(&h_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], hreg[p]);
+      st16(&h_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], hreg[buf][p]);
     }
   };
   auto compute = [&](int buf) __attribute__((always_inline)) {
@@ -160,17 +162,18 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
       }
     }
   };
-  // One barrier per chunk: the buffer written at chunk c was last read at
+  // One barrier per chunk: the LDS buffer written at chunk c was last read at
   // chunk c - 2, which every wave finished before passing barrier c - 1.
   auto stage = [&](auto buf_c, int c) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
     store_chunk(buf);
     __syncthreads();
-    if (c + 1 < n_chunks) load_chunk(c + 1);
+    if (c + 2 < n_chunks) load_chunk(buf, c + 2);
     compute(buf);
   };
 
-  load_chunk(0);
+  load_chunk(0, 0);
+  if (n_chunks > 1) load_chunk(1, 1);
   for (int c = 0; c < n_chunks; c += 2) {
     stage(std::integral_constant<int, 0>{}, c);
     if (c + 1 < n_chunks) stage(std::integral_constant<int, 1>{}, c + 1);
