@@ -86,7 +86,7 @@ int64_t tg_kept_count(int64_t n, int64_t doc_begin, int64_t doc_end, int64_t k_d
  *   w1       [gate_hidden, hidden] bf16, contiguous, 16-byte aligned
  *   b1, w2   [gate_hidden] fp32
  *   scores   [n] fp32 (output)
- * Supported: hidden % 32 == 0, gate_hidden <= 512.
+ * Supported: hidden % 64 == 0, gate_hidden <= 512.
  * n == 0 is a no-op.  Deterministic: identical inputs give identical bits.
  */
 tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidden,

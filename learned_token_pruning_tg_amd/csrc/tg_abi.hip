@@ -76,9 +76,9 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
     return fail(TG_E_INVALID, "tg_gate_score: hidden=%d gate_hidden=%d must be positive", hidden,
                 gate_hidden);
   if (ld_h < hidden) return fail(TG_E_INVALID, "tg_gate_score: ld_h=%lld < hidden=%d", (long long)ld_h, hidden);
-  if (hidden % 32 != 0 || gate_hidden > 512)
+  if (hidden % 64 != 0 || gate_hidden > 512)
     return fail(TG_E_UNSUPPORTED,
-                "tg_gate_score: hidden=%d gate_hidden=%d (need hidden %% 32 == 0, gate_hidden <= 512)",
+                "tg_gate_score: hidden=%d gate_hidden=%d (need hidden %% 64 == 0, gate_hidden <= 512)",
                 hidden, gate_hidden);
   if (ld_h % 8 != 0) return fail(TG_E_INVALID, "tg_gate_score: ld_h=%lld not a multiple of 8", (long long)ld_h);
   if (n == 0) return TG_OK;

@@ -63,15 +63,6 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
-}
-
 template <int D, bool kBias>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, int M,
@@ -190,8 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       for (int i = 0; i < 4; ++i) vreg[i] = bload16(r, v_off + i * kv_row_bytes);
     }
     if (kBias && tid < 2 * kBN)
-      breg = beta * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                  score_rsrc(t0), 4 * tid, 0, 0));
+      breg = beta * bload4f(score_rsrc(t0), 4 * tid);
   };
   auto store_k = [&](int par) __attribute__((always_inline)) {
 #pragma unroll

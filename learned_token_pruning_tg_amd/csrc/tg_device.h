@@ -57,6 +57,28 @@ __device__ __forceinline__ bf16x8 lds_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// Raw buffer descriptor (gfx9 layout: stride 0, range check on byte offset).
+// Every field goes through readfirstlane so the descriptor is provably
+// wave-uniform and lives in SGPRs; a descriptor the compiler cannot prove
+// uniform makes it wrap each buffer load in a per-lane "waterfall" loop.
+// Loads at offsets >= `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0), static_cast<int>(n), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+
 // Hardware base-2 exponential (v_exp_f32); arguments here are <= 0 or -inf.
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);

@@ -34,19 +34,6 @@ namespace {
 constexpr int kKC = 32;          // K chunk
 constexpr int kLD = kKC + 8;     // padded LDS row (80 B): conflict-free 16-byte reads
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
-}
-
-__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
-}
-
 // erf(x) by Abramowitz & Stegun 7.1.26: for x >= 0,
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
 //   t = 1 / (1 + p x);  odd symmetry for x < 0.
@@ -172,11 +159,13 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
     compute(buf);
   };
 
+  // n_chunks is even (hidden % 64 == 0): both unrolled stages run every trip,
+  // which keeps the accumulators in place across the loop back-edge.
   load_chunk(0, 0);
-  if (n_chunks > 1) load_chunk(1, 1);
+  load_chunk(1, 1);
   for (int c = 0; c < n_chunks; c += 2) {
     stage(std::integral_constant<int, 0>{}, c);
-    if (c + 1 < n_chunks) stage(std::integral_constant<int, 1>{}, c + 1);
+    stage(std::integral_constant<int, 1>{}, c + 1);
   }
 
   // Epilogue: GELU, weight by w2, reduce over gate units (padding units have

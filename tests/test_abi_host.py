@@ -73,7 +73,8 @@ def test_gate_validation(L):
     assert f(A, -1, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID
     assert f(A, 10, 200, 256, A, A, A, 0.0, 64, A, s) == INVALID         # ld_h < hidden
     assert f(A, 10, 260, 256, A, A, A, 0.0, 64, A, s) == INVALID         # ld_h % 8
-    assert f(A, 10, 256, 250, A, A, A, 0.0, 64, A, s) == UNSUPPORTED     # hidden % 32
+    assert f(A, 10, 256, 250, A, A, A, 0.0, 64, A, s) == UNSUPPORTED     # hidden % 64
+    assert f(A, 10, 256, 224, A, A, A, 0.0, 64, A, s) == UNSUPPORTED
     assert f(A, 10, 256, 256, A, A, A, 0.0, 544, A, s) == UNSUPPORTED    # gate_hidden > 512
     assert f(None, 10, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID
     assert f(A + 2, 10, 256, 256, A, A, A, 0.0, 64, A, s) == INVALID     # alignment
