@@ -87,6 +87,7 @@ def main():
     s_kept = torch.empty(m, dtype=torch.float32, device=dev)
     outs = [torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
             for _ in range(2)]
+    ws = tg.attn_workspace(m, w.n_kv_heads, w.head_dim, dev)
     # The upper layers' q/k/v of the kept rows stand for what the layers'
     # projections would produce from the kept residual; they are gathered
     # once from the full-N templates with the selection of this very input.
@@ -113,7 +114,7 @@ def main():
             ev[3].record(stream)
         for l in range(w.n_layers):
             q, k, v = kept_qkv[inputs.template_of_layer(w, l)]
-            tg.gated_attn_fwd(q, k, v, s_kept, gain_d[l], tau_d[l], out=outs[l & 1])
+            tg.gated_attn_fwd(q, k, v, s_kept, gain_d[l], tau_d[l], out=outs[l & 1], workspace=ws)
         if ev is not None:
             ev[4].record(stream)
 
@@ -142,11 +143,12 @@ def main():
     full = None
     if not args.no_full_baseline:
         fout = torch.empty((w.n, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        fws = tg.attn_workspace(w.n, w.n_kv_heads, w.head_dim, dev)
 
         def full_step():
             for l in range(w.n_layers):
                 q, k, v = full_qkv[inputs.template_of_layer(w, l)]
-                tg.full_attn_fwd(q, k, v, out=fout)
+                tg.full_attn_fwd(q, k, v, out=fout, workspace=fws)
 
         fsteps = max(1, min(args.steps, 5))
         for _ in range(min(args.warmup, 1)):
@@ -171,7 +173,7 @@ def main():
             "speedup_gated_vs_full": round(f_ms / ms_step, 2),
             "steps": fsteps,
         }
-        del fout
+        del fout, fws
 
     # ---------------------------------------------------------------- rooflines
     fl = attn_flops(m, w.n_q_heads, w.head_dim)

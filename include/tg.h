@@ -57,7 +57,7 @@ typedef enum tg_status {
   TG_OK = 0,
   TG_E_INVALID = 1,     /* bad pointer, size, range or alignment            */
   TG_E_UNSUPPORTED = 2, /* valid request outside the shapes the kernels take */
-  TG_E_WORKSPACE = 3,   /* reserved: no call takes a workspace at present    */
+  TG_E_WORKSPACE = 3,   /* workspace missing or smaller than required        */
   TG_E_HIP = 4          /* the HIP runtime reported an error at launch       */
 } tg_status;
 
@@ -125,6 +125,13 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
                      int64_t dst_stride_bytes, tg_stream_t stream);
 
 /*
+ * Bytes of device workspace tg_gated_attn_fwd / tg_full_attn_fwd need for n
+ * rows: a packed fp16 copy of V, transposed per 64-key tile
+ * (ceil(n / 64) * 64 * n_kv_heads * head_dim * 2).  Host-only arithmetic.
+ */
+size_t tg_attn_workspace_bytes(int64_t n, int32_t n_kv_heads, int32_t head_dim);
+
+/*
  * Token-gated causal GQA attention over the n kept rows (lucasainews.com
  * article, "작동 방식": each kept token's score is added to the attention
  * logits above the gate, scaled by a per-head learned gain, with a per-head
@@ -139,6 +146,10 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
  *   out  [n, n_q_heads, head_dim] bf16 (output, round-to-nearest-even)
  *   lse  [n_q_heads, n] fp32 natural-log log-sum-exp of the logits
  *        (output; may be NULL)
+ *   workspace  device scratch of at least tg_attn_workspace_bytes(n, ...)
+ *        bytes, 16-byte aligned, owned by the caller; its contents are
+ *        overwritten and carry nothing between calls.  Calls that share one
+ *        workspace must be ordered on one stream.  Too small -> TG_E_WORKSPACE.
  * Supported: head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
  * n * n_q_heads * head_dim * 2 < 2^31 (byte offsets fit 31 bits).
  * Numerics: q.k as bf16 products with fp32 accumulation; softmax in fp32;
@@ -148,17 +159,19 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
 tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                             const float* key_score, const float* gain, const float* tau,
-                            tg_bf16* out, float* lse, tg_stream_t stream);
+                            tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
+                            tg_stream_t stream);
 
 /*
  * Unpruned causal GQA attention over all n rows, softmax(q.k / sqrt(d)) v:
  * the full prefill that the pages' speed-ups are measured against
- * (lucasainews.com article, lede and "성능 결과").  Same layouts, limits and
- * numerics as tg_gated_attn_fwd with gain = 0 and tau = 1.
+ * (lucasainews.com article, lede and "성능 결과").  Same layouts, limits,
+ * workspace and numerics as tg_gated_attn_fwd with gain = 0 and tau = 1.
  */
 tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                           tg_bf16* out, float* lse, tg_stream_t stream);
+                           tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
+                           tg_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -65,18 +65,18 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
 
 template <int D, bool kBias>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, int M,
-    int Hq, int Hkv, const float* __restrict__ key_score, const float* __restrict__ gain,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const _Float16* __restrict__ vt_pack,
+    int M, int Hq, int Hkv, const float* __restrict__ key_score, const float* __restrict__ gain,
     const float* __restrict__ tau, bf16* __restrict__ out, float* __restrict__ lse) {
   constexpr int KSTEPS = D / 16;        // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;            // 32-row tiles of O^T
   constexpr int K_LD = D + 8;           // K row in LDS (bf16), padded by 16 B
   constexpr int VT_LD = kBN + 8;        // V^T row in LDS (fp16), padded by 16 B
-  constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
+  constexpr int CPR = D / 8;            // 16-byte chunks per K row
   constexpr int K_PER_T = 2 * kBN * CPR / kThreads;   // K chunks per thread per tile pair
-  constexpr int V_TASKS = (kBN / 4) * CPR;             // (4 keys x 8 dims) blocks per tile
+  constexpr int V_PER_T = 2 * D * (kBN / 8) / kThreads;  // V^T chunks per thread per pair
   static_assert((2 * kBN * CPR) % kThreads == 0, "K tile split");
-  static_assert(2 * V_TASKS <= kThreads, "V tile split");
+  static_assert((2 * D * (kBN / 8)) % kThreads == 0, "V tile split");
 
   // [step parity][wave group] tiles; the group-1 half of k_lds is reused for
   // the final merge of the two groups' partial results.
@@ -119,13 +119,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const uint32_t kv_bytes = kv_row_bytes * static_cast<uint32_t>(M);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(head) * D, q_row_bytes * M);
   const char* k_base = reinterpret_cast<const char*>(k + static_cast<size_t>(kvh) * D);
-  const char* v_base = reinterpret_cast<const char*>(v + static_cast<size_t>(kvh) * D);
+  // Packed V^T of this KV head: n_tiles blocks of [D][kBN] fp16.
+  const int n_tiles_all = (M + kBN - 1) / kBN;
+  const uint32_t vt_tile_bytes = D * kBN * 2;
+  const uint32_t vt_bytes = vt_tile_bytes * static_cast<uint32_t>(n_tiles_all);
+  const char* v_base = reinterpret_cast<const char*>(vt_pack) +
+                       static_cast<size_t>(kvh) * n_tiles_all * vt_tile_bytes;
   // Per-tile-pair descriptors: base moved to the pair's first row (scalar
   // work only), so the per-thread offsets are loop-invariant and the range
   // check still zero-fills rows >= M.
   auto pair_rsrc = [&](const char* base, int t0) __attribute__((always_inline)) {
     const uint32_t off = static_cast<uint32_t>(t0) * kv_tile_bytes;
     return make_rsrc(base + off, off < kv_bytes ? kv_bytes - off : 0u);
+  };
+  auto vt_rsrc = [&](int t0) __attribute__((always_inline)) {
+    const uint32_t off = static_cast<uint32_t>(t0) * vt_tile_bytes;
+    return make_rsrc(v_base + off, off < vt_bytes ? vt_bytes - off : 0u);
   };
   auto score_rsrc = [&](int t0) __attribute__((always_inline)) {
     const uint32_t off = static_cast<uint32_t>(t0) * kBN;
@@ -152,13 +161,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
 
   // ---- register staging of one tile pair
   u32x4 kreg[K_PER_T];
-  u32x4 vreg[4];
+  u32x4 vreg[V_PER_T];
   float breg = 0.f;
-  const int v_tp = tid / V_TASKS;       // tile of the pair this thread's V block is in
-  const int v_task = tid % V_TASKS;
-  const int v_kg = v_task % 16;         // group of 4 consecutive keys
-  const int v_dc = v_task / 16;         // 8-dim chunk
-  const bool v_active = tid < 2 * V_TASKS;
 
   uint32_t k_off[K_PER_T];
 #pragma unroll
@@ -166,8 +170,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     const int f = tid + p * kThreads;   // chunk index within the pair
     k_off[p] = static_cast<uint32_t>(f / CPR) * kv_row_bytes + 16 * (f % CPR);
   }
-  const uint32_t v_off =
-      static_cast<uint32_t>(v_tp * kBN + 4 * v_kg) * kv_row_bytes + 16 * v_dc;
 
   auto load_k = [&](int t0) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t r = pair_rsrc(k_base, t0);
@@ -175,13 +177,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int p = 0; p < K_PER_T; ++p) kreg[p] = bload16(r, k_off[p]);
   };
   auto load_v = [&](int t0) __attribute__((always_inline)) {
-    if (v_active) {
-      const __amdgpu_buffer_rsrc_t r = pair_rsrc(v_base, t0);
+    const __amdgpu_buffer_rsrc_t r = vt_rsrc(t0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = bload16(r, v_off + i * kv_row_bytes);
-    }
-    if (kBias && tid < 2 * kBN)
-      breg = beta * bload4f(score_rsrc(t0), 4 * tid);
+    for (int p = 0; p < V_PER_T; ++p) vreg[p] = bload16(r, 16u * (tid + p * kThreads));
+    if (kBias && tid < 2 * kBN) breg = beta * bload4f(score_rsrc(t0), 4 * tid);
   };
   auto store_k = [&](int par) __attribute__((always_inline)) {
 #pragma unroll
@@ -192,25 +191,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     }
   };
   auto store_v = [&](int par) __attribute__((always_inline)) {
-    if (v_active) {
-      // keys 4 kg + r sit at positions 16 s + 8 h' + 4 b + r, with
-      // s = kg / 4, h' = (kg % 4) & 1, b = (kg % 4) >> 1.
-      const int s = v_kg >> 2, j = v_kg & 3;
-      const int phys = 16 * s + 8 * (j & 1) + 4 * (j >> 1);
-      _Float16* dst = vt_lds[par][v_tp];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = bf16x2_to_f16x2(vreg[0][w]), x1 = bf16x2_to_f16x2(vreg[1][w]);
-        const uint32_t x2 = bf16x2_to_f16x2(vreg[2][w]), x3 = bf16x2_to_f16x2(vreg[3][w]);
-        uint2 lo, hi;  // dim 2w: low halves; dim 2w+1: high halves
-        lo.x = (x0 & 0xFFFFu) | (x1 << 16);
-        lo.y = (x2 & 0xFFFFu) | (x3 << 16);
-        hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
-        hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
-        const int d0 = 8 * v_dc + 2 * w;
-        *reinterpret_cast<uint2*>(&dst[d0 * VT_LD + phys]) = lo;
-        *reinterpret_cast<uint2*>(&dst[(d0 + 1) * VT_LD + phys]) = hi;
-      }
+    for (int p = 0; p < V_PER_T; ++p) {
+      const int f = tid + p * kThreads;          // 16-byte chunk within the pair
+      const int tp = f / (D * kBN / 8), rem = f % (D * kBN / 8);
+      st16(&vt_lds[par][tp][(rem / (kBN / 8)) * VT_LD + 8 * (rem % (kBN / 8))], vreg[p]);
     }
     if (kBias && tid < 2 * kBN) b_lds[par][tid / kBN][tid % kBN] = breg;
   };
@@ -381,37 +366,88 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   }
 }
 
+// V -> packed V^T: for each KV head and each 64-key tile, a [D][64] fp16 block
+// whose key order inside each 16-key group is permuted so that every lane's
+// eight keys of a P.V step are one contiguous 16-byte run.  Keys >= M are
+// zero.  One work-group per (tile, KV head); each thread moves 4 keys x 8 dims.
+template <int D>
+__global__ __launch_bounds__(256) void v_pack_kernel(const bf16* __restrict__ v, int M, int Hkv,
+                                                     _Float16* __restrict__ vt_pack) {
+  constexpr int CPR = D / 8;
+  constexpr int TASKS = (kBN / 4) * CPR;
+  const int n_tiles = (M + kBN - 1) / kBN;
+  const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+  const int tid = threadIdx.x;
+  if (tid >= TASKS) return;
+  const int kg = tid % 16, dc = tid / 16;
+  const uint32_t kv_row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
+  const uint32_t kv_bytes = kv_row_bytes * static_cast<uint32_t>(M);
+  const uint32_t off0 = static_cast<uint32_t>(tile) * kBN * kv_row_bytes;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(
+      reinterpret_cast<const char*>(v + static_cast<size_t>(kvh) * D) + off0,
+      off0 < kv_bytes ? kv_bytes - off0 : 0u);
+  u32x4 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = bload16(r, (4 * kg + i) * kv_row_bytes + 16 * dc);
+  // keys 4 kg + i sit at positions 16 s + 8 h' + 4 b + i, with
+  // s = kg / 4, h' = (kg % 4) & 1, b = (kg % 4) >> 1.
+  const int s = kg >> 2, j = kg & 3;
+  const int phys = 16 * s + 8 * (j & 1) + 4 * (j >> 1);
+  _Float16* dst = vt_pack + (static_cast<size_t>(kvh) * n_tiles + tile) * D * kBN;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x0 = bf16x2_to_f16x2(x[0][w]), x1 = bf16x2_to_f16x2(x[1][w]);
+    const uint32_t x2 = bf16x2_to_f16x2(x[2][w]), x3 = bf16x2_to_f16x2(x[3][w]);
+    uint2 lo, hi;  // dim 2w: low halves; dim 2w+1: high halves
+    lo.x = (x0 & 0xFFFFu) | (x1 << 16);
+    lo.y = (x2 & 0xFFFFu) | (x3 << 16);
+    hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
+    hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
+    const int d0 = 8 * dc + 2 * w;
+    *reinterpret_cast<uint2*>(&dst[d0 * kBN + phys]) = lo;
+    *reinterpret_cast<uint2*>(&dst[(d0 + 1) * kBN + phys]) = hi;
+  }
+}
+
 template <int D, bool kBias>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M, int Hq, int Hkv,
                   const float* s, const float* g, const float* t, uint16_t* out, float* lse,
-                  hipStream_t stream) {
+                  void* ws, hipStream_t stream) {
+  const int n_tiles = (M + kBN - 1) / kBN;
+  _Float16* vt = static_cast<_Float16*>(ws);
+  hipLaunchKernelGGL((v_pack_kernel<D>), dim3(static_cast<unsigned>(n_tiles * Hkv)), dim3(256), 0,
+                     stream, reinterpret_cast<const bf16*>(v), M, Hkv, vt);
   const int n_qt = (M + kBM - 1) / kBM;
   const dim3 grid(static_cast<unsigned>(n_qt) * static_cast<unsigned>(Hq));
   hipLaunchKernelGGL((attn_fwd_kernel<D, kBias>), grid, dim3(kThreads), 0, stream,
-                     reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
-                     reinterpret_cast<const bf16*>(v), M, Hq, Hkv, s, g, t,
-                     reinterpret_cast<bf16*>(out), lse);
+                     reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k), vt, M, Hq,
+                     Hkv, s, g, t, reinterpret_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t attn_workspace_bytes(int64_t n, int n_kv_heads, int head_dim) {
+  const int64_t n_tiles = (n + kBN - 1) / kBN;
+  return static_cast<size_t>(n_tiles) * kBN * n_kv_heads * head_dim * 2;
+}
+
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
                            int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
                            const float* gain, const float* tau, uint16_t* out, float* lse,
-                           hipStream_t stream) {
+                           void* workspace, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int M = static_cast<int>(n);
   const bool bias = gain != nullptr;
   if (head_dim == 128)
     return bias ? launch<128, true>(q, k, v, M, n_q_heads, n_kv_heads, key_score, gain, tau, out,
-                                    lse, stream)
+                                    lse, workspace, stream)
                 : launch<128, false>(q, k, v, M, n_q_heads, n_kv_heads, nullptr, nullptr,
-                                     nullptr, out, lse, stream);
+                                     nullptr, out, lse, workspace, stream);
   return bias ? launch<64, true>(q, k, v, M, n_q_heads, n_kv_heads, key_score, gain, tau, out,
-                                 lse, stream)
+                                 lse, workspace, stream)
               : launch<64, false>(q, k, v, M, n_q_heads, n_kv_heads, nullptr, nullptr, nullptr,
-                                  out, lse, stream);
+                                  out, lse, workspace, stream);
 }
 
 }  // namespace tg

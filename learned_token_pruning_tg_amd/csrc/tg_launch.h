@@ -18,10 +18,14 @@ hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, const void* s
                           int64_t src_rows, int64_t src_stride, int64_t row_bytes, void* dst,
                           int64_t dst_stride, hipStream_t stream);
 
+// Bytes of the packed-V^T scratch the attention launch needs.
+size_t attn_workspace_bytes(int64_t n, int n_kv_heads, int head_dim);
+
 // gain == nullptr selects the unbiased (full-prefill) kernel with tau = 1.
+// `workspace` holds attn_workspace_bytes(n, n_kv_heads, head_dim) bytes.
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
                            int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
                            const float* gain, const float* tau, uint16_t* out, float* lse,
-                           hipStream_t stream);
+                           void* workspace, hipStream_t stream);
 
 }  // namespace tg

@@ -29,8 +29,11 @@ _SIGNATURES = {
     "tg_gate_score": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, ctypes.c_float, _I32, _P, _P]),
     "tg_topk_select": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
     "tg_compact": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P]),
-    "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
-    "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "tg_attn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32]),
+    "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                         _P, ctypes.c_size_t, _P]),
+    "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
 }
 
 
@@ -163,6 +166,24 @@ def compact(idx: torch.Tensor, src: torch.Tensor, out: Optional[torch.Tensor] = 
     return out
 
 
+def attn_workspace_bytes(n: int, n_kv_heads: int, head_dim: int) -> int:
+    return int(lib().tg_attn_workspace_bytes(n, n_kv_heads, head_dim))
+
+
+def attn_workspace(n: int, n_kv_heads: int, head_dim: int, device="cuda") -> torch.Tensor:
+    """A device buffer large enough for one attention call over n rows."""
+    return torch.empty(max(attn_workspace_bytes(n, n_kv_heads, head_dim), 16), dtype=torch.uint8,
+                       device=device)
+
+
+def _workspace(ws, n, hkv, d, device):
+    if ws is None:
+        ws = attn_workspace(n, hkv, d, device)
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws, ws.numel() * ws.element_size()
+
+
 def _attn_out(q, out, lse, want_lse):
     n, hq, d = q.shape
     if out is None:
@@ -177,9 +198,11 @@ def _attn_out(q, out, lse, want_lse):
 
 def gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
                    gain: torch.Tensor, tau: torch.Tensor, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None):
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
     """Token-gated causal GQA attention over the kept rows.
     q [M, Hq, d], k/v [M, Hkv, d] bf16; key_score [M], gain/tau [Hq] fp32.
+    ``workspace``: scratch from attn_workspace() (allocated per call if None).
     Returns out (and lse [Hq, M] if requested or given)."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16)
@@ -191,14 +214,16 @@ def gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score:
             or gain.shape != (hq,) or tau.shape != (hq,):
         raise ValueError("attention operand shapes do not match")
     out, lse = _attn_out(q, out, lse, want_lse)
+    ws, ws_bytes = _workspace(workspace, n, hkv, d, q.device)
     _check(lib().tg_gated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(key_score),
-                                   _ptr(gain), _ptr(tau), _ptr(out), _ptr(lse), _stream(stream)))
+                                   _ptr(gain), _ptr(tau), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
     return (out, lse) if lse is not None else out
 
 
 def full_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                  want_lse: bool = False, stream=None):
+                  want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Unpruned causal GQA attention softmax(q.k / sqrt(d)) v over all rows."""
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, nm, torch.bfloat16)
@@ -207,6 +232,7 @@ def full_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if k.shape != (n, hkv, d) or v.shape != k.shape:
         raise ValueError("attention operand shapes do not match")
     out, lse = _attn_out(q, out, lse, want_lse)
+    ws, ws_bytes = _workspace(workspace, n, hkv, d, q.device)
     _check(lib().tg_full_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(out), _ptr(lse),
-                                  _stream(stream)))
+                                  _ptr(ws), ws_bytes, _stream(stream)))
     return (out, lse) if lse is not None else out

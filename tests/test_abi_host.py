@@ -106,18 +106,26 @@ def test_compact_validation(L):
 def test_attention_validation(L):
     g = L.tg_gated_attn_fwd
     full = L.tg_full_attn_fwd
-    assert g(A, A, A, 10, 16, 8, 96, A, A, A, A, None, 0) == UNSUPPORTED
+    W = 1 << 30  # a (fake) workspace size that is always large enough
+    assert g(A, A, A, 10, 16, 8, 96, A, A, A, A, None, A, W, 0) == UNSUPPORTED
     assert "head_dim" in tg.last_error()
-    assert g(A, A, A, 10, 16, 6, 128, A, A, A, A, None, 0) == INVALID
-    assert g(A, A, A, 10, 0, 8, 128, A, A, A, A, None, 0) == INVALID
-    assert g(A, A, A, -3, 16, 8, 128, A, A, A, A, None, 0) == INVALID
-    assert g(A, A, A, 10, 16, 8, 128, None, A, A, A, None, 0) == INVALID  # key_score
-    assert g(A + 8, A, A, 10, 16, 8, 128, A, A, A, A, None, 0) == INVALID
-    assert full(A, A, None, 10, 16, 8, 128, A, None, 0) == INVALID
-    assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, 0) == UNSUPPORTED
-    assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, 0) == UNSUPPORTED  # 2^31-byte offsets
-    assert g(None, None, None, 0, 16, 8, 128, None, None, None, None, None, 0) == OK
-    assert full(None, None, None, 0, 16, 8, 128, None, None, 0) == OK
+    assert g(A, A, A, 10, 16, 6, 128, A, A, A, A, None, A, W, 0) == INVALID
+    assert g(A, A, A, 10, 0, 8, 128, A, A, A, A, None, A, W, 0) == INVALID
+    assert g(A, A, A, -3, 16, 8, 128, A, A, A, A, None, A, W, 0) == INVALID
+    assert g(A, A, A, 10, 16, 8, 128, None, A, A, A, None, A, W, 0) == INVALID  # key_score
+    assert g(A + 8, A, A, 10, 16, 8, 128, A, A, A, A, None, A, W, 0) == INVALID
+    assert full(A, A, None, 10, 16, 8, 128, A, None, A, W, 0) == INVALID
+    assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, A, W, 0) == UNSUPPORTED
+    assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, A, W, 0) == UNSUPPORTED  # 2^31-byte offsets
+    need = L.tg_attn_workspace_bytes(100, 8, 128)
+    assert need == 128 * 8 * 128 * 2
+    assert full(A, A, A, 100, 16, 8, 128, A, None, A, need - 1, 0) == WORKSPACE
+    assert full(A, A, A, 100, 16, 8, 128, A, None, None, need, 0) == WORKSPACE
+    assert g(A, A, A, 100, 16, 8, 128, A, A, A, A, None, A + 4, need, 0) == WORKSPACE
+    assert "workspace" in tg.last_error()
+    assert g(None, None, None, 0, 16, 8, 128, None, None, None, None, None, None, 0, 0) == OK
+    assert full(None, None, None, 0, 16, 8, 128, None, None, None, 0, 0) == OK
+    assert L.tg_attn_workspace_bytes(0, 8, 128) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch):
