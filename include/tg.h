@@ -126,8 +126,10 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
 
 /*
  * Bytes of device workspace tg_gated_attn_fwd / tg_full_attn_fwd need for n
- * rows: a packed fp16 copy of V, transposed per 64-key tile
- * (ceil(n / 64) * 64 * n_kv_heads * head_dim * 2).  Host-only arithmetic.
+ * rows (enough for either): per KV head and 64-key tile, a packed copy of K
+ * (bf16, with the key scores appended) and of V (fp16, transposed), laid out
+ * as the kernel's LDS image -- about 2.3x the bytes of K and V.  Host-only
+ * arithmetic; 0 for unsupported head_dim.
  */
 size_t tg_attn_workspace_bytes(int64_t n, int32_t n_kv_heads, int32_t head_dim);
 

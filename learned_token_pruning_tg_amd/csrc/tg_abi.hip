@@ -30,7 +30,7 @@ hipStream_t as_hip(tg_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 tg_status check_attn(const char* fn, const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                      int64_t n, int32_t hq, int32_t hkv, int32_t d, const tg_bf16* out,
-                     const void* ws, size_t ws_bytes) {
+                     const void* ws, size_t ws_bytes, bool gated) {
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(TG_E_INVALID, "%s: n=%lld out of range", fn, (long long)n);
   if (hq <= 0 || hkv <= 0) return fail(TG_E_INVALID, "%s: head counts must be positive", fn);
   if (hq % hkv != 0)
@@ -43,7 +43,10 @@ tg_status check_attn(const char* fn, const tg_bf16* q, const tg_bf16* k, const t
   if (!q || !k || !v || !out) return fail(TG_E_INVALID, "%s: null tensor pointer", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(TG_E_INVALID, "%s: q/k/v/out must be 16-byte aligned", fn);
-  const size_t need = tg::attn_workspace_bytes(n, hkv, d);
+  const size_t need = tg::attn_workspace_bytes(n, hkv, d, gated);
+  if (need >= (size_t(1) << 32) / hkv)
+    return fail(TG_E_UNSUPPORTED, "%s: n=%lld needs %zu workspace bytes (limit 2^32 per KV head)",
+                fn, (long long)n, need);
   if (!ws || ws_bytes < need || !aligned16(ws))
     return fail(TG_E_WORKSPACE, "%s: workspace %p of %zu bytes (need %zu, 16-byte aligned)", fn, ws,
                 ws_bytes, need);
@@ -128,8 +131,8 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
 }
 
 size_t tg_attn_workspace_bytes(int64_t n, int32_t n_kv_heads, int32_t head_dim) {
-  if (n <= 0 || n_kv_heads <= 0 || head_dim <= 0) return 0;
-  return tg::attn_workspace_bytes(n, n_kv_heads, head_dim);
+  if (n <= 0 || n_kv_heads <= 0 || (head_dim != 64 && head_dim != 128)) return 0;
+  return tg::attn_workspace_bytes(n, n_kv_heads, head_dim, true);
 }
 
 tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
@@ -139,7 +142,7 @@ tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
                             tg_stream_t stream) {
   const char* fn = "tg_gated_attn_fwd";
   const tg_status st = check_attn(fn, q, k, v, n, n_q_heads, n_kv_heads, head_dim, out,
-                                  workspace, workspace_bytes);
+                                  workspace, workspace_bytes, true);
   if (st != TG_OK || n == 0) return st;
   if (!key_score || !gain || !tau) return fail(TG_E_INVALID, "%s: null key_score/gain/tau", fn);
   return hip_status(tg::launch_attn_fwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, key_score,
@@ -152,7 +155,7 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                            tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
                            tg_stream_t stream) {
   const tg_status st = check_attn("tg_full_attn_fwd", q, k, v, n, n_q_heads, n_kv_heads, head_dim,
-                                  out, workspace, workspace_bytes);
+                                  out, workspace, workspace_bytes, false);
   if (st != TG_OK || n == 0) return st;
   return hip_status(tg::launch_attn_fwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, nullptr,
                                         nullptr, nullptr, out, lse, workspace, as_hip(stream)),

@@ -5,37 +5,43 @@
 // attention logits, scaled by a per-head gain, and a per-head temperature
 // rescales q.k.  Read here as
 //     logit_ij = q_i.k_j / (sqrt(d) * tau_h) + gain_h * s_j ,   j <= i.
-// With gain = 0 and tau = 1 the same kernel is plain causal attention, the
+// With gain = 0 and tau = 1 the same kernels give plain causal attention, the
 // unpruned baseline.
 //
-// Design (flash-style; one work-group = 128 query rows of one query head,
-// four waves of 32 rows each):
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K tile from LDS, B = Q held
-//    in registers): each lane owns one query column and 16 keys of each
-//    32-key block, so the online-softmax statistics are lane-local plus one
-//    exchange between lane halves.
-//  * O^T = V^T P^T on v_mfma_f32_32x32x16_f16 takes the probabilities straight
-//    from registers as the B operand.  P and V are fp16 for this product:
-//    bf16 P (8-bit mantissa) costs up to ~3e-3 of output error on peaked
-//    rows, on top of the bf16 output rounding; fp16 P is 4x finer.  V is
-//    converted bf16 -> fp16 (exact in fp16's normal range) while it is
-//    transposed into LDS; the key order inside each 16-key group is permuted
-//    so each lane's eight keys are one 16-byte LDS read.
-//  * Scores are pre-multiplied by gain_h * log2(e) when staged into LDS; the
-//    temperature and 1/sqrt(d) are folded with log2(e) into one scale, so a
-//    logit costs one FMA before the exp2-based online softmax.  The running
-//    max is only moved when a tile raises it by more than 2^8 (lazy
-//    rescaling): probabilities stay <= 256, exact in fp16's range.
-//  * Software pipeline, one barrier per 64-key tile: while tile j's softmax
-//    and P.V run, S for tile j+1 is issued from the other LDS buffer and the
-//    global loads of tile j+2 are in flight.  Loads are raw buffer loads whose
-//    hardware range check returns zeros past the last row, so the loop has no
-//    per-row guards.
-//  * Causal masking is applied only on the (at most two) diagonal tiles of a
-//    wave, and tiles entirely above a wave's rows are skipped.
-//  * Work-groups: heads of one KV group are pinned to one XCD (work-groups are
-//    dealt round-robin over the 8 XCDs) so that group's K/V stays in that
-//    XCD's L2; within an XCD the longest (last) query tiles go first.
+// Two launches per call:
+//
+// 1. kv_pack: per KV head and 64-key tile, build the exact LDS image the main
+//    kernel consumes, in the caller's workspace:
+//      * K~ rows [k_j | s_hi, s_lo, s_hi, 0...] in bf16 (the extra 16-column
+//        k-step exists only in the gated kernel; s_hi/s_lo split the score
+//        into two bf16 parts), rows padded to avoid LDS bank conflicts;
+//      * V^T in fp16 ([d][key], key order permuted inside each 16-key group
+//        so that every lane's eight keys of a P.V step are one 16-byte run).
+//    Rows past n are zero.
+// 2. attn_fwd: one work-group = 128 query rows of one query head, eight
+//    waves: two groups of four waves of 32 rows; the groups take the even and
+//    the odd key tiles (halving the serial chain of the longest rows, two
+//    waves per SIMD so one's softmax overlaps the other's MFMAs) and merge
+//    their softmax states in LDS at the end.
+//      * S^T = K~ Q~^T on v_mfma_f32_32x32x16_bf16 (A = K~ from LDS, B = Q~
+//        held in registers for the whole key loop).  The bias rides in the
+//        extra k-step: Q~ carries c = gain * sqrt(d) * tau split as (c_hi,
+//        c_hi, c_lo), so S~ = q.k + c s_j and one multiply by
+//        alpha = log2(e) / (sqrt(d) tau) gives the logit in log2 units.
+//      * Each lane owns one query column, so the online-softmax statistics are
+//        lane-local plus one exchange between lane halves; the running max
+//        only moves when a tile raises it by more than 2^8 (lazy rescaling).
+//      * O^T = V^T P^T on v_mfma_f32_32x32x16_f16 with P taken straight from
+//        registers.  P and V are fp16 for this product: bf16 P (8-bit
+//        mantissa) costs up to ~3e-3 of output error on peaked rows on top of
+//        the bf16 output rounding.  O accumulates in fp32.
+//      * Tiles arrive by buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) one
+//        tile pair ahead into double-buffered LDS: no staging registers, no
+//        LDS store instructions, one barrier per tile pair.
+//      * Causal masking only on diagonal tiles; tiles above a wave's rows are
+//        skipped.  Heads of one KV group are pinned to one XCD (work-groups
+//        are dealt round-robin over the 8 XCDs) so its K/V stays in that L2;
+//        within an XCD the longest query tiles go first.
 #include <type_traits>
 
 #include "tg_device.h"
@@ -44,12 +50,25 @@
 namespace tg {
 namespace {
 
-constexpr int kBM = 128;     // query rows per work-group
-constexpr int kBN = 64;      // keys per tile
-constexpr int kThreads = 512;    // two groups of four waves
+constexpr int kBM = 128;       // query rows per work-group
+constexpr int kBN = 64;        // keys per tile
+constexpr int kThreads = 512;  // two groups of four waves (32 rows each)
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+template <int D, bool kBias>
+struct Tile {
+  static constexpr int KD = D + (kBias ? 16 : 0);        // K~ columns
+  static constexpr int KS = KD / 16;                      // k-steps of S^T
+  static constexpr int K_ROW = KD * 2 + 16;               // bytes, padded
+  static constexpr int K_IMG = kBN * K_ROW;
+  static constexpr int V_ROW = kBN * 2 + 16;              // bytes, padded
+  static constexpr int V_IMG = D * V_ROW;
+  static constexpr int IMG = K_IMG + V_IMG;               // one tile in LDS / workspace
+  static_assert(IMG % 1024 == 0, "tile image must be whole 1 KiB DMA chunks");
+};
+
 
 __device__ __forceinline__ floatx16 mfma_f16(f16x8 a, f16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -63,26 +82,97 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<bf16>(x));  // round to nearest even
+}
+
+// ---------------------------------------------------------------------------
+// kv_pack: one work-group per (tile, KV head).
+// ---------------------------------------------------------------------------
+template <int D, bool kBias>
+__global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ k,
+                                                      const bf16* __restrict__ v,
+                                                      const float* __restrict__ key_score, int M,
+                                                      int Hkv, char* __restrict__ ws) {
+  using T = Tile<D, kBias>;
+  const int n_tiles = (M + kBN - 1) / kBN;
+  const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+  const int tid = threadIdx.x;
+  char* img = ws + (static_cast<size_t>(kvh) * n_tiles + tile) * T::IMG;
+  const uint32_t kv_row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
+  const uint32_t kv_bytes = kv_row_bytes * static_cast<uint32_t>(M);
+  const uint32_t off0 = static_cast<uint32_t>(tile) * kBN * kv_row_bytes;
+  const uint32_t left = off0 < kv_bytes ? kv_bytes - off0 : 0u;
+
+  // K~ rows: D/8 data chunks, then (gated) the score chunk and a zero chunk,
+  // then the pad chunk.
+  {
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(reinterpret_cast<const char*>(k + static_cast<size_t>(kvh) * D) + off0, left);
+    constexpr int CHUNKS = T::K_ROW / 16;
+    for (int f = tid; f < kBN * CHUNKS; f += 256) {
+      const int row = f / CHUNKS, c = f % CHUNKS;
+      u32x4 val = zero_u32x4();
+      if (c < D / 8) {
+        val = bload16(rk, row * kv_row_bytes + 16 * c);
+      } else if (kBias && c == D / 8) {
+        const int key = tile * kBN + row;
+        const float s = key < M ? key_score[key] : 0.f;
+        const uint16_t hi = bf16_bits(s);
+        const uint16_t lo = bf16_bits(s - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+        val[0] = hi | (static_cast<uint32_t>(lo) << 16);
+        val[1] = hi;
+      }
+      st16(img + row * T::K_ROW + 16 * c, val);
+    }
+  }
+  // V^T: 4 keys x 8 dims per task; keys 4 kg + i sit at positions
+  // 16 s + 8 h' + 4 b + i with s = kg / 4, h' = (kg % 4) & 1, b = (kg % 4) >> 1.
+  {
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(reinterpret_cast<const char*>(v + static_cast<size_t>(kvh) * D) + off0, left);
+    char* vimg = img + T::K_IMG;
+    constexpr int TASKS = (kBN / 4) * (D / 8);
+    for (int f = tid; f < TASKS; f += 256) {
+      const int kg = f % 16, dc = f / 16;
+      u32x4 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = bload16(rv, (4 * kg + i) * kv_row_bytes + 16 * dc);
+      const int s = kg >> 2, j = kg & 3;
+      const int phys = 16 * s + 8 * (j & 1) + 4 * (j >> 1);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = bf16x2_to_f16x2(x[0][w]), x1 = bf16x2_to_f16x2(x[1][w]);
+        const uint32_t x2 = bf16x2_to_f16x2(x[2][w]), x3 = bf16x2_to_f16x2(x[3][w]);
+        uint2 lo, hi;  // dim 2w: low halves; dim 2w+1: high halves
+        lo.x = (x0 & 0xFFFFu) | (x1 << 16);
+        lo.y = (x2 & 0xFFFFu) | (x3 << 16);
+        hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
+        const int d0 = 8 * dc + 2 * w;
+        *reinterpret_cast<uint2*>(vimg + d0 * T::V_ROW + 2 * phys) = lo;
+        *reinterpret_cast<uint2*>(vimg + (d0 + 1) * T::V_ROW + 2 * phys) = hi;
+      }
+    }
+    for (int d = tid; d < D; d += 256) st16(vimg + d * T::V_ROW + kBN * 2, zero_u32x4());
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attn_fwd
+// ---------------------------------------------------------------------------
 template <int D, bool kBias>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const _Float16* __restrict__ vt_pack,
-    int M, int Hq, int Hkv, const float* __restrict__ key_score, const float* __restrict__ gain,
-    const float* __restrict__ tau, bf16* __restrict__ out, float* __restrict__ lse) {
-  constexpr int KSTEPS = D / 16;        // k-steps of S^T = K Q^T
-  constexpr int DT = D / 32;            // 32-row tiles of O^T
-  constexpr int K_LD = D + 8;           // K row in LDS (bf16), padded by 16 B
-  constexpr int VT_LD = kBN + 8;        // V^T row in LDS (fp16), padded by 16 B
-  constexpr int CPR = D / 8;            // 16-byte chunks per K row
-  constexpr int K_PER_T = 2 * kBN * CPR / kThreads;   // K chunks per thread per tile pair
-  constexpr int V_PER_T = 2 * D * (kBN / 8) / kThreads;  // V^T chunks per thread per pair
-  static_assert((2 * kBN * CPR) % kThreads == 0, "K tile split");
-  static_assert((2 * D * (kBN / 8)) % kThreads == 0, "V tile split");
+    const bf16* __restrict__ q, const char* __restrict__ ws, int M, int Hq, int Hkv,
+    const float* __restrict__ gain, const float* __restrict__ tau, bf16* __restrict__ out,
+    float* __restrict__ lse) {
+  using T = Tile<D, kBias>;
+  constexpr int KS = T::KS;
+  constexpr int DT = D / 32;                 // 32-row tiles of O^T
+  constexpr int N_DMA = 2 * T::IMG / 1024;   // 1 KiB DMA chunks per tile pair
+  constexpr int NW = kThreads / 64;
 
-  // [step parity][wave group] tiles; the group-1 half of k_lds is reused for
-  // the final merge of the two groups' partial results.
-  __shared__ __align__(16) bf16 k_lds[2][2][kBN * K_LD];
-  __shared__ __align__(16) _Float16 vt_lds[2][2][D * VT_LD];
-  __shared__ __align__(16) float b_lds[2][2][kBN];
+  __shared__ __align__(16) char lds[2][2][T::IMG];   // [parity][tile of the pair]
 
   // ---- work-group -> (query tile, head)
   const int n_qt = (M + kBM - 1) / kBM;
@@ -102,50 +192,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int kvh = head / (Hq / Hkv);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const int grp = wave >> 2;            // 0: even key tiles, 1: odd key tiles
+  const int grp = wave >> 2;             // 0: even key tiles, 1: odd key tiles
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int q0 = qt * kBM + (wave & 3) * 32;
+  const int q0 = qt * kBM + (wave & 3) * 32;   // first of this wave's 32 rows
   const int my_q = q0 + l32;
 
   const float t_h = kBias ? tau[head] : 1.f;
   const float alpha = kLog2e / (sqrtf(static_cast<float>(D)) * t_h);
-  const float beta = kBias ? gain[head] * kLog2e : 0.f;
 
-  const uint32_t q_row_bytes = static_cast<uint32_t>(Hq) * D * 2;
-  const uint32_t kv_row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
-  const uint32_t kv_tile_bytes = kv_row_bytes * kBN;
-  const uint32_t kv_bytes = kv_row_bytes * static_cast<uint32_t>(M);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(head) * D, q_row_bytes * M);
-  const char* k_base = reinterpret_cast<const char*>(k + static_cast<size_t>(kvh) * D);
-  // Packed V^T of this KV head: n_tiles blocks of [D][kBN] fp16.
-  const int n_tiles_all = (M + kBN - 1) / kBN;
-  const uint32_t vt_tile_bytes = D * kBN * 2;
-  const uint32_t vt_bytes = vt_tile_bytes * static_cast<uint32_t>(n_tiles_all);
-  const char* v_base = reinterpret_cast<const char*>(vt_pack) +
-                       static_cast<size_t>(kvh) * n_tiles_all * vt_tile_bytes;
-  // Per-tile-pair descriptors: base moved to the pair's first row (scalar
-  // work only), so the per-thread offsets are loop-invariant and the range
-  // check still zero-fills rows >= M.
-  auto pair_rsrc = [&](const char* base, int t0) __attribute__((always_inline)) {
-    const uint32_t off = static_cast<uint32_t>(t0) * kv_tile_bytes;
-    return make_rsrc(base + off, off < kv_bytes ? kv_bytes - off : 0u);
-  };
-  auto vt_rsrc = [&](int t0) __attribute__((always_inline)) {
-    const uint32_t off = static_cast<uint32_t>(t0) * vt_tile_bytes;
-    return make_rsrc(v_base + off, off < vt_bytes ? vt_bytes - off : 0u);
-  };
-  auto score_rsrc = [&](int t0) __attribute__((always_inline)) {
-    const uint32_t off = static_cast<uint32_t>(t0) * kBN;
-    return make_rsrc(key_score + off, off < static_cast<uint32_t>(M) ? 4u * (M - off) : 0u);
-  };
-
-  // Q fragments (B operand): lane holds Q[my_q][16 s + 8 hh .. + 7].
-  bf16x8 qf[KSTEPS];
+  // ---- Q~ fragments (B operand): lane holds Q[my_q][16 s + 8 hh .. + 7]
+  bf16x8 qf[KS];
+  {
+    const uint32_t q_row_bytes = static_cast<uint32_t>(Hq) * D * 2;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(q + static_cast<size_t>(head) * D, q_row_bytes * static_cast<uint32_t>(M));
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = as_bf16x8(bload16(rq, static_cast<uint32_t>(my_q) * q_row_bytes + (16 * s + 8 * hh) * 2));
+    for (int s = 0; s < D / 16; ++s)
+      qf[s] = as_bf16x8(bload16(rq, static_cast<uint32_t>(my_q) * q_row_bytes + (16 * s + 8 * hh) * 2));
+    if (kBias) {
+      const float c = gain[head] * sqrtf(static_cast<float>(D)) * t_h;   // gain / alpha * log2(e)
+      const uint16_t c_hi = bf16_bits(c);
+      const uint16_t c_lo = bf16_bits(c - __uint_as_float(static_cast<uint32_t>(c_hi) << 16));
+      u32x4 e = zero_u32x4();
+      if (hh == 0) {
+        e[0] = c_hi | (static_cast<uint32_t>(c_hi) << 16);
+        e[1] = c_lo;
+      }
+      qf[KS - 1] = as_bf16x8(e);
+    }
+  }
 
   floatx16 o[DT];
 #pragma unroll
@@ -156,84 +233,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int q_last = min(qt * kBM + kBM, M) - 1;
   const int n_kt = q_last / kBN + 1;                  // key tiles of the work-group
   const int n_steps = (n_kt + 1) / 2;                 // tile pairs
-  const int w_last = min(q0 + 31, q_last);            // last row this wave owns
-  const int n_vis = q0 <= q_last ? w_last / kBN + 1 : 0;  // tiles this wave sees
+  const int n_vis = q0 <= q_last ? min(q0 + 31, q_last) / kBN + 1 : 0;  // tiles this wave sees
 
-  // ---- register staging of one tile pair
-  u32x4 kreg[K_PER_T];
-  u32x4 vreg[V_PER_T];
-  float breg = 0.f;
-
-  uint32_t k_off[K_PER_T];
-#pragma unroll
-  for (int p = 0; p < K_PER_T; ++p) {
-    const int f = tid + p * kThreads;   // chunk index within the pair
-    k_off[p] = static_cast<uint32_t>(f / CPR) * kv_row_bytes + 16 * (f % CPR);
-  }
-
-  auto load_k = [&](int t0) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = pair_rsrc(k_base, t0);
-#pragma unroll
-    for (int p = 0; p < K_PER_T; ++p) kreg[p] = bload16(r, k_off[p]);
-  };
-  auto load_v = [&](int t0) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = vt_rsrc(t0);
-#pragma unroll
-    for (int p = 0; p < V_PER_T; ++p) vreg[p] = bload16(r, 16u * (tid + p * kThreads));
-    if (kBias && tid < 2 * kBN) breg = beta * bload4f(score_rsrc(t0), 4 * tid);
-  };
-  auto store_k = [&](int par) __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < K_PER_T; ++p) {
-      const int f = tid + p * kThreads;
-      const int row = f / CPR;          // 0 .. 2 kBN - 1
-      st16(&k_lds[par][row / kBN][(row % kBN) * K_LD + 8 * (f % CPR)], kreg[p]);
+  // ---- DMA of one tile pair (2 * IMG bytes) into lds[par]
+  const int n_tiles = (M + kBN - 1) / kBN;
+  const __amdgpu_buffer_rsrc_t rws =
+      make_rsrc(ws + static_cast<size_t>(kvh) * n_tiles * T::IMG,
+                static_cast<uint32_t>(n_tiles) * T::IMG);
+  auto dma_pair = [&](int par, int t0) __attribute__((always_inline)) {
+    const uint32_t base = static_cast<uint32_t>(t0) * T::IMG + 16u * lane;
+    for (int i = wave; i < N_DMA; i += NW) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rws, (__attribute__((address_space(3))) void*)(&lds[par][0][0] + 1024 * i), 16,
+          static_cast<int>(base + 1024u * i), 0, 0, 0);
     }
   };
-  auto store_v = [&](int par) __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < V_PER_T; ++p) {
-      const int f = tid + p * kThreads;          // 16-byte chunk within the pair
-      const int tp = f / (D * kBN / 8), rem = f % (D * kBN / 8);
-      st16(&vt_lds[par][tp][(rem / (kBN / 8)) * VT_LD + 8 * (rem % (kBN / 8))], vreg[p]);
-    }
-    if (kBias && tid < 2 * kBN) b_lds[par][tid / kBN][tid % kBN] = breg;
-  };
 
-  auto qk = [&](const bf16* kt_lds, floatx16* s) __attribute__((always_inline)) {
+  // ---- one 64-key tile for this wave's 32 rows; MASK (compile time) applies
+  // the causal mask, needed only on diagonal tiles.
+  auto tile = [&](auto mask_c, const char* img, int kb) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    floatx16 s[2];   // 32-key halves
     s[0] = zero16();
     s[1] = zero16();
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = lds_bf16x8(&kt_lds[(32 * t + l32) * K_LD + 16 * ks + 8 * hh]);
-        s[t] = mfma_32x32x16(a, qf[ks], s[t]);
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            img + (32 * t2 + l32) * T::K_ROW + (16 * ks + 8 * hh) * 2);
+        s[t2] = mfma_32x32x16(a, qf[ks], s[t2]);
       }
     }
-  };
-
-  // softmax of the tile held in s (in place -> probabilities), then O += P V
-  auto soft_pv = [&](const _Float16* vt, const float* bt, int kb, floatx16* s, bool mask)
-      __attribute__((always_inline)) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        float bias[4] = {0.f, 0.f, 0.f, 0.f};
-        if (kBias) {
-          const float4 b4 = *reinterpret_cast<const float4*>(&bt[32 * t + 8 * j4 + 4 * hh]);
-          bias[0] = b4.x; bias[1] = b4.y; bias[2] = b4.z; bias[3] = b4.w;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 4 * j4 + r;
-          float x = kBias ? fmaf(s[t][j], alpha, bias[r]) : s[t][j] * alpha;
-          if (mask && kb + 32 * t + 8 * j4 + 4 * hh + r > my_q) x = -INFINITY;
-          s[t][j] = x;
-          mx = fmaxf(mx, x);
-        }
+      for (int j = 0; j < 16; ++j) {
+        float x = s[t2][j] * alpha;
+        if (MASK && kb + 32 * t2 + 8 * (j >> 2) + 4 * hh + (j & 3) > my_q) x = -INFINITY;
+        s[t2][j] = x;
+        mx = fmaxf(mx, x);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -250,18 +290,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       }
     }
     float rs = 0.f;
-    uint32_t pk[2][8];
+    uint32_t pk[2][8];   // fp16 pairs of P: [32-key half][pair]
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
-        const float p0 = fast_exp2(s[t][j] - m_run);
-        const float p1 = fast_exp2(s[t][j + 1] - m_run);
+        const float p0 = fast_exp2(s[t2][j] - m_run);
+        const float p1 = fast_exp2(s[t2][j + 1] - m_run);
         rs += p0 + p1;
-        pk[t][j >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+        pk[t2][j >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
       }
     }
     l_run += rs;
+    const char* vimg = img + T::K_IMG;
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {
       const uint32_t* src = &pk[ps >> 1][4 * (ps & 1)];
@@ -269,60 +310,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       const f16x8 b = __builtin_bit_cast(f16x8, pv);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(&vt[(32 * dt + l32) * VT_LD + 16 * ps + 8 * hh]);
+        const f16x8 a = *reinterpret_cast<const f16x8*>(
+            vimg + (32 * dt + l32) * T::V_ROW + (16 * ps + 8 * hh) * 2);
         o[dt] = mfma_f16(a, b, o[dt]);
       }
     }
   };
 
-  // ---- prologue: K of tiles 0, 1 in LDS and S of this group's first tile;
-  // K of tiles 2, 3 and V of tiles 0, 1 in registers.
-  load_k(0);
-  store_k(0);
-  load_k(2);
-  load_v(0);
-  __syncthreads();
-  floatx16 s_cur[2];
-  if (grp < n_vis) qk(k_lds[0][grp], s_cur);
-
-  // One pipeline stage per tile pair: group g consumes tile 2 st + g while
-  // S of tile 2 st + 2 + g is formed from the other LDS buffer and the loads
-  // of the following pair are in flight.  One barrier per stage: a buffer
-  // written at stage st was last read at stage st - 1.
-  auto stage = [&](auto par_c, int st) __attribute__((always_inline)) {
-    constexpr int par = decltype(par_c)::value, npar = par ^ 1;
-    store_k(npar);   // K of tiles 2 st + 2, 2 st + 3
-    store_v(par);    // V (and scores) of tiles 2 st, 2 st + 1
-    __syncthreads();
-    load_k(2 * st + 4);
-    load_v(2 * st + 2);
+  // ---- main loop: one tile pair per step, one barrier per step.  The DMA
+  // issued at step st fills the parity read at step st + 1; that buffer was
+  // last read at step st - 1, which every wave finished before barrier st.
+  dma_pair(0, 0);
+  for (int st = 0; st < n_steps; ++st) {
+    const int par = st & 1;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into lds[par] has landed
+    __syncthreads();                 // ... and every other wave's
+    if (st + 1 < n_steps) dma_pair(par ^ 1, 2 * st + 2);
     const int t = 2 * st + grp;
     if (t < n_vis) {
-      const int kb = t * kBN;
-      const bool diag = kb + kBN - 1 > q0;
-      const _Float16* vt = vt_lds[par][grp];
-      const float* bt = b_lds[par][grp];
-      if (t + 2 < n_vis) {
-        floatx16 s_nxt[2];
-        qk(k_lds[npar][grp], s_nxt);
-        if (diag) soft_pv(vt, bt, kb, s_cur, true);
-        else soft_pv(vt, bt, kb, s_cur, false);
-        s_cur[0] = s_nxt[0];
-        s_cur[1] = s_nxt[1];
-      } else {
-        if (diag) soft_pv(vt, bt, kb, s_cur, true);
-        else soft_pv(vt, bt, kb, s_cur, false);
-      }
+      if (t * kBN + kBN - 1 > q0) tile(std::true_type{}, &lds[par][grp][0], t * kBN);
+      else tile(std::false_type{}, &lds[par][grp][0], t * kBN);
     }
-  };
-  for (int st = 0; st < n_steps; st += 2) {
-    stage(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < n_steps) stage(std::integral_constant<int, 1>{}, st + 1);
   }
 
   // ---- merge the two groups' partial softmax states (same query rows)
   __syncthreads();
-  float* xch = reinterpret_cast<float*>(&k_lds[0][0][0]) + ((wave & 3) * 64 + lane) * (16 * DT + 2);
+  constexpr int XU = 16 * DT + 2;         // floats per lane
+  float* xch = reinterpret_cast<float*>(&lds[0][0][0]) + ((wave & 3) * 64 + lane) * XU;
   if (grp == 1) {
 #pragma unroll
     for (int i = 0; i < DT; ++i) {
@@ -334,20 +348,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   }
   __syncthreads();
   if (grp == 1) return;
-  {
-    const float m1 = xch[16 * DT], l1 = xch[16 * DT + 1];
-    const float m = fmaxf(m_run, m1);
-    const float c0 = fast_exp2(m_run - m), c1 = fast_exp2(m1 - m);
+  const float m1 = xch[16 * DT], l1 = xch[16 * DT + 1];
+  const float m = fmaxf(m_run, m1);
+  const float c0 = fast_exp2(m_run - m), c1 = fast_exp2(m1 - m);
 #pragma unroll
-    for (int i = 0; i < DT; ++i) {
+  for (int i = 0; i < DT; ++i) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) o[i][j] = o[i][j] * c0 + xch[16 * i + j] * c1;
-    }
-    l_run = l_run * c0 + l1 * c1;
-    m_run = m;
+    for (int j = 0; j < 16; ++j) o[i][j] = o[i][j] * c0 + xch[16 * i + j] * c1;
   }
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l = l_run * c0 + l1 * c1;
+  const float l_tot = l + __shfl_xor(l, 32);
   if (my_q < M) {
     const float inv = 1.f / l_tot;
     bf16* orow = out + static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
@@ -355,57 +365,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        bf16 pk[4];
+        bf16 pkk[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pk[r] = static_cast<bf16>(o[dt][4 * jj + r] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * jj + 4 * hh) = __builtin_bit_cast(uint2, pk);
+        for (int r = 0; r < 4; ++r) pkk[r] = static_cast<bf16>(o[dt][4 * jj + r] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * jj + 4 * hh) = __builtin_bit_cast(uint2, pkk);
       }
     }
     if (lse != nullptr && hh == 0)
-      lse[static_cast<size_t>(head) * M + my_q] = (m_run + __log2f(l_tot)) * kLn2;
-  }
-}
-
-// V -> packed V^T: for each KV head and each 64-key tile, a [D][64] fp16 block
-// whose key order inside each 16-key group is permuted so that every lane's
-// eight keys of a P.V step are one contiguous 16-byte run.  Keys >= M are
-// zero.  One work-group per (tile, KV head); each thread moves 4 keys x 8 dims.
-template <int D>
-__global__ __launch_bounds__(256) void v_pack_kernel(const bf16* __restrict__ v, int M, int Hkv,
-                                                     _Float16* __restrict__ vt_pack) {
-  constexpr int CPR = D / 8;
-  constexpr int TASKS = (kBN / 4) * CPR;
-  const int n_tiles = (M + kBN - 1) / kBN;
-  const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
-  const int tid = threadIdx.x;
-  if (tid >= TASKS) return;
-  const int kg = tid % 16, dc = tid / 16;
-  const uint32_t kv_row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
-  const uint32_t kv_bytes = kv_row_bytes * static_cast<uint32_t>(M);
-  const uint32_t off0 = static_cast<uint32_t>(tile) * kBN * kv_row_bytes;
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(
-      reinterpret_cast<const char*>(v + static_cast<size_t>(kvh) * D) + off0,
-      off0 < kv_bytes ? kv_bytes - off0 : 0u);
-  u32x4 x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = bload16(r, (4 * kg + i) * kv_row_bytes + 16 * dc);
-  // keys 4 kg + i sit at positions 16 s + 8 h' + 4 b + i, with
-  // s = kg / 4, h' = (kg % 4) & 1, b = (kg % 4) >> 1.
-  const int s = kg >> 2, j = kg & 3;
-  const int phys = 16 * s + 8 * (j & 1) + 4 * (j >> 1);
-  _Float16* dst = vt_pack + (static_cast<size_t>(kvh) * n_tiles + tile) * D * kBN;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t x0 = bf16x2_to_f16x2(x[0][w]), x1 = bf16x2_to_f16x2(x[1][w]);
-    const uint32_t x2 = bf16x2_to_f16x2(x[2][w]), x3 = bf16x2_to_f16x2(x[3][w]);
-    uint2 lo, hi;  // dim 2w: low halves; dim 2w+1: high halves
-    lo.x = (x0 & 0xFFFFu) | (x1 << 16);
-    lo.y = (x2 & 0xFFFFu) | (x3 << 16);
-    hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
-    hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
-    const int d0 = 8 * dc + 2 * w;
-    *reinterpret_cast<uint2*>(&dst[d0 * kBN + phys]) = lo;
-    *reinterpret_cast<uint2*>(&dst[(d0 + 1) * kBN + phys]) = hi;
+      lse[static_cast<size_t>(head) * M + my_q] = (m + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -414,22 +381,26 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M
                   const float* s, const float* g, const float* t, uint16_t* out, float* lse,
                   void* ws, hipStream_t stream) {
   const int n_tiles = (M + kBN - 1) / kBN;
-  _Float16* vt = static_cast<_Float16*>(ws);
-  hipLaunchKernelGGL((v_pack_kernel<D>), dim3(static_cast<unsigned>(n_tiles * Hkv)), dim3(256), 0,
-                     stream, reinterpret_cast<const bf16*>(v), M, Hkv, vt);
+  char* img = static_cast<char*>(ws);
+  hipLaunchKernelGGL((kv_pack_kernel<D, kBias>), dim3(static_cast<unsigned>(n_tiles * Hkv)),
+                     dim3(256), 0, stream, reinterpret_cast<const bf16*>(k),
+                     reinterpret_cast<const bf16*>(v), s, M, Hkv, img);
   const int n_qt = (M + kBM - 1) / kBM;
   const dim3 grid(static_cast<unsigned>(n_qt) * static_cast<unsigned>(Hq));
   hipLaunchKernelGGL((attn_fwd_kernel<D, kBias>), grid, dim3(kThreads), 0, stream,
-                     reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k), vt, M, Hq,
-                     Hkv, s, g, t, reinterpret_cast<bf16*>(out), lse);
+                     reinterpret_cast<const bf16*>(q), img, M, Hq, Hkv, g, t,
+                     reinterpret_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t attn_workspace_bytes(int64_t n, int n_kv_heads, int head_dim) {
+size_t attn_workspace_bytes(int64_t n, int n_kv_heads, int head_dim, bool gated) {
   const int64_t n_tiles = (n + kBN - 1) / kBN;
-  return static_cast<size_t>(n_tiles) * kBN * n_kv_heads * head_dim * 2;
+  int64_t img;
+  if (head_dim == 128) img = gated ? Tile<128, true>::IMG : Tile<128, false>::IMG;
+  else img = gated ? Tile<64, true>::IMG : Tile<64, false>::IMG;
+  return static_cast<size_t>(n_tiles * n_kv_heads * img);
 }
 
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,

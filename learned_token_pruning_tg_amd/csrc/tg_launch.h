@@ -18,8 +18,9 @@ hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, const void* s
                           int64_t src_rows, int64_t src_stride, int64_t row_bytes, void* dst,
                           int64_t dst_stride, hipStream_t stream);
 
-// Bytes of the packed-V^T scratch the attention launch needs.
-size_t attn_workspace_bytes(int64_t n, int n_kv_heads, int head_dim);
+// Bytes of the packed K~ / V^T tile scratch the attention launch needs
+// (gated: with the score columns; else without).
+size_t attn_workspace_bytes(int64_t n, int n_kv_heads, int head_dim, bool gated);
 
 // gain == nullptr selects the unbiased (full-prefill) kernel with tau = 1.
 // `workspace` holds attn_workspace_bytes(n, n_kv_heads, head_dim) bytes.
