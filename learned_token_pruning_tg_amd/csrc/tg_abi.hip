@@ -44,7 +44,7 @@ tg_status check_attn(const char* fn, const tg_bf16* q, const tg_bf16* k, const t
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(TG_E_INVALID, "%s: q/k/v/out must be 16-byte aligned", fn);
   const size_t need = tg::attn_workspace_bytes(n, hkv, d, gated);
-  if (need >= (size_t(1) << 32) / hkv)
+  if (need / hkv >= (size_t(1) << 32))
     return fail(TG_E_UNSUPPORTED, "%s: n=%lld needs %zu workspace bytes (limit 2^32 per KV head)",
                 fn, (long long)n, need);
   if (!ws || ws_bytes < need || !aligned16(ws))

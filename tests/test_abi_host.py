@@ -119,7 +119,8 @@ def test_attention_validation(L):
     assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, A, W, 0) == UNSUPPORTED  # 2^31-byte offsets
     need = L.tg_attn_workspace_bytes(100, 8, 128)
     assert need == 2 * 8 * (64 * (2 * 144 + 16) + 128 * 144)   # 2 tiles x 8 heads x image
-    assert full(A, A, A, 100, 16, 8, 128, A, None, A, need - 1, 0) == WORKSPACE
+    assert g(A, A, A, 100, 16, 8, 128, A, A, A, A, None, A, need - 1, 0) == WORKSPACE
+    assert full(A, A, A, 100, 16, 8, 128, A, None, A, 1000, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, None, need, 0) == WORKSPACE
     assert g(A, A, A, 100, 16, 8, 128, A, A, A, A, None, A + 4, need, 0) == WORKSPACE
     assert "workspace" in tg.last_error()
