@@ -4,7 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/tg.h"
+#include "tg.h"
 #include "tg_launch.h"
 
 namespace {

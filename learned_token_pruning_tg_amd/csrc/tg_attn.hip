@@ -320,11 +320,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   // ---- main loop: one tile pair per step, one barrier per step.  The DMA
   // issued at step st fills the parity read at step st + 1; that buffer was
   // last read at step st - 1, which every wave finished before barrier st.
+  // The two waves sharing a SIMD (one per group) leave each barrier in the
+  // same phase; raising one group's priority (alternating per step) lets its
+  // MFMAs run first while the other wave's softmax fills the VALU slots.
   dma_pair(0, 0);
   for (int st = 0; st < n_steps; ++st) {
     const int par = st & 1;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into lds[par] has landed
     __syncthreads();                 // ... and every other wave's
+    if (grp == par) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     if (st + 1 < n_steps) dma_pair(par ^ 1, 2 * st + 2);
     const int t = 2 * st + grp;
     if (t < n_vis) {
@@ -334,6 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   }
 
   // ---- merge the two groups' partial softmax states (same query rows)
+  __builtin_amdgcn_s_setprio(0);
   __syncthreads();
   constexpr int XU = 16 * DT + 2;         // floats per lane
   float* xch = reinterpret_cast<float*>(&lds[0][0][0]) + ((wave & 3) * 64 + lane) * XU;
