@@ -35,7 +35,90 @@ def _parse():
     p.add_argument("--no-full-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 64 MiB copy (tg_compact with identity indices) so a "
+                        "PMC run can scale FETCH_SIZE / WRITE_SIZE")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
+                        "into the traffic record under profiles/, then exit")
+    p.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
     return p.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ATTN_SRC = os.path.join(ROOT, "learned_token_pruning_tg_amd", "csrc", "tg_attn.hip")
+COPY_BYTES = 64 << 20   # the calibration copy moves exactly this many bytes each way
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"tg_gated_attn_fwd.{workload}.traffic.json")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -> None:
+    """Per-dispatch HBM bytes of the gated-attention launch (pack + attention
+    kernels), each counter scaled by what it reads for the known-size copy."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += [r for r in csv.DictReader(open(f)) if r["Counter_Name"] == counter]
+        return rows
+
+    def kib(rows, pred):
+        vals = [float(r["Counter_Value"]) for r in rows if pred(r["Kernel_Name"])]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    is_attn = lambda n: "attn_fwd_kernel" in n and "ELb1E" in n
+    is_pack = lambda n: "kv_pack_kernel<128, true>" in n or ("kv_pack_kernel" in n and "ELb1E" in n)
+    out = {"workload": workload, "kernel_source_sha256_16": attn_source_hash(), "command": command}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = load(d, counter)
+        # the calibration copy is the compact kernel whose value is the largest
+        copies = [float(r["Counter_Value"]) for r in rows if "compact_wide_kernel" in r["Kernel_Name"]]
+        copy_kib = max(copies) if copies else None
+        scale = COPY_BYTES / (copy_kib * 1024.0) if copy_kib else None
+        a, na = kib(rows, is_attn)
+        pk, npk = kib(rows, is_pack)
+        out[counter] = {"copy_kib": copy_kib, "scale": scale, "attn_kib": a, "attn_dispatches": na,
+                        "pack_kib": pk, "pack_dispatches": npk,
+                        "bytes_per_launch": (a + pk) * 1024.0 * scale if scale and a and pk else None}
+    f, w_ = out["FETCH_SIZE"]["bytes_per_launch"], out["WRITE_SIZE"]["bytes_per_launch"]
+    out["traffic_bytes_per_launch"] = f + w_ if f is not None and w_ is not None else None
+    path = traffic_path(workload)
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    with open(path.replace(".json", ".md"), "w") as fh:
+        fh.write(f"# HBM traffic of tg_gated_attn_fwd on {workload}\n\n")
+        fh.write(f"Command (each counter in its own run):\n\n    {command}\n\n")
+        fh.write("| counter | copy reads (KiB) | scale | pack KiB/dispatch | attention KiB/dispatch | bytes per launch |\n")
+        fh.write("|---|---|---|---|---|---|\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            r = out[c]
+            fh.write(f"| {c} | {r['copy_kib']} | {r['scale']} | {r['pack_kib']} | {r['attn_kib']} | "
+                     f"{r['bytes_per_launch']} |\n")
+        fh.write(f"\nTotal HBM bytes per launch: {out['traffic_bytes_per_launch']}\n")
+        fh.write(f"Kernel source sha256[:16]: {out['kernel_source_sha256_16']}\n")
+    print(json.dumps(out))
+
+
+def load_traffic(workload: str):
+    """Measured traffic if it was taken on the current kernel source, else None."""
+    try:
+        with open(traffic_path(workload)) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != attn_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def attn_flops(m: int, hq: int, d: int) -> float:
@@ -46,6 +129,9 @@ def attn_flops(m: int, hq: int, d: int) -> float:
 
 def main():
     args = _parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design, not a measured path.", file=sys.stderr)
@@ -175,6 +261,14 @@ def main():
         }
         del fout, fws
 
+    if args.copy_calibration:
+        src = h.view(torch.uint8).view(-1)[:COPY_BYTES].view(-1, 4096)
+        ident = torch.arange(src.shape[0], dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        tg.compact(ident, src, out=dst)
+        torch.cuda.synchronize()
+        del src, ident, dst
+
     # ---------------------------------------------------------------- rooflines
     fl = attn_flops(m, w.n_q_heads, w.head_dim)
     achieved = fl / (attn_ms_launch / 1e3) / 1e12
@@ -213,10 +307,10 @@ def main():
                    "kept_rows": m, "upper_layers": w.n_layers, "hidden": w.hidden,
                    "gate_hidden": w.gate_hidden, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "parallelism": "single-gpu"},
-        "roofline": {"kernel": "tg_gated_attn_fwd", "bound": "mfma",
+        "roofline": {"kernel": "tg_gated_attn_fwd (kv_pack + attn_fwd kernels)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": load_traffic(w.name),
                      "flops_per_launch": fl, "avg_launch_ms": round(attn_ms_launch, 5)},
         "stages": stages,
         "full_prefill_baseline": full,
