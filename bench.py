@@ -47,7 +47,7 @@ def _parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SRC = os.path.join(ROOT, "learned_token_pruning_tg_amd", "csrc", "tg_attn.hip")
-COPY_BYTES = 64 << 20   # the calibration copy moves exactly this many bytes each way
+COPY_BYTES = 256 << 20  # the calibration copy moves exactly this many bytes each way
 
 
 def traffic_path(workload: str) -> str:
@@ -262,12 +262,16 @@ def main():
         del fout, fws
 
     if args.copy_calibration:
-        src = h.view(torch.uint8).view(-1)[:COPY_BYTES].view(-1, 4096)
+        # A cold copy: the source is filled, then an equally large buffer is
+        # filled to push it out of L2, then the source is copied row by row.
+        src = torch.empty((COPY_BYTES // 4096, 4096), dtype=torch.uint8, device=dev).fill_(1)
+        evict = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(2)
         ident = torch.arange(src.shape[0], dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         tg.compact(ident, src, out=dst)
         torch.cuda.synchronize()
-        del src, ident, dst
+        del src, evict, ident, dst
 
     # ---------------------------------------------------------------- rooflines
     fl = attn_flops(m, w.n_q_heads, w.head_dim)
