@@ -173,7 +173,7 @@ def main():
     s_kept = torch.empty(m, dtype=torch.float32, device=dev)
     outs = [torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
             for _ in range(2)]
-    ws = tg.attn_workspace(m, w.n_kv_heads, w.head_dim, dev)
+    ws = tg.attn_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
     # The upper layers' q/k/v of the kept rows stand for what the layers'
     # projections would produce from the kept residual; they are gathered
     # once from the full-N templates with the selection of this very input.
@@ -229,7 +229,7 @@ def main():
     full = None
     if not args.no_full_baseline:
         fout = torch.empty((w.n, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-        fws = tg.attn_workspace(w.n, w.n_kv_heads, w.head_dim, dev)
+        fws = tg.attn_workspace(w.n, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
 
         def full_step():
             for l in range(w.n_layers):

@@ -126,12 +126,17 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
 
 /*
  * Bytes of device workspace tg_gated_attn_fwd / tg_full_attn_fwd need for n
- * rows (enough for either): per KV head and 64-key tile, a packed copy of K
- * (bf16, with the key scores appended) and of V (fp16, transposed), laid out
- * as the kernel's LDS image -- about 2.3x the bytes of K and V.  Host-only
- * arithmetic; 0 for unsupported head_dim.
+ * rows (enough for either):
+ *   - per KV head and 64-key tile, a packed copy of K (bf16, with the key
+ *     scores appended) and of V (fp16, transposed), laid out as the kernel's
+ *     LDS image -- about 2.3x the bytes of K and V;
+ *   - when n is short enough that long query blocks are split over several
+ *     work-groups along the keys: one counter per split block and one
+ *     partial state (fp16 output, fp32 max and sum; 34 KiB at head_dim 128)
+ *     per split work-group.
+ * Host-only arithmetic; 0 for n <= 0 or unsupported heads / head_dim.
  */
-size_t tg_attn_workspace_bytes(int64_t n, int32_t n_kv_heads, int32_t head_dim);
+size_t tg_attn_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim);
 
 /*
  * Token-gated causal GQA attention over the n kept rows (lucasainews.com
@@ -156,7 +161,9 @@ size_t tg_attn_workspace_bytes(int64_t n, int32_t n_kv_heads, int32_t head_dim);
  * n * n_q_heads * head_dim * 2 < 2^31 (byte offsets fit 31 bits).
  * Numerics: q.k as bf16 products with fp32 accumulation; softmax in fp32;
  * probabilities and v rounded to fp16 for the p.v product (v magnitudes above
- * 65504 saturate), fp32 accumulation.  n == 0 is a no-op.
+ * 65504 saturate), fp32 accumulation; where a query block is split along the
+ * keys, each part's normalised output is rounded to fp16 before the merge.
+ * n == 0 is a no-op.
  */
 tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

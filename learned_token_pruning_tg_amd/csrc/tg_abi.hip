@@ -43,10 +43,11 @@ tg_status check_attn(const char* fn, const tg_bf16* q, const tg_bf16* k, const t
   if (!q || !k || !v || !out) return fail(TG_E_INVALID, "%s: null tensor pointer", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(TG_E_INVALID, "%s: q/k/v/out must be 16-byte aligned", fn);
-  const size_t need = tg::attn_workspace_bytes(n, hkv, d, gated);
-  if (need / hkv >= (size_t(1) << 32))
-    return fail(TG_E_UNSUPPORTED, "%s: n=%lld needs %zu workspace bytes (limit 2^32 per KV head)",
-                fn, (long long)n, need);
+  const size_t per_head = tg::attn_image_bytes_per_kv_head(n, d, gated);
+  if (per_head >= (size_t(1) << 32))
+    return fail(TG_E_UNSUPPORTED, "%s: n=%lld needs %zu tile-image bytes per KV head (limit 2^32)",
+                fn, (long long)n, per_head);
+  const size_t need = tg::attn_workspace_bytes(n, hq, hkv, d, gated);
   if (!ws || ws_bytes < need || !aligned16(ws))
     return fail(TG_E_WORKSPACE, "%s: workspace %p of %zu bytes (need %zu, 16-byte aligned)", fn, ws,
                 ws_bytes, need);
@@ -130,9 +131,11 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
                     "tg_compact launch");
 }
 
-size_t tg_attn_workspace_bytes(int64_t n, int32_t n_kv_heads, int32_t head_dim) {
-  if (n <= 0 || n_kv_heads <= 0 || (head_dim != 64 && head_dim != 128)) return 0;
-  return tg::attn_workspace_bytes(n, n_kv_heads, head_dim, true);
+size_t tg_attn_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+  if (n <= 0 || n >= (int64_t(1) << 31) || n_q_heads <= 0 || n_kv_heads <= 0 ||
+      n_q_heads % n_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
+    return 0;
+  return tg::attn_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim, true);
 }
 
 tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,

@@ -18,12 +18,16 @@ hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, const void* s
                           int64_t src_rows, int64_t src_stride, int64_t row_bytes, void* dst,
                           int64_t dst_stride, hipStream_t stream);
 
-// Bytes of the packed K~ / V^T tile scratch the attention launch needs
-// (gated: with the score columns; else without).
-size_t attn_workspace_bytes(int64_t n, int n_kv_heads, int head_dim, bool gated);
+// Bytes of workspace the attention launch needs (gated: K~ with the score
+// columns; else without): the packed K~ / V^T tile images, the split-key
+// counters and the split chunks' partial states.
+size_t attn_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_dim, bool gated);
+
+// Bytes of the tile images of one KV head (addressed with 32-bit offsets).
+size_t attn_image_bytes_per_kv_head(int64_t n, int head_dim, bool gated);
 
 // gain == nullptr selects the unbiased (full-prefill) kernel with tau = 1.
-// `workspace` holds attn_workspace_bytes(n, n_kv_heads, head_dim) bytes.
+// `workspace` holds attn_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim, gated) bytes.
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
                            int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
                            const float* gain, const float* tau, uint16_t* out, float* lse,

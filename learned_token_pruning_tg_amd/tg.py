@@ -29,7 +29,7 @@ _SIGNATURES = {
     "tg_gate_score": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, ctypes.c_float, _I32, _P, _P]),
     "tg_topk_select": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
     "tg_compact": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P]),
-    "tg_attn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32]),
+    "tg_attn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
     "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                          _P, ctypes.c_size_t, _P]),
     "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
@@ -166,19 +166,20 @@ def compact(idx: torch.Tensor, src: torch.Tensor, out: Optional[torch.Tensor] = 
     return out
 
 
-def attn_workspace_bytes(n: int, n_kv_heads: int, head_dim: int) -> int:
-    return int(lib().tg_attn_workspace_bytes(n, n_kv_heads, head_dim))
+def attn_workspace_bytes(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    return int(lib().tg_attn_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim))
 
 
-def attn_workspace(n: int, n_kv_heads: int, head_dim: int, device="cuda") -> torch.Tensor:
+def attn_workspace(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                   device="cuda") -> torch.Tensor:
     """A device buffer large enough for one attention call over n rows."""
-    return torch.empty(max(attn_workspace_bytes(n, n_kv_heads, head_dim), 16), dtype=torch.uint8,
-                       device=device)
+    return torch.empty(max(attn_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim), 16),
+                       dtype=torch.uint8, device=device)
 
 
-def _workspace(ws, n, hkv, d, device):
+def _workspace(ws, n, hq, hkv, d, device):
     if ws is None:
-        ws = attn_workspace(n, hkv, d, device)
+        ws = attn_workspace(n, hq, hkv, d, device)
     if not ws.is_cuda or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     return ws, ws.numel() * ws.element_size()
@@ -214,7 +215,7 @@ def gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score:
             or gain.shape != (hq,) or tau.shape != (hq,):
         raise ValueError("attention operand shapes do not match")
     out, lse = _attn_out(q, out, lse, want_lse)
-    ws, ws_bytes = _workspace(workspace, n, hkv, d, q.device)
+    ws, ws_bytes = _workspace(workspace, n, hq, hkv, d, q.device)
     _check(lib().tg_gated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(key_score),
                                    _ptr(gain), _ptr(tau), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
                                    _stream(stream)))
@@ -232,7 +233,7 @@ def full_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if k.shape != (n, hkv, d) or v.shape != k.shape:
         raise ValueError("attention operand shapes do not match")
     out, lse = _attn_out(q, out, lse, want_lse)
-    ws, ws_bytes = _workspace(workspace, n, hkv, d, q.device)
+    ws, ws_bytes = _workspace(workspace, n, hq, hkv, d, q.device)
     _check(lib().tg_full_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(out), _ptr(lse),
                                   _ptr(ws), ws_bytes, _stream(stream)))
     return (out, lse) if lse is not None else out

@@ -117,7 +117,7 @@ def test_attention_validation(L):
     assert full(A, A, None, 10, 16, 8, 128, A, None, A, W, 0) == INVALID
     assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, A, W, 0) == UNSUPPORTED
     assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, A, W, 0) == UNSUPPORTED  # 2^31-byte offsets
-    need = L.tg_attn_workspace_bytes(100, 8, 128)
+    need = L.tg_attn_workspace_bytes(100, 16, 8, 128)
     assert need == 2 * 8 * (64 * (2 * 144 + 16) + 128 * 144)   # 2 tiles x 8 heads x image
     assert g(A, A, A, 100, 16, 8, 128, A, A, A, A, None, A, need - 1, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, A, 1000, 0) == WORKSPACE
@@ -126,7 +126,40 @@ def test_attention_validation(L):
     assert "workspace" in tg.last_error()
     assert g(None, None, None, 0, 16, 8, 128, None, None, None, None, None, None, 0, 0) == OK
     assert full(None, None, None, 0, 16, 8, 128, None, None, None, 0, 0) == OK
-    assert L.tg_attn_workspace_bytes(0, 8, 128) == 0
+    assert L.tg_attn_workspace_bytes(0, 16, 8, 128) == 0
+    assert L.tg_attn_workspace_bytes(100, 16, 6, 128) == 0
+    assert L.tg_attn_workspace_bytes(100, 16, 8, 96) == 0
+
+
+def _split_layout(n, hq, hkv, d, gated=True):
+    """Workspace bytes restated from the split-key rule: 128-row query
+    blocks, 64-key tiles, 512 resident work-groups; block qt is cut into
+    ceil((qt + 1) / h) chunks of 2h tiles when its 2 n_qt-tile loop exceeds
+    the average per work-group."""
+    import math
+    n_qt, n_tiles = -(-n // 128), -(-n // 64)
+    avg = hq * n_qt * (n_qt + 1) / 512
+    h = n_qt
+    if 2 * n_qt > avg:
+        h = max(4, math.ceil(avg / 2))
+    h = min(h, n_qt)
+    units = sum(-(-(qt + 1) // h) for qt in range(n_qt))
+    kd = d + (16 if gated else 0)
+    img = 64 * (2 * kd + 16) + d * 144
+    n_part = units - h
+    part = 4 * (64 * d + 512)
+    return n_tiles * hkv * img + hq * n_part * part, h, units
+
+
+@pytest.mark.parametrize("n,hq,hkv,d", [(2304, 16, 8, 128), (1000, 2, 1, 128), (1280, 16, 8, 64),
+                                         (8448, 16, 8, 128), (700, 4, 2, 64), (64, 1, 1, 128)])
+def test_attention_workspace_split_layout(L, n, hq, hkv, d):
+    want, h, units = _split_layout(n, hq, hkv, d)
+    assert L.tg_attn_workspace_bytes(n, hq, hkv, d) == want
+    if (n, hq) == (2304, 16):
+        assert (h, units) == (6, 36)          # the 16k-context kept prefix splits three ways
+    if (n, hq) == (8448, 16):
+        assert h == -(-8448 // 128)           # long prefixes: no split
 
 
 def test_missing_library_fails_loudly(monkeypatch):
