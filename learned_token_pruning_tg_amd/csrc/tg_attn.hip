@@ -63,14 +63,17 @@
 namespace tg {
 namespace {
 
-constexpr int kBM = 128;       // query rows per work-group
-constexpr int kBN = 64;        // keys per tile
-constexpr int kThreads = 256;  // four waves of 32 rows
-constexpr int kSlots = 512;    // resident work-groups: 256 CUs x 2
-constexpr int kMinHalf = 4;    // chunks are at least 8 key tiles
+constexpr int kSets = 1;                  // 32-row query sets per wave (2 spills at d = 128)
+constexpr int kBM = 128 * kSets;          // query rows per work-group
+constexpr int kBN = 64;                   // keys per tile
+constexpr int kThreads = 256;             // four waves of 32 * kSets rows
+constexpr int kSlots = 512 / kSets;       // resident work-groups: 2 / kSets per CU
+constexpr int kTilesPerQt = kBM / kBN;
+constexpr int kMinChunk = 8 / kTilesPerQt;   // chunks are at least 8 key tiles
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __fp16 f16x2 __attribute__((ext_vector_type(2)));   // cvt_pkrtz / fdot2 operand type
 
 template <int D, bool kBias>
 struct Tile {
@@ -81,12 +84,14 @@ struct Tile {
   static constexpr int V_ROW = kBN * 2 + 16;              // bytes, padded
   static constexpr int V_IMG = D * V_ROW;
   static constexpr int IMG = K_IMG + V_IMG;               // one tile in LDS / workspace
-  static_assert(IMG % 1024 == 0, "tile image must be whole 1 KiB DMA chunks");
-  // One split chunk's partial state: per wave, the lane-major fp16 output
-  // (D bytes per lane in 16-byte vectors) and a (max, sum) pair per lane.
+  static_assert(K_IMG % 1024 == 0 && V_IMG % 1024 == 0,
+                "K~ and V^T images must be whole 1 KiB DMA chunks");
+  // One split chunk's partial state: per 32-row set (two per wave), the
+  // lane-major fp16 output (D bytes per lane in 16-byte vectors) and a
+  // (max, sum) pair per lane.
   static constexpr int PART_O = D * 64;
-  static constexpr int PART_WAVE = PART_O + 8 * 64;
-  static constexpr int PART = 4 * PART_WAVE;
+  static constexpr int PART_SET = PART_O + 8 * 64;
+  static constexpr int PART = 4 * kSets * PART_SET;
 };
 
 // Work-groups of one head before query tile q when query tile i has
@@ -96,11 +101,10 @@ __host__ __device__ __forceinline__ int64_t units_before(int64_t q, int64_t h) {
   return h * a * (a + 1) / 2 + r * (a + 1);
 }
 
-// Chunk half-length h (chunks are 2h key tiles): no split (h = n_qt) unless
-// the longest query tile (2 n_qt key tiles) exceeds the average number of
-// tile steps per resident work-group; then chunks of about that average, but
-// no shorter than 2 kMinHalf tiles (each split chunk pays a partial-state
-// round trip).
+// Query tile qt walks kTilesPerQt * (qt + 1) key tiles (fewer on a ragged
+// last tile).  Split chunks are kTilesPerQt * h key tiles, h query tiles'
+// worth, so query tile qt has ceil((qt + 1) / h) chunks (also on a ragged last
+// tile) and h = n_qt means no split.
 struct Plan {
   int n_qt, n_tiles, h;
   int64_t units;       // work-groups per head
@@ -109,16 +113,28 @@ struct Plan {
   size_t img_bytes, part_off, total;
 };
 
+// Chunk parameter h: no split unless the longest query tile's walk exceeds
+// the average number of tile steps per resident work-group; then chunks of
+// about that average, never shorter than 8 key tiles (each split chunk pays a
+// partial-state round trip).  A dispatch-simulation choice of h was tried and
+// measured slower at the 16k workload (more, shorter chunks: more partial
+// traffic and merge time than the better balance saved).
+int choose_h(int n_qt, int Hq) {
+  const double steps = static_cast<double>(kTilesPerQt) * n_qt * (n_qt + 1) / 2;
+  const double avg = static_cast<double>(Hq) * steps / kSlots;
+  int64_t h = n_qt;
+  if (static_cast<double>(kTilesPerQt) * n_qt > avg)
+    h = std::max<int64_t>(kMinChunk, static_cast<int64_t>(std::ceil(avg / kTilesPerQt)));
+  return static_cast<int>(std::max<int64_t>(std::min<int64_t>(h, n_qt), 1));
+}
+
 template <int D, bool kBias>
 Plan make_plan(int64_t M, int Hq, int Hkv) {
   using T = Tile<D, kBias>;
   Plan p{};
   p.n_qt = static_cast<int>((M + kBM - 1) / kBM);
   p.n_tiles = static_cast<int>((M + kBN - 1) / kBN);
-  const double avg = static_cast<double>(Hq) * p.n_qt * (p.n_qt + 1) / kSlots;
-  int64_t h = p.n_qt;
-  if (2.0 * p.n_qt > avg) h = std::max<int64_t>(kMinHalf, static_cast<int64_t>(std::ceil(avg / 2.0)));
-  if (h >= p.n_qt) h = std::max(p.n_qt, 1);
+  const int64_t h = choose_h(p.n_qt, Hq);
   p.h = static_cast<int>(h);
   p.units = units_before(p.n_qt, h);
   p.n_split = std::max<int64_t>(p.n_qt - h, 0);
@@ -128,6 +144,7 @@ Plan make_plan(int64_t M, int Hq, int Hkv) {
   p.total = p.part_off + static_cast<size_t>(Hq) * p.n_part * T::PART;
   return p;
 }
+
 __device__ __forceinline__ floatx16 mfma_f16(f16x8 a, f16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -261,18 +278,22 @@ __device__ __forceinline__ void store_out(const floatx16 (&o)[D / 32], float m, 
 // attn_fwd
 // ---------------------------------------------------------------------------
 template <int D, bool kBias>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
     const bf16* __restrict__ q, const char* __restrict__ ws, int M, int Hq, int Hkv,
     const float* __restrict__ gain, const float* __restrict__ tau, bf16* __restrict__ out,
     float* __restrict__ lse, int h, int units, char* __restrict__ part) {
   using T = Tile<D, kBias>;
   constexpr int KS = T::KS;
-  constexpr int DT = D / 32;             // 32-row tiles of O^T
-  constexpr int N_DMA = T::IMG / 1024;   // 1 KiB DMA chunks per tile
+  constexpr int DT = D / 32;                 // 32-row tiles of O^T
   constexpr int NW = kThreads / 64;
-  constexpr int NV = DT * 2;             // 16-byte fp16 vectors of partial output per lane
+  constexpr int NV = DT * 2;                 // 16-byte fp16 vectors of partial output per lane
+  constexpr int N_DMA_K = T::K_IMG / 1024;   // 1 KiB DMA chunks per K~ image
+  constexpr int N_DMA_V = T::V_IMG / 1024;   // ... per V^T image
 
-  __shared__ __align__(16) char lds[2][T::IMG];
+  // K~ ring runs one tile ahead of the V^T ring: step t reads K~(t+1) and
+  // V^T(t) while K~(t+2) and V^T(t+1) land.
+  __shared__ __align__(16) char lds_k[2][T::K_IMG];
+  __shared__ __align__(16) char lds_v[2][T::V_IMG];
 
   // ---- work-group -> (head, unit); unit -> (query tile, chunk)
   const int n_qt = (M + kBM - 1) / kBM;
@@ -309,21 +330,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int q0 = qt * kBM + wave * 32;   // first of this wave's 32 rows
-  const int my_q = q0 + l32;
+  const int q0 = qt * kBM + wave * 32 * kSets;   // first of this wave's rows
+  int my_q[kSets];   // this lane's query in each set
+#pragma unroll
+  for (int r = 0; r < kSets; ++r) my_q[r] = q0 + 32 * r + l32;
 
   const float t_h = kBias ? tau[head] : 1.f;
   const float alpha = kLog2e / (sqrtf(static_cast<float>(D)) * t_h);
 
   // ---- Q~ fragments (B operand): lane holds Q[my_q][16 s + 8 hh .. + 7]
-  bf16x8 qf[KS];
+  bf16x8 qf[kSets][KS];
   {
     const uint32_t q_row_bytes = static_cast<uint32_t>(Hq) * D * 2;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(q + static_cast<size_t>(head) * D, q_row_bytes * static_cast<uint32_t>(M));
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf[s] = as_bf16x8(bload16(rq, static_cast<uint32_t>(my_q) * q_row_bytes + (16 * s + 8 * hh) * 2));
+    for (int r = 0; r < kSets; ++r) {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        qf[r][s] = as_bf16x8(
+            bload16(rq, static_cast<uint32_t>(my_q[r]) * q_row_bytes + (16 * s + 8 * hh) * 2));
+    }
     if (kBias) {
       const float c = gain[head] * sqrtf(static_cast<float>(D)) * t_h;   // gain / alpha * log2(e)
       const uint16_t c_hi = bf16_bits(c);
@@ -333,151 +360,224 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         e[0] = c_hi | (static_cast<uint32_t>(c_hi) << 16);
         e[1] = c_lo;
       }
-      qf[KS - 1] = as_bf16x8(e);
+#pragma unroll
+      for (int r = 0; r < kSets; ++r) qf[r][KS - 1] = as_bf16x8(e);
     }
   }
 
-  floatx16 o[DT];
+  floatx16 o[kSets][DT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) o[i] = zero16();
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int r = 0; r < kSets; ++r) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) o[r][i] = zero16();
+  }
+  float m_run[kSets], l_run[kSets];
+#pragma unroll
+  for (int r = 0; r < kSets; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
 
   const int q_last = min(qt * kBM + kBM, M) - 1;
   const int n_kt = q_last / kBN + 1;                  // key tiles of the query tile
-  const int t_begin = chunk * 2 * h;
-  const int t_end = min(t_begin + 2 * h, n_kt);       // this work-group's key tiles
-  const int n_vis = q0 <= q_last ? min(q0 + 31, q_last) / kBN + 1 : 0;  // tiles this wave sees
+  const int t_begin = chunk * kTilesPerQt * h;
+  const int t_end = min(t_begin + kTilesPerQt * h, n_kt);   // this work-group's key tiles
+  // tiles this wave sees (its rows end at or before the tile holding q0 + 31 * kSets + 31)
+  const int n_vis = min(q0 <= q_last ? min(q0 + 32 * kSets - 1, q_last) / kBN + 1 : 0, t_end);
 
-  // ---- DMA of one tile (IMG bytes) into lds[par]
+  // ---- DMA of one K~ or V^T image into LDS.  Lane i of a wave instruction
+  // moves 16 bytes to M0 + 16 i; the per-lane part of the source offset is
+  // one VGPR, the rest a scalar offset.
   const int n_tiles = (M + kBN - 1) / kBN;
   const __amdgpu_buffer_rsrc_t rws =
       make_rsrc(ws + static_cast<size_t>(kvh) * n_tiles * T::IMG,
                 static_cast<uint32_t>(n_tiles) * T::IMG);
-  // Lane i of a wave instruction moves 16 bytes to M0 + 16 i; the per-lane
-  // part of the source offset is one VGPR, the rest a scalar offset.
   const int lane16 = 16 * lane;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // provably wave-uniform
-  auto dma_tile = [&](int par, int t) __attribute__((always_inline)) {
-    const int tile_off = t * T::IMG;
+  auto dma = [&](char* dst, int src_off, auto n_c) __attribute__((always_inline)) {
+    constexpr int N = decltype(n_c)::value;
 #pragma unroll
-    for (int j = 0; j < (N_DMA + NW - 1) / NW; ++j) {
+    for (int j = 0; j < (N + NW - 1) / NW; ++j) {
       const int i = wave_s + NW * j;
-      if (i < N_DMA)
+      if (i < N)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rws, (__attribute__((address_space(3))) void*)(&lds[par][0] + 1024 * i), 16, lane16,
-            tile_off + 1024 * i, 0, 0);
+            rws, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, lane16,
+            src_off + 1024 * i, 0, 0);
     }
   };
+  auto dma_k = [&](int buf, int t) __attribute__((always_inline)) {
+    dma(&lds_k[buf][0], t * T::IMG, std::integral_constant<int, N_DMA_K>{});
+  };
+  auto dma_v = [&](int buf, int t) __attribute__((always_inline)) {
+    dma(&lds_v[buf][0], t * T::IMG + T::K_IMG, std::integral_constant<int, N_DMA_V>{});
+  };
 
-  // ---- one 64-key tile for this wave's 32 rows; MASK (compile time) applies
-  // the causal mask, needed only on diagonal tiles.
-  auto tile = [&](auto mask_c, const char* img, int kb) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    floatx16 s[2];   // 32-key halves
-    s[0] = zero16();
-    s[1] = zero16();
+  // ---- S^T of one tile for both sets: every K~ fragment read feeds two MFMAs
+  auto qk = [&](const char* kimg, floatx16 (&s)[kSets][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < kSets; ++r) {
+      s[r][0] = zero16();
+      s[r][1] = zero16();
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            img + (32 * t2 + l32) * T::K_ROW + (16 * ks + 8 * hh) * 2);
-        s[t2] = mfma_32x32x16(a, qf[ks], s[t2]);
+            kimg + (32 * t2 + l32) * T::K_ROW + (16 * ks + 8 * hh) * 2);
+#pragma unroll
+        for (int r = 0; r < kSets; ++r) s[r][t2] = mfma_32x32x16(a, qf[r][ks], s[r][t2]);
       }
     }
+  };
+
+  // ---- online softmax of one set's tile, in two parts so that the next
+  // tile's QK MFMAs can go between them: (1) causal mask (compile-time MASK,
+  // diagonal tile only) and running max, raising it lazily (only when a tile
+  // exceeds it by more than 2^8, which also rescales O and l); (2) P =
+  // exp2(S * alpha - m) as fp16 pairs [32-key half][pair], the logit scale
+  // folded into the exponent's FMA.  The row sum adds the fp16 P values that
+  // the P.V product uses (v_dot2_f32_f16 against (1, 1)).
+  auto softmax_max = [&](auto mask_c, int r, floatx16 (&s)[2], int kb)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    // key kb + 32 t2 + 8 (j / 4) + 4 hh + j % 4 is visible iff
+    // 32 t2 + 8 (j / 4) + j % 4 <= my_q - kb - 4 hh
+    const int lim = my_q[r] - kb - 4 * hh;
     float mx = -INFINITY;
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        float x = s[t2][j] * alpha;
-        if (MASK && kb + 32 * t2 + 8 * (j >> 2) + 4 * hh + (j & 3) > my_q) x = -INFINITY;
+        float x = s[t2][j];
+        if (MASK && 32 * t2 + 8 * (j >> 2) + (j & 3) > lim) x = -INFINITY;
         s[t2][j] = x;
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * alpha;
     // Wave-uniform and rare after the first tiles: a real branch, not a select.
-    if (__builtin_expect(__builtin_amdgcn_readfirstlane(__any(mx > m_run + kRescaleThreshold)), 0)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= corr;
+    if (__builtin_expect(__builtin_amdgcn_readfirstlane(__any(mx > m_run[r] + kRescaleThreshold)), 0)) {
+      const float m_new = fmaxf(m_run[r], mx);
+      const float corr = fast_exp2(m_run[r] - m_new);
+      m_run[r] = m_new;
+      l_run[r] *= corr;
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[i][j] *= corr;
+        for (int j = 0; j < 16; ++j) o[r][i][j] *= corr;
       }
     }
+  };
+  auto softmax_exp = [&](int r, floatx16 (&s)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+    const float nm = -m_run[r];
+    const f16x2 ones = {static_cast<__fp16>(1.f), static_cast<__fp16>(1.f)};
     float rs = 0.f;
-    uint32_t pk[2][8];   // fp16 pairs of P: [32-key half][pair]
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
       for (int j = 0; j < 16; j += 2) {
-        const float p0 = fast_exp2(s[t2][j] - m_run);
-        const float p1 = fast_exp2(s[t2][j + 1] - m_run);
-        rs += p0 + p1;
-        pk[t2][j >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+        const float p0 = fast_exp2(__builtin_fmaf(s[t2][j], alpha, nm));
+        const float p1 = fast_exp2(__builtin_fmaf(s[t2][j + 1], alpha, nm));
+        const f16x2 h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+        rs = __builtin_amdgcn_fdot2(h, ones, rs, false);
+        pk[t2][j >> 1] = __builtin_bit_cast(uint32_t, h);
       }
     }
-    l_run += rs;
-    const char* vimg = img + T::K_IMG;
+    l_run[r] += rs;
+  };
+
+  // ---- O^T += V^T P^T for both sets: every V^T fragment read feeds two MFMAs
+  auto pv = [&](const char* vimg, uint32_t (&pk)[kSets][2][8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {
-      const uint32_t* src = &pk[ps >> 1][4 * (ps & 1)];
-      const u32x4 pv = {src[0], src[1], src[2], src[3]};
-      const f16x8 b = __builtin_bit_cast(f16x8, pv);
+      f16x8 b[kSets];
+#pragma unroll
+      for (int r = 0; r < kSets; ++r) {
+        const uint32_t* src = &pk[r][ps >> 1][4 * (ps & 1)];
+        const u32x4 pv4 = {src[0], src[1], src[2], src[3]};
+        b[r] = __builtin_bit_cast(f16x8, pv4);
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const f16x8 a = *reinterpret_cast<const f16x8*>(
             vimg + (32 * dt + l32) * T::V_ROW + (16 * ps + 8 * hh) * 2);
-        o[dt] = mfma_f16(a, b, o[dt]);
+#pragma unroll
+        for (int r = 0; r < kSets; ++r) o[r][dt] = mfma_f16(a, b[r], o[r][dt]);
       }
     }
   };
 
-  // ---- main loop: one tile per step, one barrier per step.  The DMA issued
-  // at step t fills the buffer read at step t + 1; that buffer was last read
-  // at step t - 1, which every wave finished before barrier t.
-  dma_tile(0, t_begin);
-  for (int t = t_begin; t < t_end; ++t) {
-    const int par = (t - t_begin) & 1;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into lds[par] has landed
+  // ---- one pipelined step: S(t+1) = K~(t+1) Q~^T goes to the MFMA pipe
+  // first (it does not depend on this tile's softmax), then softmax(S(t)) and
+  // O += V(t) P(t).  sc holds S(t), sn receives S(t+1); past the last tile
+  // the extra QK reads stale LDS and its result is never used.
+  auto step = [&](auto mask_c, floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2], int t, int j)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < kSets; ++r) softmax_max(mask_c, r, sc[r], t * kBN);
+    // one basic block from here: the QK MFMAs of the next tile interleave
+    // with this tile's exponentials, then the P.V MFMAs with the V^T reads
+    qk(&lds_k[(j + 1) & 1][0], sn);
+    uint32_t pk[kSets][2][8];
+#pragma unroll
+    for (int r = 0; r < kSets; ++r) softmax_exp(r, sc[r], pk[r]);
+    pv(&lds_v[j & 1][0], pk);
+  };
+
+  // ---- main loop, one barrier per tile.  At the barrier of step j the DMA of
+  // K~(t+1) and V^T(t) (issued one step earlier) has landed and every wave is
+  // done with K~(t) and V^T(t-1), whose buffers the new DMA refills.
+  floatx16 sa[kSets][2], sb[kSets][2];
+  dma_k(0, t_begin);
+  dma_v(0, t_begin);
+  if (t_begin + 1 < t_end) dma_k(1, t_begin + 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t_begin < n_vis) qk(&lds_k[0][0], sa);
+  auto run = [&](floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2], int t) __attribute__((always_inline)) {
+    const int j = t - t_begin;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA has landed
     __syncthreads();                 // ... and every other wave's
-    if (t + 1 < t_end) dma_tile(par ^ 1, t + 1);
+    if (t + 2 < t_end) dma_k(j & 1, t + 2);
+    if (t + 1 < t_end) dma_v((j + 1) & 1, t + 1);
     if (t < n_vis) {
-      if (t * kBN + kBN - 1 > q0) tile(std::true_type{}, &lds[par][0], t * kBN);
-      else tile(std::false_type{}, &lds[par][0], t * kBN);
+      if (t * kBN + kBN - 1 > q0) step(std::true_type{}, sc, sn, t, j);   // the diagonal tile
+      else step(std::false_type{}, sc, sn, t, j);
     }
+  };
+  for (int t = t_begin; t < t_end; t += 2) {
+    run(sa, sb, t);
+    if (t + 1 < t_end) run(sb, sa, t + 1);
   }
 
-  float m = m_run;
-  float l = l_run + __shfl_xor(l_run, 32);
-
-  if (n_chunks > 1) {
-    // ---- split: store this chunk's normalised partial for attn_merge
-    char* pw = part + (split_slot0(head, qt, h, units, n_qt) + chunk) * T::PART +
-               wave * T::PART_WAVE;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+  // ---- epilogue per set: the output, or this chunk's normalised partial
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      f16x8 x;
+  for (int r = 0; r < kSets; ++r) {
+    const float m = m_run[r];
+    const float l = l_run[r] + __shfl_xor(l_run[r], 32);
+    if (n_chunks > 1) {
+      char* pw = part + (split_slot0(head, qt, h, units, n_qt) + chunk) * T::PART +
+                 (kSets * wave + r) * T::PART_SET;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(o[i >> 1][8 * (i & 1) + e] * inv);
-      *reinterpret_cast<f16x8*>(pw + i * 1024 + lane * 16) = x;
+      for (int i = 0; i < NV; ++i) {
+        f16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(o[r][i >> 1][8 * (i & 1) + e] * inv);
+        *reinterpret_cast<f16x8*>(pw + i * 1024 + lane * 16) = x;
+      }
+      *reinterpret_cast<float2*>(pw + T::PART_O + lane * 8) = make_float2(m, l);
+    } else {
+      store_out<D>(o[r], m, l, my_q[r], M, Hq, head, hh, out, lse);
     }
-    *reinterpret_cast<float2*>(pw + T::PART_O + lane * 8) = make_float2(m, l);
-    return;
   }
-  store_out<D>(o, m, l, my_q, M, Hq, head, hh, out, lse);
 }
 
 // ---------------------------------------------------------------------------
-// attn_merge: one work-group (four waves, the rows of attn_fwd's waves) per
-// split query tile; lanes read their own partial vectors, so every load is a
-// contiguous 1 KiB per wave.
+// attn_merge: one work-group per split query tile; wave w merges the two
+// 32-row sets of attn_fwd's wave w.  Lanes read their own partial vectors, so
+// every load is a contiguous 1 KiB per wave.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_merge_kernel(const char* __restrict__ part, int M,
@@ -493,30 +593,48 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(const char* __rest
   const int n_chunks = (qt + h) / h;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5;
-  const int my_q = qt * kBM + wave * 32 + (lane & 31);
-  const char* p0 = part + split_slot0(head, qt, h, units, n_qt) * T::PART + wave * T::PART_WAVE;
+  const char* p_base = part + split_slot0(head, qt, h, units, n_qt) * T::PART;
 
-  floatx16 o[DT];
+  for (int r = 0; r < kSets; ++r) {
+    const int my_q = qt * kBM + wave * 32 * kSets + 32 * r + (lane & 31);
+    const char* p0 = p_base + (kSets * wave + r) * T::PART_SET;
+    floatx16 o[DT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) o[i] = zero16();
-  float m = -INFINITY, l = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const char* pr = p0 + static_cast<int64_t>(c) * T::PART;
-    const float2 st = *reinterpret_cast<const float2*>(pr + T::PART_O + lane * 8);
-    const float m_new = fmaxf(m, st.x);
-    const float a = m == m_new ? 1.f : fast_exp2(m - m_new);
-    const float b = st.y > 0.f ? st.y * fast_exp2(st.x - m_new) : 0.f;
+    for (int i = 0; i < DT; ++i) o[i] = zero16();
+    float m = -INFINITY, l = 0.f;
+    // up to four chunks' partials in flight at once, combined in chunk order
+    for (int c0 = 0; c0 < n_chunks; c0 += 4) {
+      const int nc = min(4, n_chunks - c0);
+      float2 st[4];
+      f16x8 x[4][NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const f16x8 x = *reinterpret_cast<const f16x8*>(pr + i * 1024 + lane * 16);
+      for (int k = 0; k < 4; ++k) {
+        if (k < nc) {
+          const char* pr = p0 + static_cast<int64_t>(c0 + k) * T::PART;
+          st[k] = *reinterpret_cast<const float2*>(pr + T::PART_O + lane * 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        o[i >> 1][8 * (i & 1) + e] = o[i >> 1][8 * (i & 1) + e] * a + static_cast<float>(x[e]) * b;
+          for (int i = 0; i < NV; ++i) x[k][i] = *reinterpret_cast<const f16x8*>(pr + i * 1024 + lane * 16);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k < nc) {
+          const float m_new = fmaxf(m, st[k].x);
+          const float a = m == m_new ? 1.f : fast_exp2(m - m_new);
+          const float b = st[k].y > 0.f ? st[k].y * fast_exp2(st[k].x - m_new) : 0.f;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              o[i >> 1][8 * (i & 1) + e] = o[i >> 1][8 * (i & 1) + e] * a + static_cast<float>(x[k][i][e]) * b;
+          }
+          l = l * a + b;
+          m = m_new;
+        }
+      }
     }
-    l = l * a + b;
-    m = m_new;
+    store_out<D>(o, m, l, my_q, M, Hq, head, hh, out, lse);
   }
-  store_out<D>(o, m, l, my_q, M, Hq, head, hh, out, lse);
 }
 
 template <int D, bool kBias>

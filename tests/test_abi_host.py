@@ -134,25 +134,27 @@ def test_attention_validation(L):
 def _split_layout(n, hq, hkv, d, gated=True):
     """Workspace bytes restated from the split-key rule: 128-row query
     blocks, 64-key tiles, 512 resident work-groups; block qt is cut into
-    ceil((qt + 1) / h) chunks of 2h tiles when its 2 n_qt-tile loop exceeds
+    ceil((qt + 1) / h) chunks of 2h tiles when its 2 n_qt-tile walk exceeds
     the average per work-group."""
     import math
     n_qt, n_tiles = -(-n // 128), -(-n // 64)
+    part = 4 * (64 * d + 512)
     avg = hq * n_qt * (n_qt + 1) / 512
     h = n_qt
     if 2 * n_qt > avg:
         h = max(4, math.ceil(avg / 2))
-    h = min(h, n_qt)
+    h = max(min(h, n_qt), 1)
     units = sum(-(-(qt + 1) // h) for qt in range(n_qt))
     kd = d + (16 if gated else 0)
     img = 64 * (2 * kd + 16) + d * 144
-    n_part = units - h
-    part = 4 * (64 * d + 512)
+    n_part = units - min(h, n_qt)
     return n_tiles * hkv * img + hq * n_part * part, h, units
 
 
 @pytest.mark.parametrize("n,hq,hkv,d", [(2304, 16, 8, 128), (1000, 2, 1, 128), (1280, 16, 8, 64),
-                                         (8448, 16, 8, 128), (700, 4, 2, 64), (64, 1, 1, 128)])
+                                         (8448, 16, 8, 128), (700, 4, 2, 64), (64, 1, 1, 128),
+                                         (4352, 16, 8, 128), (5000, 2, 1, 128), (3000, 1, 1, 64),
+                                         (2300, 16, 8, 128)])
 def test_attention_workspace_split_layout(L, n, hq, hkv, d):
     want, h, units = _split_layout(n, hq, hkv, d)
     assert L.tg_attn_workspace_bytes(n, hq, hkv, d) == want
