@@ -70,6 +70,7 @@ constexpr int kThreads = 256;             // four waves of 32 * kSets rows
 constexpr int kSlots = 512 / kSets;       // resident work-groups: 2 / kSets per CU
 constexpr int kTilesPerQt = kBM / kBN;
 constexpr int kMinChunk = 8 / kTilesPerQt;   // chunks are at least 8 key tiles
+constexpr double kChunkScale = 1.3;           // chunk length / average tile steps per slot
 constexpr float kRescaleThreshold = 8.f;  // log2 units
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
@@ -115,16 +116,17 @@ struct Plan {
 
 // Chunk parameter h: no split unless the longest query tile's walk exceeds
 // the average number of tile steps per resident work-group; then chunks of
-// about that average, never shorter than 8 key tiles (each split chunk pays a
-// partial-state round trip).  A dispatch-simulation choice of h was tried and
-// measured slower at the 16k workload (more, shorter chunks: more partial
-// traffic and merge time than the better balance saved).
+// 1.3x that average, never shorter than 8 key tiles (each split chunk pays a
+// partial-state round trip).  Measured at 16 heads: 1.0x-1.3x is best for
+// 2304 kept rows, 1.3x-1.5x for 4352 (25% faster than 1.0x).  A
+// dispatch-simulation choice of h was tried and measured slower at 2304
+// (more, shorter chunks: more partial traffic than the balance saved).
 int choose_h(int n_qt, int Hq) {
   const double steps = static_cast<double>(kTilesPerQt) * n_qt * (n_qt + 1) / 2;
   const double avg = static_cast<double>(Hq) * steps / kSlots;
   int64_t h = n_qt;
   if (static_cast<double>(kTilesPerQt) * n_qt > avg)
-    h = std::max<int64_t>(kMinChunk, static_cast<int64_t>(std::ceil(avg / kTilesPerQt)));
+    h = std::max<int64_t>(kMinChunk, static_cast<int64_t>(std::ceil(kChunkScale * avg / kTilesPerQt)));
   return static_cast<int>(std::max<int64_t>(std::min<int64_t>(h, n_qt), 1));
 }
 
@@ -575,23 +577,38 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// attn_merge: one work-group per split query tile; wave w merges the two
-// 32-row sets of attn_fwd's wave w.  Lanes read their own partial vectors, so
-// every load is a contiguous 1 KiB per wave.
+// attn_merge: one single-wave work-group per (head, split query tile, wave of
+// attn_fwd), on the XCD whose L2 received that head's partials (the same
+// head -> XCD rule as attn_fwd).  Lanes read their own partial vectors, so
+// every load is a contiguous 1 KiB.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void attn_merge_kernel(const char* __restrict__ part, int M,
-                                                              int Hq, int h, int units,
-                                                              int n_split, bf16* __restrict__ out,
-                                                              float* __restrict__ lse) {
+__global__ __launch_bounds__(64) void attn_merge_kernel(const char* __restrict__ part, int M,
+                                                        int Hq, int h, int units, int n_split,
+                                                        bf16* __restrict__ out,
+                                                        float* __restrict__ lse) {
   using T = Tile<D, false>;   // partial layout does not depend on the bias
   constexpr int DT = D / 32;
   constexpr int NV = DT * 2;
+  constexpr int NW = kThreads / 64;
   const int n_qt = (M + kBM - 1) / kBM;
-  const int head = blockIdx.x / n_split;
-  const int qt = h + blockIdx.x % n_split;
+  int head, rest;
+  {
+    const int b = blockIdx.x;
+    if ((Hq & 7) == 0) {
+      const int hpx = Hq >> 3;
+      const int xcd = b & 7, slot = b >> 3;
+      head = xcd * hpx + slot % hpx;
+      rest = slot / hpx;
+    } else {
+      head = b % Hq;
+      rest = b / Hq;
+    }
+  }
+  const int qt = h + rest / NW;
+  const int wave = rest % NW;
   const int n_chunks = (qt + h) / h;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x;
   const int hh = lane >> 5;
   const char* p_base = part + split_slot0(head, qt, h, units, n_qt) * T::PART;
 
@@ -652,8 +669,9 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M
                      reinterpret_cast<const bf16*>(q), img, M, Hq, Hkv, g, t,
                      reinterpret_cast<bf16*>(out), lse, p.h, static_cast<int>(p.units), part);
   if (p.n_split > 0)
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(static_cast<unsigned>(Hq * p.n_split)),
-                       dim3(kThreads), 0, stream, part, M, Hq, p.h, static_cast<int>(p.units),
+    hipLaunchKernelGGL((attn_merge_kernel<D>),
+                       dim3(static_cast<unsigned>(Hq * p.n_split * (kThreads / 64))), dim3(64), 0,
+                       stream, part, M, Hq, p.h, static_cast<int>(p.units),
                        static_cast<int>(p.n_split), reinterpret_cast<bf16*>(out), lse);
   return hipGetLastError();
 }
