@@ -61,8 +61,9 @@ def attn_source_hash() -> str:
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -> None:
-    """Per-dispatch HBM bytes of the gated-attention launch (pack + attention
-    kernels), each counter scaled by what it reads for the known-size copy."""
+    """Per-launch HBM bytes of the gated-attention call (pack, attention and,
+    where query tiles are split, merge kernels), each counter scaled by what it
+    reads for the known-size copy."""
     import csv
     import glob
 
@@ -78,6 +79,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
 
     is_attn = lambda n: "attn_fwd_kernel" in n and "ELb1E" in n
     is_pack = lambda n: "kv_pack_kernel<128, true>" in n or ("kv_pack_kernel" in n and "ELb1E" in n)
+    is_merge = lambda n: "attn_merge_kernel" in n
     out = {"workload": workload, "kernel_source_sha256_16": attn_source_hash(), "command": command}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = load(d, counter)
@@ -87,9 +89,14 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
         scale = COPY_BYTES / (copy_kib * 1024.0) if copy_kib else None
         a, na = kib(rows, is_attn)
         pk, npk = kib(rows, is_pack)
+        mg, nmg = kib(rows, is_merge)
+        # merge dispatches per attention dispatch (0 when no query tile is split)
+        mg_per = (nmg / na) if na else 0.0
+        total = (a + pk + (mg or 0.0) * mg_per) if (a is not None and pk is not None) else None
         out[counter] = {"copy_kib": copy_kib, "scale": scale, "attn_kib": a, "attn_dispatches": na,
                         "pack_kib": pk, "pack_dispatches": npk,
-                        "bytes_per_launch": (a + pk) * 1024.0 * scale if scale and a and pk else None}
+                        "merge_kib": mg, "merge_dispatches": nmg,
+                        "bytes_per_launch": total * 1024.0 * scale if scale and total else None}
     f, w_ = out["FETCH_SIZE"]["bytes_per_launch"], out["WRITE_SIZE"]["bytes_per_launch"]
     out["traffic_bytes_per_launch"] = f + w_ if f is not None and w_ is not None else None
     path = traffic_path(workload)
@@ -98,12 +105,13 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
     with open(path.replace(".json", ".md"), "w") as fh:
         fh.write(f"# HBM traffic of tg_gated_attn_fwd on {workload}\n\n")
         fh.write(f"Command (each counter in its own run):\n\n    {command}\n\n")
-        fh.write("| counter | copy reads (KiB) | scale | pack KiB/dispatch | attention KiB/dispatch | bytes per launch |\n")
-        fh.write("|---|---|---|---|---|---|\n")
+        fh.write("| counter | copy (KiB) | scale | pack KiB/dispatch | attention KiB/dispatch | "
+                 "merge KiB/dispatch | bytes per launch |\n")
+        fh.write("|---|---|---|---|---|---|---|\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             r = out[c]
             fh.write(f"| {c} | {r['copy_kib']} | {r['scale']} | {r['pack_kib']} | {r['attn_kib']} | "
-                     f"{r['bytes_per_launch']} |\n")
+                     f"{r['merge_kib']} | {r['bytes_per_launch']} |\n")
         fh.write(f"\nTotal HBM bytes per launch: {out['traffic_bytes_per_launch']}\n")
         fh.write(f"Kernel source sha256[:16]: {out['kernel_source_sha256_16']}\n")
     print(json.dumps(out))
@@ -311,7 +319,8 @@ def main():
                    "kept_rows": m, "upper_layers": w.n_layers, "hidden": w.hidden,
                    "gate_hidden": w.gate_hidden, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "parallelism": "single-gpu"},
-        "roofline": {"kernel": "tg_gated_attn_fwd (kv_pack + attn_fwd kernels)", "bound": "mfma",
+        "roofline": {"kernel": "tg_gated_attn_fwd (kv_pack + attn_fwd + attn_merge kernels)",
+                     "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": load_traffic(w.name),
