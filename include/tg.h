@@ -103,7 +103,8 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
  *   kept_idx  [tg_kept_count(n, doc_begin, doc_end, k_doc)] int32 (output),
  *             strictly ascending original row indices (they double as the
  *             rows' position ids); may be NULL when that count is 0
- * Exact: the result is unique and reproduced bit for bit.  n < 2^31.
+ * Exact: the result is unique and reproduced bit for bit.  n < 2^30 (else
+ * TG_E_INVALID).
  */
 tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
                          int64_t k_doc, int32_t* kept_idx, tg_stream_t stream);

@@ -100,8 +100,8 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
 
 tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
                          int64_t k_doc, int32_t* kept_idx, tg_stream_t stream) {
-  if (n < 0 || n >= (int64_t(1) << 31))
-    return fail(TG_E_INVALID, "tg_topk_select: n=%lld out of range", (long long)n);
+  if (n < 0 || n >= (int64_t(1) << 30))
+    return fail(TG_E_INVALID, "tg_topk_select: n=%lld out of range (n < 2^30)", (long long)n);
   if (tg_kept_count(n, doc_begin, doc_end, k_doc) < 0)
     return fail(TG_E_INVALID, "tg_topk_select: need 0 <= doc_begin=%lld <= doc_end=%lld <= n=%lld, k_doc=%lld >= 0",
                 (long long)doc_begin, (long long)doc_end, (long long)n, (long long)k_doc);

@@ -89,6 +89,7 @@ def test_topk_validation(L):
     assert f(A, 10, 0, 5, -1, A, 0) == INVALID
     assert f(None, 10, 0, 5, 3, A, 0) == INVALID
     assert f(A, 1 << 31, 0, 5, 3, A, 0) == INVALID
+    assert f(A, 1 << 30, 0, 5, 3, A, 0) == INVALID                  # n < 2^30
     assert f(None, 0, 0, 0, 3, None, 0) == OK
     assert f(A, 10, 0, 10, 0, None, 0) == OK                             # nothing kept
 
