@@ -567,9 +567,12 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
         f16x8 x;
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(o[r][i >> 1][8 * (i & 1) + e] * inv);
-        *reinterpret_cast<f16x8*>(pw + i * 1024 + lane * 16) = x;
+        // streamed past L2: read once, by the merge launch
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x),
+                                    reinterpret_cast<u32x4*>(pw + i * 1024 + lane * 16));
       }
-      *reinterpret_cast<float2*>(pw + T::PART_O + lane * 8) = make_float2(m, l);
+      __builtin_nontemporal_store(m, reinterpret_cast<float*>(pw + T::PART_O + lane * 8));
+      __builtin_nontemporal_store(l, reinterpret_cast<float*>(pw + T::PART_O + lane * 8 + 4));
     } else {
       store_out<D>(o[r], m, l, my_q[r], M, Hq, head, hh, out, lse);
     }
