@@ -78,7 +78,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
         return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
     is_attn = lambda n: "attn_fwd_kernel" in n and "ELb1E" in n
-    is_pack = lambda n: "kv_pack_kernel<128, true>" in n or ("kv_pack_kernel" in n and "ELb1E" in n)
+    is_pack = lambda n: "v_pack_kernel<128, true>" in n or ("v_pack_kernel" in n and "ELb1E" in n)
     is_merge = lambda n: "attn_merge_kernel" in n
     out = {"workload": workload, "kernel_source_sha256_16": attn_source_hash(), "command": command}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -319,7 +319,7 @@ def main():
                    "kept_rows": m, "upper_layers": w.n_layers, "hidden": w.hidden,
                    "gate_hidden": w.gate_hidden, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "parallelism": "single-gpu"},
-        "roofline": {"kernel": "tg_gated_attn_fwd (kv_pack + attn_fwd + attn_merge kernels)",
+        "roofline": {"kernel": "tg_gated_attn_fwd (v_pack + attn_fwd + attn_merge kernels)",
                      "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

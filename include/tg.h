@@ -128,9 +128,10 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
 /*
  * Bytes of device workspace tg_gated_attn_fwd / tg_full_attn_fwd need for n
  * rows (enough for either):
- *   - per KV head and 64-key tile, a packed copy of K (bf16, with the key
- *     scores appended) and of V (fp16, transposed), laid out as the kernel's
- *     LDS image -- about 2.3x the bytes of K and V;
+ *   - per KV head and 64-key tile, a packed copy of V (fp16, transposed,
+ *     laid out as the kernel's LDS image: about 1.1x the bytes of V) and, per
+ *     key, 32 bytes holding its score split into two bf16 parts (K itself is
+ *     read in place);
  *   - when n is short enough that long query blocks are split over several
  *     work-groups along the keys: one counter per split block and one
  *     partial state (fp16 output, fp32 max and sum; 34 KiB at head_dim 128)

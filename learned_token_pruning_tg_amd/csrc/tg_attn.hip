@@ -10,23 +10,23 @@
 //
 // Two or three launches per call:
 //
-// 1. kv_pack: per KV head and 64-key tile, build the exact LDS image the main
-//    kernel consumes, in the caller's workspace:
-//      * K~ rows [k_j | s_hi, s_lo, s_hi, 0...] in bf16 (the extra 16-column
-//        k-step exists only in the gated kernel; s_hi/s_lo split the score
-//        into two bf16 parts), rows padded to avoid LDS bank conflicts;
-//      * V^T in fp16 ([d][key], key order permuted inside each 16-key group
-//        so that every lane's eight keys of a P.V step are one 16-byte run).
-//    Rows past n are zero.
+// 1. v_pack: per KV head and 64-key tile, the V^T image the main kernel
+//    DMAs into LDS, in the caller's workspace: fp16 [d][key], key order
+//    permuted inside each 16-key group so that every lane's eight keys of a
+//    P.V step are one 16-byte run, rows padded; plus (gated) per key the bias
+//    k-step's A fragment (score split into bf16 s_hi, s_lo).  Keys past n are
+//    zero.  K is not copied: the main kernel DMAs K tiles straight from k.
 // 2. attn_fwd: one work-group = 128 query rows of one query head over a run
 //    of their key tiles; four waves of 32 rows; two work-groups per CU (they
 //    drift out of phase, so one's softmax and DMA waits overlap the other's
 //    MFMAs).
 //      * S^T = K~ Q~^T on v_mfma_f32_32x32x16_bf16 (A = K~ from LDS, B = Q~
-//        held in registers for the whole key loop).  The bias rides in the
-//        extra k-step: Q~ carries c = gain * sqrt(d) * tau split as (c_hi,
-//        c_hi, c_lo), so S~ = q.k + c s_j and one multiply by
-//        alpha = log2(e) / (sqrt(d) tau) gives the logit in log2 units.
+//        held in registers for the whole key loop).  K~ is k with one extra
+//        k-step carrying the bias: the key's (s_hi, s_lo, s_hi) against Q~'s
+//        c = gain * sqrt(d) * tau split as (c_hi, c_hi, c_lo), so
+//        S~ = q.k + c s_j and one multiply by alpha = log2(e) / (sqrt(d) tau)
+//        gives the logit in log2 units.  K tiles sit in LDS unpadded, 16-byte
+//        chunk c of key r at slot c ^ (r % 8) (conflict-free fragment reads).
 //      * Each lane owns one query column, so the online-softmax statistics are
 //        lane-local plus one exchange between lane halves; the running max
 //        only moves when a tile raises it by more than 2^8 (lazy rescaling).
@@ -78,15 +78,14 @@ typedef __fp16 f16x2 __attribute__((ext_vector_type(2)));   // cvt_pkrtz / fdot2
 
 template <int D, bool kBias>
 struct Tile {
-  static constexpr int KD = D + (kBias ? 16 : 0);        // K~ columns
-  static constexpr int KS = KD / 16;                      // k-steps of S^T
-  static constexpr int K_ROW = KD * 2 + 16;               // bytes, padded
-  static constexpr int K_IMG = kBN * K_ROW;
+  static constexpr int KS = D / 16 + (kBias ? 1 : 0);     // k-steps of S^T (+ the bias step)
+  static constexpr int K_ROW = D * 2;                     // LDS bytes per key: 16-byte chunks,
+  static constexpr int K_CH = D / 8;                      //   chunk c of key r at slot c ^ (r % 8)
+  static constexpr int K_IMG = kBN * K_ROW;               // one K tile in LDS
   static constexpr int V_ROW = kBN * 2 + 16;              // bytes, padded
-  static constexpr int V_IMG = D * V_ROW;
-  static constexpr int IMG = K_IMG + V_IMG;               // one tile in LDS / workspace
-  static_assert(K_IMG % 1024 == 0 && V_IMG % 1024 == 0,
-                "K~ and V^T images must be whole 1 KiB DMA chunks");
+  static constexpr int V_IMG = D * V_ROW;                 // one V^T tile (workspace and LDS)
+  static constexpr int S_TILE = kBN * 32;                 // bias A fragments of one tile
+  static_assert(K_IMG % 1024 == 0 && V_IMG % 1024 == 0, "tiles must be whole 1 KiB DMA chunks");
   // One split chunk's partial state: per 32-row set (two per wave), the
   // lane-major fp16 output (D bytes per lane in 16-byte vectors) and a
   // (max, sum) pair per lane.
@@ -111,7 +110,7 @@ struct Plan {
   int64_t units;       // work-groups per head
   int64_t n_split;     // query tiles per head with more than one chunk
   int64_t n_part;      // split chunks per head
-  size_t img_bytes, part_off, total;
+  size_t img_bytes, sc_off, part_off, total;
 };
 
 // Chunk parameter h: no split unless the longest query tile's walk exceeds
@@ -141,8 +140,9 @@ Plan make_plan(int64_t M, int Hq, int Hkv) {
   p.units = units_before(p.n_qt, h);
   p.n_split = std::max<int64_t>(p.n_qt - h, 0);
   p.n_part = p.units - std::min<int64_t>(h, p.n_qt);
-  p.img_bytes = static_cast<size_t>(p.n_tiles) * Hkv * T::IMG;
-  p.part_off = p.img_bytes;
+  p.img_bytes = static_cast<size_t>(p.n_tiles) * Hkv * T::V_IMG;
+  p.sc_off = p.img_bytes;
+  p.part_off = p.sc_off + ((static_cast<size_t>(p.n_tiles) * T::S_TILE + 255) & ~size_t(255));
   p.total = p.part_off + static_cast<size_t>(Hq) * p.n_part * T::PART;
   return p;
 }
@@ -164,70 +164,44 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// kv_pack: one work-group per (tile, KV head).
+// v_pack: one work-group per (tile, KV head) builds the tile's V^T image in
+// the workspace (fp16, [d][key] with the key order permuted inside each
+// 16-key group so that every lane's eight keys of a P.V step are one 16-byte
+// run; rows padded; keys past n zero).  The work-groups of KV head 0 of a
+// gated call also store, per key, the bias step's A fragment: the score split
+// into two bf16 parts as (s_hi, s_lo, s_hi, 0 ...) for lane half 0 and 16
+// zero bytes for lane half 1.  K needs no pass of its own: the attention
+// kernel DMAs its tiles straight from k.
 // ---------------------------------------------------------------------------
 template <int D, bool kBias>
-__global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ k,
-                                                      const bf16* __restrict__ v,
-                                                      const float* __restrict__ key_score, int M,
-                                                      int Hkv, char* __restrict__ ws) {
+__global__ __launch_bounds__(256) void v_pack_kernel(const bf16* __restrict__ v,
+                                                     const float* __restrict__ key_score, int M,
+                                                     int Hkv, char* __restrict__ ws,
+                                                     char* __restrict__ sc) {
   using T = Tile<D, kBias>;
   const int n_tiles = (M + kBN - 1) / kBN;
   const int tile = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
   const int tid = threadIdx.x;
-  char* img = ws + (static_cast<size_t>(kvh) * n_tiles + tile) * T::IMG;
+  char* vimg = ws + (static_cast<size_t>(kvh) * n_tiles + tile) * T::V_IMG;
   const uint32_t kv_row_bytes = static_cast<uint32_t>(Hkv) * D * 2;
   const uint32_t kv_bytes = kv_row_bytes * static_cast<uint32_t>(M);
   const uint32_t off0 = static_cast<uint32_t>(tile) * kBN * kv_row_bytes;
   const uint32_t left = off0 < kv_bytes ? kv_bytes - off0 : 0u;
-
-  // Every load of the tile is issued before the first store (one memory
-  // round trip per work-group).
   constexpr int DC = D / 8;                        // 16-byte data chunks per row
-  constexpr int KL = kBN * DC / 256;               // K chunks per thread
-  constexpr int XC = T::K_ROW / 16 - DC;           // extra chunks per K~ row
-  static_assert(kBN * DC % 256 == 0 && kBN * XC <= 256 && 16 * DC <= 256, "kv_pack tiling");
-  const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc(reinterpret_cast<const char*>(k + static_cast<size_t>(kvh) * D) + off0, left);
+  static_assert(16 * DC <= 256, "v_pack tiling");
   const __amdgpu_buffer_rsrc_t rv =
       make_rsrc(reinterpret_cast<const char*>(v + static_cast<size_t>(kvh) * D) + off0, left);
-  u32x4 kx[KL];
-#pragma unroll
-  for (int i = 0; i < KL; ++i) {
-    const int f = tid + 256 * i;
-    kx[i] = bload16(rk, (f / DC) * kv_row_bytes + 16 * (f % DC));
-  }
-  // V^T task of this thread: 4 keys x 8 dims; keys 4 kg + i sit at positions
+  // This thread's task: 4 keys x 8 dims; keys 4 kg + i sit at positions
   // 16 s + 8 h' + 4 b + i with s = kg / 4, h' = (kg % 4) & 1, b = (kg % 4) >> 1.
+  // Every load is issued before the first store.
   const int kg = tid % 16, dc = tid / 16;
-  const bool v_task = dc < DC;
-  u32x4 vx[4];
+  const int key = tile * kBN + tid;
+  const bool score_task = kBias && kvh == 0 && tid < kBN;
+  const float x_s = (score_task && key < M) ? key_score[key] : 0.f;
+  if (dc < DC) {
+    u32x4 vx[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    vx[i] = v_task ? bload16(rv, (4 * kg + i) * kv_row_bytes + 16 * dc) : zero_u32x4();
-  // Extra K~ chunk of this thread: (gated) the score chunk, a zero chunk,
-  // then the pad chunk.
-  const int x_row = tid / XC, x_c = tid % XC;
-  const int x_key = tile * kBN + x_row;
-  const float x_s = (kBias && tid < kBN * XC && x_c == 0 && x_key < M) ? key_score[x_key] : 0.f;
-
-#pragma unroll
-  for (int i = 0; i < KL; ++i) {
-    const int f = tid + 256 * i;
-    st16(img + (f / DC) * T::K_ROW + 16 * (f % DC), kx[i]);
-  }
-  if (tid < kBN * XC) {
-    u32x4 val = zero_u32x4();
-    if (kBias && x_c == 0) {
-      const uint16_t hi = bf16_bits(x_s);
-      const uint16_t lo = bf16_bits(x_s - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-      val[0] = hi | (static_cast<uint32_t>(lo) << 16);
-      val[1] = hi;
-    }
-    st16(img + x_row * T::K_ROW + 16 * (DC + x_c), val);
-  }
-  char* vimg = img + T::K_IMG;
-  if (v_task) {
+    for (int i = 0; i < 4; ++i) vx[i] = bload16(rv, (4 * kg + i) * kv_row_bytes + 16 * dc);
     const int sg = kg >> 2, j = kg & 3;
     const int phys = 16 * sg + 8 * (j & 1) + 4 * (j >> 1);
 #pragma unroll
@@ -245,6 +219,16 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ k
     }
   }
   if (tid < D) st16(vimg + tid * T::V_ROW + kBN * 2, zero_u32x4());
+  if (score_task) {
+    const uint16_t hi = bf16_bits(x_s);
+    const uint16_t lo = bf16_bits(x_s - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+    u32x4 f = zero_u32x4();
+    f[0] = hi | (static_cast<uint32_t>(lo) << 16);
+    f[1] = hi;
+    char* dst = sc + static_cast<size_t>(tile * kBN + tid) * 32;
+    st16(dst, f);
+    st16(dst + 16, zero_u32x4());
+  }
 }
 
 // First partial slot of split query tile qt of `head` (split chunks of a head
@@ -281,20 +265,23 @@ __device__ __forceinline__ void store_out(const floatx16 (&o)[D / 32], float m, 
 // ---------------------------------------------------------------------------
 template <int D, bool kBias>
 __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
-    const bf16* __restrict__ q, const char* __restrict__ ws, int M, int Hq, int Hkv,
-    const float* __restrict__ gain, const float* __restrict__ tau, bf16* __restrict__ out,
-    float* __restrict__ lse, int h, int units, char* __restrict__ part) {
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const char* __restrict__ ws,
+    const char* __restrict__ bias_frag, int M, int Hq, int Hkv, const float* __restrict__ gain,
+    const float* __restrict__ tau, bf16* __restrict__ out, float* __restrict__ lse, int h,
+    int units, char* __restrict__ part) {
   using T = Tile<D, kBias>;
   constexpr int KS = T::KS;
   constexpr int DT = D / 32;                 // 32-row tiles of O^T
   constexpr int NW = kThreads / 64;
   constexpr int NV = DT * 2;                 // 16-byte fp16 vectors of partial output per lane
-  constexpr int N_DMA_K = T::K_IMG / 1024;   // 1 KiB DMA chunks per K~ image
+  constexpr int N_DMA_K = T::K_IMG / 1024;   // 1 KiB DMA chunks per K tile
   constexpr int N_DMA_V = T::V_IMG / 1024;   // ... per V^T image
+  constexpr int NKJ = (N_DMA_K + NW - 1) / NW;
 
-  // K~ ring runs one tile ahead of the V^T ring: step t reads K~(t+1) and
-  // V^T(t) while K~(t+2) and V^T(t+1) land.
+  // K ring (with the tile's packed scores) runs one tile ahead of the V^T
+  // ring: step t reads K(t+1) and V^T(t) while K(t+2) and V^T(t+1) land.
   __shared__ __align__(16) char lds_k[2][T::K_IMG];
+  __shared__ __align__(16) char lds_s[2][kBias ? T::S_TILE : 16];
   __shared__ __align__(16) char lds_v[2][T::V_IMG];
 
   // ---- work-group -> (head, unit); unit -> (query tile, chunk)
@@ -387,48 +374,90 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
   // tiles this wave sees (its rows end at or before the tile holding q0 + 31 * kSets + 31)
   const int n_vis = min(q0 <= q_last ? min(q0 + 32 * kSets - 1, q_last) / kBN + 1 : 0, t_end);
 
-  // ---- DMA of one K~ or V^T image into LDS.  Lane i of a wave instruction
-  // moves 16 bytes to M0 + 16 i; the per-lane part of the source offset is
-  // one VGPR, the rest a scalar offset.
+  // ---- DMA into LDS.  Lane i of a wave instruction moves 16 bytes to
+  // M0 + 16 i.  K tiles come straight from k: the lane that fills LDS slot s
+  // of key r fetches chunk s ^ (r % 8) of that key's row (the XOR swizzle
+  // keeps the fragment reads free of bank conflicts without padding); keys
+  // past n read as zeros (buffer range check on the full per-lane offset).
+  // V^T images and packed scores come from the workspace.
   const int n_tiles = (M + kBN - 1) / kBN;
-  const __amdgpu_buffer_rsrc_t rws =
-      make_rsrc(ws + static_cast<size_t>(kvh) * n_tiles * T::IMG,
-                static_cast<uint32_t>(n_tiles) * T::IMG);
+  const uint32_t kv_row = static_cast<uint32_t>(Hkv) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k, kv_row * static_cast<uint32_t>(M));
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(ws + static_cast<size_t>(kvh) * n_tiles * T::V_IMG,
+                static_cast<uint32_t>(n_tiles) * T::V_IMG);
+  const __amdgpu_buffer_rsrc_t rsc =
+      make_rsrc(bias_frag, static_cast<uint32_t>(n_tiles) * T::S_TILE);
   const int lane16 = 16 * lane;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // provably wave-uniform
-  auto dma = [&](char* dst, int src_off, auto n_c) __attribute__((always_inline)) {
-    constexpr int N = decltype(n_c)::value;
+  uint32_t koff[NKJ];   // this lane's source offset (within a tile) per K DMA instruction
 #pragma unroll
-    for (int j = 0; j < (N + NW - 1) / NW; ++j) {
-      const int i = wave_s + NW * j;
-      if (i < N)
+  for (int jj = 0; jj < NKJ; ++jj) {
+    const int byte = 1024 * (wave_s + NW * jj) + lane16;
+    const int r = byte / T::K_ROW, slot = (byte % T::K_ROW) / 16;
+    koff[jj] = static_cast<uint32_t>(r) * kv_row + static_cast<uint32_t>(kvh) * D * 2 +
+               static_cast<uint32_t>((slot ^ (r & 7)) * 16);
+  }
+  auto dma_k = [&](int buf, int t) __attribute__((always_inline)) {
+    const uint32_t tile_off = static_cast<uint32_t>(t) * kBN * kv_row;
+#pragma unroll
+    for (int jj = 0; jj < NKJ; ++jj) {
+      const int j = wave_s + NW * jj;
+      if (j < N_DMA_K)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rws, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, lane16,
-            src_off + 1024 * i, 0, 0);
+            rk, (__attribute__((address_space(3))) void*)(&lds_k[buf][0] + 1024 * j), 16,
+            static_cast<int>(tile_off + koff[jj]), 0, 0, 0);
+    }
+    if (kBias && wave_s >= NW - T::S_TILE / 1024) {
+      const int js = wave_s - (NW - T::S_TILE / 1024);
+      const int s_off = t * T::S_TILE + 1024 * js;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsc, (__attribute__((address_space(3))) void*)(&lds_s[buf][0] + 1024 * js), 16, lane16,
+          s_off, 0, 0);
     }
   };
-  auto dma_k = [&](int buf, int t) __attribute__((always_inline)) {
-    dma(&lds_k[buf][0], t * T::IMG, std::integral_constant<int, N_DMA_K>{});
-  };
   auto dma_v = [&](int buf, int t) __attribute__((always_inline)) {
-    dma(&lds_v[buf][0], t * T::IMG + T::K_IMG, std::integral_constant<int, N_DMA_V>{});
+    // (the tile offset is formed outside the loop: written inline in the
+    // builtin's offset argument, the host pass drops this kernel's stub)
+    const int tile_off = t * T::V_IMG;
+#pragma unroll
+    for (int jj = 0; jj < (N_DMA_V + NW - 1) / NW; ++jj) {
+      const int j = wave_s + NW * jj;
+      if (j < N_DMA_V)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(&lds_v[buf][0] + 1024 * j), 16, lane16,
+            tile_off + 1024 * j, 0, 0);
+    }
   };
 
-  // ---- S^T of one tile for both sets: every K~ fragment read feeds two MFMAs
-  auto qk = [&](const char* kimg, floatx16 (&s)[kSets][2]) __attribute__((always_inline)) {
+  // ---- S^T of one tile for both sets: every K fragment read feeds kSets
+  // MFMAs.  Lane (l32, hh) reads chunk 2 ks + hh of key 32 t2 + l32, stored at
+  // slot (2 ks + hh) ^ (l32 % 8): the per-k-step address is one XOR.  The
+  // bias step's A fragment comes prebuilt (see v_pack).
+  const uint32_t k_base = static_cast<uint32_t>(l32) * T::K_ROW + ((hh ^ (l32 & 7)) << 4);
+  auto qk = [&](const char* kimg, const char* simg, floatx16 (&s)[kSets][2])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < kSets; ++r) {
       s[r][0] = zero16();
       s[r][1] = zero16();
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const uint32_t off = k_base ^ static_cast<uint32_t>(32 * ks);
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            kimg + (32 * t2 + l32) * T::K_ROW + (16 * ks + 8 * hh) * 2);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kimg + off + 32 * t2 * T::K_ROW);
 #pragma unroll
         for (int r = 0; r < kSets; ++r) s[r][t2] = mfma_32x32x16(a, qf[r][ks], s[r][t2]);
+      }
+    }
+    if (kBias) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(simg + (32 * t2 + l32) * 32 + 16 * hh);
+#pragma unroll
+        for (int r = 0; r < kSets; ++r) s[r][t2] = mfma_32x32x16(a, qf[r][KS - 1], s[r][t2]);
       }
     }
   };
@@ -520,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
     for (int r = 0; r < kSets; ++r) softmax_max(mask_c, r, sc[r], t * kBN);
     // one basic block from here: the QK MFMAs of the next tile interleave
     // with this tile's exponentials, then the P.V MFMAs with the V^T reads
-    qk(&lds_k[(j + 1) & 1][0], sn);
+    qk(&lds_k[(j + 1) & 1][0], &lds_s[(j + 1) & 1][0], sn);
     uint32_t pk[kSets][2][8];
 #pragma unroll
     for (int r = 0; r < kSets; ++r) softmax_exp(r, sc[r], pk[r]);
@@ -536,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
   if (t_begin + 1 < t_end) dma_k(1, t_begin + 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (t_begin < n_vis) qk(&lds_k[0][0], sa);
+  if (t_begin < n_vis) qk(&lds_k[0][0], &lds_s[0][0], sa);
   auto run = [&](floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2], int t) __attribute__((always_inline)) {
     const int j = t - t_begin;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA has landed
@@ -663,14 +692,15 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M
                   void* ws, hipStream_t stream) {
   const Plan p = make_plan<D, kBias>(M, Hq, Hkv);
   char* img = static_cast<char*>(ws);
+  char* sc = img + p.sc_off;
   char* part = img + p.part_off;
-  hipLaunchKernelGGL((kv_pack_kernel<D, kBias>), dim3(static_cast<unsigned>(p.n_tiles * Hkv)),
-                     dim3(256), 0, stream, reinterpret_cast<const bf16*>(k),
-                     reinterpret_cast<const bf16*>(v), s, M, Hkv, img);
+  hipLaunchKernelGGL((v_pack_kernel<D, kBias>), dim3(static_cast<unsigned>(p.n_tiles * Hkv)),
+                     dim3(256), 0, stream, reinterpret_cast<const bf16*>(v), s, M, Hkv, img, sc);
   const dim3 grid(static_cast<unsigned>(p.units * Hq));
   hipLaunchKernelGGL((attn_fwd_kernel<D, kBias>), grid, dim3(kThreads), 0, stream,
-                     reinterpret_cast<const bf16*>(q), img, M, Hq, Hkv, g, t,
-                     reinterpret_cast<bf16*>(out), lse, p.h, static_cast<int>(p.units), part);
+                     reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k), img, sc, M,
+                     Hq, Hkv, g, t, reinterpret_cast<bf16*>(out), lse, p.h,
+                     static_cast<int>(p.units), part);
   if (p.n_split > 0)
     hipLaunchKernelGGL((attn_merge_kernel<D>),
                        dim3(static_cast<unsigned>(Hq * p.n_split * (kThreads / 64))), dim3(64), 0,
@@ -693,9 +723,8 @@ size_t attn_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_d
 
 size_t attn_image_bytes_per_kv_head(int64_t n, int head_dim, bool gated) {
   const int64_t n_tiles = (n + kBN - 1) / kBN;
-  int64_t img;
-  if (head_dim == 128) img = gated ? Tile<128, true>::IMG : Tile<128, false>::IMG;
-  else img = gated ? Tile<64, true>::IMG : Tile<64, false>::IMG;
+  const int64_t img = head_dim == 128 ? Tile<128, true>::V_IMG : Tile<64, true>::V_IMG;
+  (void)gated;
   return static_cast<size_t>(n_tiles * img);
 }
 

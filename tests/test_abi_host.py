@@ -119,7 +119,7 @@ def test_attention_validation(L):
     assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, A, W, 0) == UNSUPPORTED
     assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, A, W, 0) == UNSUPPORTED  # 2^31-byte offsets
     need = L.tg_attn_workspace_bytes(100, 16, 8, 128)
-    assert need == 2 * 8 * (64 * (2 * 144 + 16) + 128 * 144)   # 2 tiles x 8 heads x image
+    assert need == 2 * 8 * 128 * 144 + 2 * 2048  # V^T images (2 tiles x 8 heads) + bias fragments
     assert g(A, A, A, 100, 16, 8, 128, A, A, A, A, None, A, need - 1, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, A, 1000, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, None, need, 0) == WORKSPACE
@@ -146,10 +146,10 @@ def _split_layout(n, hq, hkv, d, gated=True):
         h = max(4, math.ceil(1.3 * avg / 2))
     h = max(min(h, n_qt), 1)
     units = sum(-(-(qt + 1) // h) for qt in range(n_qt))
-    kd = d + (16 if gated else 0)
-    img = 64 * (2 * kd + 16) + d * 144
+    img = d * 144                              # V^T image of one tile (fp16, padded rows)
+    sc = n_tiles * 64 * 32                     # per key: the bias step's A fragment + zeros
     n_part = units - min(h, n_qt)
-    return n_tiles * hkv * img + hq * n_part * part, h, units
+    return n_tiles * hkv * img + sc + hq * n_part * part, h, units
 
 
 @pytest.mark.parametrize("n,hq,hkv,d", [(2304, 16, 8, 128), (1000, 2, 1, 128), (1280, 16, 8, 64),
