@@ -265,6 +265,8 @@ def main():
             "attn_tflops": round(f_fl / (f_launch / 1e3) / 1e12, 2),
             "attn_frac_bf16_peak": round(f_fl / (f_launch / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "speedup_gated_vs_full": round(f_ms / ms_step, 2),
+            # both sides also pay the gate layer's own attention over all N rows
+            "speedup_incl_gate_layer": round((f_ms + f_launch) / (ms_step + f_launch), 2),
             "steps": fsteps,
         }
         del fout, fws

@@ -202,6 +202,29 @@ def test_gated_attention_ragged(m, hq, hkv, d):
         assert np.array_equal(got0[h], v[0, h // g])
 
 
+@pytest.mark.parametrize("m,hq,hkv", [(200, 4, 2), (2304, 16, 8)])
+def test_gated_attention_dominant_bias(m, hq, hkv):
+    # one key with a huge biased logit: every row that sees it returns its v
+    # (the softmax collapses onto it); exact up to the fp16 step of v in the
+    # P.V product, which only bites below fp16's normal range (|v| < 6.1e-5,
+    # error < 6e-8).  Rows before it are ordinary attention.
+    rng = np.random.default_rng(m + 5)
+    q, k, v, _, _, tau = _rand_attn(rng, m, hq, hkv, 128)
+    j = m // 3
+    s = np.zeros(m, np.float32); s[j] = 1.0
+    gain = np.full(hq, 80.0, np.float32)
+    say(f"dominant bias m={m} hq={hq}")
+    out = host_bf16(tg.gated_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(s),
+                                      dev_f32(gain), dev_f32(tau)))
+    torch.cuda.synchronize()
+    g = hq // hkv
+    for h in range(hq):
+        assert np.max(np.abs(out[j:, h] - v[j, h // g][None, :])) <= 1e-6
+    rows = np.arange(0, j)
+    ref = O.gated_attention(q, k, v, s, gain, tau, rows=rows)
+    check_attn(out[rows], ref, "rows before the dominant key")
+
+
 @pytest.mark.parametrize("m,d", [(300, 128), (777, 64)])
 def test_no_gain_unit_temperature_equals_full(m, d):
     rng = np.random.default_rng(m)

@@ -247,6 +247,23 @@ def test_attention_two_key_closed_form_and_first_row():
     assert abs(lse[0, 0] - l00) < 1e-13
 
 
+def test_attention_dominant_bias_selects_one_key():
+    """gain * s_j -> +inf for a single key j drives every row that sees it to
+    v_j (the softmax collapses onto that key); rows before j are untouched."""
+    rng = np.random.default_rng(12)
+    n, d, j = 12, 8, 5
+    q, k, v = _rand_qkv(rng, n, 2, 1, d)
+    s = np.zeros(n); s[j] = 1.0
+    base = O.gated_attention(q, k, v, s, np.array([0.0, 0.0]), np.ones(2))
+    big = O.gated_attention(q, k, v, s, np.array([60.0, 80.0]), np.ones(2))
+    for i in range(n):
+        for h in range(2):
+            if i >= j:
+                assert np.max(np.abs(big[i, h] - v[j, 0])) < 1e-12
+            else:
+                assert np.array_equal(big[i, h], base[i, h])   # key j is not visible yet
+
+
 def test_attention_uniform_logits_lse_and_mean():
     # q = 0 and s = 0: every visible key has logit 0, so lse_i = log(i+1) and
     # out_i is the running mean of v.
