@@ -141,7 +141,7 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: only one GPU is measured (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design, not a measured path.", file=sys.stderr)
         sys.exit(2)
 
