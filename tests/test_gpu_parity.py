@@ -179,7 +179,7 @@ def _rand_attn(rng, m, hq, hkv, d):
                                         (64, 4, 4, 128), (65, 8, 1, 128), (127, 4, 2, 64),
                                         (129, 16, 8, 128), (200, 4, 2, 64), (515, 16, 8, 128),
                                         (1000, 2, 1, 128), (2304, 16, 8, 128), (3000, 1, 1, 64),
-                                        (5000, 2, 1, 128)])
+                                        (5000, 2, 1, 128), (1800, 8, 1, 128), (2600, 8, 4, 64)])
 def test_gated_attention_ragged(m, hq, hkv, d):
     rng = np.random.default_rng(m * 7 + d)
     q, k, v, s, gain, tau = _rand_attn(rng, m, hq, hkv, d)
@@ -223,6 +223,20 @@ def test_gated_attention_dominant_bias(m, hq, hkv):
     rows = np.arange(0, j)
     ref = O.gated_attention(q, k, v, s, gain, tau, rows=rows)
     check_attn(out[rows], ref, "rows before the dominant key")
+
+
+@pytest.mark.parametrize("m,hq,hkv,d", [(2304, 16, 8, 128), (1500, 4, 2, 64)])
+def test_full_attention_split_keys(m, hq, hkv, d):
+    # unbiased kernel on a short prefix: its longest query tiles are split
+    # along the keys and merged
+    rng = np.random.default_rng(m + d)
+    q, k, v, _, _, _ = _rand_attn(rng, m, hq, hkv, d)
+    say(f"full attn split m={m} hq={hq} d={d}")
+    out, lse = tg.full_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.full_attention(q, k, v, return_lse=True)
+    check_attn(host_bf16(out), ref, f"full m={m} d={d}")
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) < 2e-3
 
 
 @pytest.mark.parametrize("m,d", [(300, 128), (777, 64)])
