@@ -34,25 +34,33 @@
 //        registers.  P and V are fp16 for this product: bf16 P (8-bit
 //        mantissa) costs up to ~3e-3 of output error on peaked rows on top of
 //        the bf16 output rounding.  O accumulates in fp32.
-//      * Tiles arrive by buffer-to-LDS DMA (buffer_load_dwordx4 ... lds) one
-//        tile ahead into double-buffered LDS: no staging registers, no LDS
-//        store instructions, one barrier per tile.
+//      * The softmax runs on fp32 logits in log2 units: the logit scale is
+//        folded into the exponent's FMA, and the row sum adds the fp16 P
+//        values that the P.V product uses (v_dot2_f32_f16 against (1, 1)).
+//      * Software-pipelined steps: step t issues the QK MFMAs of tile t + 1
+//        before the exponentials of tile t (independent work for the MFMA
+//        pipe while the VALU runs the softmax).
+//      * Tiles arrive by buffer-to-LDS DMA (buffer_load_dwordx4 ... lds): K
+//        (with the bias fragments) straight from k, two tiles ahead, V^T
+//        images one tile ahead, each in its own double-buffered LDS ring; no
+//        staging registers, no LDS store instructions, one barrier per tile.
 //      * Causal masking only on diagonal tiles; tiles above a wave's rows are
 //        skipped.
+//      * Heads of one KV group are pinned to one XCD (work-groups are dealt
+//        round-robin over the 8 XCDs) so its K/V stays in that L2; within an
+//        XCD the units of the longest query tiles go first.
 //      * Split keys.  When few query tiles exist (short kept prefixes), the
 //        longest query tile's key loop would outlast the average work of a
 //        resident work-group many times over.  Then the key tiles of query
 //        tile qt are cut into ceil((qt + 1) / h) chunks of 2h tiles, each a
 //        work-group of its own.  Every chunk stores its normalised partial
 //        output (fp16) and its running max and sum in the workspace.
-// 3. attn_merge (only when some query tile is split): one work-group per
-//    split query tile combines its chunks' partials in chunk order and writes
-//    the output.  A third launch rather than a last-arriver merge inside
-//    attn_fwd: the agent-scope fences such a merge needs (L2 write-back and
-//    invalidate on every chunk) cost more than the whole split saves.
-//      * Heads of one KV group are pinned to one XCD (work-groups are dealt
-//        round-robin over the 8 XCDs) so its K/V stays in that L2; within an
-//        XCD the units of the longest query tiles go first.
+// 3. attn_merge (only when some query tile is split): one single-wave
+//    work-group per (head, split query tile, wave) combines the chunks'
+//    partials in chunk order and writes the output.  A third launch rather
+//    than a last-arriver merge inside attn_fwd: the agent-scope fences such a
+//    merge needs (L2 write-back and invalidate on every chunk) cost more than
+//    the whole split saves.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -80,13 +88,13 @@ template <int D, bool kBias>
 struct Tile {
   static constexpr int KS = D / 16 + (kBias ? 1 : 0);     // k-steps of S^T (+ the bias step)
   static constexpr int K_ROW = D * 2;                     // LDS bytes per key: 16-byte chunks,
-  static constexpr int K_CH = D / 8;                      //   chunk c of key r at slot c ^ (r % 8)
+                                                          //   chunk c of key r at slot c ^ (r % 8)
   static constexpr int K_IMG = kBN * K_ROW;               // one K tile in LDS
   static constexpr int V_ROW = kBN * 2 + 16;              // bytes, padded
   static constexpr int V_IMG = D * V_ROW;                 // one V^T tile (workspace and LDS)
   static constexpr int S_TILE = kBN * 32;                 // bias A fragments of one tile
   static_assert(K_IMG % 1024 == 0 && V_IMG % 1024 == 0, "tiles must be whole 1 KiB DMA chunks");
-  // One split chunk's partial state: per 32-row set (two per wave), the
+  // One split chunk's partial state: per 32-row set (kSets per wave), the
   // lane-major fp16 output (D bytes per lane in 16-byte vectors) and a
   // (max, sum) pair per lane.
   static constexpr int PART_O = D * 64;
@@ -152,7 +160,8 @@ __device__ __forceinline__ floatx16 mfma_f16(f16x8 a, f16x8 b, floatx16 c) {
 }
 
 // Two bf16 (one dword) -> two fp16 (one dword), round toward zero.  Exact for
-// bf16 values in fp16's normal range; larger magnitudes saturate at 65504.
+// bf16 values in fp16's normal range; larger magnitudes saturate at 65504,
+// smaller ones lose low bits as fp16 subnormals (absolute error < 6e-8).
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
   const float lo = __uint_as_float(x << 16);
   const float hi = __uint_as_float(x & 0xFFFF0000u);
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
     }
   };
 
-  // ---- S^T of one tile for both sets: every K fragment read feeds kSets
+  // ---- S^T of one tile for every set: each K fragment read feeds kSets
   // MFMAs.  Lane (l32, hh) reads chunk 2 ks + hh of key 32 t2 + l32, stored at
   // slot (2 ks + hh) ^ (l32 % 8): the per-k-step address is one XOR.  The
   // bias step's A fragment comes prebuilt (see v_pack).
@@ -518,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
     l_run[r] += rs;
   };
 
-  // ---- O^T += V^T P^T for both sets: every V^T fragment read feeds two MFMAs
+  // ---- O^T += V^T P^T for every set: each V^T fragment read feeds kSets MFMAs
   auto pv = [&](const char* vimg, uint32_t (&pk)[kSets][2][8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {
