@@ -48,7 +48,8 @@ Pins (tests in ``tests/test_oracle_pins.py``):
   compact_rows     -- bytewise definition on random bytes.
   gated_attention  -- torch SDPA (fp64) with K=N, g=0, tau=1; masking identity
                       vs torch SDPA with an additive float mask on the full-N
-                      problem; two-key closed form; first-row identity; shift
+                      problem; two-key closed form; first-row identity; a
+                      dominant bias on one key returns that key's v; shift
                       invariance; temperature equivalence; golden fixture.
   full_attention   -- torch SDPA (fp64, causal, GQA by repetition).
 No function is "parity unpinned".
