@@ -115,8 +115,15 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
   auto load_chunk = [&](int set, int c) __attribute__((always_inline)) {
     const int k0 = ((start + c) % n_chunks) * kKC;
     const uint32_t kb = static_cast<uint32_t>(k0) * 2;
-    const __amdgpu_buffer_rsrc_t rw_ = make_rsrc(w_base + kb, w_bytes > kb ? w_bytes - kb : 0u);
-    const __amdgpu_buffer_rsrc_t rh_ = make_rsrc(h_base + kb, h_bytes > kb ? h_bytes - kb : 0u);
+    // Past the last chunk the loads still issue, against empty ranges (they
+    // return zeros and touch no memory): every stage then issues the same
+    // loads, and the compiler waits for exactly the set a stage stores while
+    // the other set stays in flight.
+    const bool live = c < n_chunks;
+    const __amdgpu_buffer_rsrc_t rw_ =
+        make_rsrc(w_base + kb, live && w_bytes > kb ? w_bytes - kb : 0u);
+    const __amdgpu_buffer_rsrc_t rh_ =
+        make_rsrc(h_base + kb, live && h_bytes > kb ? h_bytes - kb : 0u);
 #pragma unroll
     for (int p = 0; p < W_PER_T; ++p) wreg[set][p] = bload16(rw_, w_off[p]);
 #pragma unroll
@@ -155,13 +162,15 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
     constexpr int buf = decltype(buf_c)::value;
     store_chunk(buf);
     __syncthreads();
-    if (c + 2 < n_chunks) load_chunk(buf, c + 2);
+    load_chunk(buf, c + 2);
+    __builtin_amdgcn_sched_barrier(0);   // issue the loads before this chunk's MFMAs
     compute(buf);
   };
 
   // n_chunks is even (hidden % 64 == 0): both unrolled stages run every trip,
   // which keeps the accumulators in place across the loop back-edge.
   load_chunk(0, 0);
+  __builtin_amdgcn_sched_barrier(0);   // keep chunk 0's loads older than chunk 1's
   load_chunk(1, 1);
   for (int c = 0; c < n_chunks; c += 2) {
     stage(std::integral_constant<int, 0>{}, c);
