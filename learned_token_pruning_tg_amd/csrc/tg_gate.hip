@@ -8,17 +8,21 @@
 // MFMA, computed as Z^T = W1 . h^T so that each lane owns one token column and
 // 16 gate units per 32x32 tile: GELU, the w2 weighting and the reduction over
 // gate units stay lane-local, plus one exchange between lane halves and a
-// fixed-order sum over the four column waves in LDS (deterministic, no
-// atomics, no workspace).
+// fixed-order sum over the column waves in LDS (deterministic, no atomics, no
+// workspace).
 //  * One work-group takes BM tokens and all gate units (padded to 128 * CT;
 //    padding units read as zeros and contribute nothing), so h streams from
 //    HBM exactly once while W1 (2 MiB at Qwen3 shapes) is re-read from L2
 //    once per BM tokens.
+//  * Eight column waves per 64 tokens (two per SIMD) where the gate units
+//    split evenly over them, else four.
 //  * K is streamed in 32-wide chunks through double-buffered, padded LDS tiles
 //    with one barrier per chunk; raw buffer loads run two chunks ahead of the
-//    MFMAs (two register stage sets).  Per-chunk descriptors put
-//    the hardware range check on the row boundary, so rows past n read as
-//    zeros without per-row guards.
+//    MFMAs (two register stage sets).  Scheduling barriers keep every chunk's
+//    loads issued in chunk order, so the wait before storing chunk c counts
+//    only chunk c's loads and chunk c + 1's stay in flight.  Per-chunk
+//    descriptors put the hardware range check on the row boundary, so rows
+//    past n read as zeros without per-row guards.
 //  * Work-groups start their K loop at staggered chunks so the CUs of one XCD
 //    do not all hit the same W1 lines of L2 at the same time.
 //  * erf uses Abramowitz & Stegun formula 7.1.26 (|error| <= 1.5e-7),
@@ -54,28 +58,31 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.f + erf_as(z * 0.70710678118654752f));
 }
 
-// BM tokens per work-group (BM / 64 row groups x 4 column waves); each wave
-// owns CT gate-unit tiles of 32, so the work-group covers 128 * CT units.
-template <int BM, int CT>
-__global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
+// BM tokens per work-group (BM / 64 row groups x CW column waves); the
+// work-group covers 128 * CT gate units, each wave UT = 4 CT / CW tiles of 32.
+template <int BM, int CT, int CW>
+__global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
     const bf16* __restrict__ h, int64_t n, int64_t ld_h, int H, const bf16* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2, int Hg,
     float* __restrict__ scores) {
-  constexpr int NT = BM / 64 * 256;
+  constexpr int NT = BM / 64 * CW * 64;
   constexpr int HGP = 128 * CT;                 // padded gate units
-  constexpr int W_PER_T = HGP * (kKC / 8) / NT;
-  constexpr int H_PER_T = BM * (kKC / 8) / NT;
-  static_assert(HGP * (kKC / 8) % NT == 0 && BM * (kKC / 8) % NT == 0, "chunk split");
+  constexpr int UT = 4 * CT / CW;               // 32-unit tiles per wave
+  constexpr int W_PIECES = HGP * (kKC / 8);    // 16-byte pieces of a W1 chunk
+  constexpr int H_PIECES = BM * (kKC / 8);      // ... of an h chunk
+  constexpr int W_PER_T = (W_PIECES + NT - 1) / NT;
+  constexpr int H_PER_T = (H_PIECES + NT - 1) / NT;
+  static_assert(4 * CT % CW == 0, "unit tiles split over the column waves");
 
   __shared__ __align__(16) bf16 w_lds[2][HGP * kLD];
   __shared__ __align__(16) bf16 h_lds[2][BM * kLD];
-  __shared__ float red[4][BM];
+  __shared__ float red[CW][BM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int rw = wave >> 2;   // 64-token group
-  const int cw = wave & 3;    // column wave: gate-unit tiles cw + 4 i
+  const int rw = wave / CW;   // 64-token group
+  const int cw = wave % CW;   // column wave: gate-unit tiles cw + CW i
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int64_t rows_left = n - row0;
   const uint32_t rows_valid = static_cast<uint32_t>(rows_left < BM ? rows_left : BM);
@@ -90,25 +97,31 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
 #pragma unroll
   for (int p = 0; p < W_PER_T; ++p) {
     const int f = tid + p * NT;
-    w_off[p] = static_cast<uint32_t>(f >> 2) * w_row_bytes + 16 * (f & 3);
+    // threads without a piece read past every range (zeros, no memory access)
+    w_off[p] = f < W_PIECES ? static_cast<uint32_t>(f / (kKC / 8)) * w_row_bytes + 16 * (f % (kKC / 8))
+                            : 0x80000000u;
   }
 #pragma unroll
   for (int p = 0; p < H_PER_T; ++p) {
     const int f = tid + p * NT;
-    h_off[p] = static_cast<uint32_t>(f >> 2) * h_row_bytes + 16 * (f & 3);
+    // threads without a piece read past every range (zeros, no memory access)
+    h_off[p] = f < H_PIECES ? static_cast<uint32_t>(f / (kKC / 8)) * h_row_bytes + 16 * (f % (kKC / 8))
+                            : 0x80000000u;
   }
 
-  floatx16 acc[CT][2];
+  floatx16 acc[UT][2];
 #pragma unroll
-  for (int i = 0; i < CT; ++i) {
+  for (int i = 0; i < UT; ++i) {
     acc[i][0] = zero16();
     acc[i][1] = zero16();
   }
 
-  // Two register stage sets: chunk c is loaded at stage c - 2 into set c & 1,
-  // so each load has two chunks of MFMA work to arrive.
-  u32x4 wreg[2][W_PER_T];
-  u32x4 hreg[2][H_PER_T];
+  // NS register stage sets: chunk c is loaded at stage c - NS into set
+  // c % NS, so each load has NS chunks of work to arrive (four sets measured
+  // no faster).
+  constexpr int NS = 2;
+  u32x4 wreg[NS][W_PER_T];
+  u32x4 hreg[NS][H_PER_T];
   const int n_chunks = H / kKC;
   const int start = static_cast<int>(blockIdx.x >> 3) % n_chunks;
 
@@ -129,16 +142,18 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
 #pragma unroll
     for (int p = 0; p < H_PER_T; ++p) hreg[set][p] = bload16(rh_, h_off[p]);
   };
-  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
+  auto store_chunk = [&](int set, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < W_PER_T; ++p) {
       const int f = tid + p * NT;
-      st16(&w_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], wreg[buf][p]);
+      if (W_PIECES % NT == 0 || f < W_PIECES)
+        st16(&w_lds[buf][(f / (kKC / 8)) * kLD + 8 * (f % (kKC / 8))], wreg[set][p]);
     }
 #pragma unroll
     for (int p = 0; p < H_PER_T; ++p) {
       const int f = tid + p * NT;
-      st16(&h_lds[buf][(f >> 2) * kLD + 8 * (f & 3)], hreg[buf][p]);
+      if (H_PIECES % NT == 0 || f < H_PIECES)
+        st16(&h_lds[buf][(f / (kKC / 8)) * kLD + 8 * (f % (kKC / 8))], hreg[set][p]);
     }
   };
   auto compute = [&](int buf) __attribute__((always_inline)) {
@@ -149,8 +164,8 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
       for (int tt = 0; tt < 2; ++tt)
         hb[tt] = lds_bf16x8(&h_lds[buf][(64 * rw + 32 * tt + l32) * kLD + 16 * ks + 8 * hh]);
 #pragma unroll
-      for (int i = 0; i < CT; ++i) {
-        const bf16x8 a = lds_bf16x8(&w_lds[buf][(32 * (cw + 4 * i) + l32) * kLD + 16 * ks + 8 * hh]);
+      for (int i = 0; i < UT; ++i) {
+        const bf16x8 a = lds_bf16x8(&w_lds[buf][(32 * (cw + CW * i) + l32) * kLD + 16 * ks + 8 * hh]);
         acc[i][0] = mfma_32x32x16(a, hb[0], acc[i][0]);
         acc[i][1] = mfma_32x32x16(a, hb[1], acc[i][1]);
       }
@@ -158,21 +173,25 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
   };
   // One barrier per chunk: the LDS buffer written at chunk c was last read at
   // chunk c - 2, which every wave finished before passing barrier c - 1.
-  auto stage = [&](auto buf_c, int c) __attribute__((always_inline)) {
-    constexpr int buf = decltype(buf_c)::value;
-    store_chunk(buf);
+  auto stage = [&](auto set_c, int c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    constexpr int buf = set & 1;          // = c & 1 (NS is even)
+    store_chunk(set, buf);
     __syncthreads();
-    load_chunk(buf, c + 2);
+    load_chunk(set, c + NS);
     __builtin_amdgcn_sched_barrier(0);   // issue the loads before this chunk's MFMAs
     compute(buf);
   };
 
-  // n_chunks is even (hidden % 64 == 0): both unrolled stages run every trip,
-  // which keeps the accumulators in place across the loop back-edge.
+  // Every trip runs all NS stages (keeping the accumulators in place across
+  // the back-edge); stages past the last chunk load and add zeros.
   load_chunk(0, 0);
-  __builtin_amdgcn_sched_barrier(0);   // keep chunk 0's loads older than chunk 1's
-  load_chunk(1, 1);
-  for (int c = 0; c < n_chunks; c += 2) {
+#pragma unroll
+  for (int c = 1; c < NS; ++c) {
+    __builtin_amdgcn_sched_barrier(0);   // keep chunk c - 1's loads older than chunk c's
+    load_chunk(c, c);
+  }
+  for (int c = 0; c < n_chunks; c += NS) {
     stage(std::integral_constant<int, 0>{}, c);
     stage(std::integral_constant<int, 1>{}, c + 1);
   }
@@ -183,10 +202,10 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
   const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(w2, 4u * Hg);
   float part[2] = {0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < CT; ++i) {
+  for (int i = 0; i < UT; ++i) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const uint32_t u = 32 * (cw + 4 * i) + 8 * (j >> 2) + 4 * hh + (j & 3);
+      const uint32_t u = 32 * (cw + CW * i) + 8 * (j >> 2) + 4 * hh + (j & 3);
       const float bu = bload4f(rb1, 4 * u), wu = bload4f(rw2, 4 * u);
       part[0] = fmaf(wu, gelu_erf(acc[i][0][j] + bu), part[0]);
       part[1] = fmaf(wu, gelu_erf(acc[i][1][j] + bu), part[1]);
@@ -199,27 +218,34 @@ __global__ __launch_bounds__(BM / 64 * 256) void gate_score_kernel(
   }
   __syncthreads();
   for (int r = tid; r < BM; r += NT) {
-    if (r < static_cast<int>(rows_valid))
-      scores[row0 + r] = (((red[0][r] + red[1][r]) + red[2][r]) + red[3][r]) + b2;
+    if (r < static_cast<int>(rows_valid)) {
+      float acc_r = red[0][r];
+#pragma unroll
+      for (int c = 1; c < CW; ++c) acc_r += red[c][r];   // fixed order
+      scores[row0 + r] = acc_r + b2;
+    }
   }
 }
 
-template <int BM, int CT>
+template <int BM, int CT, int CW = 4>
 void launch_bm_ct(const bf16* h, int64_t n, int64_t ld_h, int H, const bf16* w1, const float* b1,
                   const float* w2, float b2, int Hg, float* scores, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((n + BM - 1) / BM));
-  hipLaunchKernelGGL((gate_score_kernel<BM, CT>), grid, dim3(BM / 64 * 256), 0, stream, h, n,
-                     ld_h, H, w1, b1, w2, b2, Hg, scores);
+  hipLaunchKernelGGL((gate_score_kernel<BM, CT, CW>), grid, dim3(BM / 64 * CW * 64), 0, stream,
+                     h, n, ld_h, H, w1, b1, w2, b2, Hg, scores);
 }
 
-template <int BM>
+// CW8: eight column waves where the unit tiles split evenly (Hg > 128 and
+// not in (256, 384]); else four.
+template <int BM, bool CW8>
 void launch_bm(const bf16* h, int64_t n, int64_t ld_h, int H, const bf16* w1, const float* b1,
                const float* w2, float b2, int Hg, float* scores, hipStream_t stream) {
+  constexpr int CW = CW8 ? 8 : 4;
   switch ((Hg + 127) / 128) {
     case 1: launch_bm_ct<BM, 1>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
-    case 2: launch_bm_ct<BM, 2>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    case 2: launch_bm_ct<BM, 2, CW>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
     case 3: launch_bm_ct<BM, 3>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
-    default: launch_bm_ct<BM, 4>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    default: launch_bm_ct<BM, 4, CW>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
   }
 }
 
@@ -234,9 +260,9 @@ hipError_t launch_gate_score(const uint16_t* h, int64_t n, int64_t ld_h, int hid
   // 128-token tiles halve the W1 re-reads; use them once they still give at
   // least two work-groups per compute unit.
   if (n >= 128 * 512)
-    launch_bm<128>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
+    launch_bm<128, true>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
   else
-    launch_bm<64>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
+    launch_bm<64, true>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
   return hipGetLastError();
 }
 

@@ -43,7 +43,8 @@ def test_gate_tiny(random_bias):
 
 @pytest.mark.parametrize("n,hidden,hg,ld", [(1000, 256, 96, 264), (1, 64, 32, 64),
                                            (130, 512, 512, 520), (64, 128, 64, 128),
-                                           (333, 192, 200, 200), (77, 64, 1, 64)])
+                                           (333, 192, 200, 200), (77, 64, 1, 64),
+                                           (300, 128, 384, 136), (66000, 64, 256, 64)])
 def test_gate_ragged_strided(n, hidden, hg, ld):
     rng = np.random.default_rng(n + hg)
     base = inputs.round_bf16(rng.standard_normal((n, ld)).astype(np.float32))
