@@ -16,8 +16,8 @@
 //    once per BM tokens.
 //  * Eight column waves per 64 tokens (two per SIMD) where the gate units
 //    split evenly over them, else four.
-//  * K is streamed in 32-wide chunks through double-buffered, padded LDS tiles
-//    with one barrier per chunk; raw buffer loads run two chunks ahead of the
+//  * K is streamed in 64-wide (64-token work-groups) or 32-wide chunks
+//    through double-buffered LDS tiles with one barrier per chunk; raw buffer loads run two chunks ahead of the
 //    MFMAs (two register stage sets).  Scheduling barriers keep every chunk's
 //    loads issued in chunk order, so the wait before storing chunk c counts
 //    only chunk c's loads and chunk c + 1's stay in flight.  Per-chunk
@@ -35,8 +35,6 @@
 namespace tg {
 namespace {
 
-constexpr int kKC = 32;          // K chunk
-constexpr int kLD = kKC + 8;     // padded LDS row (80 B): conflict-free 16-byte reads
 
 // erf(x) by Abramowitz & Stegun 7.1.26: for x >= 0,
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
@@ -60,7 +58,11 @@ __device__ __forceinline__ float gelu_erf(float z) {
 
 // BM tokens per work-group (BM / 64 row groups x CW column waves); the
 // work-group covers 128 * CT gate units, each wave UT = 4 CT / CW tiles of 32.
-template <int BM, int CT, int CW>
+// KC: K chunk (32 or 64).  LDS rows of a 32-wide chunk are padded to 80 B;
+// rows of a 64-wide chunk are 128 B with 16-byte piece j of row r stored at
+// slot j ^ (r % 8).  Either way the fragment reads are free of bank
+// conflicts.
+template <int BM, int CT, int CW, int KC>
 __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
     const bf16* __restrict__ h, int64_t n, int64_t ld_h, int H, const bf16* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2, int Hg,
@@ -68,14 +70,20 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
   constexpr int NT = BM / 64 * CW * 64;
   constexpr int HGP = 128 * CT;                 // padded gate units
   constexpr int UT = 4 * CT / CW;               // 32-unit tiles per wave
-  constexpr int W_PIECES = HGP * (kKC / 8);    // 16-byte pieces of a W1 chunk
-  constexpr int H_PIECES = BM * (kKC / 8);      // ... of an h chunk
+  static_assert(KC == 32 || KC == 64, "K chunk");
+  constexpr int P = KC / 8;                     // 16-byte pieces per row of a chunk
+  constexpr int LD = KC == 32 ? 40 : 64;        // LDS row, bf16 elements
+  constexpr int W_PIECES = HGP * P;             // 16-byte pieces of a W1 chunk
+  constexpr int H_PIECES = BM * P;              // ... of an h chunk
   constexpr int W_PER_T = (W_PIECES + NT - 1) / NT;
   constexpr int H_PER_T = (H_PIECES + NT - 1) / NT;
   static_assert(4 * CT % CW == 0, "unit tiles split over the column waves");
 
-  __shared__ __align__(16) bf16 w_lds[2][HGP * kLD];
-  __shared__ __align__(16) bf16 h_lds[2][BM * kLD];
+  __shared__ __align__(16) bf16 w_lds[2][HGP * LD];
+  __shared__ __align__(16) bf16 h_lds[2][BM * LD];
+  auto lds_at = [](int row, int piece) {
+    return row * LD + 8 * (KC == 64 ? piece ^ (row & 7) : piece);
+  };
   __shared__ float red[CW][BM];
 
   const int tid = threadIdx.x;
@@ -98,14 +106,14 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
   for (int p = 0; p < W_PER_T; ++p) {
     const int f = tid + p * NT;
     // threads without a piece read past every range (zeros, no memory access)
-    w_off[p] = f < W_PIECES ? static_cast<uint32_t>(f / (kKC / 8)) * w_row_bytes + 16 * (f % (kKC / 8))
+    w_off[p] = f < W_PIECES ? static_cast<uint32_t>(f / P) * w_row_bytes + 16 * (f % P)
                             : 0x80000000u;
   }
 #pragma unroll
   for (int p = 0; p < H_PER_T; ++p) {
     const int f = tid + p * NT;
     // threads without a piece read past every range (zeros, no memory access)
-    h_off[p] = f < H_PIECES ? static_cast<uint32_t>(f / (kKC / 8)) * h_row_bytes + 16 * (f % (kKC / 8))
+    h_off[p] = f < H_PIECES ? static_cast<uint32_t>(f / P) * h_row_bytes + 16 * (f % P)
                             : 0x80000000u;
   }
 
@@ -122,11 +130,11 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
   constexpr int NS = 2;
   u32x4 wreg[NS][W_PER_T];
   u32x4 hreg[NS][H_PER_T];
-  const int n_chunks = H / kKC;
+  const int n_chunks = H / KC;
   const int start = static_cast<int>(blockIdx.x >> 3) % n_chunks;
 
   auto load_chunk = [&](int set, int c) __attribute__((always_inline)) {
-    const int k0 = ((start + c) % n_chunks) * kKC;
+    const int k0 = ((start + c) % n_chunks) * KC;
     const uint32_t kb = static_cast<uint32_t>(k0) * 2;
     // Past the last chunk the loads still issue, against empty ranges (they
     // return zeros and touch no memory): every stage then issues the same
@@ -147,25 +155,25 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
     for (int p = 0; p < W_PER_T; ++p) {
       const int f = tid + p * NT;
       if (W_PIECES % NT == 0 || f < W_PIECES)
-        st16(&w_lds[buf][(f / (kKC / 8)) * kLD + 8 * (f % (kKC / 8))], wreg[set][p]);
+        st16(&w_lds[buf][lds_at(f / P, f % P)], wreg[set][p]);
     }
 #pragma unroll
     for (int p = 0; p < H_PER_T; ++p) {
       const int f = tid + p * NT;
       if (H_PIECES % NT == 0 || f < H_PIECES)
-        st16(&h_lds[buf][(f / (kKC / 8)) * kLD + 8 * (f % (kKC / 8))], hreg[set][p]);
+        st16(&h_lds[buf][lds_at(f / P, f % P)], hreg[set][p]);
     }
   };
   auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < kKC / 16; ++ks) {
+    for (int ks = 0; ks < KC / 16; ++ks) {
       bf16x8 hb[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        hb[tt] = lds_bf16x8(&h_lds[buf][(64 * rw + 32 * tt + l32) * kLD + 16 * ks + 8 * hh]);
+        hb[tt] = lds_bf16x8(&h_lds[buf][lds_at(64 * rw + 32 * tt + l32, 2 * ks + hh)]);
 #pragma unroll
       for (int i = 0; i < UT; ++i) {
-        const bf16x8 a = lds_bf16x8(&w_lds[buf][(32 * (cw + CW * i) + l32) * kLD + 16 * ks + 8 * hh]);
+        const bf16x8 a = lds_bf16x8(&w_lds[buf][lds_at(32 * (cw + CW * i) + l32, 2 * ks + hh)]);
         acc[i][0] = mfma_32x32x16(a, hb[0], acc[i][0]);
         acc[i][1] = mfma_32x32x16(a, hb[1], acc[i][1]);
       }
@@ -227,25 +235,25 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
   }
 }
 
-template <int BM, int CT, int CW = 4>
+template <int BM, int CT, int CW, int KC>
 void launch_bm_ct(const bf16* h, int64_t n, int64_t ld_h, int H, const bf16* w1, const float* b1,
                   const float* w2, float b2, int Hg, float* scores, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>((n + BM - 1) / BM));
-  hipLaunchKernelGGL((gate_score_kernel<BM, CT, CW>), grid, dim3(BM / 64 * CW * 64), 0, stream,
+  hipLaunchKernelGGL((gate_score_kernel<BM, CT, CW, KC>), grid, dim3(BM / 64 * CW * 64), 0, stream,
                      h, n, ld_h, H, w1, b1, w2, b2, Hg, scores);
 }
 
 // CW8: eight column waves where the unit tiles split evenly (Hg > 128 and
 // not in (256, 384]); else four.
-template <int BM, bool CW8>
+template <int BM, bool CW8, int KC>
 void launch_bm(const bf16* h, int64_t n, int64_t ld_h, int H, const bf16* w1, const float* b1,
                const float* w2, float b2, int Hg, float* scores, hipStream_t stream) {
   constexpr int CW = CW8 ? 8 : 4;
   switch ((Hg + 127) / 128) {
-    case 1: launch_bm_ct<BM, 1>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
-    case 2: launch_bm_ct<BM, 2, CW>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
-    case 3: launch_bm_ct<BM, 3>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
-    default: launch_bm_ct<BM, 4, CW>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    case 1: launch_bm_ct<BM, 1, 4, KC>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    case 2: launch_bm_ct<BM, 2, CW, KC>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    case 3: launch_bm_ct<BM, 3, 4, KC>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
+    default: launch_bm_ct<BM, 4, CW, KC>(h, n, ld_h, H, w1, b1, w2, b2, Hg, scores, stream); break;
   }
 }
 
@@ -258,11 +266,12 @@ hipError_t launch_gate_score(const uint16_t* h, int64_t n, int64_t ld_h, int hid
   const bf16* hp = reinterpret_cast<const bf16*>(h);
   const bf16* wp = reinterpret_cast<const bf16*>(w1);
   // 128-token tiles halve the W1 re-reads; use them once they still give at
-  // least two work-groups per compute unit.
+  // least two work-groups per compute unit.  64-wide K chunks (half the
+  // barriers) fit LDS only with 64-token tiles.
   if (n >= 128 * 512)
-    launch_bm<128, true>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
+    launch_bm<128, true, 32>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
   else
-    launch_bm<64, true>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
+    launch_bm<64, true, 64>(hp, n, ld_h, hidden, wp, b1, w2, b2, gate_hidden, scores, stream);
   return hipGetLastError();
 }
 
