@@ -60,8 +60,8 @@ __device__ __forceinline__ float gelu_erf(float z) {
 // work-group covers 128 * CT gate units, each wave UT = 4 CT / CW tiles of 32.
 // KC: K chunk (32 or 64).  LDS rows of a 32-wide chunk are padded to 80 B;
 // rows of a 64-wide chunk are 128 B with 16-byte piece j of row r stored at
-// slot j ^ (r % 8).  Either way the fragment reads are free of bank
-// conflicts.
+// slot j ^ ((r / 2) % 8).  Either way the 16 lanes that one pass of a 16-byte
+// LDS read serves (64 banks of 4 bytes) hit 16 different bank groups.
 template <int BM, int CT, int CW, int KC>
 __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
     const bf16* __restrict__ h, int64_t n, int64_t ld_h, int H, const bf16* __restrict__ w1,
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
   __shared__ __align__(16) bf16 w_lds[2][HGP * LD];
   __shared__ __align__(16) bf16 h_lds[2][BM * LD];
   auto lds_at = [](int row, int piece) {
-    return row * LD + 8 * (KC == 64 ? piece ^ (row & 7) : piece);
+    return row * LD + 8 * (KC == 64 ? piece ^ ((row >> 1) & 7) : piece);
   };
   __shared__ float red[CW][BM];
 
