@@ -182,11 +182,12 @@ def main():
     outs = [torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
             for _ in range(2)]
     ws = tg.attn_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
+    tws = tg.topk_workspace(w.n, dev)
     # The upper layers' q/k/v of the kept rows stand for what the layers'
     # projections would produce from the kept residual; they are gathered
     # once from the full-N templates with the selection of this very input.
     tg.gate_score(h, w1, b1, w2, g["b2"], out=scores)
-    tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx)
+    tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx, workspace=tws)
     kept_qkv = [tuple(tg.compact(idx, x) for x in full_qkv[t]) for t in range(n_t)]
     torch.cuda.synchronize()
 
@@ -199,7 +200,7 @@ def main():
         tg.gate_score(h, w1, b1, w2, g["b2"], out=scores)
         if ev is not None:
             ev[1].record(stream)
-        tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx)
+        tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx, workspace=tws)
         if ev is not None:
             ev[2].record(stream)
         tg.compact(idx, h, out=h_kept)

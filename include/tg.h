@@ -94,6 +94,14 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
                         int32_t gate_hidden, float* scores, tg_stream_t stream);
 
 /*
+ * Bytes of device workspace tg_topk_select needs for n scores: three digit
+ * histograms (20 KiB), the selection state and two counters per range of
+ * rows (at most 1024 ranges): under 29 KiB for any n.  Host-only
+ * arithmetic; 0 for n <= 0 or n >= 2^30.
+ */
+size_t tg_topk_workspace_bytes(int64_t n);
+
+/*
  * Top-K selection over the document rows [doc_begin, doc_end) with every
  * other row kept (lucasainews.com article, "작동 방식": only the document is
  * pruned, the question stays; "사용법과 비용": the budget is a token count).
@@ -103,11 +111,17 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
  *   kept_idx  [tg_kept_count(n, doc_begin, doc_end, k_doc)] int32 (output),
  *             strictly ascending original row indices (they double as the
  *             rows' position ids); may be NULL when that count is 0
- * Exact: the result is unique and reproduced bit for bit.  n < 2^30 (else
- * TG_E_INVALID).
+ *   workspace device scratch of at least tg_topk_workspace_bytes(n) bytes,
+ *             16-byte aligned, owned by the caller; overwritten, carries
+ *             nothing between calls; calls sharing one must be ordered on one
+ *             stream.  Too small or NULL -> TG_E_WORKSPACE.
+ * Exact: the result is unique and reproduced bit for bit (the global
+ * histograms are integer sums, independent of the order of their atomics).
+ * n < 2^30 (else TG_E_INVALID).
  */
 tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
-                         int64_t k_doc, int32_t* kept_idx, tg_stream_t stream);
+                         int64_t k_doc, int32_t* kept_idx, void* workspace,
+                         size_t workspace_bytes, tg_stream_t stream);
 
 /*
  * Row compaction (lucasainews.com article, "작동 방식": only kept rows go

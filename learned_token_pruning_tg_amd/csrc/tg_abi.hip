@@ -98,16 +98,27 @@ tg_status tg_gate_score(const tg_bf16* h, int64_t n, int64_t ld_h, int32_t hidde
                     "tg_gate_score launch");
 }
 
+size_t tg_topk_workspace_bytes(int64_t n) {
+  if (n <= 0 || n >= (int64_t(1) << 30)) return 0;
+  return tg::topk_workspace_bytes(n);
+}
+
 tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
-                         int64_t k_doc, int32_t* kept_idx, tg_stream_t stream) {
+                         int64_t k_doc, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
+                         tg_stream_t stream) {
   if (n < 0 || n >= (int64_t(1) << 30))
     return fail(TG_E_INVALID, "tg_topk_select: n=%lld out of range (n < 2^30)", (long long)n);
   if (tg_kept_count(n, doc_begin, doc_end, k_doc) < 0)
     return fail(TG_E_INVALID, "tg_topk_select: need 0 <= doc_begin=%lld <= doc_end=%lld <= n=%lld, k_doc=%lld >= 0",
                 (long long)doc_begin, (long long)doc_end, (long long)n, (long long)k_doc);
+  const size_t need = tg::topk_workspace_bytes(n);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(TG_E_WORKSPACE, "tg_topk_select: workspace %p of %zu bytes (need %zu, 16-byte aligned)",
+                workspace, workspace_bytes, need);
   if (n == 0 || tg_kept_count(n, doc_begin, doc_end, k_doc) == 0) return TG_OK;  // nothing kept
   if (!scores || !kept_idx) return fail(TG_E_INVALID, "tg_topk_select: null pointer");
-  return hip_status(tg::launch_topk_select(scores, n, doc_begin, doc_end, k_doc, kept_idx, as_hip(stream)),
+  return hip_status(tg::launch_topk_select(scores, n, doc_begin, doc_end, k_doc, kept_idx, workspace,
+                                           as_hip(stream)),
                     "tg_topk_select launch");
 }
 

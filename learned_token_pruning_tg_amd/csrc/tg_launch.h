@@ -11,16 +11,19 @@ hipError_t launch_gate_score(const uint16_t* h, int64_t n, int64_t ld_h, int hid
                              const uint16_t* w1, const float* b1, const float* w2, float b2,
                              int gate_hidden, float* scores, hipStream_t stream);
 
+// Bytes of workspace the top-K launch needs for n scores.
+size_t topk_workspace_bytes(int64_t n);
+
 hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
-                              int64_t k_doc, int32_t* kept_idx, hipStream_t stream);
+                              int64_t k_doc, int32_t* kept_idx, void* workspace,
+                              hipStream_t stream);
 
 hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, const void* src,
                           int64_t src_rows, int64_t src_stride, int64_t row_bytes, void* dst,
                           int64_t dst_stride, hipStream_t stream);
 
-// Bytes of workspace the attention launch needs (gated: K~ with the score
-// columns; else without): the packed K~ / V^T tile images, the split-key
-// counters and the split chunks' partial states.
+// Bytes of workspace the attention launch needs: the packed V^T tile images,
+// (gated) the per-key bias fragments, and the split chunks' partial states.
 size_t attn_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_dim, bool gated);
 
 // Bytes of the tile images of one KV head (addressed with 32-bit offsets).

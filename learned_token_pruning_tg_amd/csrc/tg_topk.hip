@@ -10,16 +10,19 @@
 // Design: the kept set is fixed by a threshold key T and a tie budget: every
 // document key > T is kept, and the first `ties` keys == T in index order.
 // T is found by a 3-pass MSB radix select (11 + 11 + 10 bits) with LDS
-// histograms; the ordered output is one pass of block-wide scans.  The whole
-// problem (<= 512 KiB of scores at 128k tokens, L2-resident after the first
-// pass) is latency-bound, so one 1024-thread work-group does all of it: no
-// global atomics, no workspace, no inter-block ordering, bit-exact and
-// deterministic by construction.  Scores are read 16 bytes per lane (buffer
-// loads: reads past n return zeros and are ignored); each pair of waves
-// counts into its own copy of the histogram (scores bunch into a few top
-// digits, so one shared histogram serialises on LDS atomics); the output pass
-// works on 16-row-per-thread chunks laid out so that wave-wide loads and
-// stores are contiguous, and loads the next chunk before scanning this one.
+// histograms; the ordered output is one pass of block-wide scans.  Bit-exact
+// and deterministic by construction on both paths below.
+//  * Short inputs: one 1024-thread work-group does all of it (no global
+//    atomics, no inter-block ordering).  Scores are read 16 bytes per lane
+//    (buffer loads: reads past n return zeros and are ignored); each pair of
+//    waves counts into its own copy of the histogram (scores bunch into a few
+//    top digits, so one shared histogram serialises on LDS atomics); the
+//    output pass works on 16-row-per-thread chunks laid out so that wave-wide
+//    loads and stores are contiguous, and loads the next chunk before
+//    scanning this one.
+//  * Long inputs: the same passes spread over up to 1024 work-groups with
+//    global histograms and per-range counts in the caller's workspace (see
+//    the multi-work-group section).
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -32,6 +35,10 @@ constexpr int kBins = 2048;
 constexpr int kCopies = 8;                         // histogram copies (two waves each)
 constexpr int kPerThread = 16;                     // rows per thread per output chunk
 constexpr int kChunk = kThreads * kPerThread;      // block counts stay below 2^16
+// Rows up to which one work-group does it all: below this the multi-group
+// path's six dependent launches cost more than they save (measured: 20 vs
+// 23 us at 16k rows, 33 vs 23 us at 32k, 108 vs 24 us at 128k).
+constexpr int64_t kSingleGroupMax = 24576;
 
 // Monotone 32-bit key of a float32 score.
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -41,8 +48,9 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (x != x) ? 0u : key;                      // NaN below -inf
 }
 
-// Block-wide exclusive scan of one uint32 per thread; returns the prefix and
-// writes the total to *total.  Uses `tmp` (kWaves entries of LDS).
+// Block-wide exclusive scan of one uint32 per thread (NW waves); returns the
+// prefix and writes the total to *total.  Uses `tmp` (NW entries of LDS).
+template <int NW>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* tmp,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -56,7 +64,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* t
   __syncthreads();
   uint32_t wave_base = 0, sum = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t t = tmp[w];
     wave_base += (w < wave) ? t : 0u;
     sum += t;
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
         hb += hist[c][bb];
       }
       uint32_t tot;
-      const uint32_t above = block_exclusive_scan(ha + hb, scan_tmp, &tot);
+      const uint32_t above = block_exclusive_scan<kWaves>(ha + hb, scan_tmp, &tot);
       if (above < remaining && remaining <= above + ha) {
         sel_digit = static_cast<uint32_t>(ba);
         sel_above = above;
@@ -226,17 +234,301 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Multi-work-group select for long score vectors.  The same threshold key
+// and tie budget, found by the same three digit passes, but every pass is a
+// launch of G work-groups over contiguous row ranges that add their LDS
+// histograms into global ones (integer sums: the totals, and so the result,
+// do not depend on the order of the atomics).  Each pass starts by
+// re-deriving the digits chosen so far from the previous histograms; work-group
+// 0 also records them for the later launches.  A count launch then gives
+// every row range its number of surely kept rows and of threshold ties, and
+// the write launch places each range's kept rows at the offset the ranges
+// before it imply (ties go to the lowest indices).
+// ---------------------------------------------------------------------------
+constexpr int kMThreads = 256;
+constexpr int kMWaves = kMThreads / 64;
+constexpr int kMRowsPerThread = 8;                     // two 16-byte loads per sub-range
+constexpr int kMSub = kMThreads * kMRowsPerThread;     // rows per sub-range (block counts < 2^16)
+constexpr int kMaxGroups = 1024;
+
+// Workspace words: three global histograms, the selection state, then a
+// (sure, ties) count pair per work-group.
+constexpr int kWsHist1 = 0, kWsHist2 = 2048, kWsHist3 = 4096;
+constexpr int kWsSel = 5120;      // [0..2] after digit 1, [3..5] after digit 2, [6..7] T, ties
+constexpr int kWsCounts = 5136;
+
+struct TopkPlan {
+  int groups, rows_per_group;
+};
+
+TopkPlan topk_plan(int64_t n) {
+  const int64_t subs = (n + kMSub - 1) / kMSub;
+  const int64_t subs_per_group = (subs + kMaxGroups - 1) / kMaxGroups;
+  TopkPlan p;
+  p.rows_per_group = static_cast<int>(subs_per_group * kMSub);
+  p.groups = static_cast<int>((n + p.rows_per_group - 1) / p.rows_per_group);
+  return p;
+}
+
+// Digit d (descending order over NB bins of global histogram h) with
+// above(d) < rem <= above(d) + h[d], above(d) = sum of the bins above d.
+// Needs 1 <= rem <= sum of h.  Every thread returns the same (d, above).
+template <int NB>
+__device__ __forceinline__ void select_digit(const uint32_t* __restrict__ h, uint32_t rem,
+                                             uint32_t* tmp, uint32_t* sel, uint32_t& d,
+                                             uint32_t& above) {
+  constexpr int PER = NB / kMThreads;
+  const int t = threadIdx.x;
+  uint32_t v[PER], sum = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    v[e] = h[NB - 1 - (PER * t + e)];
+    sum += v[e];
+  }
+  uint32_t tot;
+  uint32_t a = block_exclusive_scan<kMWaves>(sum, tmp, &tot);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (a < rem && rem <= a + v[e]) {
+      sel[0] = static_cast<uint32_t>(NB - 1 - (PER * t + e));
+      sel[1] = a;
+    }
+    a += v[e];
+  }
+  __syncthreads();
+  d = sel[0];
+  above = sel[1];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kMThreads) void topk_clear_kernel(uint32_t* __restrict__ ws) {
+  for (int i = threadIdx.x; i < kWsSel; i += kMThreads) ws[i] = 0u;
+}
+
+// Digit pass P (1: bits 31..21, 2: bits 20..10, 3: bits 9..0) over the
+// document rows of this work-group's range that match the digits chosen so far.
+template <int P>
+__global__ __launch_bounds__(kMThreads) void topk_hist_kernel(const float* __restrict__ scores,
+                                                              int n, int db, int de, int k,
+                                                              int rows_per_group,
+                                                              uint32_t* __restrict__ ws) {
+  constexpr int NB = P == 3 ? 1024 : 2048;
+  constexpr int SHIFT = P == 1 ? 21 : P == 2 ? 10 : 0;
+  __shared__ uint32_t hist[kMWaves][NB];   // one copy per wave: few top digits take most rows
+  __shared__ uint32_t tmp[kMWaves], sel[2];
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  if (P == 2) {
+    uint32_t d, above;
+    select_digit<2048>(ws + kWsHist1, static_cast<uint32_t>(k), tmp, sel, d, above);
+    prefix = d << 21;
+    pmask = 0x7FFu << 21;
+    if (blockIdx.x == 0 && tid == 0) {
+      ws[kWsSel + 0] = prefix;
+      ws[kWsSel + 1] = pmask;
+      ws[kWsSel + 2] = static_cast<uint32_t>(k) - above;
+    }
+  } else if (P == 3) {
+    const uint32_t rem = ws[kWsSel + 2];
+    uint32_t d, above;
+    select_digit<2048>(ws + kWsHist2, rem, tmp, sel, d, above);
+    prefix = ws[kWsSel + 0] | (d << 10);
+    pmask = ws[kWsSel + 1] | (0x7FFu << 10);
+    if (blockIdx.x == 0 && tid == 0) {
+      ws[kWsSel + 3] = prefix;
+      ws[kWsSel + 4] = pmask;
+      ws[kWsSel + 5] = rem - above;
+    }
+  }
+  for (int b = tid; b < kMWaves * NB; b += kMThreads) (&hist[0][0])[b] = 0u;
+  __syncthreads();
+  uint32_t* my_hist = hist[tid >> 6];
+  const int r0 = blockIdx.x * rows_per_group;
+  const int lo = max(r0, db), hi = min(min(r0 + rows_per_group, n), de);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(scores, static_cast<uint32_t>(n) * 4u);
+  for (int j = (lo & ~3) + 4 * tid; j < hi; j += 4 * kMThreads) {
+    const u32x4 x = bload16(rs, static_cast<uint32_t>(j) * 4u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = score_key(__uint_as_float(x[e]));
+      if (j + e >= lo && j + e < hi && (key & pmask) == prefix)
+        atomicAdd(&my_hist[(key >> SHIFT) & (NB - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = ws + (P == 1 ? kWsHist1 : P == 2 ? kWsHist2 : kWsHist3);
+  for (int b = tid; b < NB; b += kMThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) c += hist[w][b];
+    if (c != 0u) atomicAdd(&gh[b], c);
+  }
+}
+
+// Row r of [0, n): is it kept for sure (non-document, or key > T), or a tie?
+__device__ __forceinline__ void classify(uint32_t bits, int r, int n, int db, int de, uint32_t T,
+                                         bool& sure, bool& eq) {
+  sure = false;
+  eq = false;
+  if (r < n) {
+    if (r < db || r >= de) {
+      sure = true;
+    } else {
+      const uint32_t key = score_key(__uint_as_float(bits));
+      sure = key > T;
+      eq = key == T;
+    }
+  }
+}
+
+// T and the tie budget (from the third histogram, or given), then this
+// range's (sure, ties) counts.
+__global__ __launch_bounds__(kMThreads) void topk_count_kernel(const float* __restrict__ scores,
+                                                               int n, int db, int de, int derive,
+                                                               uint32_t t_given, uint32_t ties_given,
+                                                               int rows_per_group,
+                                                               uint32_t* __restrict__ ws) {
+  __shared__ uint32_t tmp[kMWaves], sel[2];
+  const int tid = threadIdx.x;
+  uint32_t T = t_given, ties = ties_given;
+  if (derive) {
+    const uint32_t rem = ws[kWsSel + 5];
+    uint32_t d, above;
+    select_digit<1024>(ws + kWsHist3, rem, tmp, sel, d, above);
+    T = ws[kWsSel + 3] | d;
+    ties = rem - above;
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    ws[kWsSel + 6] = T;
+    ws[kWsSel + 7] = ties;
+  }
+  const int r0 = blockIdx.x * rows_per_group;
+  const int r1 = min(r0 + rows_per_group, n);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(scores, static_cast<uint32_t>(n) * 4u);
+  uint32_t sure_n = 0, eq_n = 0;
+  for (int j = r0 + 4 * tid; j < r1; j += 4 * kMThreads) {
+    const u32x4 x = bload16(rs, static_cast<uint32_t>(j) * 4u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bool sure, eq;
+      classify(x[e], j + e, r1, db, de, T, sure, eq);
+      sure_n += sure;
+      eq_n += eq;
+    }
+  }
+  uint32_t tot_s, tot_e;
+  block_exclusive_scan<kMWaves>(sure_n, tmp, &tot_s);
+  block_exclusive_scan<kMWaves>(eq_n, tmp, &tot_e);
+  if (tid == 0) {
+    ws[kWsCounts + 2 * blockIdx.x] = tot_s;
+    ws[kWsCounts + 2 * blockIdx.x + 1] = tot_e;
+  }
+}
+
+// Ordered output: this range's offset from the counts of the ranges before
+// it, then sub-ranges of kMSub rows, thread t taking rows 8 t .. 8 t + 7 of
+// each, positions from block scans.
+__global__ __launch_bounds__(kMThreads) void topk_write_kernel(const float* __restrict__ scores,
+                                                               int n, int db, int de,
+                                                               int rows_per_group, int m_total,
+                                                               const uint32_t* __restrict__ ws,
+                                                               int32_t* __restrict__ out) {
+  __shared__ uint32_t tmp[kMWaves];
+  const int tid = threadIdx.x;
+  const uint32_t T = ws[kWsSel + 6], ties = ws[kWsSel + 7];
+  uint32_t out_base = 0, eq_before = 0;
+  for (int i0 = 0; i0 < static_cast<int>(blockIdx.x); i0 += kMThreads) {
+    const int i = i0 + tid;
+    const bool live = i < static_cast<int>(blockIdx.x);
+    const uint32_t sure = live ? ws[kWsCounts + 2 * i] : 0u;
+    const uint32_t eq = live ? ws[kWsCounts + 2 * i + 1] : 0u;
+    uint32_t tot_eq, tot_kept;
+    const uint32_t tb = eq_before + block_exclusive_scan<kMWaves>(eq, tmp, &tot_eq);
+    const uint32_t left = ties > tb ? ties - tb : 0u;
+    block_exclusive_scan<kMWaves>(sure + (eq < left ? eq : left), tmp, &tot_kept);
+    out_base += tot_kept;
+    eq_before += tot_eq;
+  }
+  const int r0 = blockIdx.x * rows_per_group;
+  const int r1 = min(r0 + rows_per_group, n);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(scores, static_cast<uint32_t>(n) * 4u);
+  for (int s0 = r0; s0 < r1; s0 += kMSub) {
+    const int row0 = s0 + kMRowsPerThread * tid;
+    const u32x4 xa = bload16(rs, static_cast<uint32_t>(row0) * 4u);
+    const u32x4 xb = bload16(rs, static_cast<uint32_t>(row0 + 4) * 4u);
+    uint32_t sure_m = 0, eq_m = 0;   // bit e: row row0 + e
+#pragma unroll
+    for (int e = 0; e < kMRowsPerThread; ++e) {
+      bool sure, eq;
+      classify(e < 4 ? xa[e] : xb[e - 4], row0 + e, r1, db, de, T, sure, eq);
+      sure_m |= static_cast<uint32_t>(sure) << e;
+      eq_m |= static_cast<uint32_t>(eq) << e;
+    }
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan<kMWaves>(
+        static_cast<uint32_t>(__builtin_popcount(sure_m)) |
+            (static_cast<uint32_t>(__builtin_popcount(eq_m)) << 16), tmp, &tot);
+    const uint32_t left = ties > eq_before ? ties - eq_before : 0u;   // ties still to take
+    uint32_t sp = pre & 0xFFFFu, ep = pre >> 16;
+#pragma unroll
+    for (int e = 0; e < kMRowsPerThread; ++e) {
+      const bool sure = (sure_m >> e) & 1u, eq = (eq_m >> e) & 1u;
+      const uint32_t pos = out_base + sp + (ep < left ? ep : left);
+      // pos < m_total holds by construction; the guard keeps a logic error
+      // from ever writing past the caller's buffer.
+      if ((sure || (eq && ep < left)) && pos < static_cast<uint32_t>(m_total)) out[pos] = row0 + e;
+      sp += sure;
+      ep += eq;
+    }
+    const uint32_t eq_tot = tot >> 16;
+    out_base += (tot & 0xFFFFu) + (eq_tot < left ? eq_tot : left);
+    eq_before += eq_tot;
+  }
+}
+
 }  // namespace
 
+size_t topk_workspace_bytes(int64_t n) {
+  if (n <= 0) return 0;
+  return static_cast<size_t>(kWsCounts + 2 * topk_plan(n).groups) * 4u;
+}
+
 hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
-                              int64_t k_doc, int32_t* kept_idx, hipStream_t stream) {
+                              int64_t k_doc, int32_t* kept_idx, void* workspace,
+                              hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int64_t n_doc = doc_end - doc_begin;
   const int k = static_cast<int>(k_doc < n_doc ? k_doc : n_doc);
   const int m_total = static_cast<int>(k + (n - n_doc));
-  hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, stream, scores,
-                     static_cast<int>(n), static_cast<int>(doc_begin), static_cast<int>(doc_end), k,
-                     m_total, kept_idx);
+  const int ni = static_cast<int>(n), db = static_cast<int>(doc_begin), de = static_cast<int>(doc_end);
+  if (n <= kSingleGroupMax) {
+    hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, stream, scores, ni, db, de,
+                       k, m_total, kept_idx);
+    return hipGetLastError();
+  }
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  const TopkPlan p = topk_plan(n);
+  const dim3 grid(static_cast<unsigned>(p.groups)), block(kMThreads);
+  const bool derive = k > 0 && k < n_doc;
+  if (derive) {
+    hipLaunchKernelGGL(topk_clear_kernel, dim3(1), block, 0, stream, ws);
+    hipLaunchKernelGGL(topk_hist_kernel<1>, grid, block, 0, stream, scores, ni, db, de, k,
+                       p.rows_per_group, ws);
+    hipLaunchKernelGGL(topk_hist_kernel<2>, grid, block, 0, stream, scores, ni, db, de, k,
+                       p.rows_per_group, ws);
+    hipLaunchKernelGGL(topk_hist_kernel<3>, grid, block, 0, stream, scores, ni, db, de, k,
+                       p.rows_per_group, ws);
+  }
+  // k == 0: nothing exceeds or equals the threshold; k == n_doc: everything
+  // is kept (every key is >= 0, the ties budget covers all rows).
+  const uint32_t t_given = k == 0 ? 0xFFFFFFFFu : 0u;
+  const uint32_t ties_given = k == 0 ? 0u : static_cast<uint32_t>(n_doc);
+  hipLaunchKernelGGL(topk_count_kernel, grid, block, 0, stream, scores, ni, db, de,
+                     derive ? 1 : 0, t_given, ties_given, p.rows_per_group, ws);
+  hipLaunchKernelGGL(topk_write_kernel, grid, block, 0, stream, scores, ni, db, de,
+                     p.rows_per_group, m_total, ws, kept_idx);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ _SIGNATURES = {
     "tg_last_error": (ctypes.c_char_p, []),
     "tg_kept_count": (_I64, [_I64, _I64, _I64, _I64]),
     "tg_gate_score": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, ctypes.c_float, _I32, _P, _P]),
-    "tg_topk_select": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
+    "tg_topk_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "tg_topk_select": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
     "tg_compact": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "tg_attn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
     "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
@@ -123,10 +124,21 @@ def gate_score(h: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Te
     return out
 
 
+def topk_workspace_bytes(n: int) -> int:
+    return int(lib().tg_topk_workspace_bytes(n))
+
+
+def topk_workspace(n: int, device="cuda") -> torch.Tensor:
+    """A device buffer large enough for one top-K call over n scores."""
+    return torch.empty(max(topk_workspace_bytes(n), 16), dtype=torch.uint8, device=device)
+
+
 def topk_select(scores: torch.Tensor, doc_begin: int, doc_end: int, k_doc: int,
-                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
     """Kept row indices (ascending int32) of a top-K over the document rows
-    [doc_begin, doc_end) with every other row kept."""
+    [doc_begin, doc_end) with every other row kept.
+    ``workspace``: scratch from topk_workspace() (allocated per call if None)."""
     _need(scores, "scores", torch.float32)
     n = scores.numel()
     m = kept_count(n, doc_begin, doc_end, k_doc)
@@ -135,7 +147,12 @@ def topk_select(scores: torch.Tensor, doc_begin: int, doc_end: int, k_doc: int,
     _need(out, "out", torch.int32)
     if out.numel() < m:
         raise ValueError(f"out holds {out.numel()} < {m} indices")
+    if workspace is None:
+        workspace = topk_workspace(n, scores.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
     _check(lib().tg_topk_select(_ptr(scores), n, doc_begin, doc_end, k_doc, _ptr(out),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
     return out
 

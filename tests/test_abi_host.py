@@ -36,8 +36,9 @@ def L():
 
 def test_header_declares_the_five_entry_points():
     names = _declared()
-    for fn in ("tg_gate_score", "tg_topk_select", "tg_compact", "tg_gated_attn_fwd",
-               "tg_full_attn_fwd", "tg_kept_count", "tg_status_str", "tg_last_error"):
+    for fn in ("tg_gate_score", "tg_topk_select", "tg_topk_workspace_bytes", "tg_compact",
+               "tg_gated_attn_fwd", "tg_full_attn_fwd", "tg_attn_workspace_bytes",
+               "tg_kept_count", "tg_status_str", "tg_last_error"):
         assert fn in names
 
 
@@ -84,14 +85,39 @@ def test_gate_validation(L):
 
 def test_topk_validation(L):
     f = L.tg_topk_select
-    assert f(A, 10, 0, 11, 3, A, 0) == INVALID
-    assert f(A, 10, 6, 5, 3, A, 0) == INVALID
-    assert f(A, 10, 0, 5, -1, A, 0) == INVALID
-    assert f(None, 10, 0, 5, 3, A, 0) == INVALID
-    assert f(A, 1 << 31, 0, 5, 3, A, 0) == INVALID
-    assert f(A, 1 << 30, 0, 5, 3, A, 0) == INVALID                  # n < 2^30
-    assert f(None, 0, 0, 0, 3, None, 0) == OK
-    assert f(A, 10, 0, 10, 0, None, 0) == OK                             # nothing kept
+    W = 1 << 20  # a (fake) workspace size that is always large enough
+    assert f(A, 10, 0, 11, 3, A, A, W, 0) == INVALID
+    assert f(A, 10, 6, 5, 3, A, A, W, 0) == INVALID
+    assert f(A, 10, 0, 5, -1, A, A, W, 0) == INVALID
+    assert f(None, 10, 0, 5, 3, A, A, W, 0) == INVALID
+    assert f(A, 1 << 31, 0, 5, 3, A, A, W, 0) == INVALID
+    assert f(A, 1 << 30, 0, 5, 3, A, A, W, 0) == INVALID                 # n < 2^30
+    need = L.tg_topk_workspace_bytes(10)
+    assert f(A, 10, 0, 5, 3, A, None, W, 0) == WORKSPACE
+    assert f(A, 10, 0, 5, 3, A, A, need - 1, 0) == WORKSPACE
+    assert f(A, 10, 0, 5, 3, A, A + 4, need, 0) == WORKSPACE             # alignment
+    assert "workspace" in tg.last_error()
+    assert f(None, 0, 0, 0, 3, None, None, 0, 0) == OK
+    assert f(A, 10, 0, 10, 0, None, A, W, 0) == OK                       # nothing kept
+
+
+def _topk_ws(n):
+    """The top-K workspace size restated: 5136 words (three histograms of
+    2048, 2048 and 1024 bins, 16 words of selection state) plus two words per
+    range of rows; ranges are whole multiples of 2048 rows, at most 1024."""
+    subs = -(-n // 2048)
+    rows = 2048 * -(-subs // 1024)
+    groups = -(-n // rows)
+    return (5136 + 2 * groups) * 4
+
+
+@pytest.mark.parametrize("n", [1, 2047, 2048, 2049, 16384, 131072, 2048 * 1024,
+                               2048 * 1024 + 1, (1 << 30) - 1])
+def test_topk_workspace_bytes(L, n):
+    assert L.tg_topk_workspace_bytes(n) == _topk_ws(n)
+    assert L.tg_topk_workspace_bytes(n) < 29 * 1024 + 1
+    assert L.tg_topk_workspace_bytes(0) == 0
+    assert L.tg_topk_workspace_bytes(1 << 30) == 0
 
 
 def test_compact_validation(L):

@@ -110,7 +110,8 @@ def test_topk_special_values_and_ties(seed):
 
 @pytest.mark.parametrize("n,db,de,k", [(131072, 0, 130816, 8192), (131072, 1000, 130000, 8192),
                                        (65536, 0, 65280, 1024), (65536, 0, 65280, 16384),
-                                       (16384, 0, 16128, 2048), (70001, 3, 69999, 33333)])
+                                       (16384, 0, 16128, 2048), (70001, 3, 69999, 33333),
+                                       (2 * 1024 * 2048 + 4099, 517, 2 * 1024 * 2048, 300007)])
 def test_topk_large_quantised(n, db, de, k):
     rng = np.random.default_rng(n + k)
     s32 = (np.round(rng.standard_normal(n) * 64) / 64).astype(np.float32)   # many exact ties
