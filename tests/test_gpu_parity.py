@@ -120,6 +120,24 @@ def test_topk_large_quantised(n, db, de, k):
     assert np.array_equal(a, _topk_gpu(s32, db, de, k))                     # deterministic
 
 
+def test_topk_long_special_values_and_shared_workspace():
+    # The multi-work-group path on NaN/inf/signed-zero/tie-heavy scores, its two
+    # trivial budgets (0 and all), and one workspace reused across calls of
+    # different lengths (nothing may carry over between calls).
+    rng = np.random.default_rng(7)
+    pool = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, 1e-45, -1e-45, 0.5, -2.0, 3.0],
+                    dtype=np.float32)
+    ws = tg.topk_workspace(300000)
+    for n, db, de in ((300000, 17, 299990), (120001, 0, 120001), (40000, 5000, 35000)):
+        s32 = rng.choice(pool, size=n).astype(np.float32)
+        sd = dev_f32(s32)
+        for k in (0, 1, 12345, de - db - 1, de - db, de - db + 7):
+            say(f"topk long n={n} doc=[{db},{de}) k={k}")
+            out = tg.topk_select(sd, db, de, k, workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), O.topk_select(s32, db, de, k)), (n, db, de, k)
+
+
 def test_topk_all_equal():
     s32 = np.full(9000, 1.25, dtype=np.float32)
     assert np.array_equal(_topk_gpu(s32, 10, 8990, 4000), O.topk_select(s32, 10, 8990, 4000))
