@@ -290,13 +290,18 @@ def main():
     gate_bytes = 2.0 * w.n * w.hidden + 2.0 * w.gate_hidden * w.hidden + 4.0 * w.n
     gate_flops = 2.0 * w.n * w.hidden * w.gate_hidden
     compact_bytes = 2.0 * m * (2 * w.hidden + 4)
+    topk_bytes = 4.0 * w.n + 4.0 * m
+
+    def rate(nbytes, ms):
+        gbs = nbytes / (ms / 1e3) / 1e9
+        return {"gb_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
     stages = {
-        "gate": {"ms": round(stage[0], 5),
-                 "gb_s": round(gate_bytes / (stage[0] / 1e3) / 1e9, 1),
-                 "tflops": round(gate_flops / (stage[0] / 1e3) / 1e12, 1)},
-        "topk": {"ms": round(stage[1], 5)},
-        "compact": {"ms": round(stage[2], 5),
-                    "gb_s": round(compact_bytes / (stage[2] / 1e3) / 1e9, 1)},
+        "gate": {"ms": round(stage[0], 5), **rate(gate_bytes, stage[0]),
+                 "tflops": round(gate_flops / (stage[0] / 1e3) / 1e12, 1),
+                 "frac_bf16_peak": round(gate_flops / (stage[0] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "topk": {"ms": round(stage[1], 5), **rate(topk_bytes, stage[1])},
+        "compact": {"ms": round(stage[2], 5), **rate(compact_bytes, stage[2])},
         "gated_attn": {"ms_total": round(stage[3], 4), "ms_per_layer": round(attn_ms_launch, 5),
                        "tflops": round(achieved, 2)},
     }
