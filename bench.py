@@ -234,6 +234,24 @@ def main():
     stage /= args.steps
     attn_ms_launch = stage[3] / w.n_layers
 
+    # The key bias's own cost: the same 27 calls over the same kept rows as
+    # plain causal attention (gain 0, tau 1), timed like the gated loop.
+    def plain_layers():
+        for l in range(w.n_layers):
+            q, k, v = kept_qkv[inputs.template_of_layer(w, l)]
+            tg.full_attn_fwd(q, k, v, out=outs[l & 1], workspace=ws)
+
+    plain_layers()
+    pa = torch.cuda.Event(enable_timing=True)
+    pb = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    pa.record(stream)
+    for _ in range(max(1, min(args.steps, 5))):
+        plain_layers()
+    pb.record(stream)
+    torch.cuda.synchronize()
+    plain_ms_launch = pa.elapsed_time(pb) / max(1, min(args.steps, 5)) / w.n_layers
+
     # ---------------------------------------------------------------- full-N baseline
     full = None
     if not args.no_full_baseline:
@@ -303,7 +321,10 @@ def main():
         "topk": {"ms": round(stage[1], 5), **rate(topk_bytes, stage[1])},
         "compact": {"ms": round(stage[2], 5), **rate(compact_bytes, stage[2])},
         "gated_attn": {"ms_total": round(stage[3], 4), "ms_per_layer": round(attn_ms_launch, 5),
-                       "tflops": round(achieved, 2)},
+                       "tflops": round(achieved, 2),
+                       # the pages put the key-bias kernel at 1.0-1.1x a plain call
+                       "plain_ms_per_layer_same_rows": round(plain_ms_launch, 5),
+                       "bias_cost_ratio": round(attn_ms_launch / plain_ms_launch, 3)},
     }
 
     cpu = None
