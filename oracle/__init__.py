@@ -35,5 +35,6 @@ from .tokengate import (  # noqa: F401
     compact_rows,
     gated_attention,
     full_attention,
+    gated_decode,
     gated_prefill,
 )

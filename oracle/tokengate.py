@@ -52,6 +52,10 @@ Pins (tests in ``tests/test_oracle_pins.py``):
                       dominant bias on one key returns that key's v; shift
                       invariance; temperature equivalence; golden fixture.
   full_attention   -- torch SDPA (fp64, causal, GQA by repetition).
+  gated_decode     -- torch SDPA (fp64) for one query with the additive float
+                      bias and the head's scale; equals the last row of
+                      gated_attention when the new token is the last row;
+                      one key returns its v; a dominant bias selects one key.
 No function is "parity unpinned".
 """
 
@@ -222,6 +226,47 @@ def full_attention(q, k, v, rows=None, return_lse=False):
     n, hq, _ = np.asarray(q).shape
     return gated_attention(q, k, v, np.zeros(n), np.zeros(hq), np.ones(hq),
                            rows=rows, return_lse=return_lse)
+
+
+# ---------------------------------------------------------------------------
+# One decode step over the pruned KV cache ([KO] lede: time to first token;
+# [KO] "작동 방식": above the gate only the kept tokens have KV entries, and
+# their scores bias the logits there).
+# ---------------------------------------------------------------------------
+
+def gated_decode(q, k, v, key_score, gain, tau, return_lse=False):
+    """One new query row per head against every cached key, with the score bias.
+
+    q [Hq, d] (the new token's queries); k, v [n, Hkv, d] (the cache: the kept
+    rows plus the new token's own row, appended by the caller); key_score [n];
+    gain, tau [Hq].  For query head h (KV head h // (Hq/Hkv)):
+        logit_j = q.k_j / (sqrt(d) tau_h) + gain_h * key_score_j,  0 <= j < n
+        out     = sum_j softmax_j(logit) v_j
+    (every cached row precedes or is the new token, so no key is masked).
+    Returns float64 out [Hq, d] and, if asked, the natural-log log-sum-exp [Hq].
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    hq, d = q.shape
+    n, hkv, _ = k.shape
+    assert k.shape == (n, hkv, d) and v.shape == (n, hkv, d) and hq % hkv == 0 and n > 0
+    group = hq // hkv
+    s = np.asarray(key_score, dtype=np.float64).reshape(n)
+    gain = np.asarray(gain, dtype=np.float64).reshape(hq)
+    tau = np.asarray(tau, dtype=np.float64).reshape(hq)
+    out = np.zeros((hq, d), dtype=np.float64)
+    lse = np.zeros(hq, dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        logits = (k[:, g, :].astype(np.float64) @ q[h].astype(np.float64)) / (math.sqrt(d) * tau[h])
+        logits = logits + gain[h] * s
+        mx = logits.max()
+        p = np.exp(logits - mx)
+        l = p.sum()
+        out[h] = (p @ v[:, g, :].astype(np.float64)) / l
+        lse[h] = mx + math.log(l)
+    return (out, lse) if return_lse else out
 
 
 # ---------------------------------------------------------------------------

@@ -264,6 +264,49 @@ def test_attention_dominant_bias_selects_one_key():
                 assert np.array_equal(big[i, h], base[i, h])   # key j is not visible yet
 
 
+def test_decode_vs_sdpa_one_query_with_bias():
+    """One query per head against n cached keys == torch SDPA with the additive
+    float bias gain_h * s_j and scale 1/(sqrt(d) tau_h), GQA by repetition."""
+    rng = np.random.default_rng(21)
+    n, hq, hkv, d = 37, 8, 2, 16
+    q = rng.standard_normal((hq, d))
+    k = rng.standard_normal((n, hkv, d)); v = rng.standard_normal((n, hkv, d))
+    s = rng.standard_normal(n) * 2
+    gain = rng.uniform(0.5, 1.5, hq); tau = rng.uniform(0.8, 1.2, hq)
+    got, lse = O.gated_decode(q, k, v, s, gain, tau, return_lse=True)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        ref = _sdpa(q[None, h:h + 1], k[:, g:g + 1], v[:, g:g + 1],
+                    mask=(gain[h] * s)[None, :], scale=1.0 / (math.sqrt(d) * tau[h]))
+        assert np.max(np.abs(got[h] - ref[0, 0])) < 1e-12
+        logits = torch.from_numpy(k[:, g] @ q[h] / (math.sqrt(d) * tau[h]) + gain[h] * s)
+        assert abs(lse[h] - torch.logsumexp(logits, 0).item()) < 1e-12
+
+
+def test_decode_is_the_last_row_of_prefill_attention():
+    """With the new token appended as the last cached row, its decode output is
+    the last row of causal gated attention over the cache (that row sees every key)."""
+    rng = np.random.default_rng(22)
+    n, hq, hkv, d = 29, 4, 2, 8
+    q, k, v = _rand_qkv(rng, n, hq, hkv, d)
+    s = rng.standard_normal(n)
+    gain = rng.uniform(0.5, 1.5, hq); tau = rng.uniform(0.8, 1.2, hq)
+    pre, pre_lse = O.gated_attention(q, k, v, s, gain, tau, return_lse=True)
+    dec, dec_lse = O.gated_decode(q[-1], k, v, s, gain, tau, return_lse=True)
+    assert np.max(np.abs(dec - pre[-1])) < 1e-13
+    assert np.max(np.abs(dec_lse - pre_lse[:, -1])) < 1e-13
+
+
+def test_decode_single_key_and_dominant_bias():
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((2, 8)); k = rng.standard_normal((6, 1, 8)); v = rng.standard_normal((6, 1, 8))
+    one = O.gated_decode(q, k[:1], v[:1], np.array([0.7]), np.ones(2), np.ones(2))
+    assert np.array_equal(one, np.repeat(v[:1, 0], 2, axis=0))      # softmax of one logit is 1
+    s = np.zeros(6); s[3] = 1.0
+    big = O.gated_decode(q, k, v, s, np.array([70.0, 90.0]), np.ones(2))
+    assert np.max(np.abs(big - v[3, 0][None, :])) < 1e-12
+
+
 def test_attention_uniform_logits_lse_and_mean():
     # q = 0 and s = 0: every visible key has logit 0, so lse_i = log(i+1) and
     # out_i is the running mean of v.
