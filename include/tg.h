@@ -198,6 +198,44 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                            tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
                            tg_stream_t stream);
 
+/*
+ * Bytes of device workspace tg_gated_decode_fwd needs for n cached rows:
+ * per KV head and chunk of 64-256 keys, a (max, sum, head_dim outputs) fp32
+ * state for each of its query heads.  Host-only arithmetic; 0 for arguments
+ * tg_gated_decode_fwd would reject as invalid or unsupported.
+ */
+size_t tg_decode_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim);
+
+/*
+ * One decode step over the pruned KV cache (lucasainews.com article, lede:
+ * the gains are in time to first token; "작동 방식": above the gate only the
+ * kept tokens have KV entries, and their scores bias the logits there with a
+ * per-head gain and temperature).  One new query row per head against every
+ * cached row (the kept rows plus the new token's own row, appended by the
+ * caller, so no key is masked):
+ *     logit_j = q_h . k_j,g / (sqrt(head_dim) * tau[h]) + gain[h] * key_score[j]
+ *     out_h   = sum_j softmax_j(logit) v_j,g,   g = h / (n_q_heads / n_kv_heads)
+ *   q        [n_q_heads, head_dim] bf16, 16-byte aligned
+ *   k_cache, v_cache [n, n_kv_heads, head_dim] bf16, contiguous, 16-byte aligned
+ *   key_score [n], gain, tau [n_q_heads] fp32: all three given (gated, the
+ *            layers above the gate) or all three NULL (plain softmax(q.k/sqrt(d)),
+ *            the gate layer's decode over all rows); else TG_E_INVALID
+ *   out      [n_q_heads, head_dim] bf16 (output, round-to-nearest-even)
+ *   lse      [n_q_heads] fp32 natural-log log-sum-exp (output; may be NULL)
+ *   workspace device scratch of at least tg_decode_workspace_bytes(...) bytes,
+ *            16-byte aligned, caller-owned; overwritten; calls sharing one
+ *            must be ordered on one stream.  Too small -> TG_E_WORKSPACE.
+ * Supported: head_dim in {64, 128}, n_q_heads / n_kv_heads in {1, 2, 4, 8},
+ * n * n_kv_heads * head_dim * 2 < 2^31.  n must be >= 1 (TG_E_INVALID).
+ * Numerics: bf16 inputs, fp32 dot products, softmax and P.V; deterministic.
+ */
+tg_status tg_gated_decode_fwd(const tg_bf16* q, const tg_bf16* k_cache, const tg_bf16* v_cache,
+                              int64_t n, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              const float* key_score, const float* gain, const float* tau,
+                              tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
+                              tg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -176,4 +176,49 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                     "tg_full_attn_fwd launch");
 }
 
+namespace {
+bool decode_shape_ok(int64_t n, int32_t hq, int32_t hkv, int32_t d) {
+  if (n <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;
+  const int32_t g = hq / hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return false;
+  if (d != 64 && d != 128) return false;
+  return n * hkv * d * 2 < (int64_t(1) << 31);
+}
+}  // namespace
+
+size_t tg_decode_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim) {
+  if (!decode_shape_ok(n, n_q_heads, n_kv_heads, head_dim)) return 0;
+  return tg::decode_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim);
+}
+
+tg_status tg_gated_decode_fwd(const tg_bf16* q, const tg_bf16* k_cache, const tg_bf16* v_cache,
+                              int64_t n, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                              const float* key_score, const float* gain, const float* tau,
+                              tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
+                              tg_stream_t stream) {
+  const char* fn = "tg_gated_decode_fwd";
+  if (n <= 0 || n >= (int64_t(1) << 31))
+    return fail(TG_E_INVALID, "%s: n=%lld out of range (n >= 1 cached rows)", fn, (long long)n);
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+    return fail(TG_E_INVALID, "%s: n_q_heads=%d, n_kv_heads=%d", fn, n_q_heads, n_kv_heads);
+  if (!decode_shape_ok(n, n_q_heads, n_kv_heads, head_dim))
+    return fail(TG_E_UNSUPPORTED,
+                "%s: head_dim=%d, group %d, n=%lld (need head_dim 64/128, group 1/2/4/8, "
+                "n * n_kv_heads * head_dim * 2 < 2^31)",
+                fn, head_dim, n_q_heads / n_kv_heads, (long long)n);
+  if (!q || !k_cache || !v_cache || !out) return fail(TG_E_INVALID, "%s: null tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(TG_E_INVALID, "%s: q/k/v/out must be 16-byte aligned", fn);
+  const int nb = (key_score != nullptr) + (gain != nullptr) + (tau != nullptr);
+  if (nb != 0 && nb != 3)
+    return fail(TG_E_INVALID, "%s: key_score, gain and tau must all be given or all be NULL", fn);
+  const size_t need = tg::decode_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(TG_E_WORKSPACE, "%s: workspace %p of %zu bytes (need %zu, 16-byte aligned)", fn,
+                workspace, workspace_bytes, need);
+  return hip_status(tg::launch_decode(q, k_cache, v_cache, n, n_q_heads, n_kv_heads, head_dim,
+                                      key_score, gain, tau, out, lse, workspace, as_hip(stream)),
+                    "tg_gated_decode_fwd launch");
+}
+
 }  // extern "C"

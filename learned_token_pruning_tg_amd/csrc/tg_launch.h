@@ -36,4 +36,13 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const float* gain, const float* tau, uint16_t* out, float* lse,
                            void* workspace, hipStream_t stream);
 
+// Bytes of workspace one decode call needs (the per-chunk partial states).
+size_t decode_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_dim);
+
+// gain == nullptr selects plain attention (no bias, tau = 1).
+hipError_t launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
+                         int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
+                         const float* gain, const float* tau, uint16_t* out, float* lse,
+                         void* workspace, hipStream_t stream);
+
 }  // namespace tg

@@ -35,6 +35,9 @@ _SIGNATURES = {
                                          _P, ctypes.c_size_t, _P]),
     "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
+    "tg_decode_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
+    "tg_gated_decode_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P,
+                                           _P, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -253,4 +256,55 @@ def full_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ws, ws_bytes = _workspace(workspace, n, hq, hkv, d, q.device)
     _check(lib().tg_full_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(out), _ptr(lse),
                                   _ptr(ws), ws_bytes, _stream(stream)))
+    return (out, lse) if lse is not None else out
+
+
+def decode_workspace_bytes(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    return int(lib().tg_decode_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim))
+
+
+def decode_workspace(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                     device="cuda") -> torch.Tensor:
+    """A device buffer large enough for one decode call over n cached rows."""
+    return torch.empty(max(decode_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim), 16),
+                       dtype=torch.uint8, device=device)
+
+
+def gated_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 key_score: Optional[torch.Tensor] = None, gain: Optional[torch.Tensor] = None,
+                 tau: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """One decode step: q [Hq, d] against the cache k/v [n, Hkv, d] (bf16).
+    key_score [n], gain/tau [Hq] (fp32) add the score bias; all None gives
+    plain attention.  Returns out [Hq, d] (and lse [Hq] if requested or given)."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, torch.bfloat16)
+    hq, d = q.shape
+    n, hkv, _ = k_cache.shape
+    if k_cache.shape != (n, hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("decode operand shapes do not match")
+    given = [x is not None for x in (key_score, gain, tau)]
+    if any(given) and not all(given):
+        raise ValueError("key_score, gain and tau go together")
+    if all(given):
+        _need(key_score, "key_score", torch.float32); _need(gain, "gain", torch.float32)
+        _need(tau, "tau", torch.float32)
+        if key_score.shape != (n,) or gain.shape != (hq,) or tau.shape != (hq,):
+            raise ValueError("key_score / gain / tau shapes do not match")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16)
+    if want_lse and lse is None:
+        lse = torch.empty(hq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    if workspace is None:
+        workspace = decode_workspace(n, hq, hkv, d, q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    _check(lib().tg_gated_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), n, hq, hkv, d,
+                                     _ptr(key_score), _ptr(gain), _ptr(tau), _ptr(out), _ptr(lse),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
     return (out, lse) if lse is not None else out

@@ -38,6 +38,7 @@ def test_header_declares_the_five_entry_points():
     names = _declared()
     for fn in ("tg_gate_score", "tg_topk_select", "tg_topk_workspace_bytes", "tg_compact",
                "tg_gated_attn_fwd", "tg_full_attn_fwd", "tg_attn_workspace_bytes",
+               "tg_gated_decode_fwd", "tg_decode_workspace_bytes",
                "tg_kept_count", "tg_status_str", "tg_last_error"):
         assert fn in names
 
@@ -206,3 +207,39 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), fn
                 assert "oracle/" not in text, fn
+
+
+def _decode_ws(n, hq, hkv, d):
+    """The decode workspace restated: chunks of 256, 128 or 64 keys (the largest
+    that still gives >= 512 work-groups over the KV heads, else 64); per (KV
+    head, chunk, query head of its group) a (max, sum, d outputs) fp32 state."""
+    c = 256
+    while c > 64 and -(-n // c) * hkv < 512:
+        c //= 2
+    return hkv * -(-n // c) * (hq // hkv) * (d + 2) * 4
+
+
+@pytest.mark.parametrize("n,hq,hkv,d", [(1, 16, 8, 128), (2304, 16, 8, 128), (8448, 16, 8, 128),
+                                        (131072, 16, 8, 128), (300, 8, 1, 64), (5000, 32, 4, 128),
+                                        (64, 4, 4, 64)])
+def test_decode_workspace_bytes(L, n, hq, hkv, d):
+    assert L.tg_decode_workspace_bytes(n, hq, hkv, d) == _decode_ws(n, hq, hkv, d)
+
+
+def test_decode_validation(L):
+    f = L.tg_gated_decode_fwd
+    W = 1 << 30
+    assert f(A, A, A, 0, 16, 8, 128, A, A, A, A, None, A, W, 0) == INVALID       # no cached row
+    assert f(A, A, A, 10, 16, 6, 128, A, A, A, A, None, A, W, 0) == INVALID      # Hq % Hkv
+    assert f(A, A, A, 10, 16, 8, 96, A, A, A, A, None, A, W, 0) == UNSUPPORTED   # head_dim
+    assert f(A, A, A, 10, 48, 3, 128, A, A, A, A, None, A, W, 0) == UNSUPPORTED  # group 16
+    assert f(A, A, A, 1 << 20, 16, 8, 128, A, A, A, A, None, A, W, 0) == UNSUPPORTED  # 2^31 bytes
+    assert f(A, A, None, 10, 16, 8, 128, A, A, A, A, None, A, W, 0) == INVALID
+    assert f(A, A, A, 10, 16, 8, 128, A, None, A, A, None, A, W, 0) == INVALID   # partial bias
+    assert "all be given" in tg.last_error()
+    assert f(A + 8, A, A, 10, 16, 8, 128, A, A, A, A, None, A, W, 0) == INVALID  # alignment
+    need = L.tg_decode_workspace_bytes(10, 16, 8, 128)
+    assert f(A, A, A, 10, 16, 8, 128, A, A, A, A, None, A, need - 1, 0) == WORKSPACE
+    assert f(A, A, A, 10, 16, 8, 128, None, None, None, A, None, None, W, 0) == WORKSPACE
+    assert L.tg_decode_workspace_bytes(0, 16, 8, 128) == 0
+    assert L.tg_decode_workspace_bytes(10, 16, 8, 96) == 0
