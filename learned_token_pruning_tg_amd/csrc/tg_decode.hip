@@ -13,9 +13,10 @@
 //
 // Design: a single query row makes this a pass over the K and V cache bytes
 // (HBM-bound; a 16-row MFMA tile would be 1/8 used).  Split-KV: a work-group
-// takes a chunk of C keys (C in {64, 128, 256}, the largest that still gives
-// >= 512 work-groups) of one KV head for all G = Hq / Hkv query heads that
-// share it, so each cache byte is read once.  Eight lanes share a key row (16
+// takes a chunk of C keys (C in {64, 128, 256}, see decode_plan) of one KV
+// head for all G = Hq / Hkv query heads that share it, so each cache byte is
+// read once, and requests all of the chunk's K and V bytes before it
+// computes anything.  Eight lanes share a key row (16
 // bytes each per 128 bytes of row: every wave-wide load covers whole 128-byte
 // lines); fp32 dot products reduced across the eight lanes; the chunk's
 // softmax in log2 units with block reductions; P.V again eight lanes per row,
@@ -34,16 +35,20 @@ constexpr int kDThreads = 256;
 constexpr int kDWaves = kDThreads / 64;
 constexpr int kParts = 8;                          // lanes per key row
 constexpr int kRowsPerPass = kDThreads / kParts;   // 32 key rows per pass
-constexpr int kMaxChunk = 256;
 
 struct DecodePlan {
   int chunk, n_chunks;
   size_t bytes;
 };
 
+// Chunk length: the largest of 64, 128, 256 (capped so that the chunk's K and
+// V pieces and the group's query and accumulator registers fit: 256 for
+// groups of up to 2 query heads, 128 for 4, 64 for 8) that still gives >= 512
+// work-groups.
 DecodePlan decode_plan(int64_t n, int Hq, int Hkv, int d) {
   DecodePlan p{};
-  int c = kMaxChunk;
+  const int g = Hq / Hkv;
+  int c = g <= 2 ? 256 : g == 4 ? 128 : 64;
   while (c > 64 && ((n + c - 1) / c) * Hkv < 512) c >>= 1;
   p.chunk = c;
   p.n_chunks = static_cast<int>((n + c - 1) / c);
@@ -74,14 +79,15 @@ __device__ __forceinline__ float block_reduce(float x, float* tmp) {
 
 // One chunk of C keys of KV head blockIdx.y for its G query heads.
 // part layout: [Hkv][n_chunks][G] x (max in log2 units, sum, out[D]).
-template <int D, int G, bool kBias>
+template <int D, int G, int C, bool kBias>
 __global__ __launch_bounds__(kDThreads) void decode_chunk_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, int n,
     int Hq, int Hkv, const float* __restrict__ key_score, const float* __restrict__ gain,
-    const float* __restrict__ tau, int C, float* __restrict__ part) {
+    const float* __restrict__ tau, float* __restrict__ part) {
   constexpr int NL = D / 64;        // 16-byte pieces per lane per key row
   constexpr int DPT = 8 * NL;       // dims per lane: [64 i + 8 r, +8) for i < NL
-  __shared__ float logit[G][kMaxChunk];
+  constexpr int NP = C / kRowsPerPass;   // rows per lane
+  __shared__ float logit[G][C];
   __shared__ float osum[kDWaves][G][D];
   __shared__ float tmp[kDWaves];
 
@@ -94,6 +100,23 @@ __global__ __launch_bounds__(kDThreads) void decode_chunk_kernel(
   const uint32_t cache_bytes = row_bytes * static_cast<uint32_t>(n);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + static_cast<size_t>(kvh) * D, cache_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + static_cast<size_t>(kvh) * D, cache_bytes);
+
+  // Every K and V piece of this lane's rows is requested before any
+  // arithmetic (V does not wait for the softmax): the chunk's whole cache
+  // traffic is in flight at once.  Rows past n read as zeros.
+  u32x4 kx[NP][NL], vx[NP][NL];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const uint32_t off = static_cast<uint32_t>(j0 + kRowsPerPass * pp + slot) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kx[pp][i] = bload16(rk, off + (64 * i + 8 * r) * 2);
+  }
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const uint32_t off = static_cast<uint32_t>(j0 + kRowsPerPass * pp + slot) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vx[pp][i] = bload16(rv, off + (64 * i + 8 * r) * 2);
+  }
 
   // ---- logits of the chunk, log2 units: (q.k) * alpha_h + beta_h * s_j
   {
@@ -114,14 +137,16 @@ __global__ __launch_bounds__(kDThreads) void decode_chunk_kernel(
         }
       }
     }
-    for (int p0 = 0; p0 < C; p0 += kRowsPerPass) {
-      const int j = j0 + p0 + slot;   // rows past n read as zeros
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int p0 = kRowsPerPass * pp;
+      const int j = j0 + p0 + slot;
       float dot[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) dot[g] = 0.f;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const u32x4 x = bload16(rk, static_cast<uint32_t>(j) * row_bytes + (64 * i + 8 * r) * 2);
+        const u32x4 x = kx[pp][i];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float k0 = bf16_lo(x[w]), k1 = bf16_hi(x[w]);
@@ -169,14 +194,15 @@ __global__ __launch_bounds__(kDThreads) void decode_chunk_kernel(
 #pragma unroll
     for (int e = 0; e < DPT; ++e) acc[g][e] = 0.f;
   }
-  for (int p0 = 0; p0 < C; p0 += kRowsPerPass) {
-    const int j = j0 + p0 + slot;
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const int p0 = kRowsPerPass * pp;
     float pj[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) pj[g] = logit[g][p0 + slot];   // 0 past n
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const u32x4 x = bload16(rv, static_cast<uint32_t>(j) * row_bytes + (64 * i + 8 * r) * 2);
+      const u32x4 x = vx[pp][i];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const float v0 = bf16_lo(x[w]), v1 = bf16_hi(x[w]);
@@ -220,40 +246,74 @@ __global__ __launch_bounds__(kDThreads) void decode_chunk_kernel(
   }
 }
 
-// Merge the chunks of one query head (one work-group of D threads, thread =
-// output dim), in chunk order.
+// Merge the chunks of one query head: one work-group of 256 threads; the
+// global max from a strided scan of the chunk maxima, then 256 / D groups of D
+// threads (thread = output dim) each sum a fixed, strided subset of the
+// chunks, and the groups are added in group order (deterministic).
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part,
-                                                           int n_chunks, int G,
-                                                           bf16* __restrict__ out,
-                                                           float* __restrict__ lse) {
+__global__ __launch_bounds__(kDThreads) void decode_combine_kernel(const float* __restrict__ part,
+                                                                  int n_chunks, int G,
+                                                                  bf16* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+  constexpr int NG = kDThreads / D;
+  __shared__ float so[NG][D];
+  __shared__ float sl[NG];
+  __shared__ float tmp[kDWaves];
   const int h = blockIdx.x, kvh = h / G, g = h % G;
-  const int dim = threadIdx.x;
+  const int tid = threadIdx.x, dim = tid % D, cg = tid / D;
   const size_t stride = static_cast<size_t>(G) * (D + 2);
   const float* base = part + static_cast<size_t>(kvh) * n_chunks * stride + g * (D + 2);
   float mx = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) mx = fmaxf(mx, base[c * stride]);
+  for (int c = tid; c < n_chunks; c += kDThreads) mx = fmaxf(mx, base[c * stride]);
+  mx = block_reduce<true>(mx, tmp);
   float l = 0.f, o = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const float w = fast_exp2(base[c * stride] - mx);
-    l = fmaf(base[c * stride + 1], w, l);
-    o = fmaf(base[c * stride + 2 + dim], w, o);
+#pragma unroll 8
+  for (int c = cg; c < n_chunks; c += NG) {
+    const float* pc = base + c * stride;
+    const float w = fast_exp2(pc[0] - mx);
+    l = fmaf(pc[1], w, l);
+    o = fmaf(pc[2 + dim], w, o);
   }
-  out[static_cast<size_t>(h) * D + dim] = static_cast<bf16>(o / l);
-  if (lse != nullptr && dim == 0) lse[h] = (mx + __log2f(l)) * kLn2;
+  so[cg][dim] = o;
+  if (dim == 0) sl[cg] = l;
+  __syncthreads();
+  if (cg == 0) {
+    float ot = so[0][dim], lt = sl[0];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) {
+      ot += so[i][dim];
+      lt += sl[i];
+    }
+    out[static_cast<size_t>(h) * D + dim] = static_cast<bf16>(ot / lt);
+    if (lse != nullptr && dim == 0) lse[h] = (mx + __log2f(lt)) * kLn2;
+  }
+}
+
+template <int D, int G, int C, bool kBias>
+void launch_chunks(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int Hq,
+                   int Hkv, const float* s, const float* gain, const float* tau,
+                   const DecodePlan& p, float* part, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_chunk_kernel<D, G, C, kBias>),
+                     dim3(static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(Hkv)),
+                     dim3(kDThreads), 0, stream, reinterpret_cast<const bf16*>(q),
+                     reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(v), n, Hq,
+                     Hkv, s, gain, tau, part);
 }
 
 template <int D, int G, bool kBias>
 void launch_dg(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, int Hq, int Hkv,
                const float* s, const float* gain, const float* tau, uint16_t* out, float* lse,
                const DecodePlan& p, float* part, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_chunk_kernel<D, G, kBias>),
-                     dim3(static_cast<unsigned>(p.n_chunks), static_cast<unsigned>(Hkv)),
-                     dim3(kDThreads), 0, stream, reinterpret_cast<const bf16*>(q),
-                     reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(v), n, Hq,
-                     Hkv, s, gain, tau, p.chunk, part);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(static_cast<unsigned>(Hq)), dim3(D), 0,
-                     stream, part, p.n_chunks, G, reinterpret_cast<bf16*>(out), lse);
+  if (p.chunk == 64)
+    launch_chunks<D, G, 64, kBias>(q, k, v, n, Hq, Hkv, s, gain, tau, p, part, stream);
+  else if constexpr (G <= 4) {
+    if (p.chunk == 128)
+      launch_chunks<D, G, 128, kBias>(q, k, v, n, Hq, Hkv, s, gain, tau, p, part, stream);
+    else if constexpr (G <= 2)
+      launch_chunks<D, G, 256, kBias>(q, k, v, n, Hq, Hkv, s, gain, tau, p, part, stream);
+  }
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(static_cast<unsigned>(Hq)), dim3(kDThreads),
+                     0, stream, part, p.n_chunks, G, reinterpret_cast<bf16*>(out), lse);
 }
 
 template <int D, bool kBias>
