@@ -252,6 +252,71 @@ def main():
     torch.cuda.synchronize()
     plain_ms_launch = pa.elapsed_time(pb) / max(1, min(args.steps, 5)) / w.n_layers
 
+    # ---------------------------------------------------------------- first decode step
+    # One new token per layer against the pruned cache: the gate layer over all
+    # N rows (plain), the 27 layers above it over the M kept rows (gated).  The
+    # new query is the last kept row's (its own row is then the cache's last).
+    dws = tg.decode_workspace(w.n, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
+    dout = torch.empty((w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    q_new = [kept_qkv[t][0][-1].contiguous() for t in range(n_t)]
+
+    def decode_upper():
+        for l in range(w.n_layers):
+            t = inputs.template_of_layer(w, l)
+            tg.gated_decode(q_new[t], kept_qkv[t][1], kept_qkv[t][2], s_kept, gain_d[l], tau_d[l],
+                            out=dout, workspace=dws)
+
+    q_gate = full_qkv[0][0][-1].contiguous()
+
+    def decode_gate_layer():   # ten calls per replay: one alone would time the graph launch
+        for _ in range(10):
+            tg.gated_decode(q_gate, full_qkv[0][1], full_qkv[0][2], out=dout, workspace=dws)
+
+    def graphed(fn):
+        # A decode loop is launch-bound from Python (two small launches per
+        # layer); it is timed as a captured HIP graph, as a serving loop runs it.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        return graph
+
+    def time_calls(fn, reps):
+        fn()
+        ea = torch.cuda.Event(enable_timing=True)
+        eb = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record(stream)
+        for _ in range(reps):
+            fn()
+        eb.record(stream)
+        torch.cuda.synchronize()
+        return ea.elapsed_time(eb) / reps
+
+    g_upper, g_gate = graphed(decode_upper), graphed(decode_gate_layer)
+    dec_upper_ms = time_calls(g_upper.replay, 20) / w.n_layers
+    dec_full_ms = time_calls(g_gate.replay, 20) / 10
+    del g_upper, g_gate
+    cache_row = 2.0 * w.n_kv_heads * w.head_dim * 2          # K and V bytes per cached row
+    dec_upper_gbs = m * cache_row / (dec_upper_ms / 1e3) / 1e9
+    dec_full_gbs = w.n * cache_row / (dec_full_ms / 1e3) / 1e9
+    decode = {
+        "upper_layer_ms": round(dec_upper_ms, 5), "upper_layer_cache_rows": m,
+        "upper_layer_gb_s": round(dec_upper_gbs, 1),
+        "upper_layer_frac_hbm_peak": round(dec_upper_gbs / PEAK_HBM_GBS, 4),
+        "gate_layer_ms": round(dec_full_ms, 5), "gate_layer_cache_rows": w.n,
+        "gate_layer_gb_s": round(dec_full_gbs, 1),
+        "gate_layer_frac_hbm_peak": round(dec_full_gbs / PEAK_HBM_GBS, 4),
+        # one decode step through the 28 attention layers: pruned cache vs all N rows
+        "step_speedup_vs_unpruned_cache": round((w.n_layers + 1) * dec_full_ms /
+                                                (dec_full_ms + w.n_layers * dec_upper_ms), 2),
+    }
+    del dws
+
     # ---------------------------------------------------------------- full-N baseline
     full = None
     if not args.no_full_baseline:
@@ -356,6 +421,7 @@ def main():
                      "flops_per_launch": fl, "avg_launch_ms": round(attn_ms_launch, 5)},
         "stages": stages,
         "full_prefill_baseline": full,
+        "first_decode_step": decode,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
