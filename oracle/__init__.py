@@ -36,5 +36,6 @@ from .tokengate import (  # noqa: F401
     gated_attention,
     full_attention,
     gated_decode,
+    qk_norm_rope,
     gated_prefill,
 )

@@ -52,6 +52,11 @@ Pins (tests in ``tests/test_oracle_pins.py``):
                       dominant bias on one key returns that key's v; shift
                       invariance; temperature equivalence; golden fixture.
   full_attention   -- torch SDPA (fp64, causal, GQA by repetition).
+  qk_norm_rope     -- transformers' Qwen3 apply_rotary_pos_emb (with this
+                      function's cos/sin) and Qwen3RMSNorm; Qwen3RotaryEmbedding's
+                      cos/sin at small positions; position 0 is the identity;
+                      rotation keeps each pair's norm; q.k after RoPE depends
+                      only on the position difference.
   gated_decode     -- torch SDPA (fp64) for one query with the additive float
                       bias and the head's scale; equals the last row of
                       gated_attention when the new token is the last row;
@@ -226,6 +231,38 @@ def full_attention(q, k, v, rows=None, return_lse=False):
     n, hq, _ = np.asarray(q).shape
     return gated_attention(q, k, v, np.zeros(n), np.zeros(hq), np.ones(hq),
                            rows=rows, return_lse=return_lse)
+
+
+# ---------------------------------------------------------------------------
+# The upper layers' query/key prologue at the kept tokens' own positions
+# ([KO] "작동 방식": only the kept tokens go up, as the tokens they are; their
+# positions are their original ones).  Qwen3's per-head RMS normalisation of
+# q and k followed by rotary position embedding (rotate-half) is model
+# plumbing, not on the pages: written here from its definition.
+# ---------------------------------------------------------------------------
+
+def qk_norm_rope(x, positions, norm_weight=None, eps=1e-6, theta=1.0e6):
+    """x [n, heads, d] -> RoPE(RMSNorm(x) * w) at the given positions, float64.
+
+    RMSNorm over each head vector: x / sqrt(mean(x^2) + eps) * w (skipped when
+    ``norm_weight`` is None).  RoPE, rotate-half form: for f < d/2 with angle
+    a = position * theta^(-2f/d),
+        out[f]       = y[f] cos a - y[f + d/2] sin a
+        out[f + d/2] = y[f + d/2] cos a + y[f] sin a.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, heads, d = x.shape
+    assert d % 2 == 0
+    if norm_weight is not None:
+        w = np.asarray(norm_weight, dtype=np.float64).reshape(d)
+        x = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+    half = d // 2
+    inv_freq = theta ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = np.asarray(positions, dtype=np.float64).reshape(n)[:, None] * inv_freq[None, :]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
 # ---------------------------------------------------------------------------

@@ -307,6 +307,65 @@ def test_decode_single_key_and_dominant_bias():
     assert np.max(np.abs(big - v[3, 0][None, :])) < 1e-12
 
 
+def test_qk_norm_rope_vs_transformers_qwen3():
+    """The rotation convention against transformers' Qwen3 apply_rotary_pos_emb
+    (fed this oracle's own angles), the normalisation against Qwen3RMSNorm, and
+    the frequency table against Qwen3RotaryEmbedding at small positions (it
+    computes in float32)."""
+    from transformers import Qwen3Config
+    from transformers.models.qwen3 import modeling_qwen3 as q3
+    rng = np.random.default_rng(31)
+    n, heads, d, theta, eps = 9, 3, 16, 1.0e6, 1e-6
+    x = rng.standard_normal((n, heads, d)) * 2
+    w = rng.uniform(0.5, 1.5, d)
+    pos = rng.integers(0, 1500, n)
+    got = O.qk_norm_rope(x, pos, w, eps=eps, theta=theta)
+    # RMSNorm (float32 inside the library)
+    norm = q3.Qwen3RMSNorm(d, eps=eps).double()
+    with torch.no_grad():
+        norm.weight.copy_(torch.from_numpy(w))
+        xn = norm(torch.from_numpy(x)).numpy()
+    # rotation with the oracle's cos/sin in the library's [n, 1, d] layout
+    ang = pos[:, None].astype(np.float64) * theta ** (-2.0 * np.arange(d // 2) / d)[None, :]
+    cos = torch.from_numpy(np.cos(np.concatenate([ang, ang], -1)))[None]
+    sin = torch.from_numpy(np.sin(np.concatenate([ang, ang], -1)))[None]
+    xt = torch.from_numpy(xn).permute(1, 0, 2)[None]            # [1, heads, n, d]
+    rq, _ = q3.apply_rotary_pos_emb(xt, xt, cos, sin)
+    ref = rq[0].permute(1, 0, 2).numpy()
+    assert np.max(np.abs(got - ref)) < 1e-5 * np.max(np.abs(ref))   # the norm ran in float32
+    no_norm = O.qk_norm_rope(x, pos, None, theta=theta)
+    rq2, _ = q3.apply_rotary_pos_emb(torch.from_numpy(x).permute(1, 0, 2)[None],
+                                     torch.from_numpy(x).permute(1, 0, 2)[None], cos, sin)
+    assert np.max(np.abs(no_norm - rq2[0].permute(1, 0, 2).numpy())) < 1e-12
+    # the library's own frequency table (float32) at these positions
+    cfg = Qwen3Config(head_dim=d, rope_parameters={"rope_type": "default", "rope_theta": theta},
+                      max_position_embeddings=4096)
+    rot = q3.Qwen3RotaryEmbedding(cfg)
+    c32, s32 = rot(torch.zeros(1, dtype=torch.float32), torch.from_numpy(pos)[None])
+    assert np.max(np.abs(c32[0].double().numpy() - cos[0].numpy())) < 2e-4
+    assert np.max(np.abs(s32[0].double().numpy() - sin[0].numpy())) < 2e-4
+
+
+def test_qk_norm_rope_invariants():
+    rng = np.random.default_rng(32)
+    n, heads, d = 6, 2, 32
+    x = rng.standard_normal((n, heads, d))
+    # position 0: rotation is the identity
+    assert np.max(np.abs(O.qk_norm_rope(x, np.zeros(n), None) - x)) < 1e-15
+    # each (f, f + d/2) pair keeps its length
+    y = O.qk_norm_rope(x, rng.integers(0, 10 ** 5, n), None)
+    h = d // 2
+    assert np.max(np.abs((y[..., :h] ** 2 + y[..., h:] ** 2) - (x[..., :h] ** 2 + x[..., h:] ** 2))) < 1e-9
+    # q.k after rotation depends only on the position difference
+    q = rng.standard_normal((1, 1, d)); k = rng.standard_normal((1, 1, d))
+    dots = [np.sum(O.qk_norm_rope(q, [p + 37], None) * O.qk_norm_rope(k, [p], None))
+            for p in (0, 11, 5000, 123456)]
+    assert np.max(np.abs(np.array(dots) - dots[0])) < 1e-9
+    # RMSNorm with unit weight gives unit root-mean-square
+    z = O.qk_norm_rope(x * 7, np.zeros(n), np.ones(d), eps=0.0)
+    assert np.max(np.abs(np.sqrt(np.mean(z ** 2, axis=-1)) - 1)) < 1e-12
+
+
 def test_attention_uniform_logits_lse_and_mean():
     # q = 0 and s = 0: every visible key has logit 0, so lse_i = log(i+1) and
     # out_i is the running mean of v.
