@@ -236,6 +236,32 @@ tg_status tg_gated_decode_fwd(const tg_bf16* q, const tg_bf16* k_cache, const tg
                               tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
                               tg_stream_t stream);
 
+/*
+ * Query/key prologue of the layers above the gate, fused with the row gather
+ * (lucasainews.com article, "작동 방식": the kept tokens go up as the tokens
+ * they are, so their rotary positions are their original indices; the
+ * normalisation and rotation themselves are Qwen3's, not the method's):
+ *     y = x / sqrt(mean_f x_f^2 + eps) * norm_weight       (per head vector)
+ *     a_f = positions[i] * rope_theta^(-2 f / head_dim),   f < head_dim / 2
+ *     dst[i, h, f]     = y_f cos a_f - y_{f+d/2} sin a_f
+ *     dst[i, h, f+d/2] = y_{f+d/2} cos a_f + y_f sin a_f
+ * with x = src[rows[i], h, :] (rows may be NULL: x = src[i, h, :]).
+ *   src        [src_rows, n_heads, head_dim] bf16, contiguous, 16-byte aligned
+ *   rows       [n] int32 or NULL; entries outside [0, src_rows) skip the
+ *              row (dst row left unwritten)
+ *   positions  [n] int32 rotary positions
+ *   norm_weight [head_dim] fp32, or NULL for no normalisation
+ *   dst        [n, n_heads, head_dim] bf16 (output); may equal src only when
+ *              rows is NULL (in place); any other overlap -> TG_E_INVALID
+ * Supported: head_dim in {64, 128}.  Angles are formed in fp64 (positions up
+ * to 2^31 keep their phase); the rest is fp32, output rounded to nearest even.
+ * n == 0 is a no-op.
+ */
+tg_status tg_qk_norm_rope(const tg_bf16* src, int64_t src_rows, const int32_t* rows,
+                          const int32_t* positions, int64_t n, int32_t n_heads, int32_t head_dim,
+                          const float* norm_weight, float eps, double rope_theta, tg_bf16* dst,
+                          tg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

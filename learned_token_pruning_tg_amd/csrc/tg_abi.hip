@@ -221,4 +221,33 @@ tg_status tg_gated_decode_fwd(const tg_bf16* q, const tg_bf16* k_cache, const tg
                     "tg_gated_decode_fwd launch");
 }
 
+tg_status tg_qk_norm_rope(const tg_bf16* src, int64_t src_rows, const int32_t* rows,
+                          const int32_t* positions, int64_t n, int32_t n_heads, int32_t head_dim,
+                          const float* norm_weight, float eps, double rope_theta, tg_bf16* dst,
+                          tg_stream_t stream) {
+  const char* fn = "tg_qk_norm_rope";
+  if (n < 0 || n >= (int64_t(1) << 31) || src_rows < 0)
+    return fail(TG_E_INVALID, "%s: n=%lld, src_rows=%lld", fn, (long long)n, (long long)src_rows);
+  if (n_heads <= 0) return fail(TG_E_INVALID, "%s: n_heads=%d", fn, n_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TG_E_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", fn, head_dim);
+  if (!(rope_theta > 0.0) || !(eps >= 0.f))
+    return fail(TG_E_INVALID, "%s: rope_theta=%g, eps=%g", fn, rope_theta, (double)eps);
+  if (rows == nullptr && n > src_rows)
+    return fail(TG_E_INVALID, "%s: n=%lld rows > src_rows=%lld without a row index", fn,
+                (long long)n, (long long)src_rows);
+  if (n == 0) return TG_OK;
+  if (!src || !dst || !positions) return fail(TG_E_INVALID, "%s: null pointer", fn);
+  if (!aligned16(src) || !aligned16(dst)) return fail(TG_E_INVALID, "%s: src/dst must be 16-byte aligned", fn);
+  const int64_t row = int64_t(n_heads) * head_dim * 2;
+  const char* s0 = reinterpret_cast<const char*>(src);
+  const char* d0 = reinterpret_cast<const char*>(dst);
+  const bool in_place = rows == nullptr && s0 == d0;
+  if (!in_place && s0 < d0 + n * row && d0 < s0 + src_rows * row)
+    return fail(TG_E_INVALID, "%s: src and dst overlap (only exact in-place without rows)", fn);
+  return hip_status(tg::launch_qk_norm_rope(src, src_rows, rows, positions, n, n_heads, head_dim,
+                                            norm_weight, eps, rope_theta, dst, as_hip(stream)),
+                    "tg_qk_norm_rope launch");
+}
+
 }  // extern "C"

@@ -45,4 +45,10 @@ hipError_t launch_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          const float* gain, const float* tau, uint16_t* out, float* lse,
                          void* workspace, hipStream_t stream);
 
+// dst[i] = RoPE(RMSNorm(src[rows ? rows[i] : i]) * w) at pos[i]; w == nullptr skips the norm.
+hipError_t launch_qk_norm_rope(const uint16_t* src, int64_t src_rows, const int32_t* rows,
+                               const int32_t* pos, int64_t n, int n_heads, int head_dim,
+                               const float* norm_weight, float eps, double theta, uint16_t* dst,
+                               hipStream_t stream);
+
 }  // namespace tg

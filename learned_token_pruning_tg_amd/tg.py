@@ -36,6 +36,8 @@ _SIGNATURES = {
     "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
     "tg_decode_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
+    "tg_qk_norm_rope": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, ctypes.c_float,
+                                       ctypes.c_double, _P, _P]),
     "tg_gated_decode_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P,
                                            _P, _P, ctypes.c_size_t, _P]),
 }
@@ -308,3 +310,32 @@ def gated_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
     return (out, lse) if lse is not None else out
+
+
+def qk_norm_rope(src: torch.Tensor, positions: torch.Tensor, rows: Optional[torch.Tensor] = None,
+                 norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                 theta: float = 1.0e6, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """out[i] = RoPE(RMSNorm(src[rows[i]]) * norm_weight) at positions[i].
+    src [rows, heads, d] bf16; positions / rows [n] int32 (rows None: src[i]);
+    norm_weight [d] fp32 or None (no normalisation)."""
+    _need(src, "src", torch.bfloat16)
+    _need(positions, "positions", torch.int32)
+    src_rows, heads, d = src.shape
+    n = positions.numel()
+    if rows is not None:
+        _need(rows, "rows", torch.int32)
+        if rows.numel() != n:
+            raise ValueError("rows and positions differ in length")
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", torch.float32)
+        if norm_weight.numel() != d:
+            raise ValueError("norm_weight must have head_dim entries")
+    if out is None:
+        out = torch.empty((n, heads, d), dtype=torch.bfloat16, device=src.device)
+    _need(out, "out", torch.bfloat16)
+    if tuple(out.shape) != (n, heads, d):
+        raise ValueError("out shape does not match")
+    _check(lib().tg_qk_norm_rope(_ptr(src), src_rows, _ptr(rows), _ptr(positions), n, heads, d,
+                                 _ptr(norm_weight), eps, theta, _ptr(out), _stream(stream)))
+    return out

@@ -38,7 +38,7 @@ def test_header_declares_the_five_entry_points():
     names = _declared()
     for fn in ("tg_gate_score", "tg_topk_select", "tg_topk_workspace_bytes", "tg_compact",
                "tg_gated_attn_fwd", "tg_full_attn_fwd", "tg_attn_workspace_bytes",
-               "tg_gated_decode_fwd", "tg_decode_workspace_bytes",
+               "tg_gated_decode_fwd", "tg_decode_workspace_bytes", "tg_qk_norm_rope",
                "tg_kept_count", "tg_status_str", "tg_last_error"):
         assert fn in names
 
@@ -243,3 +243,18 @@ def test_decode_validation(L):
     assert f(A, A, A, 10, 16, 8, 128, None, None, None, A, None, None, W, 0) == WORKSPACE
     assert L.tg_decode_workspace_bytes(0, 16, 8, 128) == 0
     assert L.tg_decode_workspace_bytes(10, 16, 8, 96) == 0
+
+
+def test_qk_norm_rope_validation(L):
+    f = L.tg_qk_norm_rope
+    B = A * 64   # a second fake address far from A
+    assert f(A, 10, None, A, -1, 4, 128, None, 1e-6, 1e6, B, 0) == INVALID
+    assert f(A, 10, None, A, 5, 0, 128, None, 1e-6, 1e6, B, 0) == INVALID
+    assert f(A, 10, None, A, 5, 4, 96, None, 1e-6, 1e6, B, 0) == UNSUPPORTED
+    assert f(A, 10, None, A, 5, 4, 128, None, 1e-6, 0.0, B, 0) == INVALID       # theta
+    assert f(A, 10, None, A, 11, 4, 128, None, 1e-6, 1e6, B, 0) == INVALID      # n > src_rows
+    assert f(A, 10, None, None, 5, 4, 128, None, 1e-6, 1e6, B, 0) == INVALID    # positions
+    assert f(A + 8, 10, None, A, 5, 4, 128, None, 1e-6, 1e6, B, 0) == INVALID   # alignment
+    assert f(A, 10, A, A, 5, 4, 128, None, 1e-6, 1e6, A + 1024, 0) == INVALID   # overlap
+    assert "overlap" in tg.last_error()
+    assert f(None, 0, None, None, 0, 4, 128, None, 1e-6, 1e6, None, 0) == OK    # n == 0
