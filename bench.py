@@ -317,6 +317,25 @@ def main():
     }
     del dws
 
+    # ---------------------------------------------------------------- upper-layer q/k prologue
+    # Gather + per-head RMS norm + RoPE at the original positions for one upper
+    # layer's q and k (from full-N rows; the templates stand for pre-RoPE rows).
+    qn_w = torch.ones(w.head_dim, dtype=torch.float32, device=dev)
+    q_pro = torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    k_pro = torch.empty((m, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+
+    def prologue():
+        tg.qk_norm_rope(full_qkv[0][0], idx, rows=idx, norm_weight=qn_w, out=q_pro)
+        tg.qk_norm_rope(full_qkv[0][1], idx, rows=idx, norm_weight=qn_w, out=k_pro)
+
+    g_pro = graphed(lambda: [prologue() for _ in range(10)])
+    pro_ms = time_calls(g_pro.replay, 20) / 10
+    del g_pro
+    pro_bytes = 2.0 * m * (w.n_q_heads + w.n_kv_heads) * w.head_dim * 2
+    prologue_stats = {"ms_per_layer": round(pro_ms, 5),
+                      "gb_s": round(pro_bytes / (pro_ms / 1e3) / 1e9, 1),
+                      "frac_hbm_peak": round(pro_bytes / (pro_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
+
     # ---------------------------------------------------------------- full-N baseline
     full = None
     if not args.no_full_baseline:
@@ -422,6 +441,7 @@ def main():
         "stages": stages,
         "full_prefill_baseline": full,
         "first_decode_step": decode,
+        "upper_layer_qk_prologue": prologue_stats,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

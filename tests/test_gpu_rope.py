@@ -29,7 +29,8 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("n_src,n,heads,d,norm,gather", [
     (1, 1, 8, 128, True, False), (300, 300, 16, 128, True, False), (300, 77, 8, 64, False, True),
     (16384, 2304, 16, 128, True, True), (131072, 8448, 8, 128, True, True),
-    (5000, 5000, 3, 64, True, False)])
+    (5000, 5000, 3, 64, True, False), (1000, 333, 32, 128, True, True),
+    (300, 50, 80, 128, True, True), (700, 123, 40, 64, False, True)])
 def test_qk_norm_rope_vs_oracle(n_src, n, heads, d, norm, gather):
     rng = np.random.default_rng(n + heads + d)
     x = inputs.round_bf16((rng.standard_normal((n_src, heads, d)) * 1.7).astype(np.float32))
