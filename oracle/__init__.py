@@ -34,6 +34,7 @@ from .tokengate import (  # noqa: F401
     topk_select,
     compact_rows,
     gated_attention,
+    gated_attention_bwd,
     full_attention,
     gated_decode,
     qk_norm_rope,

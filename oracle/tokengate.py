@@ -51,6 +51,12 @@ Pins (tests in ``tests/test_oracle_pins.py``):
                       problem; two-key closed form; first-row identity; a
                       dominant bias on one key returns that key's v; shift
                       invariance; temperature equivalence; golden fixture.
+  gated_attention_bwd
+                   -- central finite differences of gated_attention (every
+                      input element, tiny sizes, float64); torch autograd
+                      through torch SDPA (fp64) with the bias as an additive
+                      float mask and q divided by tau; the score gradient sums
+                      to zero (a common shift of all scores changes nothing).
   full_attention   -- torch SDPA (fp64, causal, GQA by repetition).
   qk_norm_rope     -- transformers' Qwen3 apply_rotary_pos_emb (with this
                       function's cos/sin) and Qwen3RMSNorm; Qwen3RotaryEmbedding's
@@ -79,7 +85,10 @@ __all__ = [
     "topk_select",
     "compact_rows",
     "gated_attention",
+    "gated_attention_bwd",
     "full_attention",
+    "qk_norm_rope",
+    "gated_decode",
     "gated_prefill",
 ]
 
@@ -223,6 +232,71 @@ def gated_attention(q, k, v, key_score, gain, tau, rows=None, return_lse=False,
             out[b0:b0 + row_block, h, :] = (p @ vh[:kend]) / l
             lse[h, b0:b0 + row_block] = (mx + np.log(l))[:, 0]
     return (out, lse) if return_lse else out
+
+
+def gated_attention_bwd(q, k, v, key_score, gain, tau, dout, row_block: int = 256):
+    """Gradients of the token-gated attention above, for training the gate
+    through the bias ([KO] "작동 방식": the score enters the logits as a bias, so
+    the loss reaches the gate's scores through it; [ABS]).
+
+    Given dout = dLoss/dout [M, Hq, d], returns float64 arrays
+        dq [M, Hq, d], dk [M, Hkv, d], dv [M, Hkv, d],
+        dscore [M], dgain [Hq], dtau [Hq].
+    Chain rule, head by head, with the softmax recomputed from the inputs:
+        p_ij      = softmax_j(logit_i.)            (causal: p_ij = 0 for j > i)
+        dp_ij     = dout_i . v_j
+        dlogit_ij = p_ij (dp_ij - sum_l p_il dp_il)   (softmax Jacobian)
+        dq_i     += sum_j dlogit_ij k_j / (sqrt(d) tau_h)
+        dk_j     += sum_i dlogit_ij q_i / (sqrt(d) tau_h)
+        dv_j     += sum_i p_ij dout_i
+        dscore_j += gain_h sum_i dlogit_ij
+        dgain_h   = sum_ij dlogit_ij key_score_j
+        dtau_h    = sum_ij dlogit_ij q_i.k_j * (-1 / (sqrt(d) tau_h^2))
+    (K/V rows are shared by the heads of a group, so their gradients sum over
+    those heads.)
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    assert k.shape == (m, hkv, d) and v.shape == (m, hkv, d) and hq % hkv == 0
+    dout = np.asarray(dout, dtype=np.float64).reshape(m, hq, d)
+    group = hq // hkv
+    s = np.asarray(key_score, dtype=np.float64).reshape(m)
+    gain = np.asarray(gain, dtype=np.float64).reshape(hq)
+    tau = np.asarray(tau, dtype=np.float64).reshape(hq)
+    dq = np.zeros((m, hq, d), dtype=np.float64)
+    dk = np.zeros((m, hkv, d), dtype=np.float64)
+    dv = np.zeros((m, hkv, d), dtype=np.float64)
+    dscore = np.zeros(m, dtype=np.float64)
+    dgain = np.zeros(hq, dtype=np.float64)
+    dtau = np.zeros(hq, dtype=np.float64)
+    for h in range(hq):
+        g = h // group
+        kh = k[:, g, :].astype(np.float64)
+        vh = v[:, g, :].astype(np.float64)
+        scale = 1.0 / (math.sqrt(d) * tau[h])
+        for b0 in range(0, m, row_block):
+            rb = np.arange(b0, min(b0 + row_block, m))
+            kend = int(rb[-1]) + 1
+            qb = q[rb, h, :].astype(np.float64)
+            dob = dout[rb, h, :]
+            qk = qb @ kh[:kend].T
+            logits = qk * scale + gain[h] * s[None, :kend]
+            visible = np.arange(kend)[None, :] <= rb[:, None]
+            logits = np.where(visible, logits, -np.inf)
+            p = np.exp(logits - logits.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = dob @ vh[:kend].T
+            dlogit = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[rb, h, :] += (dlogit @ kh[:kend]) * scale
+            dk[:kend, g, :] += (dlogit.T @ qb) * scale
+            dv[:kend, g, :] += p.T @ dob
+            dscore[:kend] += gain[h] * dlogit.sum(axis=0)
+            dgain[h] += (dlogit * s[None, :kend]).sum()
+            dtau[h] += (dlogit * qk).sum() * (-1.0 / (math.sqrt(d) * tau[h] ** 2))
+    return dict(dq=dq, dk=dk, dv=dv, dscore=dscore, dgain=dgain, dtau=dtau)
 
 
 def full_attention(q, k, v, rows=None, return_lse=False):

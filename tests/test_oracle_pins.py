@@ -231,6 +231,73 @@ def test_gated_attention_masking_identity_vs_sdpa():
         assert np.max(np.abs(got[:, h] - ref[idx, 0])) < 1e-12
 
 
+# ----------------------------------------------------------- attention backward
+
+def _bwd_case(seed, m=6, hq=4, hkv=2, d=4, row_block=256):
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand_qkv(rng, m, hq, hkv, d)
+    s = rng.standard_normal(m) * 1.5
+    gain = rng.uniform(0.5, 1.5, hq); tau = rng.uniform(0.8, 1.2, hq)
+    dout = rng.standard_normal((m, hq, d))
+    return q, k, v, s, gain, tau, dout
+
+
+def test_attention_bwd_finite_differences_every_input():
+    """Central differences of sum(dout * gated_attention(...)) in float64, for
+    every element of q, k, v, the scores, the gains and the temperatures.
+    row_block=2 also exercises the row blocking of both functions."""
+    q, k, v, s, gain, tau, dout = _bwd_case(11)
+    args = dict(q=q, k=k, v=v, key_score=s, gain=gain, tau=tau)
+    got = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, row_block=2)
+    names = dict(q="dq", k="dk", v="dv", key_score="dscore", gain="dgain", tau="dtau")
+    eps = 1e-6
+    for arg, gname in names.items():
+        base = args[arg]
+        fd = np.zeros_like(base)
+        for ix in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[ix] += eps; minus[ix] -= eps
+            lp = np.sum(dout * O.gated_attention(**{**args, arg: plus}, row_block=3))
+            lm = np.sum(dout * O.gated_attention(**{**args, arg: minus}, row_block=3))
+            fd[ix] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(got[gname] - fd)) / max(np.max(np.abs(fd)), 1e-3)
+        assert err < 1e-6, (gname, err)
+
+
+def test_attention_bwd_matches_torch_autograd_through_sdpa():
+    """torch autograd (float64) through torch SDPA, one head at a time: q/tau_h
+    at scale 1/sqrt(d), the bias gain_h * s_j as an additive float mask with -inf
+    above the diagonal; K/V rows gathered per head so their gradients sum over
+    the group."""
+    m, hq, hkv, d = 37, 4, 2, 16
+    q, k, v, s, gain, tau, dout = _bwd_case(12, m, hq, hkv, d)
+    got = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, row_block=16)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    tq, tk, tv, ts, tg, tt = T(q), T(k), T(v), T(s), T(gain), T(tau)
+    causal = torch.tril(torch.ones(m, m, dtype=torch.bool))
+    loss = 0
+    for h in range(hq):
+        g = h // (hq // hkv)
+        mask = torch.where(causal, tg[h] * ts[None, :], torch.tensor(-math.inf, dtype=torch.float64))
+        o = F.scaled_dot_product_attention((tq[:, h] / tt[h])[None], tk[:, g][None], tv[:, g][None],
+                                           attn_mask=mask[None], scale=1.0 / math.sqrt(d))
+        loss = loss + (o[0] * torch.from_numpy(dout[:, h])).sum()
+    loss.backward()
+    for gname, t in dict(dq=tq, dk=tk, dv=tv, dscore=ts, dgain=tg, dtau=tt).items():
+        assert np.max(np.abs(got[gname] - t.grad.numpy())) < 1e-10, gname
+
+
+def test_attention_bwd_score_gradient_sums_to_zero():
+    """Adding one constant to every score moves each row's logits together, so
+    the output and hence the loss do not change: sum_j dscore_j = 0; with all
+    scores equal the gains get no gradient either."""
+    q, k, v, s, gain, tau, dout = _bwd_case(13, 40, 4, 1, 8)
+    got = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, row_block=8)
+    assert abs(got["dscore"].sum()) < 1e-10 * np.abs(got["dscore"]).sum()
+    flat = O.gated_attention_bwd(q, k, v, np.full(40, 0.7), gain, tau, dout)
+    assert np.max(np.abs(flat["dgain"])) < 1e-10
+
+
 def test_attention_two_key_closed_form_and_first_row():
     rng = np.random.default_rng(7)
     d = 6
