@@ -199,6 +199,53 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                            tg_stream_t stream);
 
 /*
+ * Bytes of device workspace tg_gated_attn_bwd needs for n rows: transposed
+ * bf16 tile images of q, dout and k (about 1.25x their bytes), per row and
+ * query head its log-sum-exp and dout.out, per query head and key the column
+ * sum of the logit gradient, fp32 per-query-head dk and dv partials
+ * (2 * 4 * n * n_q_heads * head_dim bytes) and one float per query head and
+ * 128-row block.  Host-only arithmetic; 0 for arguments tg_gated_attn_bwd
+ * would reject as invalid or unsupported (n <= 0 included).
+ */
+size_t tg_attn_bwd_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim);
+
+/*
+ * Backward of tg_gated_attn_fwd: the gradients through which a training loss
+ * reaches the gate's scores, gains and temperatures (lucasainews.com
+ * article, "작동 방식": the score is a bias on the logits of the layers above
+ * the gate, with a learned per-head gain and temperature; fugumt.com
+ * abstract).  With c_h = 1 / (sqrt(head_dim) * tau[h]), P the causal softmax
+ * of logit_ij = c_h q_i.k_j + gain[h] key_score[j] and dS_ij = P_ij (dout_i.v_j
+ * - dout_i.out_i):
+ *     dq_i = c_h sum_j dS_ij k_j          dk_j = sum_h c_h sum_i dS_ij q_i
+ *     dv_j = sum_h sum_i P_ij dout_i      dscore_j = sum_h gain[h] sum_i dS_ij
+ *     dgain[h] = sum_ij dS_ij key_score[j]
+ *     dtau[h]  = -(1 / tau[h]) sum_i q_i.dq_i     (sums over i, j within head h)
+ *   q, k, v, key_score, gain, tau  as given to tg_gated_attn_fwd
+ *   out   [n, n_q_heads, head_dim] bf16: that call's output
+ *   lse   [n_q_heads, n] fp32: that call's natural-log log-sum-exp
+ *   dout  [n, n_q_heads, head_dim] bf16: gradient of the loss w.r.t. out
+ *   dq    [n, n_q_heads, head_dim], dk, dv [n, n_kv_heads, head_dim] bf16
+ *         (outputs, round-to-nearest-even; no overlap with the inputs)
+ *   dscore [n], dgain [n_q_heads], dtau [n_q_heads] fp32 (outputs, overwritten)
+ *   workspace  device scratch of at least tg_attn_bwd_workspace_bytes(...)
+ *         bytes, 16-byte aligned, caller-owned; overwritten.
+ * Every pointer is required (TG_E_INVALID); tensors 16-byte aligned.
+ * Supported: head_dim in {64, 128}, n * n_q_heads * head_dim * 2 < 2^31.
+ * Numerics: bf16 MFMA products with fp32 accumulation; P and dS enter the
+ * dv, dk and dq products as bf16; softmax, dS and every reduction in fp32, in
+ * a fixed order (deterministic).  n == 0 is a no-op (nothing written).
+ */
+tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            const float* key_score, const float* gain, const float* tau,
+                            const tg_bf16* out, const float* lse, const tg_bf16* dout,
+                            tg_bf16* dq, tg_bf16* dk, tg_bf16* dv, float* dscore, float* dgain,
+                            float* dtau, void* workspace, size_t workspace_bytes,
+                            tg_stream_t stream);
+
+/*
  * Bytes of device workspace tg_gated_decode_fwd needs for n cached rows:
  * per KV head and chunk of 64-256 keys, a (max, sum, head_dim outputs) fp32
  * state for each of its query heads.  Host-only arithmetic; 0 for arguments

@@ -176,6 +176,50 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                     "tg_full_attn_fwd launch");
 }
 
+size_t tg_attn_bwd_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim) {
+  if (n <= 0 || n >= (int64_t(1) << 31) || n_q_heads <= 0 || n_kv_heads <= 0 ||
+      n_q_heads % n_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
+    return 0;
+  return tg::attn_bwd_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim);
+}
+
+tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            const float* key_score, const float* gain, const float* tau,
+                            const tg_bf16* out, const float* lse, const tg_bf16* dout,
+                            tg_bf16* dq, tg_bf16* dk, tg_bf16* dv, float* dscore, float* dgain,
+                            float* dtau, void* workspace, size_t workspace_bytes,
+                            tg_stream_t stream) {
+  const char* fn = "tg_gated_attn_bwd";
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(TG_E_INVALID, "%s: n=%lld out of range", fn, (long long)n);
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
+    return fail(TG_E_INVALID, "%s: n_q_heads=%d, n_kv_heads=%d", fn, n_q_heads, n_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(TG_E_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", fn, head_dim);
+  if (n * n_q_heads * head_dim * 2 >= (int64_t(1) << 31))
+    return fail(TG_E_UNSUPPORTED, "%s: n=%lld rows of %d heads x %d exceed 2^31 bytes", fn,
+                (long long)n, n_q_heads, head_dim);
+  if (n == 0) return TG_OK;
+  if (!q || !k || !v || !out || !dout || !dq || !dk || !dv)
+    return fail(TG_E_INVALID, "%s: null tensor pointer", fn);
+  if (!key_score || !gain || !tau || !lse || !dscore || !dgain || !dtau)
+    return fail(TG_E_INVALID, "%s: null key_score/gain/tau/lse/dscore/dgain/dtau", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(TG_E_INVALID, "%s: q/k/v/out/dout/dq/dk/dv must be 16-byte aligned", fn);
+  if (tg::attn_bwd_image_bytes_per_head(n, head_dim) >= (size_t(1) << 32))
+    return fail(TG_E_UNSUPPORTED, "%s: n=%lld too long for one head's tile images", fn, (long long)n);
+  const size_t need = tg::attn_bwd_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(TG_E_WORKSPACE, "%s: workspace %p of %zu bytes (need %zu, 16-byte aligned)", fn,
+                workspace, workspace_bytes, need);
+  return hip_status(tg::launch_attn_bwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, key_score,
+                                        gain, tau, out, lse, dout, dq, dk, dv, dscore, dgain, dtau,
+                                        workspace, as_hip(stream)),
+                    "tg_gated_attn_bwd launch");
+}
+
 namespace {
 bool decode_shape_ok(int64_t n, int32_t hq, int32_t hkv, int32_t d) {
   if (n <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;

@@ -1,0 +1,712 @@
+// Token-gated causal GQA attention, backward, for gfx950.
+//
+// Method (lucasainews.com TokenGate article, section "작동 방식"; fugumt.com
+// abstract): the kept keys' gate scores enter the logits as a bias, scaled by
+// a per-head gain, with a per-head temperature on q.k; the bias is how a
+// training loss reaches the gate.  With c_h = 1 / (sqrt(d) tau_h),
+//     logit_ij = c_h q_i.k_j + g_h s_j (j <= i),  P = softmax_j,  O_i = sum_j P_ij v_j,
+// and given dO the gradients are (chain rule; D_i = dO_i.O_i = sum_j P_ij dP_ij):
+//     dP_ij = dO_i.v_j,   dS_ij = P_ij (dP_ij - D_i)
+//     dv_j = sum_h sum_i P_ij dO_i          dk_j = sum_h c_h sum_i dS_ij q_i
+//     dq_i = c_h sum_j dS_ij k_j            ds_j = sum_h g_h sum_i dS_ij
+//     dg_h = sum_ij dS_ij s_j               dtau_h = -(1 / tau_h) sum_i q_i.dq_i
+// (the last because d logit / d tau_h = -c_h q.k / tau_h).
+//
+// Launches, all deterministic (every sum in a fixed order, no atomics):
+// 1. bwd_pack: per (query head, 32-row tile) the Q^T and dO^T tile images
+//    ([d][row], rows permuted inside 16-row groups so that each lane's eight
+//    rows of an MFMA k-step are one 16-byte run) and the rows' lse (log2
+//    units; +inf past n) and D; per (KV head, 32-key tile) the K^T image.
+// 2. bwd_dkdv: one work-group per (query head, 128 keys), a wave per 32 keys
+//    with their K and V fragments in registers, over 32-query steps from the
+//    diagonal on: S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16_bf16 (lane
+//    = key, registers = queries), P and dS in fp32, then dV += P^T dO and
+//    dK += dS^T Q with P and dS as bf16 A fragments straight from registers.
+//    Q and dO rows and their images arrive by buffer-to-LDS DMA into a
+//    double-buffered ring, one barrier per step.  Writes fp32 per-head dK/dV
+//    partials and the per-head column sums sum_i dS_ij.
+// 3. bwd_dq: one work-group per (query head, 128 queries), a wave per 32
+//    queries with their Q and dO fragments in registers, over 32-key steps up
+//    to the diagonal: S^T = K Q^T, dP^T = V dO^T (lane = query), dS^T, then
+//    dQ^T += K^T dS^T.  Writes dQ (bf16) and per work-group sum_i q_i.dq_i.
+// 4. bwd_reduce: dK, dV = sum over the heads of each KV group (bf16).
+// 5. bwd_score: ds_j = sum_h g_h colsum_hj.  6. bwd_head: dg_h, dtau_h.
+#include <cmath>
+#include <type_traits>
+
+#include "tg_device.h"
+#include "tg_launch.h"
+
+namespace tg {
+namespace {
+
+constexpr int kThreads = 256;           // four waves
+constexpr int kRows = 32;               // rows of a tile image / of one wave
+constexpr int kWgRows = 128;            // rows (keys or queries) of a work-group
+
+template <int D>
+struct Bwd {
+  static constexpr int KS = D / 16;                 // k-steps over d
+  static constexpr int DT = D / 32;                 // 32-wide d tiles
+  static constexpr int ROW = D * 2;                 // bytes of one row tile row (LDS, unpadded)
+  static constexpr int ROWS_TILE = kRows * ROW;     // a 32-row tile in LDS
+  static constexpr int IMG_ROW = kRows * 2 + 16;    // image row: 32 bf16 + 16 pad bytes
+  static constexpr int IMG = D * IMG_ROW;           // one tile image
+  static constexpr int N_ROW_DMA = ROWS_TILE / 1024;
+  static constexpr int N_IMG_DMA = IMG / 1024;
+  static_assert(ROWS_TILE % 1024 == 0 && IMG % 1024 == 0, "whole 1 KiB DMA chunks");
+  // XOR key of LDS row r: 16 consecutive rows hit 16 different 16-byte slots
+  // modulo 256 bytes, so the A-fragment reads are free of bank conflicts.
+  static __host__ __device__ constexpr int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+};
+
+// Workspace layout (byte offsets, each region 256-byte aligned).
+struct BwdPlan {
+  int64_t n_t32;     // 32-row tiles, rounded up to whole 128-row work-groups
+  int64_t n_t128;
+  int64_t mp;        // rows padded to n_t32 * 32
+  size_t qimg, doimg, kimg, ld, colsum, dkp, dvp, qdot, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwdPlan bwd_plan(int64_t n, int hq, int hkv, int d) {
+  BwdPlan p{};
+  p.n_t128 = (n + kWgRows - 1) / kWgRows;
+  p.n_t32 = p.n_t128 * (kWgRows / kRows);
+  p.mp = p.n_t32 * kRows;
+  const size_t img = static_cast<size_t>(d) * (kRows * 2 + 16);
+  size_t o = 0;
+  p.qimg = o;   o = align256(o + static_cast<size_t>(hq) * p.n_t32 * img);
+  p.doimg = o;  o = align256(o + static_cast<size_t>(hq) * p.n_t32 * img);
+  p.kimg = o;   o = align256(o + static_cast<size_t>(hkv) * p.n_t32 * img);
+  p.ld = o;     o = align256(o + static_cast<size_t>(hq) * p.n_t32 * 64 * 4);
+  p.colsum = o; o = align256(o + static_cast<size_t>(hq) * p.mp * 4);
+  p.dkp = o;    o = align256(o + static_cast<size_t>(hq) * p.mp * d * 4);
+  p.dvp = o;    o = align256(o + static_cast<size_t>(hq) * p.mp * d * 4);
+  p.qdot = o;   o = align256(o + static_cast<size_t>(hq) * p.n_t128 * 4);
+  p.total = o;
+  return p;
+}
+
+// Work-group b -> (head, v): heads of one KV group on one XCD (work-groups
+// are dealt round-robin over the 8 XCDs), v counting that head's units.
+__device__ __forceinline__ void head_unit(int b, int hq, int& head, int& v) {
+  if ((hq & 7) == 0) {
+    const int hpx = hq >> 3, xcd = b & 7, slot = b >> 3;
+    head = xcd * hpx + slot % hpx;
+    v = slot / hpx;
+  } else {
+    head = b % hq;
+    v = b / hq;
+  }
+}
+
+// Round-to-nearest-even bf16 pair (lo in the low half).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<bf16>(lo));
+  const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<bf16>(hi));
+  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
+
+// Sum of x over lane l and lane l ^ 32.
+__device__ __forceinline__ float add_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Tile images.  Row (query or key) 16 g + 8 b + 4 h' + i of a 32-row tile sits
+// at position 16 g + 8 h' + 4 b + i of every image row d, so that MFMA k-step
+// g, lane half h', element e = 4 b + i reads row 16 g + 8 (e / 4) + 4 h' + e % 4:
+// the row a C-layout register 8 g + e of lane half h' holds.  Task (kg, dc)
+// moves rows 4 kg .. 4 kg + 3, dims 8 dc .. 8 dc + 7 (D tasks per tile).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void transpose_tile(__amdgpu_buffer_rsrc_t r, uint32_t row_stride,
+                                               uint32_t row0, char* __restrict__ img, int task) {
+  using T = Bwd<D>;
+  const int kg = task & 7, dc = task >> 3;
+  u32x4 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = bload16(r, (row0 + 4 * kg + i) * row_stride + 16 * dc);
+  const int p = 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint2 lo, hi;   // dim 2w: low halves; dim 2w+1: high halves
+    lo.x = (x[0][w] & 0xFFFFu) | (x[1][w] << 16);
+    lo.y = (x[2][w] & 0xFFFFu) | (x[3][w] << 16);
+    hi.x = (x[0][w] >> 16) | (x[1][w] & 0xFFFF0000u);
+    hi.y = (x[2][w] >> 16) | (x[3][w] & 0xFFFF0000u);
+    const int d0 = 8 * dc + 2 * w;
+    *reinterpret_cast<uint2*>(img + d0 * T::IMG_ROW + 2 * p) = lo;
+    *reinterpret_cast<uint2*>(img + (d0 + 1) * T::IMG_ROW + 2 * p) = hi;
+  }
+}
+
+// Blocks [0, Hq * n_t32): query head h, tile t -> Q^T, dO^T images and the
+// rows' (lse2, D); blocks after that: KV head, tile -> K^T image.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_pack_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ out,
+    const float* __restrict__ lse, const bf16* __restrict__ dout, int M, int Hq, int Hkv,
+    int n_t32, char* __restrict__ qimg, char* __restrict__ doimg, char* __restrict__ kimg,
+    float* __restrict__ ld) {
+  using T = Bwd<D>;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  if (b >= Hq * n_t32) {
+    const int kvh = (b - Hq * n_t32) / n_t32, t = (b - Hq * n_t32) % n_t32;
+    const uint32_t stride = static_cast<uint32_t>(Hkv) * D * 2;
+    if (tid < D) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + static_cast<size_t>(kvh) * D, stride * static_cast<uint32_t>(M));
+      transpose_tile<D>(rk, stride, static_cast<uint32_t>(t) * kRows,
+                        kimg + (static_cast<size_t>(kvh) * n_t32 + t) * T::IMG, tid);
+    }
+    return;
+  }
+  const int h = b / n_t32, t = b % n_t32;
+  const uint32_t stride = static_cast<uint32_t>(Hq) * D * 2;
+  const uint32_t range = stride * static_cast<uint32_t>(M);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(h) * D, range);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + static_cast<size_t>(h) * D, range);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + static_cast<size_t>(h) * D, range);
+  const size_t tile = static_cast<size_t>(h) * n_t32 + t;
+  const uint32_t row0 = static_cast<uint32_t>(t) * kRows;
+  if (tid < D) transpose_tile<D>(rq, stride, row0, qimg + tile * T::IMG, tid);
+  else if (tid < 2 * D) transpose_tile<D>(rd, stride, row0, doimg + tile * T::IMG, tid - D);
+  // D_i = dO_i . O_i: eight lanes per row, D / 8 dims each, combined in a
+  // fixed butterfly.
+  const int qi = tid >> 3, part = tid & 7;
+  constexpr int PER = D / 8;        // dims per lane: 16 or 8
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < PER / 8; ++c) {
+    const uint32_t off = (row0 + qi) * stride + (part * PER + 8 * c) * 2;
+    const u32x4 a = bload16(rd, off), o = bload16(ro, off);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(o[w] << 16), acc);
+      acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(o[w] & 0xFFFF0000u), acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (part == 0) {
+    const int64_t row = static_cast<int64_t>(row0) + qi;
+    float* dst = ld + tile * 64;
+    dst[qi] = row < M ? lse[static_cast<int64_t>(h) * M + row] * kLog2e : INFINITY;
+    dst[32 + qi] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dkdv
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ key_score,
+    const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
+    int n_t32, int mp, const char* __restrict__ qimg, const char* __restrict__ doimg,
+    const float* __restrict__ ld, float* __restrict__ colsum, float* __restrict__ dkp,
+    float* __restrict__ dvp) {
+  using T = Bwd<D>;
+  constexpr int KS = T::KS, DT = T::DT;
+  constexpr int NW = kThreads / 64;
+  constexpr int NJR = T::N_ROW_DMA / NW;                     // row-tile DMA chunks per wave
+  constexpr int NJI = (T::N_IMG_DMA + NW - 1) / NW;          // image chunks per wave (last partial)
+  static_assert(T::N_ROW_DMA % NW == 0, "row tiles split evenly over the waves");
+
+  __shared__ __align__(16) char lds_qr[2][T::ROWS_TILE];
+  __shared__ __align__(16) char lds_dr[2][T::ROWS_TILE];
+  __shared__ __align__(16) char lds_qi[2][T::IMG];
+  __shared__ __align__(16) char lds_di[2][T::IMG];
+  __shared__ __align__(16) float lds_ld[2][64];
+
+  int head, kt;
+  head_unit(blockIdx.x, Hq, head, kt);            // kt ascending: longest walks first
+  const int kvh = head / (Hq / Hkv);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int key0 = kt * kWgRows + wave * kRows;   // this wave's first key
+  const int my_key = key0 + l32;
+
+  // K and V fragments of this lane's key (B operands of S = Q K^T, dP = dO V^T)
+  const uint32_t kv_row = static_cast<uint32_t>(Hkv) * D * 2;
+  bf16x8 kf[KS], vf[KS];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + static_cast<size_t>(kvh) * D, kv_row * static_cast<uint32_t>(M));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + static_cast<size_t>(kvh) * D, kv_row * static_cast<uint32_t>(M));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t off = static_cast<uint32_t>(my_key) * kv_row + (16 * s + 8 * hh) * 2;
+      kf[s] = as_bf16x8(bload16(rk, off));
+      vf[s] = as_bf16x8(bload16(rv, off));
+    }
+  }
+  const float c_h = 1.f / (sqrtf(static_cast<float>(D)) * tau[head]);
+  const float alpha = kLog2e * c_h;
+  const float bkey = my_key < M ? gain[head] * key_score[my_key] * kLog2e : 0.f;
+
+  floatx16 dk[DT], dv[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) {
+    dk[i] = zero16();
+    dv[i] = zero16();
+  }
+  float csum = 0.f;
+
+  // ---- DMA of one 32-query step into ring slot `buf`
+  const uint32_t q_row = static_cast<uint32_t>(Hq) * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(head) * D, q_row * static_cast<uint32_t>(M));
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + static_cast<size_t>(head) * D, q_row * static_cast<uint32_t>(M));
+  const size_t img_head = static_cast<size_t>(head) * n_t32 * T::IMG;
+  const uint32_t img_bytes = static_cast<uint32_t>(n_t32) * T::IMG;
+  const __amdgpu_buffer_rsrc_t rqi = make_rsrc(qimg + img_head, img_bytes);
+  const __amdgpu_buffer_rsrc_t rdi = make_rsrc(doimg + img_head, img_bytes);
+  const __amdgpu_buffer_rsrc_t rld = make_rsrc(ld + static_cast<size_t>(head) * n_t32 * 64,
+                                               static_cast<uint32_t>(n_t32) * 256);
+  const int lane16 = 16 * lane;
+  // Row tiles: the lane filling LDS slot s of row r fetches chunk s ^ swz(r)
+  // of that row (Q and dO rows share the stride, hence these offsets).
+  uint32_t roff[NJR];
+#pragma unroll
+  for (int jj = 0; jj < NJR; ++jj) {
+    const int byte = 1024 * (wave_s + NW * jj) + lane16;
+    const int r = byte / T::ROW, slot = (byte % T::ROW) / 16;
+    roff[jj] = static_cast<uint32_t>(r) * q_row + static_cast<uint32_t>((slot ^ T::swz(r)) * 16);
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto dma = [&](int buf, int t) __attribute__((always_inline)) {
+    const uint32_t row_off = static_cast<uint32_t>(t) * kRows * q_row;
+    const int img_off = t * T::IMG;
+#pragma unroll
+    for (int jj = 0; jj < NJR; ++jj) {
+      const int c = wave_s + NW * jj;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr)(&lds_qr[buf][0] + 1024 * c), 16,
+                                               static_cast<int>(row_off + roff[jj]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)(&lds_dr[buf][0] + 1024 * c), 16,
+                                               static_cast<int>(row_off + roff[jj]), 0, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < NJI; ++jj) {
+      const int c = wave_s + NW * jj;
+      if (c < T::N_IMG_DMA) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rqi, (lds_ptr)(&lds_qi[buf][0] + 1024 * c), 16, lane16,
+                                                 img_off + 1024 * c, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdi, (lds_ptr)(&lds_di[buf][0] + 1024 * c), 16, lane16,
+                                                 img_off + 1024 * c, 0, 0);
+      }
+    }
+    if (wave_s == NW - 1 && lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_ptr)(&lds_ld[buf][0]), 16, lane16, t * 256, 0, 0);
+  };
+
+  // ---- one step: queries 32 t .. 32 t + 31 against this wave's keys
+  const uint32_t a_base = static_cast<uint32_t>(l32) * T::ROW + ((hh ^ T::swz(l32)) << 4);
+  auto step = [&](auto diag_c, int buf, int t) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_c)::value;
+    const char* qr = &lds_qr[buf][0];
+    const char* dr = &lds_dr[buf][0];
+    floatx16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t off = a_base ^ static_cast<uint32_t>(32 * ks);
+      s = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(qr + off), kf[ks], s);
+      dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(dr + off), vf[ks], dp);
+    }
+    // P and dS for this lane's key and its 16 queries 8 (j/4) + 4 hh + j%4
+    uint32_t pk[8], dsk[8];
+    const int qbase = t * kRows + 4 * hh;
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const float4 l2 = *reinterpret_cast<const float4*>(&lds_ld[buf][8 * jg + 4 * hh]);
+      const float4 dd = *reinterpret_cast<const float4*>(&lds_ld[buf][32 + 8 * jg + 4 * hh]);
+      const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+      const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
+      float pj[4], dsj[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * jg + i;
+        float p = fast_exp2(fmaf(s[j], alpha, bkey - lv[i]));
+        if (DIAG && qbase + 8 * jg + i < my_key) p = 0.f;
+        const float ds = p * (dp[j] - dv4[i]);
+        csum += ds;
+        pj[i] = p;
+        dsj[i] = ds;
+      }
+      pk[2 * jg] = pack_bf16(pj[0], pj[1]);
+      pk[2 * jg + 1] = pack_bf16(pj[2], pj[3]);
+      dsk[2 * jg] = pack_bf16(dsj[0], dsj[1]);
+      dsk[2 * jg + 1] = pack_bf16(dsj[2], dsj[3]);
+    }
+    // dV += P^T dO, dK += dS^T Q: k-step ks2 takes registers 8 ks2 .. 8 ks2 + 7
+    const char* qi = &lds_qi[buf][0];
+    const char* di = &lds_di[buf][0];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const u32x4 pa = {pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2], pk[4 * ks2 + 3]};
+      const u32x4 da = {dsk[4 * ks2], dsk[4 * ks2 + 1], dsk[4 * ks2 + 2], dsk[4 * ks2 + 3]};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int off = (32 * dt + l32) * T::IMG_ROW + 32 * ks2 + 16 * hh;
+        dv[dt] = mfma_32x32x16(as_bf16x8(pa), *reinterpret_cast<const bf16x8*>(di + off), dv[dt]);
+        dk[dt] = mfma_32x32x16(as_bf16x8(da), *reinterpret_cast<const bf16x8*>(qi + off), dk[dt]);
+      }
+    }
+  };
+
+  // ---- main loop over query tiles t0 .. n_real - 1, one barrier per step
+  const int t0 = kt * (kWgRows / kRows);
+  const int t_end = (M + kRows - 1) / kRows;
+  const int t_vis = t0 + wave;                    // first tile this wave sees (its diagonal)
+  dma(0, t0);
+  for (int t = t0; t < t_end; ++t) {
+    const int buf = (t - t0) & 1;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA has landed
+    __syncthreads();                 // ... and every other wave's; the other slot is free
+    if (t + 1 < t_end) dma(buf ^ 1, t + 1);
+    if (t == t_vis) step(std::true_type{}, buf, t);
+    else if (t > t_vis) step(std::false_type{}, buf, t);
+  }
+
+  // ---- epilogue: fp32 partials of this head (rows = keys, columns = d)
+  float* dkh = dkp + static_cast<size_t>(head) * mp * D;
+  float* dvh = dvp + static_cast<size_t>(head) * mp * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const size_t row = static_cast<size_t>(key0 + 8 * (j >> 2) + 4 * hh + (j & 3));
+      dkh[row * D + 32 * dt + l32] = dk[dt][j] * c_h;
+      dvh[row * D + 32 * dt + l32] = dv[dt][j];
+    }
+  }
+  csum = add_halves(csum);
+  if (hh == 0) colsum[static_cast<size_t>(head) * mp + my_key] = csum;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ key_score,
+    const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
+    int n_t32, int n_t128, const char* __restrict__ kimg, const float* __restrict__ ld,
+    bf16* __restrict__ dq, float* __restrict__ qdot) {
+  using T = Bwd<D>;
+  constexpr int KS = T::KS, DT = T::DT;
+  constexpr int NW = kThreads / 64;
+  constexpr int NJR = T::N_ROW_DMA / NW;
+  constexpr int NJI = (T::N_IMG_DMA + NW - 1) / NW;
+  static_assert(T::N_ROW_DMA % NW == 0, "row tiles split evenly over the waves");
+
+  __shared__ __align__(16) char lds_kr[2][T::ROWS_TILE];
+  __shared__ __align__(16) char lds_vr[2][T::ROWS_TILE];
+  __shared__ __align__(16) char lds_ki[2][T::IMG];
+  __shared__ __align__(16) float lds_s[2][32];
+  __shared__ float lds_red[kThreads / 64];
+
+  int head, v_;
+  head_unit(blockIdx.x, Hq, head, v_);
+  const int qt = n_t128 - 1 - v_;                // longest walks first
+  const int kvh = head / (Hq / Hkv);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int q0 = qt * kWgRows + wave * kRows;
+  const int my_q = q0 + l32;
+
+  const uint32_t q_row = static_cast<uint32_t>(Hq) * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(head) * D, q_row * static_cast<uint32_t>(M));
+  bf16x8 qf[KS], df[KS];
+  {
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + static_cast<size_t>(head) * D, q_row * static_cast<uint32_t>(M));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t off = static_cast<uint32_t>(my_q) * q_row + (16 * s + 8 * hh) * 2;
+      qf[s] = as_bf16x8(bload16(rq, off));
+      df[s] = as_bf16x8(bload16(rd, off));
+    }
+  }
+  const float c_h = 1.f / (sqrtf(static_cast<float>(D)) * tau[head]);
+  const float alpha = kLog2e * c_h;
+  const float gl = gain[head] * kLog2e;
+  const float* ldt = ld + (static_cast<size_t>(head) * n_t32 + (q0 >> 5)) * 64;
+  const float lse2 = ldt[l32], dd = ldt[32 + l32];
+
+  floatx16 acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc[i] = zero16();
+
+  const uint32_t kv_row = static_cast<uint32_t>(Hkv) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + static_cast<size_t>(kvh) * D, kv_row * static_cast<uint32_t>(M));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + static_cast<size_t>(kvh) * D, kv_row * static_cast<uint32_t>(M));
+  const __amdgpu_buffer_rsrc_t rki = make_rsrc(kimg + static_cast<size_t>(kvh) * n_t32 * T::IMG,
+                                               static_cast<uint32_t>(n_t32) * T::IMG);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(key_score, static_cast<uint32_t>(M) * 4);
+  const int lane16 = 16 * lane;
+  uint32_t roff[NJR];   // as in bwd_dkdv: K and V rows share the stride
+#pragma unroll
+  for (int jj = 0; jj < NJR; ++jj) {
+    const int byte = 1024 * (wave_s + NW * jj) + lane16;
+    const int r = byte / T::ROW, slot = (byte % T::ROW) / 16;
+    roff[jj] = static_cast<uint32_t>(r) * kv_row + static_cast<uint32_t>((slot ^ T::swz(r)) * 16);
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto dma = [&](int buf, int u) __attribute__((always_inline)) {
+    const uint32_t row_off = static_cast<uint32_t>(u) * kRows * kv_row;
+    const int img_off = u * T::IMG;
+#pragma unroll
+    for (int jj = 0; jj < NJR; ++jj) {
+      const int c = wave_s + NW * jj;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr)(&lds_kr[buf][0] + 1024 * c), 16,
+                                               static_cast<int>(row_off + roff[jj]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(&lds_vr[buf][0] + 1024 * c), 16,
+                                               static_cast<int>(row_off + roff[jj]), 0, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < NJI; ++jj) {
+      const int c = wave_s + NW * jj;
+      if (c < T::N_IMG_DMA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rki, (lds_ptr)(&lds_ki[buf][0] + 1024 * c), 16, lane16,
+                                                 img_off + 1024 * c, 0, 0);
+    }
+    if (wave_s == NW - 1 && lane < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(&lds_s[buf][0]), 16, lane16, u * 128, 0, 0);
+  };
+
+  const uint32_t a_base = static_cast<uint32_t>(l32) * T::ROW + ((hh ^ T::swz(l32)) << 4);
+  auto step = [&](auto diag_c, int buf, int u) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_c)::value;
+    const char* kr = &lds_kr[buf][0];
+    const char* vr = &lds_vr[buf][0];
+    floatx16 st = zero16(), dpt = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t off = a_base ^ static_cast<uint32_t>(32 * ks);
+      st = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(kr + off), qf[ks], st);
+      dpt = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(vr + off), df[ks], dpt);
+    }
+    // dS^T for this lane's query and its 16 keys 8 (j/4) + 4 hh + j%4
+    uint32_t dsk[8];
+    const int kbase = u * kRows + 4 * hh;
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const float4 sv = *reinterpret_cast<const float4*>(&lds_s[buf][8 * jg + 4 * hh]);
+      const float sk[4] = {sv.x, sv.y, sv.z, sv.w};
+      float dsj[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * jg + i;
+        float p = fast_exp2(fmaf(st[j], alpha, fmaf(sk[i], gl, -lse2)));
+        if (DIAG && kbase + 8 * jg + i > my_q) p = 0.f;
+        dsj[i] = p * (dpt[j] - dd);
+      }
+      dsk[2 * jg] = pack_bf16(dsj[0], dsj[1]);
+      dsk[2 * jg + 1] = pack_bf16(dsj[2], dsj[3]);
+    }
+    // dQ^T += K^T dS^T
+    const char* ki = &lds_ki[buf][0];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const u32x4 b = {dsk[4 * ks2], dsk[4 * ks2 + 1], dsk[4 * ks2 + 2], dsk[4 * ks2 + 3]};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int off = (32 * dt + l32) * T::IMG_ROW + 32 * ks2 + 16 * hh;
+        acc[dt] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ki + off), as_bf16x8(b), acc[dt]);
+      }
+    }
+  };
+
+  // ---- key tiles 0 .. u_end - 1; this wave's diagonal tile is q0 / 32
+  const int q_last = min(qt * kWgRows + kWgRows, M) - 1;
+  const int u_end = q_last / kRows + 1;
+  const int u_diag = q0 / kRows;
+  dma(0, 0);
+  for (int u = 0; u < u_end; ++u) {
+    const int buf = u & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (u + 1 < u_end) dma(buf ^ 1, u + 1);
+    if (u == u_diag) step(std::true_type{}, buf, u);
+    else if (u < u_diag) step(std::false_type{}, buf, u);
+  }
+
+  // ---- epilogue: dq = c_h (K^T dS^T)^T; lane = query, registers = dims
+  // 32 dt + 8 (j/4) + 4 hh + j%4.  Also q.dq for the temperature gradient.
+  float qd = 0.f;
+  if (my_q < M) {
+    bf16* orow = dq + static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
+    const bf16* qrow = q + static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * dt + 8 * jj + 4 * hh;
+        const uint2 qv = *reinterpret_cast<const uint2*>(qrow + d0);
+        const float qx[4] = {__uint_as_float(qv.x << 16), __uint_as_float(qv.x & 0xFFFF0000u),
+                             __uint_as_float(qv.y << 16), __uint_as_float(qv.y & 0xFFFF0000u)};
+        bf16 o4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = acc[dt][4 * jj + r] * c_h;
+          qd = fmaf(qx[r], g, qd);
+          o4[r] = static_cast<bf16>(g);
+        }
+        *reinterpret_cast<uint2*>(orow + d0) = __builtin_bit_cast(uint2, o4);
+      }
+    }
+  }
+  qd = add_halves(qd);
+  if (hh == 1) qd = 0.f;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) qd += __shfl_xor(qd, o);
+  if (lane == 0) lds_red[wave] = qd;
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
+    for (int w = 0; w < NW; ++w) s += lds_red[w];
+    qdot[static_cast<size_t>(head) * n_t128 + qt] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reductions (fixed order)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const float* __restrict__ dkp,
+                                                              const float* __restrict__ dvp, int M,
+                                                              int Hq, int Hkv, int mp,
+                                                              bf16* __restrict__ dk,
+                                                              bf16* __restrict__ dv) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // one 4-dim group
+  const int64_t per_row = static_cast<int64_t>(Hkv) * (D / 4);
+  if (e >= static_cast<int64_t>(M) * per_row) return;
+  const int64_t key = e / per_row;
+  const int kvh = static_cast<int>((e % per_row) / (D / 4));
+  const int d4 = static_cast<int>(e % (D / 4));
+  const int G = Hq / Hkv;
+  float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < G; ++g) {
+    const size_t src = (static_cast<size_t>(kvh * G + g) * mp + key) * D + 4 * d4;
+    const float4 x = *reinterpret_cast<const float4*>(dkp + src);
+    const float4 y = *reinterpret_cast<const float4*>(dvp + src);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+  }
+  const size_t dst = (static_cast<size_t>(key) * Hkv + kvh) * D + 4 * d4;
+  const bf16 ka[4] = {static_cast<bf16>(a.x), static_cast<bf16>(a.y), static_cast<bf16>(a.z), static_cast<bf16>(a.w)};
+  const bf16 va[4] = {static_cast<bf16>(b.x), static_cast<bf16>(b.y), static_cast<bf16>(b.z), static_cast<bf16>(b.w)};
+  *reinterpret_cast<uint2*>(dk + dst) = __builtin_bit_cast(uint2, ka);
+  *reinterpret_cast<uint2*>(dv + dst) = __builtin_bit_cast(uint2, va);
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_score_kernel(const float* __restrict__ colsum,
+                                                             const float* __restrict__ gain, int M,
+                                                             int Hq, int mp,
+                                                             float* __restrict__ dscore) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (j >= M) return;
+  float s = 0.f;
+  for (int h = 0; h < Hq; ++h) s = fmaf(gain[h], colsum[static_cast<size_t>(h) * mp + j], s);
+  dscore[j] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_head_kernel(const float* __restrict__ colsum,
+                                                            const float* __restrict__ key_score,
+                                                            const float* __restrict__ qdot,
+                                                            const float* __restrict__ tau, int M,
+                                                            int mp, int n_t128,
+                                                            float* __restrict__ dgain,
+                                                            float* __restrict__ dtau) {
+  __shared__ float red[kThreads];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float* cs = colsum + static_cast<size_t>(h) * mp;
+  float s = 0.f;
+  for (int j = tid; j < M; j += kThreads) s = fmaf(key_score[j], cs[j], s);
+  red[tid] = s;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    dgain[h] = red[0];
+    float t = 0.f;
+    for (int i = 0; i < n_t128; ++i) t += qdot[static_cast<size_t>(h) * n_t128 + i];
+    dtau[h] = -t / tau[h];
+  }
+}
+
+template <int D>
+hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M, int Hq,
+                    int Hkv, const float* s, const float* g, const float* t, const uint16_t* out,
+                    const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
+                    uint16_t* dv, float* dscore, float* dgain, float* dtau, void* workspace,
+                    hipStream_t stream) {
+  const BwdPlan p = bwd_plan(M, Hq, Hkv, D);
+  char* ws = static_cast<char*>(workspace);
+  const bf16* bq = reinterpret_cast<const bf16*>(q);
+  const bf16* bk = reinterpret_cast<const bf16*>(k);
+  const bf16* bv = reinterpret_cast<const bf16*>(v);
+  const bf16* bd = reinterpret_cast<const bf16*>(dout);
+  const int n_t32 = static_cast<int>(p.n_t32), n_t128 = static_cast<int>(p.n_t128);
+  const int mp = static_cast<int>(p.mp);
+  float* ld = reinterpret_cast<float*>(ws + p.ld);
+  float* colsum = reinterpret_cast<float*>(ws + p.colsum);
+  float* dkp = reinterpret_cast<float*>(ws + p.dkp);
+  float* dvp = reinterpret_cast<float*>(ws + p.dvp);
+  float* qdot = reinterpret_cast<float*>(ws + p.qdot);
+  hipLaunchKernelGGL((bwd_pack_kernel<D>), dim3(static_cast<unsigned>((Hq + Hkv) * n_t32)),
+                     dim3(kThreads), 0, stream, bq, bk, reinterpret_cast<const bf16*>(out), lse, bd,
+                     M, Hq, Hkv, n_t32, ws + p.qimg, ws + p.doimg, ws + p.kimg, ld);
+  const int n_kt = (M + kWgRows - 1) / kWgRows;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(Hq * n_kt)), dim3(kThreads),
+                     0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, mp, ws + p.qimg,
+                     ws + p.doimg, ld, colsum, dkp, dvp);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128)), dim3(kThreads),
+                     0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, n_t128, ws + p.kimg, ld,
+                     reinterpret_cast<bf16*>(dq), qdot);
+  const int64_t groups = static_cast<int64_t>(M) * Hkv * (D / 4);
+  hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3(static_cast<unsigned>((groups + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, dkp, dvp, M, Hq, Hkv, mp,
+                     reinterpret_cast<bf16*>(dk), reinterpret_cast<bf16*>(dv));
+  hipLaunchKernelGGL(bwd_score_kernel, dim3(static_cast<unsigned>((M + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, colsum, g, M, Hq, mp, dscore);
+  hipLaunchKernelGGL(bwd_head_kernel, dim3(static_cast<unsigned>(Hq)), dim3(kThreads), 0, stream,
+                     colsum, s, qdot, t, M, mp, n_t128, dgain, dtau);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_dim) {
+  if (n <= 0) return 0;
+  return bwd_plan(n, n_q_heads, n_kv_heads, head_dim).total;
+}
+
+size_t attn_bwd_image_bytes_per_head(int64_t n, int head_dim) {
+  const BwdPlan p = bwd_plan(n, 1, 1, head_dim);
+  return static_cast<size_t>(p.n_t32) * head_dim * (kRows * 2 + 16);
+}
+
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
+                           int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
+                           const float* gain, const float* tau, const uint16_t* out,
+                           const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
+                           uint16_t* dv, float* dscore, float* dgain, float* dtau,
+                           void* workspace, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int M = static_cast<int>(n);
+  if (head_dim == 128)
+    return launch_d<128>(q, k, v, M, n_q_heads, n_kv_heads, key_score, gain, tau, out, lse, dout,
+                         dq, dk, dv, dscore, dgain, dtau, workspace, stream);
+  return launch_d<64>(q, k, v, M, n_q_heads, n_kv_heads, key_score, gain, tau, out, lse, dout, dq,
+                      dk, dv, dscore, dgain, dtau, workspace, stream);
+}
+
+}  // namespace tg

@@ -35,6 +35,9 @@ _SIGNATURES = {
                                          _P, ctypes.c_size_t, _P]),
     "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
+    "tg_attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
+    "tg_gated_attn_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "tg_decode_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
     "tg_qk_norm_rope": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, ctypes.c_float,
                                        ctypes.c_double, _P, _P]),
@@ -259,6 +262,57 @@ def full_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check(lib().tg_full_attn_fwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(out), _ptr(lse),
                                   _ptr(ws), ws_bytes, _stream(stream)))
     return (out, lse) if lse is not None else out
+
+
+def attn_bwd_workspace_bytes(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    return int(lib().tg_attn_bwd_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim))
+
+
+def attn_bwd_workspace(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                       device="cuda") -> torch.Tensor:
+    """A device buffer large enough for one attention backward over n rows."""
+    return torch.empty(max(attn_bwd_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim), 16),
+                       dtype=torch.uint8, device=device)
+
+
+def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
+                   gain: torch.Tensor, tau: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                   dout: torch.Tensor, grads: Optional[dict] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of gated_attn_fwd given its out, its lse [Hq, M] and dout.
+    Returns dict(dq, dk, dv (bf16, shaped like q, k, v), dscore [M], dgain [Hq],
+    dtau [Hq] (fp32)); ``grads`` may hold preallocated tensors under those names."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _need(t, nm, torch.bfloat16)
+    for t, nm in ((key_score, "key_score"), (gain, "gain"), (tau, "tau"), (lse, "lse")):
+        _need(t, nm, torch.float32)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (n, hkv, d) or v.shape != k.shape or out.shape != q.shape \
+            or dout.shape != q.shape or lse.shape != (hq, n) or key_score.shape != (n,) \
+            or gain.shape != (hq,) or tau.shape != (hq,):
+        raise ValueError("attention backward operand shapes do not match")
+    g = dict(grads or {})
+    g.setdefault("dq", torch.empty_like(q))
+    g.setdefault("dk", torch.empty_like(k))
+    g.setdefault("dv", torch.empty_like(v))
+    g.setdefault("dscore", torch.empty(n, dtype=torch.float32, device=q.device))
+    g.setdefault("dgain", torch.empty(hq, dtype=torch.float32, device=q.device))
+    g.setdefault("dtau", torch.empty(hq, dtype=torch.float32, device=q.device))
+    for nm in ("dq", "dk", "dv"):
+        _need(g[nm], nm, torch.bfloat16)
+    for nm in ("dscore", "dgain", "dtau"):
+        _need(g[nm], nm, torch.float32)
+    if workspace is None:
+        workspace = attn_bwd_workspace(n, hq, hkv, d, q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    _check(lib().tg_gated_attn_bwd(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _ptr(key_score),
+                                   _ptr(gain), _ptr(tau), _ptr(out), _ptr(lse), _ptr(dout),
+                                   _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dscore"]),
+                                   _ptr(g["dgain"]), _ptr(g["dtau"]), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return g
 
 
 def decode_workspace_bytes(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:

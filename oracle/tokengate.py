@@ -234,7 +234,8 @@ def gated_attention(q, k, v, key_score, gain, tau, rows=None, return_lse=False,
     return (out, lse) if return_lse else out
 
 
-def gated_attention_bwd(q, k, v, key_score, gain, tau, dout, row_block: int = 256):
+def gated_attention_bwd(q, k, v, key_score, gain, tau, dout, row_block: int = 256,
+                        return_scales: bool = False):
     """Gradients of the token-gated attention above, for training the gate
     through the bias ([KO] "작동 방식": the score enters the logits as a bias, so
     the loss reaches the gate's scores through it; [ABS]).
@@ -254,6 +255,13 @@ def gated_attention_bwd(q, k, v, key_score, gain, tau, dout, row_block: int = 25
         dtau_h    = sum_ij dlogit_ij q_i.k_j * (-1 / (sqrt(d) tau_h^2))
     (K/V rows are shared by the heads of a group, so their gradients sum over
     those heads.)
+
+    ``return_scales`` adds, for the score, gain and temperature gradients, the
+    sums of their terms' magnitudes with each dlogit_ij replaced by
+    p_ij (|dp_ij - D_i| + A_i), where D_i = sum_l p_il dp_il and A_i =
+    sum_f |dout_if out_if|: what an error bound for a computation of these
+    sums from a rounded output (D taken as dout.out) is proportional to.
+    Keys "dscore_scale", "dgain_scale", "dtau_scale".  They are not gradients.
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -272,6 +280,9 @@ def gated_attention_bwd(q, k, v, key_score, gain, tau, dout, row_block: int = 25
     dscore = np.zeros(m, dtype=np.float64)
     dgain = np.zeros(hq, dtype=np.float64)
     dtau = np.zeros(hq, dtype=np.float64)
+    sc_score = np.zeros(m, dtype=np.float64)
+    sc_gain = np.zeros(hq, dtype=np.float64)
+    sc_tau = np.zeros(hq, dtype=np.float64)
     for h in range(hq):
         g = h // group
         kh = k[:, g, :].astype(np.float64)
@@ -296,7 +307,17 @@ def gated_attention_bwd(q, k, v, key_score, gain, tau, dout, row_block: int = 25
             dscore[:kend] += gain[h] * dlogit.sum(axis=0)
             dgain[h] += (dlogit * s[None, :kend]).sum()
             dtau[h] += (dlogit * qk).sum() * (-1.0 / (math.sqrt(d) * tau[h] ** 2))
-    return dict(dq=dq, dk=dk, dv=dv, dscore=dscore, dgain=dgain, dtau=dtau)
+            if return_scales:
+                dsum = (p * dp).sum(axis=1, keepdims=True)
+                a = np.abs(dob * (p @ vh[:kend])).sum(axis=1, keepdims=True)
+                mag = p * (np.abs(dp - dsum) + a)
+                sc_score[:kend] += abs(gain[h]) * mag.sum(axis=0)
+                sc_gain[h] += (mag * np.abs(s[None, :kend])).sum()
+                sc_tau[h] += (mag * np.abs(qk)).sum() / (math.sqrt(d) * tau[h] ** 2)
+    res = dict(dq=dq, dk=dk, dv=dv, dscore=dscore, dgain=dgain, dtau=dtau)
+    if return_scales:
+        res.update(dscore_scale=sc_score, dgain_scale=sc_gain, dtau_scale=sc_tau)
+    return res
 
 
 def full_attention(q, k, v, rows=None, return_lse=False):

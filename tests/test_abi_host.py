@@ -39,6 +39,7 @@ def test_header_declares_the_five_entry_points():
     for fn in ("tg_gate_score", "tg_topk_select", "tg_topk_workspace_bytes", "tg_compact",
                "tg_gated_attn_fwd", "tg_full_attn_fwd", "tg_attn_workspace_bytes",
                "tg_gated_decode_fwd", "tg_decode_workspace_bytes", "tg_qk_norm_rope",
+               "tg_gated_attn_bwd", "tg_attn_bwd_workspace_bytes",
                "tg_kept_count", "tg_status_str", "tg_last_error"):
         assert fn in names
 
@@ -258,3 +259,50 @@ def test_qk_norm_rope_validation(L):
     assert f(A, 10, A, A, 5, 4, 128, None, 1e-6, 1e6, A + 1024, 0) == INVALID   # overlap
     assert "overlap" in tg.last_error()
     assert f(None, 0, None, None, 0, 4, 128, None, 1e-6, 1e6, None, 0) == OK    # n == 0
+
+
+def _bwd_ws(n, hq, hkv, d):
+    """The backward workspace restated: rows padded to whole 128-row blocks;
+    q^T, dout^T (per query head) and k^T (per KV head) images of 32-row tiles,
+    d rows of 80 bytes each; (lse, D) as 64 floats per query head and tile;
+    per query head and padded row one column-sum float and d fp32 each of the
+    dk and dv partials; one float per query head and 128-row block; every
+    region rounded up to 256 bytes."""
+    t128 = -(-n // 128)
+    t32, mp = 4 * t128, 128 * t128
+    img = d * 80
+    o = 0
+    for size in (hq * t32 * img, hq * t32 * img, hkv * t32 * img, hq * t32 * 256, hq * mp * 4,
+                 hq * mp * d * 4, hq * mp * d * 4, hq * t128 * 4):
+        o = -(-(o + size) // 256) * 256
+    return o
+
+
+@pytest.mark.parametrize("n,hq,hkv,d", [(1, 16, 8, 128), (2304, 16, 8, 128), (8448, 16, 8, 128),
+                                        (300, 8, 1, 64), (129, 4, 2, 64)])
+def test_attn_bwd_workspace_bytes(L, n, hq, hkv, d):
+    assert L.tg_attn_bwd_workspace_bytes(n, hq, hkv, d) == _bwd_ws(n, hq, hkv, d)
+
+
+def test_attn_bwd_validation(L):
+    f = L.tg_gated_attn_bwd
+    W = 1 << 34
+    P = [A] * 13   # key_score, gain, tau, out, lse, dout, dq, dk, dv, dscore, dgain, dtau
+    def call(n=10, hq=16, hkv=8, d=128, q=A, ptrs=None, ws=A, wsb=W):
+        p = list(P[:12] if ptrs is None else ptrs)
+        return f(q, A, A, n, hq, hkv, d, *p, ws, wsb, 0)
+    assert call(n=-1) == INVALID
+    assert call(hkv=6) == INVALID                                   # Hq % Hkv
+    assert call(d=96) == UNSUPPORTED
+    assert call(n=1 << 20) == UNSUPPORTED                           # 2^31 bytes of q
+    assert call(n=0, q=None, ptrs=[None] * 12, ws=None, wsb=0) == OK   # no-op
+    for i in range(12):                                             # every pointer required
+        ptrs = [A] * 12
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == INVALID, i
+    assert call(q=A + 8) == INVALID                                 # alignment
+    need = L.tg_attn_bwd_workspace_bytes(10, 16, 8, 128)
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=A + 8, wsb=need + 64) == WORKSPACE               # workspace alignment
+    assert L.tg_attn_bwd_workspace_bytes(0, 16, 8, 128) == 0
+    assert L.tg_attn_bwd_workspace_bytes(10, 16, 8, 96) == 0

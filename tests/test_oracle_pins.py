@@ -298,6 +298,17 @@ def test_attention_bwd_score_gradient_sums_to_zero():
     assert np.max(np.abs(flat["dgain"])) < 1e-10
 
 
+def test_attention_bwd_scales_bound_their_gradients():
+    """The term-magnitude sums dominate the gradients they describe
+    (|sum dS x| <= sum |dS| |x| and |dS_ij| <= p_ij |dp_ij - D_i|)."""
+    q, k, v, s, gain, tau, dout = _bwd_case(14, 50, 4, 2, 8)
+    got = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, row_block=16, return_scales=True)
+    plain = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, row_block=16)
+    for name in ("dscore", "dgain", "dtau"):
+        assert np.all(got[name + "_scale"] >= np.abs(got[name])), name
+        assert np.array_equal(got[name], plain[name])
+
+
 def test_attention_two_key_closed_form_and_first_row():
     rng = np.random.default_rng(7)
     d = 6
