@@ -336,6 +336,32 @@ def main():
                       "gb_s": round(pro_bytes / (pro_ms / 1e3) / 1e9, 1),
                       "frac_hbm_peak": round(pro_bytes / (pro_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
 
+    # ---------------------------------------------------------------- upper-layer backward
+    # One gated layer's backward over the kept rows (the gradients through
+    # which a training loss reaches the gate: its scores, gains and
+    # temperatures), given that layer's forward output and lse and a seeded
+    # random upstream gradient.  Algorithmic work: the four products dV, dP,
+    # dK, dQ over the causal pairs; the deterministic kernels execute seven
+    # (S and dP are formed again for dQ).
+    q0, k0, v0 = kept_qkv[0]
+    fo, flse = tg.gated_attn_fwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], want_lse=True,
+                                 workspace=ws)
+    gen = torch.Generator(device=dev).manual_seed(2024)
+    dout_b = (torch.randn(fo.shape, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+    bws = tg.attn_bwd_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
+    grads = tg.gated_attn_bwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], fo, flse, dout_b,
+                              workspace=bws)
+    bwd_ms = time_calls(lambda: tg.gated_attn_bwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], fo,
+                                                  flse, dout_b, grads=grads, workspace=bws),
+                        max(3, min(args.steps, 10)))
+    bwd_flop = 4.0 * w.n_q_heads * w.head_dim * m * (m + 1)
+    bwd_tf = bwd_flop / (bwd_ms / 1e3) / 1e12
+    bwd_stats = {"ms_per_layer": round(bwd_ms, 5), "tflops": round(bwd_tf, 1),
+                 "frac_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                 "tflops_executed": round(bwd_tf * 7 / 4, 1),
+                 "bwd_over_fwd": round(bwd_ms / attn_ms_launch, 2)}
+    del bws, grads, fo, flse, dout_b
+
     # ---------------------------------------------------------------- full-N baseline
     full = None
     if not args.no_full_baseline:
@@ -442,6 +468,7 @@ def main():
         "full_prefill_baseline": full,
         "first_decode_step": decode,
         "upper_layer_qk_prologue": prologue_stats,
+        "upper_layer_backward": bwd_stats,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
