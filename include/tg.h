@@ -203,9 +203,12 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
  * bf16 tile images of q, dout and k (about 1.25x their bytes), per row and
  * query head its log-sum-exp and dout.out, per query head and key the column
  * sum of the logit gradient, fp32 per-query-head dk and dv partials
- * (2 * 4 * n * n_q_heads * head_dim bytes) and one float per query head and
- * 128-row block.  Host-only arithmetic; 0 for arguments tg_gated_attn_bwd
- * would reject as invalid or unsupported (n <= 0 included).
+ * (2 * 4 * n * n_q_heads * head_dim bytes) and a few floats per query head
+ * and 128-row block.  For short n, where the causal walks are split over
+ * several work-groups, the column sums and partials are held per split
+ * chunk (up to ~3x at 2304 rows) and fp32 dq partials are added.
+ * Host-only arithmetic; 0 for arguments tg_gated_attn_bwd would reject as
+ * invalid or unsupported (n <= 0 included).
  */
 size_t tg_attn_bwd_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads,
                                    int32_t head_dim);

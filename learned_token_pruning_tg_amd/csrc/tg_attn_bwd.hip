@@ -29,8 +29,12 @@
 //    queries with their Q and dO fragments in registers, over 32-key steps up
 //    to the diagonal: S^T = K Q^T, dP^T = V dO^T (lane = query), dS^T, then
 //    dQ^T += K^T dS^T.  Writes dQ (bf16) and per work-group sum_i q_i.dq_i.
-// 4. bwd_reduce: dK, dV = sum over the heads of each KV group (bf16).
-// 5. bwd_score: ds_j = sum_h g_h colsum_hj.  6. bwd_head: dg_h, dtau_h.
+// 4. bwd_reduce: dK, dV = sum over the heads of each KV group (bf16) and the
+//    score gradient ds_j = sum_h g_h colsum_hj; bwd_dq_reduce when the dQ
+//    walks are split.  5. bwd_head: dg_h, dtau_h.
+// Short kept prefixes leave too few long walks to fill the chip; then walks
+// are cut into chunks whose fp32 partials the reduce launches add in order.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -60,12 +64,34 @@ struct Bwd {
   static __host__ __device__ constexpr int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 };
 
+// Split walks.  A dK/dV work-group walks the 32-query steps from its
+// diagonal to the end (key block kt: n_t - 4 kt steps), a dQ work-group the
+// 32-key steps up to its diagonal (query block qt: at most 4 qt + 4).  When
+// the longest walk exceeds 1.3x the average number of steps per resident
+// work-group (512 of them), walks are cut into chunks of that length (never
+// shorter than 8 steps), each a work-group writing its own fp32 partials;
+// the reduce launches add the chunks in order.
+struct Split {
+  int len;   // steps per chunk
+  int nc;    // chunks of the longest walk
+};
+
+Split choose_split(int64_t longest, double total_steps) {
+  const double avg = total_steps / 512.0;
+  int64_t len = longest;
+  if (static_cast<double>(longest) > 1.3 * avg)
+    len = std::max<int64_t>(8, static_cast<int64_t>(std::ceil(1.3 * avg)));
+  len = std::max<int64_t>(1, std::min<int64_t>(len, longest));
+  return Split{static_cast<int>(len), static_cast<int>((longest + len - 1) / len)};
+}
+
 // Workspace layout (byte offsets, each region 256-byte aligned).
 struct BwdPlan {
   int64_t n_t32;     // 32-row tiles, rounded up to whole 128-row work-groups
   int64_t n_t128;
   int64_t mp;        // rows padded to n_t32 * 32
-  size_t qimg, doimg, kimg, ld, colsum, dkp, dvp, qdot, total;
+  Split kv, q;       // chunking of the dK/dV and dQ walks
+  size_t qimg, doimg, kimg, ld, colsum, dkp, dvp, dgp, qdot, dqp, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -75,18 +101,37 @@ BwdPlan bwd_plan(int64_t n, int hq, int hkv, int d) {
   p.n_t128 = (n + kWgRows - 1) / kWgRows;
   p.n_t32 = p.n_t128 * (kWgRows / kRows);
   p.mp = p.n_t32 * kRows;
+  const int64_t t_real = (n + kRows - 1) / kRows;   // 32-row tiles holding rows
+  double kv_steps = 0.0, q_steps = 0.0;
+  for (int64_t b = 0; b < p.n_t128; ++b) {
+    kv_steps += static_cast<double>(t_real - 4 * b);
+    q_steps += static_cast<double>(std::min<int64_t>(4 * b + 4, t_real));
+  }
+  p.kv = choose_split(t_real, kv_steps * hq);
+  p.q = choose_split(t_real, q_steps * hq);
   const size_t img = static_cast<size_t>(d) * (kRows * 2 + 16);
+  const size_t nkv = static_cast<size_t>(p.kv.nc), nq = static_cast<size_t>(p.q.nc);
   size_t o = 0;
   p.qimg = o;   o = align256(o + static_cast<size_t>(hq) * p.n_t32 * img);
   p.doimg = o;  o = align256(o + static_cast<size_t>(hq) * p.n_t32 * img);
   p.kimg = o;   o = align256(o + static_cast<size_t>(hkv) * p.n_t32 * img);
   p.ld = o;     o = align256(o + static_cast<size_t>(hq) * p.n_t32 * 64 * 4);
-  p.colsum = o; o = align256(o + static_cast<size_t>(hq) * p.mp * 4);
-  p.dkp = o;    o = align256(o + static_cast<size_t>(hq) * p.mp * d * 4);
-  p.dvp = o;    o = align256(o + static_cast<size_t>(hq) * p.mp * d * 4);
-  p.qdot = o;   o = align256(o + static_cast<size_t>(hq) * p.n_t128 * 4);
+  p.colsum = o; o = align256(o + nkv * hq * p.mp * 4);
+  p.dkp = o;    o = align256(o + nkv * hq * p.mp * d * 4);
+  p.dvp = o;    o = align256(o + nkv * hq * p.mp * d * 4);
+  p.dgp = o;    o = align256(o + nkv * hq * p.n_t128 * 4);
+  p.qdot = o;   o = align256(o + nq * hq * p.n_t128 * 4);
+  p.dqp = o;    o = align256(o + (nq > 1 ? nq * p.mp * hq * d * 4 : 0));
   p.total = o;
   return p;
+}
+
+// Chunks of key block kt's dK/dV walk and of query block qt's dQ walk.
+__host__ __device__ __forceinline__ int kv_chunks(int kt, int t_real, int len) {
+  return (t_real - 4 * kt + len - 1) / len;
+}
+__host__ __device__ __forceinline__ int q_walk(int qt, int M) {
+  return (min(qt * kWgRows + kWgRows, M) - 1) / kRows + 1;
 }
 
 // Work-group b -> (head, v): heads of one KV group on one XCD (work-groups
@@ -209,9 +254,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
-    int n_t32, int mp, const char* __restrict__ qimg, const char* __restrict__ doimg,
-    const float* __restrict__ ld, float* __restrict__ colsum, float* __restrict__ dkp,
-    float* __restrict__ dvp) {
+    int n_t32, int mp, int clen, int nc, const char* __restrict__ qimg,
+    const char* __restrict__ doimg, const float* __restrict__ ld, float* __restrict__ colsum,
+    float* __restrict__ dkp, float* __restrict__ dvp, float* __restrict__ dgp) {
   using T = Bwd<D>;
   constexpr int KS = T::KS, DT = T::DT;
   constexpr int NW = kThreads / 64;
@@ -224,9 +269,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   __shared__ __align__(16) char lds_qi[2][T::IMG];
   __shared__ __align__(16) char lds_di[2][T::IMG];
   __shared__ __align__(16) float lds_ld[2][64];
+  __shared__ float lds_red[kThreads / 64];
 
-  int head, kt;
-  head_unit(blockIdx.x, Hq, head, kt);            // kt ascending: longest walks first
+  int head, unit;
+  head_unit(blockIdx.x, Hq, head, unit);
+  const int kt = unit / nc, ch = unit % nc;       // kt ascending: longest walks first
+  const int t_end = (M + kRows - 1) / kRows;
+  const int t_begin = kt * (kWgRows / kRows) + ch * clen;   // this chunk's query steps
+  if (t_begin >= t_end) return;                   // past the walk: no chunk here
+  const int t_stop = min(t_begin + clen, t_end);
+  const int n_kt = (M + kWgRows - 1) / kWgRows;
   const int kvh = head / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -358,23 +410,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     }
   };
 
-  // ---- main loop over query tiles t0 .. n_real - 1, one barrier per step
-  const int t0 = kt * (kWgRows / kRows);
-  const int t_end = (M + kRows - 1) / kRows;
-  const int t_vis = t0 + wave;                    // first tile this wave sees (its diagonal)
-  dma(0, t0);
-  for (int t = t0; t < t_end; ++t) {
-    const int buf = (t - t0) & 1;
+  // ---- main loop over this chunk's query tiles, one barrier per step
+  const int t_vis = kt * (kWgRows / kRows) + wave;   // this wave's diagonal tile
+  dma(0, t_begin);
+  for (int t = t_begin; t < t_stop; ++t) {
+    const int buf = (t - t_begin) & 1;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA has landed
     __syncthreads();                 // ... and every other wave's; the other slot is free
-    if (t + 1 < t_end) dma(buf ^ 1, t + 1);
+    if (t + 1 < t_stop) dma(buf ^ 1, t + 1);
     if (t == t_vis) step(std::true_type{}, buf, t);
     else if (t > t_vis) step(std::false_type{}, buf, t);
   }
 
-  // ---- epilogue: fp32 partials of this head (rows = keys, columns = d)
-  float* dkh = dkp + static_cast<size_t>(head) * mp * D;
-  float* dvh = dvp + static_cast<size_t>(head) * mp * D;
+  // ---- epilogue: fp32 partials of this head and chunk (rows = keys, columns = d)
+  const size_t slot = static_cast<size_t>(ch) * Hq + head;
+  float* dkh = dkp + slot * mp * D;
+  float* dvh = dvp + slot * mp * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -385,7 +436,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     }
   }
   csum = add_halves(csum);
-  if (hh == 0) colsum[static_cast<size_t>(head) * mp + my_key] = csum;
+  if (hh == 0) colsum[slot * mp + my_key] = csum;
+  // this chunk's share of the gain gradient: sum over the 128 keys of s_j colsum_j
+  float gs = (hh == 0 && my_key < M) ? csum * key_score[my_key] : 0.f;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) gs += __shfl_xor(gs, o);
+  if (lane == 0) lds_red[wave] = gs;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < NW; ++w) t += lds_red[w];
+    dgp[slot * n_kt + kt] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -396,8 +458,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
-    int n_t32, int n_t128, const char* __restrict__ kimg, const float* __restrict__ ld,
-    bf16* __restrict__ dq, float* __restrict__ qdot) {
+    int n_t32, int n_t128, int mp, int clen, int nc, const char* __restrict__ kimg,
+    const float* __restrict__ ld, bf16* __restrict__ dq, float* __restrict__ dqp,
+    float* __restrict__ qdot) {
   using T = Bwd<D>;
   constexpr int KS = T::KS, DT = T::DT;
   constexpr int NW = kThreads / 64;
@@ -411,9 +474,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   __shared__ __align__(16) float lds_s[2][32];
   __shared__ float lds_red[kThreads / 64];
 
-  int head, v_;
-  head_unit(blockIdx.x, Hq, head, v_);
-  const int qt = n_t128 - 1 - v_;                // longest walks first
+  int head, unit;
+  head_unit(blockIdx.x, Hq, head, unit);
+  const int qt = n_t128 - 1 - unit / nc, ch = unit % nc;   // longest walks first
+  const int u_end = q_walk(qt, M);
+  const int u_begin = ch * clen;                 // this chunk's key steps
+  if (u_begin >= u_end) return;                  // past the walk: no chunk here
+  const int u_stop = min(u_begin + clen, u_end);
   const int kvh = head / (Hq / Hkv);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
@@ -522,26 +589,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     }
   };
 
-  // ---- key tiles 0 .. u_end - 1; this wave's diagonal tile is q0 / 32
-  const int q_last = min(qt * kWgRows + kWgRows, M) - 1;
-  const int u_end = q_last / kRows + 1;
+  // ---- this chunk's key tiles; this wave's diagonal tile is q0 / 32
   const int u_diag = q0 / kRows;
-  dma(0, 0);
-  for (int u = 0; u < u_end; ++u) {
-    const int buf = u & 1;
+  dma(0, u_begin);
+  for (int u = u_begin; u < u_stop; ++u) {
+    const int buf = (u - u_begin) & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (u + 1 < u_end) dma(buf ^ 1, u + 1);
+    if (u + 1 < u_stop) dma(buf ^ 1, u + 1);
     if (u == u_diag) step(std::true_type{}, buf, u);
     else if (u < u_diag) step(std::false_type{}, buf, u);
   }
 
   // ---- epilogue: dq = c_h (K^T dS^T)^T; lane = query, registers = dims
-  // 32 dt + 8 (j/4) + 4 hh + j%4.  Also q.dq for the temperature gradient.
+  // 32 dt + 8 (j/4) + 4 hh + j%4: bf16 dq, or this chunk's fp32 partial when
+  // the walk is split.  Also q.dq for the temperature gradient.
   float qd = 0.f;
   if (my_q < M) {
-    bf16* orow = dq + static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
-    const bf16* qrow = q + static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
+    const size_t row = static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
+    bf16* orow = dq + row;
+    float* prow = dqp + static_cast<size_t>(ch) * mp * Hq * D + row;
+    const bf16* qrow = q + row;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -550,14 +618,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         const uint2 qv = *reinterpret_cast<const uint2*>(qrow + d0);
         const float qx[4] = {__uint_as_float(qv.x << 16), __uint_as_float(qv.x & 0xFFFF0000u),
                              __uint_as_float(qv.y << 16), __uint_as_float(qv.y & 0xFFFF0000u)};
-        bf16 o4[4];
+        float g[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float g = acc[dt][4 * jj + r] * c_h;
-          qd = fmaf(qx[r], g, qd);
-          o4[r] = static_cast<bf16>(g);
+          g[r] = acc[dt][4 * jj + r] * c_h;
+          qd = fmaf(qx[r], g[r], qd);
         }
-        *reinterpret_cast<uint2*>(orow + d0) = __builtin_bit_cast(uint2, o4);
+        if (nc == 1) {
+          const bf16 o4[4] = {static_cast<bf16>(g[0]), static_cast<bf16>(g[1]),
+                              static_cast<bf16>(g[2]), static_cast<bf16>(g[3])};
+          *reinterpret_cast<uint2*>(orow + d0) = __builtin_bit_cast(uint2, o4);
+        } else {
+          *reinterpret_cast<float4*>(prow + d0) = make_float4(g[0], g[1], g[2], g[3]);
+        }
       }
     }
   }
@@ -570,19 +643,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   if (tid == 0) {
     float s = 0.f;
     for (int w = 0; w < NW; ++w) s += lds_red[w];
-    qdot[static_cast<size_t>(head) * n_t128 + qt] = s;
+    qdot[(static_cast<size_t>(ch) * Hq + head) * n_t128 + qt] = s;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Reductions (fixed order)
 // ---------------------------------------------------------------------------
+// dk, dv [key][kvh][d] = sum over the group's heads, then over the key block's
+// chunks, of the fp32 partials (bf16 out); the threads of (key, KV head 0,
+// dims 0..3) also form the score gradient ds_j = sum_h g_h sum_c colsum_chj.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const float* __restrict__ dkp,
-                                                              const float* __restrict__ dvp, int M,
-                                                              int Hq, int Hkv, int mp,
-                                                              bf16* __restrict__ dk,
-                                                              bf16* __restrict__ dv) {
+__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(
+    const float* __restrict__ dkp, const float* __restrict__ dvp,
+    const float* __restrict__ colsum, const float* __restrict__ gain, int M, int Hq, int Hkv,
+    int mp, int clen, int nc, bf16* __restrict__ dk, bf16* __restrict__ dv,
+    float* __restrict__ dscore) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // one 4-dim group
   const int64_t per_row = static_cast<int64_t>(Hkv) * (D / 4);
   if (e >= static_cast<int64_t>(M) * per_row) return;
@@ -590,56 +666,75 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const float* __res
   const int kvh = static_cast<int>((e % per_row) / (D / 4));
   const int d4 = static_cast<int>(e % (D / 4));
   const int G = Hq / Hkv;
+  const int t_real = (M + kRows - 1) / kRows;
+  const int nch = min(nc, kv_chunks(static_cast<int>(key / kWgRows), t_real, clen));
   float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
   for (int g = 0; g < G; ++g) {
-    const size_t src = (static_cast<size_t>(kvh * G + g) * mp + key) * D + 4 * d4;
-    const float4 x = *reinterpret_cast<const float4*>(dkp + src);
-    const float4 y = *reinterpret_cast<const float4*>(dvp + src);
-    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
-    b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    for (int c = 0; c < nch; ++c) {
+      const size_t src = ((static_cast<size_t>(c) * Hq + kvh * G + g) * mp + key) * D + 4 * d4;
+      const float4 x = *reinterpret_cast<const float4*>(dkp + src);
+      const float4 y = *reinterpret_cast<const float4*>(dvp + src);
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    }
   }
   const size_t dst = (static_cast<size_t>(key) * Hkv + kvh) * D + 4 * d4;
   const bf16 ka[4] = {static_cast<bf16>(a.x), static_cast<bf16>(a.y), static_cast<bf16>(a.z), static_cast<bf16>(a.w)};
   const bf16 va[4] = {static_cast<bf16>(b.x), static_cast<bf16>(b.y), static_cast<bf16>(b.z), static_cast<bf16>(b.w)};
   *reinterpret_cast<uint2*>(dk + dst) = __builtin_bit_cast(uint2, ka);
   *reinterpret_cast<uint2*>(dv + dst) = __builtin_bit_cast(uint2, va);
+  if (kvh == 0 && d4 == 0) {
+    float sc = 0.f;
+    for (int h = 0; h < Hq; ++h) {
+      float cs = 0.f;
+      for (int c = 0; c < nch; ++c) cs += colsum[(static_cast<size_t>(c) * Hq + h) * mp + key];
+      sc = fmaf(gain[h], cs, sc);
+    }
+    dscore[key] = sc;
+  }
 }
 
-__global__ __launch_bounds__(kThreads) void bwd_score_kernel(const float* __restrict__ colsum,
-                                                             const float* __restrict__ gain, int M,
-                                                             int Hq, int mp,
-                                                             float* __restrict__ dscore) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (j >= M) return;
-  float s = 0.f;
-  for (int h = 0; h < Hq; ++h) s = fmaf(gain[h], colsum[static_cast<size_t>(h) * mp + j], s);
-  dscore[j] = s;
+// dq [row][h][d] = sum over the query block's chunks of the fp32 partials
+// (only launched when the dQ walks are split).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_reduce_kernel(const float* __restrict__ dqp,
+                                                                 int M, int Hq, int mp, int clen,
+                                                                 int nc, bf16* __restrict__ dq) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t per_row = static_cast<int64_t>(Hq) * (D / 4);
+  if (e >= static_cast<int64_t>(M) * per_row) return;
+  const int64_t row = e / per_row;
+  const int nch = min(nc, (q_walk(static_cast<int>(row / kWgRows), M) + clen - 1) / clen);
+  float4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nch; ++c) {
+    const float4 x = *reinterpret_cast<const float4*>(dqp + static_cast<size_t>(c) * mp * Hq * D + 4 * e);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+  }
+  const bf16 o[4] = {static_cast<bf16>(a.x), static_cast<bf16>(a.y), static_cast<bf16>(a.z), static_cast<bf16>(a.w)};
+  *reinterpret_cast<uint2*>(dq + 4 * e) = __builtin_bit_cast(uint2, o);
 }
 
-__global__ __launch_bounds__(kThreads) void bwd_head_kernel(const float* __restrict__ colsum,
-                                                            const float* __restrict__ key_score,
-                                                            const float* __restrict__ qdot,
-                                                            const float* __restrict__ tau, int M,
-                                                            int mp, int n_t128,
-                                                            float* __restrict__ dgain,
-                                                            float* __restrict__ dtau) {
-  __shared__ float red[kThreads];
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const float* cs = colsum + static_cast<size_t>(h) * mp;
-  float s = 0.f;
-  for (int j = tid; j < M; j += kThreads) s = fmaf(key_score[j], cs[j], s);
-  red[tid] = s;
-  __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
+// One thread per head: dg_h = sum over key blocks and their chunks of the
+// work-groups' sum_j s_j colsum_j; dtau_h = -(1 / tau_h) sum of q.dq over query
+// blocks and chunks (fixed order).
+__global__ __launch_bounds__(64) void bwd_head_kernel(const float* __restrict__ dgp,
+                                                      const float* __restrict__ qdot,
+                                                      const float* __restrict__ tau, int M, int Hq,
+                                                      int n_t128, int kv_len, int kv_nc, int q_len,
+                                                      int q_nc, float* __restrict__ dgain,
+                                                      float* __restrict__ dtau) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= Hq) return;
+  const int t_real = (M + kRows - 1) / kRows;
+  float g = 0.f, t = 0.f;
+  for (int b = 0; b < n_t128; ++b) {
+    const int nkv = min(kv_nc, kv_chunks(b, t_real, kv_len));
+    for (int c = 0; c < nkv; ++c) g += dgp[(static_cast<size_t>(c) * Hq + h) * n_t128 + b];
+    const int nq = min(q_nc, (q_walk(b, M) + q_len - 1) / q_len);
+    for (int c = 0; c < nq; ++c) t += qdot[(static_cast<size_t>(c) * Hq + h) * n_t128 + b];
   }
-  if (tid == 0) {
-    dgain[h] = red[0];
-    float t = 0.f;
-    for (int i = 0; i < n_t128; ++i) t += qdot[static_cast<size_t>(h) * n_t128 + i];
-    dtau[h] = -t / tau[h];
-  }
+  dgain[h] = g;
+  dtau[h] = -t / tau[h];
 }
 
 template <int D>
@@ -660,25 +755,32 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   float* colsum = reinterpret_cast<float*>(ws + p.colsum);
   float* dkp = reinterpret_cast<float*>(ws + p.dkp);
   float* dvp = reinterpret_cast<float*>(ws + p.dvp);
+  float* dgp = reinterpret_cast<float*>(ws + p.dgp);
   float* qdot = reinterpret_cast<float*>(ws + p.qdot);
+  float* dqp = reinterpret_cast<float*>(ws + p.dqp);
   hipLaunchKernelGGL((bwd_pack_kernel<D>), dim3(static_cast<unsigned>((Hq + Hkv) * n_t32)),
                      dim3(kThreads), 0, stream, bq, bk, reinterpret_cast<const bf16*>(out), lse, bd,
                      M, Hq, Hkv, n_t32, ws + p.qimg, ws + p.doimg, ws + p.kimg, ld);
-  const int n_kt = (M + kWgRows - 1) / kWgRows;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(Hq * n_kt)), dim3(kThreads),
-                     0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, mp, ws + p.qimg,
-                     ws + p.doimg, ld, colsum, dkp, dvp);
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128)), dim3(kThreads),
-                     0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, n_t128, ws + p.kimg, ld,
-                     reinterpret_cast<bf16*>(dq), qdot);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.kv.nc)),
+                     dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, mp,
+                     p.kv.len, p.kv.nc, ws + p.qimg, ws + p.doimg, ld, colsum, dkp, dvp, dgp);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.q.nc)),
+                     dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, n_t128,
+                     mp, p.q.len, p.q.nc, ws + p.kimg, ld, reinterpret_cast<bf16*>(dq), dqp, qdot);
   const int64_t groups = static_cast<int64_t>(M) * Hkv * (D / 4);
   hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3(static_cast<unsigned>((groups + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, dkp, dvp, M, Hq, Hkv, mp,
-                     reinterpret_cast<bf16*>(dk), reinterpret_cast<bf16*>(dv));
-  hipLaunchKernelGGL(bwd_score_kernel, dim3(static_cast<unsigned>((M + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, colsum, g, M, Hq, mp, dscore);
-  hipLaunchKernelGGL(bwd_head_kernel, dim3(static_cast<unsigned>(Hq)), dim3(kThreads), 0, stream,
-                     colsum, s, qdot, t, M, mp, n_t128, dgain, dtau);
+                     dim3(kThreads), 0, stream, dkp, dvp, colsum, g, M, Hq, Hkv, mp, p.kv.len,
+                     p.kv.nc, reinterpret_cast<bf16*>(dk), reinterpret_cast<bf16*>(dv), dscore);
+  if (p.q.nc > 1) {
+    const int64_t qgroups = static_cast<int64_t>(M) * Hq * (D / 4);
+    hipLaunchKernelGGL((bwd_dq_reduce_kernel<D>),
+                       dim3(static_cast<unsigned>((qgroups + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, dqp, M, Hq, mp, p.q.len, p.q.nc,
+                       reinterpret_cast<bf16*>(dq));
+  }
+  hipLaunchKernelGGL(bwd_head_kernel, dim3(static_cast<unsigned>((Hq + 63) / 64)), dim3(64), 0,
+                     stream, dgp, qdot, t, M, Hq, n_t128, p.kv.len, p.kv.nc, p.q.len, p.q.nc,
+                     dgain, dtau);
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@ reaches a kernel launch.
 """
 
 import ctypes
+import math
 import os
 import re
 import subprocess
@@ -261,25 +262,46 @@ def test_qk_norm_rope_validation(L):
     assert f(None, 0, None, None, 0, 4, 128, None, 1e-6, 1e6, None, 0) == OK    # n == 0
 
 
+def _bwd_split(longest, total):
+    """Walks longer than 1.3x the average steps per resident work-group (512)
+    are cut into chunks of that length (at least 8 steps)."""
+    avg = total / 512.0
+    ln = longest
+    if longest > 1.3 * avg:
+        ln = max(8, math.ceil(1.3 * avg))
+    ln = max(1, min(ln, longest))
+    return ln, -(-longest // ln)
+
+
 def _bwd_ws(n, hq, hkv, d):
     """The backward workspace restated: rows padded to whole 128-row blocks;
     q^T, dout^T (per query head) and k^T (per KV head) images of 32-row tiles,
     d rows of 80 bytes each; (lse, D) as 64 floats per query head and tile;
-    per query head and padded row one column-sum float and d fp32 each of the
-    dk and dv partials; one float per query head and 128-row block; every
-    region rounded up to 256 bytes."""
+    per dK/dV chunk, query head and padded row one column-sum float and d fp32
+    each of the dk and dv partials; per dK/dV chunk, query head and 128-row
+    block one float (gain partial); per dQ chunk the same for q.dq; fp32 dq
+    partials when the dQ walks are split; every region rounded up to 256 bytes."""
     t128 = -(-n // 128)
     t32, mp = 4 * t128, 128 * t128
+    t_real = -(-n // 32)
+    _, nkv = _bwd_split(t_real, hq * sum(t_real - 4 * b for b in range(t128)))
+    _, nq = _bwd_split(t_real, hq * sum(min(4 * b + 4, t_real) for b in range(t128)))
     img = d * 80
     o = 0
-    for size in (hq * t32 * img, hq * t32 * img, hkv * t32 * img, hq * t32 * 256, hq * mp * 4,
-                 hq * mp * d * 4, hq * mp * d * 4, hq * t128 * 4):
+    for size in (hq * t32 * img, hq * t32 * img, hkv * t32 * img, hq * t32 * 256,
+                 nkv * hq * mp * 4, nkv * hq * mp * d * 4, nkv * hq * mp * d * 4,
+                 nkv * hq * t128 * 4, nq * hq * t128 * 4, nq * mp * hq * d * 4 if nq > 1 else 0):
         o = -(-(o + size) // 256) * 256
     return o
 
 
-@pytest.mark.parametrize("n,hq,hkv,d", [(1, 16, 8, 128), (2304, 16, 8, 128), (8448, 16, 8, 128),
-                                        (300, 8, 1, 64), (129, 4, 2, 64)])
+def test_attn_bwd_split_rule():
+    assert _bwd_split(264, 16 * 8844) == (264, 1)       # 8448 rows: balanced, no split
+    assert _bwd_split(72, 16 * 684) == (28, 3)          # 2304 rows: three chunks
+
+
+@pytest.mark.parametrize("n,hq,hkv,d", [(1, 16, 8, 128), (2304, 16, 8, 128), (4352, 16, 8, 128),
+                                        (8448, 16, 8, 128), (300, 8, 1, 64), (129, 4, 2, 64)])
 def test_attn_bwd_workspace_bytes(L, n, hq, hkv, d):
     assert L.tg_attn_bwd_workspace_bytes(n, hq, hkv, d) == _bwd_ws(n, hq, hkv, d)
 
