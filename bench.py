@@ -35,8 +35,12 @@ def _parse():
     p.add_argument("--no-full-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--step-only", action="store_true",
+                   help="time only the gated-prefill step (and the full-N baseline unless "
+                        "--no-full-baseline); skip the decode, q/k prologue and backward stages "
+                        "(for counter runs)")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="also run a plain 64 MiB copy (tg_compact with identity indices) so a "
+                   help="also run a cold 256 MiB copy (tg_compact with identity indices) so a "
                         "PMC run can scale FETCH_SIZE / WRITE_SIZE")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
@@ -252,115 +256,118 @@ def main():
     torch.cuda.synchronize()
     plain_ms_launch = pa.elapsed_time(pb) / max(1, min(args.steps, 5)) / w.n_layers
 
-    # ---------------------------------------------------------------- first decode step
-    # One new token per layer against the pruned cache: the gate layer over all
-    # N rows (plain), the 27 layers above it over the M kept rows (gated).  The
-    # new query is the last kept row's (its own row is then the cache's last).
-    dws = tg.decode_workspace(w.n, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
-    dout = torch.empty((w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-    q_new = [kept_qkv[t][0][-1].contiguous() for t in range(n_t)]
+    # The stages below are measured beside the step (not part of it).
+    decode = prologue_stats = bwd_stats = None
+    if not args.step_only:
+        # ---------------------------------------------------------------- first decode step
+        # One new token per layer against the pruned cache: the gate layer over all
+        # N rows (plain), the 27 layers above it over the M kept rows (gated).  The
+        # new query is the last kept row's (its own row is then the cache's last).
+        dws = tg.decode_workspace(w.n, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
+        dout = torch.empty((w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        q_new = [kept_qkv[t][0][-1].contiguous() for t in range(n_t)]
 
-    def decode_upper():
-        for l in range(w.n_layers):
-            t = inputs.template_of_layer(w, l)
-            tg.gated_decode(q_new[t], kept_qkv[t][1], kept_qkv[t][2], s_kept, gain_d[l], tau_d[l],
-                            out=dout, workspace=dws)
+        def decode_upper():
+            for l in range(w.n_layers):
+                t = inputs.template_of_layer(w, l)
+                tg.gated_decode(q_new[t], kept_qkv[t][1], kept_qkv[t][2], s_kept, gain_d[l], tau_d[l],
+                                out=dout, workspace=dws)
 
-    q_gate = full_qkv[0][0][-1].contiguous()
+        q_gate = full_qkv[0][0][-1].contiguous()
 
-    def decode_gate_layer():   # ten calls per replay: one alone would time the graph launch
-        for _ in range(10):
-            tg.gated_decode(q_gate, full_qkv[0][1], full_qkv[0][2], out=dout, workspace=dws)
+        def decode_gate_layer():   # ten calls per replay: one alone would time the graph launch
+            for _ in range(10):
+                tg.gated_decode(q_gate, full_qkv[0][1], full_qkv[0][2], out=dout, workspace=dws)
 
-    def graphed(fn):
-        # A decode loop is launch-bound from Python (two small launches per
-        # layer); it is timed as a captured HIP graph, as a serving loop runs it.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
+        def graphed(fn):
+            # A decode loop is launch-bound from Python (two small launches per
+            # layer); it is timed as a captured HIP graph, as a serving loop runs it.
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            return graph
+
+        def time_calls(fn, reps):
             fn()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            fn()
-        return graph
+            ea = torch.cuda.Event(enable_timing=True)
+            eb = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ea.record(stream)
+            for _ in range(reps):
+                fn()
+            eb.record(stream)
+            torch.cuda.synchronize()
+            return ea.elapsed_time(eb) / reps
 
-    def time_calls(fn, reps):
-        fn()
-        ea = torch.cuda.Event(enable_timing=True)
-        eb = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ea.record(stream)
-        for _ in range(reps):
-            fn()
-        eb.record(stream)
-        torch.cuda.synchronize()
-        return ea.elapsed_time(eb) / reps
+        g_upper, g_gate = graphed(decode_upper), graphed(decode_gate_layer)
+        dec_upper_ms = time_calls(g_upper.replay, 20) / w.n_layers
+        dec_full_ms = time_calls(g_gate.replay, 20) / 10
+        del g_upper, g_gate
+        cache_row = 2.0 * w.n_kv_heads * w.head_dim * 2          # K and V bytes per cached row
+        dec_upper_gbs = m * cache_row / (dec_upper_ms / 1e3) / 1e9
+        dec_full_gbs = w.n * cache_row / (dec_full_ms / 1e3) / 1e9
+        decode = {
+            "upper_layer_ms": round(dec_upper_ms, 5), "upper_layer_cache_rows": m,
+            "upper_layer_gb_s": round(dec_upper_gbs, 1),
+            "upper_layer_frac_hbm_peak": round(dec_upper_gbs / PEAK_HBM_GBS, 4),
+            "gate_layer_ms": round(dec_full_ms, 5), "gate_layer_cache_rows": w.n,
+            "gate_layer_gb_s": round(dec_full_gbs, 1),
+            "gate_layer_frac_hbm_peak": round(dec_full_gbs / PEAK_HBM_GBS, 4),
+            # one decode step through the 28 attention layers: pruned cache vs all N rows
+            "step_speedup_vs_unpruned_cache": round((w.n_layers + 1) * dec_full_ms /
+                                                    (dec_full_ms + w.n_layers * dec_upper_ms), 2),
+        }
+        del dws
 
-    g_upper, g_gate = graphed(decode_upper), graphed(decode_gate_layer)
-    dec_upper_ms = time_calls(g_upper.replay, 20) / w.n_layers
-    dec_full_ms = time_calls(g_gate.replay, 20) / 10
-    del g_upper, g_gate
-    cache_row = 2.0 * w.n_kv_heads * w.head_dim * 2          # K and V bytes per cached row
-    dec_upper_gbs = m * cache_row / (dec_upper_ms / 1e3) / 1e9
-    dec_full_gbs = w.n * cache_row / (dec_full_ms / 1e3) / 1e9
-    decode = {
-        "upper_layer_ms": round(dec_upper_ms, 5), "upper_layer_cache_rows": m,
-        "upper_layer_gb_s": round(dec_upper_gbs, 1),
-        "upper_layer_frac_hbm_peak": round(dec_upper_gbs / PEAK_HBM_GBS, 4),
-        "gate_layer_ms": round(dec_full_ms, 5), "gate_layer_cache_rows": w.n,
-        "gate_layer_gb_s": round(dec_full_gbs, 1),
-        "gate_layer_frac_hbm_peak": round(dec_full_gbs / PEAK_HBM_GBS, 4),
-        # one decode step through the 28 attention layers: pruned cache vs all N rows
-        "step_speedup_vs_unpruned_cache": round((w.n_layers + 1) * dec_full_ms /
-                                                (dec_full_ms + w.n_layers * dec_upper_ms), 2),
-    }
-    del dws
+        # ---------------------------------------------------------------- upper-layer q/k prologue
+        # Gather + per-head RMS norm + RoPE at the original positions for one upper
+        # layer's q and k (from full-N rows; the templates stand for pre-RoPE rows).
+        qn_w = torch.ones(w.head_dim, dtype=torch.float32, device=dev)
+        q_pro = torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        k_pro = torch.empty((m, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
 
-    # ---------------------------------------------------------------- upper-layer q/k prologue
-    # Gather + per-head RMS norm + RoPE at the original positions for one upper
-    # layer's q and k (from full-N rows; the templates stand for pre-RoPE rows).
-    qn_w = torch.ones(w.head_dim, dtype=torch.float32, device=dev)
-    q_pro = torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-    k_pro = torch.empty((m, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        def prologue():
+            tg.qk_norm_rope(full_qkv[0][0], idx, rows=idx, norm_weight=qn_w, out=q_pro)
+            tg.qk_norm_rope(full_qkv[0][1], idx, rows=idx, norm_weight=qn_w, out=k_pro)
 
-    def prologue():
-        tg.qk_norm_rope(full_qkv[0][0], idx, rows=idx, norm_weight=qn_w, out=q_pro)
-        tg.qk_norm_rope(full_qkv[0][1], idx, rows=idx, norm_weight=qn_w, out=k_pro)
+        g_pro = graphed(lambda: [prologue() for _ in range(10)])
+        pro_ms = time_calls(g_pro.replay, 20) / 10
+        del g_pro
+        pro_bytes = 2.0 * m * (w.n_q_heads + w.n_kv_heads) * w.head_dim * 2
+        prologue_stats = {"ms_per_layer": round(pro_ms, 5),
+                          "gb_s": round(pro_bytes / (pro_ms / 1e3) / 1e9, 1),
+                          "frac_hbm_peak": round(pro_bytes / (pro_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
 
-    g_pro = graphed(lambda: [prologue() for _ in range(10)])
-    pro_ms = time_calls(g_pro.replay, 20) / 10
-    del g_pro
-    pro_bytes = 2.0 * m * (w.n_q_heads + w.n_kv_heads) * w.head_dim * 2
-    prologue_stats = {"ms_per_layer": round(pro_ms, 5),
-                      "gb_s": round(pro_bytes / (pro_ms / 1e3) / 1e9, 1),
-                      "frac_hbm_peak": round(pro_bytes / (pro_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}
-
-    # ---------------------------------------------------------------- upper-layer backward
-    # One gated layer's backward over the kept rows (the gradients through
-    # which a training loss reaches the gate: its scores, gains and
-    # temperatures), given that layer's forward output and lse and a seeded
-    # random upstream gradient.  Algorithmic work: the four products dV, dP,
-    # dK, dQ over the causal pairs; the deterministic kernels execute seven
-    # (S and dP are formed again for dQ).
-    q0, k0, v0 = kept_qkv[0]
-    fo, flse = tg.gated_attn_fwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], want_lse=True,
-                                 workspace=ws)
-    gen = torch.Generator(device=dev).manual_seed(2024)
-    dout_b = (torch.randn(fo.shape, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
-    bws = tg.attn_bwd_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
-    grads = tg.gated_attn_bwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], fo, flse, dout_b,
-                              workspace=bws)
-    bwd_ms = time_calls(lambda: tg.gated_attn_bwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], fo,
-                                                  flse, dout_b, grads=grads, workspace=bws),
-                        max(3, min(args.steps, 10)))
-    bwd_flop = 4.0 * w.n_q_heads * w.head_dim * m * (m + 1)
-    bwd_tf = bwd_flop / (bwd_ms / 1e3) / 1e12
-    bwd_stats = {"ms_per_layer": round(bwd_ms, 5), "tflops": round(bwd_tf, 1),
-                 "frac_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                 "tflops_executed": round(bwd_tf * 7 / 4, 1),
-                 "bwd_over_fwd": round(bwd_ms / attn_ms_launch, 2)}
-    del bws, grads, fo, flse, dout_b
+        # ---------------------------------------------------------------- upper-layer backward
+        # One gated layer's backward over the kept rows (the gradients through
+        # which a training loss reaches the gate: its scores, gains and
+        # temperatures), given that layer's forward output and lse and a seeded
+        # random upstream gradient.  Algorithmic work: the four products dV, dP,
+        # dK, dQ over the causal pairs; the deterministic kernels execute seven
+        # (S and dP are formed again for dQ).
+        q0, k0, v0 = kept_qkv[0]
+        fo, flse = tg.gated_attn_fwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], want_lse=True,
+                                     workspace=ws)
+        gen = torch.Generator(device=dev).manual_seed(2024)
+        dout_b = (torch.randn(fo.shape, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+        bws = tg.attn_bwd_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
+        grads = tg.gated_attn_bwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], fo, flse, dout_b,
+                                  workspace=bws)
+        bwd_ms = time_calls(lambda: tg.gated_attn_bwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], fo,
+                                                      flse, dout_b, grads=grads, workspace=bws),
+                            max(3, min(args.steps, 10)))
+        bwd_flop = 4.0 * w.n_q_heads * w.head_dim * m * (m + 1)
+        bwd_tf = bwd_flop / (bwd_ms / 1e3) / 1e12
+        bwd_stats = {"ms_per_layer": round(bwd_ms, 5), "tflops": round(bwd_tf, 1),
+                     "frac_bf16_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                     "tflops_executed": round(bwd_tf * 7 / 4, 1),
+                     "bwd_over_fwd": round(bwd_ms / attn_ms_launch, 2)}
+        del bws, grads, fo, flse, dout_b
 
     # ---------------------------------------------------------------- full-N baseline
     full = None
