@@ -78,12 +78,23 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
         return rows
 
     def kib(rows, pred):
-        vals = [float(r["Counter_Value"]) for r in rows if pred(r["Kernel_Name"])]
+        vals = [float(r["Counter_Value"]) for r in rows if pred(r)]
         return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
-    is_attn = lambda n: "attn_fwd_kernel" in n and "ELb1E" in n
-    is_pack = lambda n: "v_pack_kernel<128, true>" in n or ("v_pack_kernel" in n and "ELb1E" in n)
-    is_merge = lambda n: "attn_merge_kernel" in n
+    def gated_merges(rows):
+        # The merge kernel serves the gated and the plain calls alike: keep the
+        # merges whose preceding attention dispatch is a gated one.
+        keep, last_gated = set(), False
+        for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+            n = r["Kernel_Name"]
+            if "attn_fwd_kernel" in n:
+                last_gated = "ELb1E" in n
+            elif "attn_merge_kernel" in n and last_gated:
+                keep.add(r["Dispatch_Id"])
+        return keep
+
+    is_attn = lambda r: "attn_fwd_kernel" in r["Kernel_Name"] and "ELb1E" in r["Kernel_Name"]
+    is_pack = lambda r: "v_pack_kernel" in r["Kernel_Name"] and "ELb1E" in r["Kernel_Name"]
     out = {"workload": workload, "kernel_source_sha256_16": attn_source_hash(), "command": command}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = load(d, counter)
@@ -91,9 +102,10 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
         copies = [float(r["Counter_Value"]) for r in rows if "compact_wide_kernel" in r["Kernel_Name"]]
         copy_kib = max(copies) if copies else None
         scale = COPY_BYTES / (copy_kib * 1024.0) if copy_kib else None
+        merges = gated_merges(rows)
         a, na = kib(rows, is_attn)
         pk, npk = kib(rows, is_pack)
-        mg, nmg = kib(rows, is_merge)
+        mg, nmg = kib(rows, lambda r: r["Dispatch_Id"] in merges)
         # merge dispatches per attention dispatch (0 when no query tile is split)
         mg_per = (nmg / na) if na else 0.0
         total = (a + pk + (mg or 0.0) * mg_per) if (a is not None and pk is not None) else None

@@ -714,27 +714,38 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_reduce_kernel(const float* __
   *reinterpret_cast<uint2*>(dq + 4 * e) = __builtin_bit_cast(uint2, o);
 }
 
-// One thread per head: dg_h = sum over key blocks and their chunks of the
-// work-groups' sum_j s_j colsum_j; dtau_h = -(1 / tau_h) sum of q.dq over query
-// blocks and chunks (fixed order).
-__global__ __launch_bounds__(64) void bwd_head_kernel(const float* __restrict__ dgp,
-                                                      const float* __restrict__ qdot,
-                                                      const float* __restrict__ tau, int M, int Hq,
-                                                      int n_t128, int kv_len, int kv_nc, int q_len,
-                                                      int q_nc, float* __restrict__ dgain,
-                                                      float* __restrict__ dtau) {
-  const int h = blockIdx.x * 64 + threadIdx.x;
-  if (h >= Hq) return;
+// One work-group per head: dg_h = sum over key blocks and their chunks of the
+// work-groups' sum_j s_j colsum_j; dtau_h = -(1 / tau_h) sum of q.dq over
+// query blocks and chunks.  Thread i takes blocks i, i + 256, ..., then a
+// fixed tree (deterministic).
+__global__ __launch_bounds__(kThreads) void bwd_head_kernel(
+    const float* __restrict__ dgp, const float* __restrict__ qdot, const float* __restrict__ tau,
+    int M, int Hq, int n_t128, int kv_len, int kv_nc, int q_len, int q_nc,
+    float* __restrict__ dgain, float* __restrict__ dtau) {
+  __shared__ float red_g[kThreads], red_t[kThreads];
+  const int h = blockIdx.x, tid = threadIdx.x;
   const int t_real = (M + kRows - 1) / kRows;
   float g = 0.f, t = 0.f;
-  for (int b = 0; b < n_t128; ++b) {
+  for (int b = tid; b < n_t128; b += kThreads) {
     const int nkv = min(kv_nc, kv_chunks(b, t_real, kv_len));
     for (int c = 0; c < nkv; ++c) g += dgp[(static_cast<size_t>(c) * Hq + h) * n_t128 + b];
     const int nq = min(q_nc, (q_walk(b, M) + q_len - 1) / q_len);
     for (int c = 0; c < nq; ++c) t += qdot[(static_cast<size_t>(c) * Hq + h) * n_t128 + b];
   }
-  dgain[h] = g;
-  dtau[h] = -t / tau[h];
+  red_g[tid] = g;
+  red_t[tid] = t;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      red_g[tid] += red_g[tid + w];
+      red_t[tid] += red_t[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    dgain[h] = red_g[0];
+    dtau[h] = -red_t[0] / tau[h];
+  }
 }
 
 template <int D>
@@ -778,9 +789,8 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
                        dim3(kThreads), 0, stream, dqp, M, Hq, mp, p.q.len, p.q.nc,
                        reinterpret_cast<bf16*>(dq));
   }
-  hipLaunchKernelGGL(bwd_head_kernel, dim3(static_cast<unsigned>((Hq + 63) / 64)), dim3(64), 0,
-                     stream, dgp, qdot, t, M, Hq, n_t128, p.kv.len, p.kv.nc, p.q.len, p.q.nc,
-                     dgain, dtau);
+  hipLaunchKernelGGL(bwd_head_kernel, dim3(static_cast<unsigned>(Hq)), dim3(kThreads), 0, stream,
+                     dgp, qdot, t, M, Hq, n_t128, p.kv.len, p.kv.nc, p.q.len, p.q.nc, dgain, dtau);
   return hipGetLastError();
 }
 
