@@ -147,11 +147,12 @@ __device__ __forceinline__ void head_unit(int b, int hq, int& head, int& v) {
   }
 }
 
-// Round-to-nearest-even bf16 pair (lo in the low half).
+// Round-to-nearest-even bf16 pair (lo in the low half): one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<bf16>(lo));
-  const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<bf16>(hi));
-  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+  const f32x2_v v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
 
 // Sum of x over lane l and lane l ^ 32.
