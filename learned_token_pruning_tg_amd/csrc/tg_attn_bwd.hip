@@ -15,15 +15,16 @@
 // Launches, all deterministic (every sum in a fixed order, no atomics):
 // 1. bwd_pack: per (query head, 32-row tile) the Q^T and dO^T tile images
 //    ([d][row], rows permuted inside 16-row groups so that each lane's eight
-//    rows of an MFMA k-step are one 16-byte run) and the rows' lse (log2
-//    units; +inf past n) and D; per (KV head, 32-key tile) the K^T image.
+//    rows of an MFMA k-step are one 16-byte run) and the rows' -lse / c_h
+//    (-inf past n) and -D; per (KV head, 32-key tile) the K^T image.
 // 2. bwd_dkdv: one work-group per (query head, 128 keys), a wave per 32 keys
 //    with their K and V fragments in registers, over 32-query steps from the
 //    diagonal on: S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16_bf16 (lane
 //    = key, registers = queries), P and dS in fp32, then dV += P^T dO and
 //    dK += dS^T Q with P and dS as bf16 A fragments straight from registers.
 //    Q and dO rows and their images arrive by buffer-to-LDS DMA into a
-//    double-buffered ring, one barrier per step.  Writes fp32 per-head dK/dV
+//    double-buffered ring, one barrier per step; the S and dP accumulators
+//    start from -lse / c_h and -D.  Writes fp32 per-head dK/dV
 //    partials and the per-head column sums sum_i dS_ij.
 // 3. bwd_dq: one work-group per (query head, 128 queries), a wave per 32
 //    queries with their Q and dO fragments in registers, over 32-key steps up
@@ -191,13 +192,13 @@ __device__ __forceinline__ void transpose_tile(__amdgpu_buffer_rsrc_t r, uint32_
 }
 
 // Blocks [0, Hq * n_t32): query head h, tile t -> Q^T, dO^T images and the
-// rows' (lse2, D); blocks after that: KV head, tile -> K^T image.
+// rows' (-lse / c_h, -D); blocks after that: KV head, tile -> K^T image.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pack_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ out,
-    const float* __restrict__ lse, const bf16* __restrict__ dout, int M, int Hq, int Hkv,
-    int n_t32, char* __restrict__ qimg, char* __restrict__ doimg, char* __restrict__ kimg,
-    float* __restrict__ ld) {
+    const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ tau,
+    int M, int Hq, int Hkv, int n_t32, char* __restrict__ qimg, char* __restrict__ doimg,
+    char* __restrict__ kimg, float* __restrict__ ld) {
   using T = Bwd<D>;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -240,10 +241,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pack_kernel(
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
   if (part == 0) {
+    // stored negated, lse in units of the head's q.k (lse / c_h): the dK/dV
+    // steps start their S and dP accumulators from these values
     const int64_t row = static_cast<int64_t>(row0) + qi;
+    const float inv_c = sqrtf(static_cast<float>(D)) * tau[h];
     float* dst = ld + tile * 64;
-    dst[qi] = row < M ? lse[static_cast<int64_t>(h) * M + row] * kLog2e : INFINITY;
-    dst[32 + qi] = acc;
+    dst[qi] = row < M ? -lse[static_cast<int64_t>(h) * M + row] * inv_c : -INFINITY;
+    dst[32 + qi] = -acc;
   }
 }
 
@@ -363,29 +367,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     constexpr bool DIAG = decltype(diag_c)::value;
     const char* qr = &lds_qr[buf][0];
     const char* dr = &lds_dr[buf][0];
-    floatx16 s = zero16(), dp = zero16();
+    // S and dP start from -lse_i / c_h and -D_i of their query rows (register
+    // j holds query 8 (j/4) + 4 hh + j%4), so S = q.k - lse / c_h and dP = dO.v - D
+    floatx16 s, dp;
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const float4 l2 = *reinterpret_cast<const float4*>(&lds_ld[buf][8 * jg + 4 * hh]);
+      const float4 dd = *reinterpret_cast<const float4*>(&lds_ld[buf][32 + 8 * jg + 4 * hh]);
+      s[4 * jg] = l2.x; s[4 * jg + 1] = l2.y; s[4 * jg + 2] = l2.z; s[4 * jg + 3] = l2.w;
+      dp[4 * jg] = dd.x; dp[4 * jg + 1] = dd.y; dp[4 * jg + 2] = dd.z; dp[4 * jg + 3] = dd.w;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t off = a_base ^ static_cast<uint32_t>(32 * ks);
       s = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(qr + off), kf[ks], s);
       dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(dr + off), vf[ks], dp);
     }
-    // P and dS for this lane's key and its 16 queries 8 (j/4) + 4 hh + j%4
+    // P and dS for this lane's key and its 16 queries
     uint32_t pk[8], dsk[8];
     const int qbase = t * kRows + 4 * hh;
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
-      const float4 l2 = *reinterpret_cast<const float4*>(&lds_ld[buf][8 * jg + 4 * hh]);
-      const float4 dd = *reinterpret_cast<const float4*>(&lds_ld[buf][32 + 8 * jg + 4 * hh]);
-      const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-      const float dv4[4] = {dd.x, dd.y, dd.z, dd.w};
       float pj[4], dsj[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * jg + i;
-        float p = fast_exp2(fmaf(s[j], alpha, bkey - lv[i]));
+        float p = fast_exp2(fmaf(s[j], alpha, bkey));
         if (DIAG && qbase + 8 * jg + i < my_key) p = 0.f;
-        const float ds = p * (dp[j] - dv4[i]);
+        const float ds = p * dp[j];
         csum += ds;
         pj[i] = p;
         dsj[i] = ds;
@@ -504,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const float alpha = kLog2e * c_h;
   const float gl = gain[head] * kLog2e;
   const float* ldt = ld + (static_cast<size_t>(head) * n_t32 + (q0 >> 5)) * 64;
-  const float lse2 = ldt[l32], dd = ldt[32 + l32];
+  const float nlse2 = ldt[l32] * alpha, ndd = ldt[32 + l32];   // -lse (log2 units), -D
 
   floatx16 acc[DT];
 #pragma unroll
@@ -570,9 +579,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * jg + i;
-        float p = fast_exp2(fmaf(st[j], alpha, fmaf(sk[i], gl, -lse2)));
+        float p = fast_exp2(fmaf(st[j], alpha, fmaf(sk[i], gl, nlse2)));
         if (DIAG && kbase + 8 * jg + i > my_q) p = 0.f;
-        dsj[i] = p * (dpt[j] - dd);
+        dsj[i] = p * (dpt[j] + ndd);
       }
       dsk[2 * jg] = pack_bf16(dsj[0], dsj[1]);
       dsk[2 * jg + 1] = pack_bf16(dsj[2], dsj[3]);
@@ -772,7 +781,7 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   float* dqp = reinterpret_cast<float*>(ws + p.dqp);
   hipLaunchKernelGGL((bwd_pack_kernel<D>), dim3(static_cast<unsigned>((Hq + Hkv) * n_t32)),
                      dim3(kThreads), 0, stream, bq, bk, reinterpret_cast<const bf16*>(out), lse, bd,
-                     M, Hq, Hkv, n_t32, ws + p.qimg, ws + p.doimg, ws + p.kimg, ld);
+                     t, M, Hq, Hkv, n_t32, ws + p.qimg, ws + p.doimg, ws + p.kimg, ld);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.kv.nc)),
                      dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, mp,
                      p.kv.len, p.kv.nc, ws + p.qimg, ws + p.doimg, ld, colsum, dkp, dvp, dgp);
