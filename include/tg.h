@@ -144,8 +144,8 @@ tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, i
  * rows (enough for either):
  *   - per KV head and 64-key tile, a packed copy of V (fp16, transposed,
  *     laid out as the kernel's LDS image: about 1.1x the bytes of V) and, per
- *     key, 32 bytes holding its score split into two bf16 parts (K itself is
- *     read in place);
+ *     query head and key, the fp32 bias gain * sqrt(head_dim) * tau * score
+ *     (K itself is read in place);
  *   - when n is short enough that long query blocks are split over several
  *     work-groups along the keys: one counter per split block and one
  *     partial state (fp16 output, fp32 max and sum; 34 KiB at head_dim 128)
@@ -175,7 +175,8 @@ size_t tg_attn_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads,
  *        workspace must be ordered on one stream.  Too small -> TG_E_WORKSPACE.
  * Supported: head_dim in {64, 128}, n_q_heads % n_kv_heads == 0,
  * n * n_q_heads * head_dim * 2 < 2^31 (byte offsets fit 31 bits).
- * Numerics: q.k as bf16 products with fp32 accumulation; softmax in fp32;
+ * Numerics: q.k as bf16 products with fp32 accumulation, starting from the
+ * fp32 bias gain * sqrt(head_dim) * tau * key_score; softmax in fp32;
  * probabilities and v rounded to fp16 for the p.v product (v magnitudes above
  * 65504 saturate), fp32 accumulation; where a query block is split along the
  * keys, each part's normalised output is rounded to fp16 before the merge.

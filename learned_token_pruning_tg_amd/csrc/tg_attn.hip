@@ -13,20 +13,22 @@
 // 1. v_pack: per KV head and 64-key tile, the V^T image the main kernel
 //    DMAs into LDS, in the caller's workspace: fp16 [d][key], key order
 //    permuted inside each 16-key group so that every lane's eight keys of a
-//    P.V step are one 16-byte run, rows padded; plus (gated) per key the bias
-//    k-step's A fragment (score split into bf16 s_hi, s_lo).  Keys past n are
-//    zero.  K is not copied: the main kernel DMAs K tiles straight from k.
+//    P.V step are one 16-byte run, rows padded; plus (gated) per query head
+//    and key the bias in units of q.k, c_h s_j with c_h = gain_h sqrt(d)
+//    tau_h, in fp32.  Keys past n are zero.  K is not copied: the main kernel
+//    DMAs K tiles straight from k.
 // 2. attn_fwd: one work-group = 128 query rows of one query head over a run
 //    of their key tiles; four waves of 32 rows; two work-groups per CU (they
 //    drift out of phase, so one's softmax and DMA waits overlap the other's
 //    MFMAs).
-//      * S^T = K~ Q~^T on v_mfma_f32_32x32x16_bf16 (A = K~ from LDS, B = Q~
-//        held in registers for the whole key loop).  K~ is k with one extra
-//        k-step carrying the bias: the key's (s_hi, s_lo, s_hi) against Q~'s
-//        c = gain * sqrt(d) * tau split as (c_hi, c_hi, c_lo), so
-//        S~ = q.k + c s_j and one multiply by alpha = log2(e) / (sqrt(d) tau)
-//        gives the logit in log2 units.  K tiles sit in LDS unpadded, 16-byte
-//        chunk c of key r at slot c ^ swz(r) (see Tile::swz for the choice).
+//      * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held
+//        in registers for the whole key loop), with the accumulators starting
+//        from the tile's bias values c_h s_j (register j holds a fixed key,
+//        so the 64 values of a tile are four 16-byte LDS reads per 32-key
+//        half), so S~ = q.k + c_h s_j exactly in fp32 and one multiply by
+//        alpha = log2(e) / (sqrt(d) tau) gives the logit in log2 units.  K
+//        tiles sit in LDS unpadded, 16-byte chunk c of key r at slot
+//        c ^ swz(r) (see Tile::swz).
 //      * Each lane owns one query column, so the online-softmax statistics are
 //        lane-local plus one exchange between lane halves; the running max
 //        only moves when a tile raises it by more than 2^8 (lazy rescaling).
@@ -41,7 +43,7 @@
 //        before the exponentials of tile t (independent work for the MFMA
 //        pipe while the VALU runs the softmax).
 //      * Tiles arrive by buffer-to-LDS DMA (buffer_load_dwordx4 ... lds): K
-//        (with the bias fragments) straight from k, two tiles ahead, V^T
+//        straight from k (and the tile's bias values), two tiles ahead, V^T
 //        images one tile ahead, each in its own double-buffered LDS ring; no
 //        staging registers, no LDS store instructions, one barrier per tile.
 //      * Causal masking only on diagonal tiles; tiles above a wave's rows are
@@ -86,21 +88,18 @@ typedef __fp16 f16x2 __attribute__((ext_vector_type(2)));   // cvt_pkrtz / fdot2
 
 template <int D, bool kBias>
 struct Tile {
-  static constexpr int KS = D / 16 + (kBias ? 1 : 0);     // k-steps of S^T (+ the bias step)
+  static constexpr int KS = D / 16;                       // k-steps of S^T
   static constexpr int K_ROW = D * 2;                     // LDS bytes per key: 16-byte chunks,
                                                           //   chunk c of key r at slot c ^ swz(r)
   static constexpr int K_IMG = kBN * K_ROW;               // one K tile in LDS
   static constexpr int V_ROW = kBN * 2 + 16;              // bytes, padded
   static constexpr int V_IMG = D * V_ROW;                 // one V^T tile (workspace and LDS)
-  static constexpr int S_TILE = kBN * 32;                 // bias A fragments of one tile
-  // XOR key of K row r.  Without the bias: 16 consecutive rows hit 16
-  // different 16-byte slots modulo 256 bytes (rows are 256 bytes at d = 128,
-  // 128 bytes at d = 64), so the fragment reads are free of bank conflicts.
-  // With the bias: r % 8, which leaves 2-way conflicts on those reads but
-  // measured 0.5-4 % faster on the gated kernel (the conflict-free key gains
-  // 1.5 % on the plain one).
+  static constexpr int S_TILE = kBN * 4;                  // one head's bias values of a tile (fp32)
+  // XOR key of K row r: 16 consecutive rows hit 16 different 16-byte slots
+  // modulo 256 bytes (rows are 256 bytes at d = 128, 128 bytes at d = 64), so
+  // the fragment reads are free of bank conflicts.
   static __host__ __device__ constexpr int swz(int r) {
-    return kBias ? (r & 7) : D == 128 ? (r & 15) : ((r >> 1) & 7);
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
   }
   static_assert(K_IMG % 1024 == 0 && V_IMG % 1024 == 0, "tiles must be whole 1 KiB DMA chunks");
   // One split chunk's partial state: per 32-row set (kSets per wave), the
@@ -159,7 +158,7 @@ Plan make_plan(int64_t M, int Hq, int Hkv) {
   p.n_part = p.units - std::min<int64_t>(h, p.n_qt);
   p.img_bytes = static_cast<size_t>(p.n_tiles) * Hkv * T::V_IMG;
   p.sc_off = p.img_bytes;
-  p.part_off = p.sc_off + ((static_cast<size_t>(p.n_tiles) * T::S_TILE + 255) & ~size_t(255));
+  p.part_off = p.sc_off + ((static_cast<size_t>(Hq) * p.n_tiles * T::S_TILE + 255) & ~size_t(255));
   p.total = p.part_off + static_cast<size_t>(Hq) * p.n_part * T::PART;
   return p;
 }
@@ -185,15 +184,16 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // v_pack: one work-group per (tile, KV head) builds the tile's V^T image in
 // the workspace (fp16, [d][key] with the key order permuted inside each
 // 16-key group so that every lane's eight keys of a P.V step are one 16-byte
-// run; rows padded; keys past n zero).  The work-groups of KV head 0 of a
-// gated call also store, per key, the bias step's A fragment: the score split
-// into two bf16 parts as (s_hi, s_lo, s_hi, 0 ...) for lane half 0 and 16
-// zero bytes for lane half 1.  K needs no pass of its own: the attention
+// run; rows padded; keys past n zero).  In a gated call each work-group also
+// stores, for the query heads of its KV group and the tile's keys, the bias
+// c_h s_j (fp32, [head][key]).  K needs no pass of its own: the attention
 // kernel DMAs its tiles straight from k.
 // ---------------------------------------------------------------------------
 template <int D, bool kBias>
 __global__ __launch_bounds__(256) void v_pack_kernel(const bf16* __restrict__ v,
-                                                     const float* __restrict__ key_score, int M,
+                                                     const float* __restrict__ key_score,
+                                                     const float* __restrict__ gain,
+                                                     const float* __restrict__ tau, int M, int Hq,
                                                      int Hkv, char* __restrict__ ws,
                                                      char* __restrict__ sc) {
   using T = Tile<D, kBias>;
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void v_pack_kernel(const bf16* __restrict__ v,
   // Every load is issued before the first store.
   const int kg = tid % 16, dc = tid / 16;
   const int key = tile * kBN + tid;
-  const bool score_task = kBias && kvh == 0 && tid < kBN;
+  const bool score_task = kBias && tid < kBN;
   const float x_s = (score_task && key < M) ? key_score[key] : 0.f;
   if (dc < DC) {
     u32x4 vx[4];
@@ -238,14 +238,14 @@ __global__ __launch_bounds__(256) void v_pack_kernel(const bf16* __restrict__ v,
   }
   if (tid < D) st16(vimg + tid * T::V_ROW + kBN * 2, zero_u32x4());
   if (score_task) {
-    const uint16_t hi = bf16_bits(x_s);
-    const uint16_t lo = bf16_bits(x_s - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-    u32x4 f = zero_u32x4();
-    f[0] = hi | (static_cast<uint32_t>(lo) << 16);
-    f[1] = hi;
-    char* dst = sc + static_cast<size_t>(tile * kBN + tid) * 32;
-    st16(dst, f);
-    st16(dst + 16, zero_u32x4());
+    // the key's bias in units of q.k for each head of this group:
+    // c_h s_j with c_h = gain_h sqrt(d) tau_h
+    const int G = Hq / Hkv;
+    for (int g = 0; g < G; ++g) {
+      const int h = kvh * G + g;
+      const float c = gain[h] * sqrtf(static_cast<float>(D)) * tau[h];
+      reinterpret_cast<float*>(sc)[(static_cast<size_t>(h) * n_tiles + tile) * kBN + tid] = c * x_s;
+    }
   }
 }
 
@@ -358,18 +358,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
         qf[r][s] = as_bf16x8(
             bload16(rq, static_cast<uint32_t>(my_q[r]) * q_row_bytes + (16 * s + 8 * hh) * 2));
     }
-    if (kBias) {
-      const float c = gain[head] * sqrtf(static_cast<float>(D)) * t_h;   // gain / alpha * log2(e)
-      const uint16_t c_hi = bf16_bits(c);
-      const uint16_t c_lo = bf16_bits(c - __uint_as_float(static_cast<uint32_t>(c_hi) << 16));
-      u32x4 e = zero_u32x4();
-      if (hh == 0) {
-        e[0] = c_hi | (static_cast<uint32_t>(c_hi) << 16);
-        e[1] = c_lo;
-      }
-#pragma unroll
-      for (int r = 0; r < kSets; ++r) qf[r][KS - 1] = as_bf16x8(e);
-    }
+
   }
 
   floatx16 o[kSets][DT];
@@ -405,7 +394,8 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
       make_rsrc(ws + static_cast<size_t>(kvh) * n_tiles * T::V_IMG,
                 static_cast<uint32_t>(n_tiles) * T::V_IMG);
   const __amdgpu_buffer_rsrc_t rsc =
-      make_rsrc(bias_frag, static_cast<uint32_t>(n_tiles) * T::S_TILE);
+      make_rsrc(bias_frag + static_cast<size_t>(head) * n_tiles * T::S_TILE,
+                static_cast<uint32_t>(n_tiles) * T::S_TILE);
   const int lane16 = 16 * lane;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // provably wave-uniform
   uint32_t koff[NKJ];   // this lane's source offset (within a tile) per K DMA instruction
@@ -426,12 +416,10 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
             rk, (__attribute__((address_space(3))) void*)(&lds_k[buf][0] + 1024 * j), 16,
             static_cast<int>(tile_off + koff[jj]), 0, 0, 0);
     }
-    if (kBias && wave_s >= NW - T::S_TILE / 1024) {
-      const int js = wave_s - (NW - T::S_TILE / 1024);
-      const int s_off = t * T::S_TILE + 1024 * js;
+    if (kBias && wave_s == NW - 1 && lane < T::S_TILE / 16) {
+      const int s_off = t * T::S_TILE;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsc, (__attribute__((address_space(3))) void*)(&lds_s[buf][0] + 1024 * js), 16, lane16,
-          s_off, 0, 0);
+          rsc, (__attribute__((address_space(3))) void*)(&lds_s[buf][0]), 16, lane16, s_off, 0, 0);
     }
   };
   auto dma_v = [&](int buf, int t) __attribute__((always_inline)) {
@@ -450,15 +438,27 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
 
   // ---- S^T of one tile for every set: each K fragment read feeds kSets
   // MFMAs.  Lane (l32, hh) reads chunk 2 ks + hh of key 32 t2 + l32, stored at
-  // slot (2 ks + hh) ^ swz(l32): the per-k-step address is one XOR.  The
-  // bias step's A fragment comes prebuilt (see v_pack).
+  // slot (2 ks + hh) ^ swz(l32): the per-k-step address is one XOR.
   const uint32_t k_base = static_cast<uint32_t>(l32) * T::K_ROW + ((hh ^ T::swz(l32)) << 4);
   auto qk = [&](const char* kimg, const char* simg, floatx16 (&s)[kSets][2])
       __attribute__((always_inline)) {
+    // S~ starts from the keys' bias c_h s_j (register j of 32-key half t2
+    // holds key 32 t2 + 8 (j/4) + 4 hh + j%4), so S~ = q.k + c_h s_j
 #pragma unroll
     for (int r = 0; r < kSets; ++r) {
-      s[r][0] = zero16();
-      s[r][1] = zero16();
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        if (kBias) {
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const float4 b = *reinterpret_cast<const float4*>(simg + 4 * (32 * t2 + 8 * jg + 4 * hh));
+            s[r][t2][4 * jg] = b.x; s[r][t2][4 * jg + 1] = b.y;
+            s[r][t2][4 * jg + 2] = b.z; s[r][t2][4 * jg + 3] = b.w;
+          }
+        } else {
+          s[r][t2] = zero16();
+        }
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -470,14 +470,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
         for (int r = 0; r < kSets; ++r) s[r][t2] = mfma_32x32x16(a, qf[r][ks], s[r][t2]);
       }
     }
-    if (kBias) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(simg + (32 * t2 + l32) * 32 + 16 * hh);
-#pragma unroll
-        for (int r = 0; r < kSets; ++r) s[r][t2] = mfma_32x32x16(a, qf[r][KS - 1], s[r][t2]);
-      }
-    }
+
   };
 
   // ---- online softmax of one set's tile, in two parts so that the next
@@ -504,7 +497,10 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * alpha;
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * alpha;
+    }
     // Wave-uniform and rare after the first tiles: a real branch, not a select.
     if (__builtin_expect(__builtin_amdgcn_readfirstlane(__any(mx > m_run[r] + kRescaleThreshold)), 0)) {
       const float m_new = fmaxf(m_run[r], mx);
@@ -713,7 +709,8 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M
   char* sc = img + p.sc_off;
   char* part = img + p.part_off;
   hipLaunchKernelGGL((v_pack_kernel<D, kBias>), dim3(static_cast<unsigned>(p.n_tiles * Hkv)),
-                     dim3(256), 0, stream, reinterpret_cast<const bf16*>(v), s, M, Hkv, img, sc);
+                     dim3(256), 0, stream, reinterpret_cast<const bf16*>(v), s, g, t, M, Hq, Hkv, img,
+                     sc);
   const dim3 grid(static_cast<unsigned>(p.units * Hq));
   hipLaunchKernelGGL((attn_fwd_kernel<D, kBias>), grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k), img, sc, M,

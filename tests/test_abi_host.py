@@ -148,7 +148,7 @@ def test_attention_validation(L):
     assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, A, W, 0) == UNSUPPORTED
     assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, A, W, 0) == UNSUPPORTED  # 2^31-byte offsets
     need = L.tg_attn_workspace_bytes(100, 16, 8, 128)
-    assert need == 2 * 8 * 128 * 144 + 2 * 2048  # V^T images (2 tiles x 8 heads) + bias fragments
+    assert need == 2 * 8 * 128 * 144 + 16 * 2 * 256  # V^T images (2 tiles x 8 heads) + fp32 biases
     assert g(A, A, A, 100, 16, 8, 128, A, A, A, A, None, A, need - 1, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, A, 1000, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, None, need, 0) == WORKSPACE
@@ -176,9 +176,9 @@ def _split_layout(n, hq, hkv, d, gated=True):
     h = max(min(h, n_qt), 1)
     units = sum(-(-(qt + 1) // h) for qt in range(n_qt))
     img = d * 144                              # V^T image of one tile (fp16, padded rows)
-    sc = n_tiles * 64 * 32                     # per key: the bias step's A fragment + zeros
+    sc = hq * n_tiles * 64 * 4                 # per query head and key: the fp32 bias
     n_part = units - min(h, n_qt)
-    return n_tiles * hkv * img + sc + hq * n_part * part, h, units
+    return n_tiles * hkv * img + -(-sc // 256) * 256 + hq * n_part * part, h, units
 
 
 @pytest.mark.parametrize("n,hq,hkv,d", [(2304, 16, 8, 128), (1000, 2, 1, 128), (1280, 16, 8, 64),
