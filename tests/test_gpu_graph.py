@@ -51,3 +51,47 @@ def test_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(idx, ref[0]) and torch.equal(out, ref[1]) and torch.equal(dout, ref[2]), rep
+
+
+def test_graph_replays_of_the_backward_match_eager():
+    """Forward with lse, then the backward (seven launches, split walks at
+    this size), captured together; every replay matches the eager gradients."""
+    rng = np.random.default_rng(92)
+    m, hq, hkv, d = 2304, 16, 8, 128
+    r = lambda *shape: dev_bf16(np.clip(rng.standard_normal(shape), -3.5, 3.5).astype(np.float32))
+    q, k, v, do = r(m, hq, d), r(m, hkv, d), r(m, hkv, d), r(m, hq, d)
+    s, gain, tau = dev_f32(rng.standard_normal(m)), dev_f32(rng.uniform(0.5, 1.5, hq)), \
+        dev_f32(rng.uniform(0.8, 1.2, hq))
+    out = torch.empty_like(q)
+    lse = torch.empty((hq, m), dtype=torch.float32, device="cuda")
+    ws = tg.attn_workspace(m, hq, hkv, d)
+    bws = tg.attn_bwd_workspace(m, hq, hkv, d)
+    grads = tg.gated_attn_bwd(q, k, v, s, gain, tau, *tg.gated_attn_fwd(q, k, v, s, gain, tau,
+                                                                           want_lse=True), do,
+                              workspace=bws)
+
+    def work():
+        tg.gated_attn_fwd(q, k, v, s, gain, tau, out=out, lse=lse, workspace=ws)
+        tg.gated_attn_bwd(q, k, v, s, gain, tau, out, lse, do, grads=grads, workspace=bws)
+
+    say("graph capture: gated attention forward + backward")
+    work()
+    torch.cuda.synchronize()
+    ref = {nm: t.clone() for nm, t in grads.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(4):
+        for t in grads.values():                              # eager work between replays
+            t.zero_()
+        bws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for nm, t in grads.items():
+            assert torch.equal(t, ref[nm]), (rep, nm)
