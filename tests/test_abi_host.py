@@ -212,11 +212,13 @@ def test_product_path_never_imports_the_oracle():
 
 
 def _decode_ws(n, hq, hkv, d):
-    """The decode workspace restated: chunks of 256, 128 or 64 keys (the largest
-    that still gives >= 512 work-groups over the KV heads, else 64); per (KV
-    head, chunk, query head of its group) a (max, sum, d outputs) fp32 state."""
-    c = 256
-    while c > 64 and -(-n // c) * hkv < 512:
+    """The decode workspace restated: chunks of 256 keys when that gives >= 512
+    work-groups over the KV heads, else 128 when that gives >= 128, else 64
+    (at most 128 for groups of 4 query heads, 64 for 8); per (KV head, chunk,
+    query head of its group) a (max, sum, d outputs) fp32 state."""
+    g = hq // hkv
+    c = 256 if g <= 2 else 128 if g == 4 else 64
+    while c > 64 and -(-n // c) * hkv < (512 if c == 256 else 128):
         c //= 2
     return hkv * -(-n // c) * (hq // hkv) * (d + 2) * 4
 
