@@ -65,7 +65,9 @@
 //    the whole split saves.
 #include <algorithm>
 #include <cmath>
+#include <functional>
 #include <type_traits>
+#include <vector>
 
 #include "tg_device.h"
 #include "tg_launch.h"
@@ -133,10 +135,8 @@ struct Plan {
 // the average number of tile steps per resident work-group; then chunks of
 // 1.3x that average, never shorter than 8 key tiles (each split chunk pays a
 // partial-state round trip).  Measured at 16 heads: 1.0x-1.3x is best for
-// 2304 kept rows, 1.3x-1.5x for 4352 (25% faster than 1.0x).  A
-// dispatch-simulation choice of h was tried and measured slower at 2304
-// (more, shorter chunks: more partial traffic than the balance saved).
-int choose_h(int n_qt, int Hq) {
+// 2304 kept rows, 1.3x-1.5x for 4352 (25% faster than 1.0x).
+int base_h(int n_qt, int Hq) {
   const double steps = static_cast<double>(kTilesPerQt) * n_qt * (n_qt + 1) / 2;
   const double avg = static_cast<double>(Hq) * steps / kSlots;
   int64_t h = n_qt;
@@ -145,13 +145,60 @@ int choose_h(int n_qt, int Hq) {
   return static_cast<int>(std::max<int64_t>(std::min<int64_t>(h, n_qt), 1));
 }
 
+// Makespan of the launch in key-tile steps: work-groups in launch order (the
+// kernel's: longest query tiles first, last chunk first, heads interleaved)
+// onto kSlots resident slots, each busy for its key tiles plus two (three
+// when it writes a split partial).
+double simulate_split(int64_t M, int n_qt, int h, int Hq) {
+  std::vector<double> slot(kSlots, 0.0);   // min-heap of the slots' free times
+  double end = 0.0;
+  for (int qt = n_qt - 1; qt >= 0; --qt) {
+    const int walk = static_cast<int>((std::min<int64_t>(static_cast<int64_t>(kBM) * (qt + 1), M) + kBN - 1) / kBN);
+    const int nch = (qt + h) / h;
+    for (int c = nch - 1; c >= 0; --c) {
+      const int len = std::min(kTilesPerQt * h, walk - kTilesPerQt * h * c);
+      const double d = len + 2.0 + (nch > 1 ? 1.0 : 0.0);
+      for (int head = 0; head < Hq; ++head) {
+        std::pop_heap(slot.begin(), slot.end(), std::greater<double>());
+        slot.back() += d;
+        end = std::max(end, slot.back());
+        std::push_heap(slot.begin(), slot.end(), std::greater<double>());
+      }
+    }
+  }
+  return end;
+}
+
+// Short prefixes: the chunk one step shorter than base_h's when the dispatch
+// simulation finishes more than 6 % sooner with it.  The simulation ignores
+// the merge and partial traffic that more chunks add and that a lone
+// work-group runs faster on its CU, so only clear wins are taken.  Measured
+// at 16 heads (base -> chosen h): 2000 rows 43.4 -> 38.5 us, 2304 rows 45.1 ->
+// 43.5 us, 2600 rows 52.9 -> 51.6 us, 3000 rows 63.0 -> 61.1 us; at 1800 and
+// 3500-7000 rows, where the simulation keeps base_h, the shorter chunk
+// measured 0-12 % slower.  The last choice is cached (the layers of one
+// model call this with the same shape).
+int choose_h(int64_t M, int n_qt, int Hq) {
+  thread_local int64_t c_m = -1;
+  thread_local int c_hq = -1, c_h = 0;
+  if (M == c_m && Hq == c_hq) return c_h;
+  int h = base_h(n_qt, Hq);
+  if (h > kMinChunk && h < n_qt &&
+      simulate_split(M, n_qt, h - 1, Hq) < 0.94 * simulate_split(M, n_qt, h, Hq))
+    h -= 1;
+  c_m = M;
+  c_hq = Hq;
+  c_h = h;
+  return h;
+}
+
 template <int D, bool kBias>
 Plan make_plan(int64_t M, int Hq, int Hkv) {
   using T = Tile<D, kBias>;
   Plan p{};
   p.n_qt = static_cast<int>((M + kBM - 1) / kBM);
   p.n_tiles = static_cast<int>((M + kBN - 1) / kBN);
-  const int64_t h = choose_h(p.n_qt, Hq);
+  const int64_t h = choose_h(M, p.n_qt, Hq);
   p.h = static_cast<int>(h);
   p.units = units_before(p.n_qt, h);
   p.n_split = std::max<int64_t>(p.n_qt - h, 0);
