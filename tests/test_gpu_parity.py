@@ -199,7 +199,8 @@ def _rand_attn(rng, m, hq, hkv, d):
                                         (64, 4, 4, 128), (65, 8, 1, 128), (127, 4, 2, 64),
                                         (129, 16, 8, 128), (200, 4, 2, 64), (515, 16, 8, 128),
                                         (1000, 2, 1, 128), (2304, 16, 8, 128), (3000, 1, 1, 64),
-                                        (5000, 2, 1, 128), (1800, 8, 1, 128), (2600, 8, 4, 64)])
+                                        (5000, 2, 1, 128), (1800, 8, 1, 128), (2600, 8, 4, 64),
+                                        (2000, 16, 8, 128), (3000, 16, 8, 128)])
 def test_gated_attention_ragged(m, hq, hkv, d):
     rng = np.random.default_rng(m * 7 + d)
     q, k, v, s, gain, tau = _rand_attn(rng, m, hq, hkv, d)
