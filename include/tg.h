@@ -200,8 +200,7 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                            tg_stream_t stream);
 
 /*
- * Bytes of device workspace tg_gated_attn_bwd needs for n rows: transposed
- * bf16 tile images of q, dout and k (about 1.25x their bytes), per row and
+ * Bytes of device workspace tg_gated_attn_bwd needs for n rows: per row and
  * query head its log-sum-exp and dout.out, per query head and key the column
  * sum of the logit gradient, fp32 per-query-head dk and dv partials
  * (2 * 4 * n * n_q_heads * head_dim bytes) and a few floats per query head

@@ -208,8 +208,6 @@ tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return fail(TG_E_INVALID, "%s: q/k/v/out/dout/dq/dk/dv must be 16-byte aligned", fn);
-  if (tg::attn_bwd_image_bytes_per_head(n, head_dim) >= (size_t(1) << 32))
-    return fail(TG_E_UNSUPPORTED, "%s: n=%lld too long for one head's tile images", fn, (long long)n);
   const size_t need = tg::attn_bwd_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(TG_E_WORKSPACE, "%s: workspace %p of %zu bytes (need %zu, 16-byte aligned)", fn,

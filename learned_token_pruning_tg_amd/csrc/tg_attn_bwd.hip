@@ -13,23 +13,23 @@
 // (the last because d logit / d tau_h = -c_h q.k / tau_h).
 //
 // Launches, all deterministic (every sum in a fixed order, no atomics):
-// 1. bwd_pack: per (query head, 32-row tile) the Q^T and dO^T tile images
-//    ([d][row], rows permuted inside 16-row groups so that each lane's eight
-//    rows of an MFMA k-step are one 16-byte run) and the rows' -lse / c_h
-//    (-inf past n) and -D; per (KV head, 32-key tile) the K^T image.
+// 1. bwd_pack: per (query head, 32-row tile) the rows' -lse / c_h (-inf past
+//    n) and -D.
 // 2. bwd_dkdv: one work-group per (query head, 128 keys), a wave per 32 keys
 //    with their K and V fragments in registers, over 32-query steps from the
 //    diagonal on: S = Q K^T and dP = dO V^T on v_mfma_f32_32x32x16_bf16 (lane
 //    = key, registers = queries), P and dS in fp32, then dV += P^T dO and
-//    dK += dS^T Q with P and dS as bf16 A fragments straight from registers.
-//    Q and dO rows and their images arrive by buffer-to-LDS DMA into a
-//    double-buffered ring, one barrier per step; the S and dP accumulators
-//    start from -lse / c_h and -D.  Writes fp32 per-head dK/dV
-//    partials and the per-head column sums sum_i dS_ij.
+//    dK += dS^T Q with P and dS as bf16 A fragments straight from registers
+//    and the dO and Q B fragments read transposed (ds_read_b64_tr_b16) out of
+//    the same row tiles the S and dP steps read.  Q and dO rows arrive by
+//    buffer-to-LDS DMA into a double-buffered ring, one barrier per step; the
+//    S and dP accumulators start from -lse / c_h and -D.  Writes fp32
+//    per-head dK/dV partials and the per-head column sums sum_i dS_ij.
 // 3. bwd_dq: one work-group per (query head, 128 queries), a wave per 32
 //    queries with their Q and dO fragments in registers, over 32-key steps up
 //    to the diagonal: S^T = K Q^T, dP^T = V dO^T (lane = query), dS^T, then
-//    dQ^T += K^T dS^T.  Writes dQ (bf16) and per work-group sum_i q_i.dq_i.
+//    dQ^T += K^T dS^T with the K^T A fragments read transposed out of the K
+//    rows tile.  Writes dQ (bf16) and per work-group sum_i q_i.dq_i.
 // 4. bwd_reduce: dK, dV = sum over the heads of each KV group (bf16) and the
 //    score gradient ds_j = sum_h g_h colsum_hj; bwd_dq_reduce when the dQ
 //    walks are split.  5. bwd_head: dg_h, dtau_h.
@@ -55,15 +55,41 @@ struct Bwd {
   static constexpr int DT = D / 32;                 // 32-wide d tiles
   static constexpr int ROW = D * 2;                 // bytes of one row tile row (LDS, unpadded)
   static constexpr int ROWS_TILE = kRows * ROW;     // a 32-row tile in LDS
-  static constexpr int IMG_ROW = kRows * 2 + 16;    // image row: 32 bf16 + 16 pad bytes
-  static constexpr int IMG = D * IMG_ROW;           // one tile image
   static constexpr int N_ROW_DMA = ROWS_TILE / 1024;
-  static constexpr int N_IMG_DMA = IMG / 1024;
-  static_assert(ROWS_TILE % 1024 == 0 && IMG % 1024 == 0, "whole 1 KiB DMA chunks");
+  static_assert(ROWS_TILE % 1024 == 0, "whole 1 KiB DMA chunks");
   // XOR key of LDS row r: 16 consecutive rows hit 16 different 16-byte slots
   // modulo 256 bytes, so the A-fragment reads are free of bank conflicts.
   static __host__ __device__ constexpr int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// MFMA fragment with the tile's rows as k and its dims as the 32 lanes of m
+// (or n), read transposed out of a swizzled row tile (row r: 16-byte chunk c
+// at slot c ^ swz(r)) by two ds_read_b64_tr_b16.  That instruction hands lane
+// i = 4 a + c of each 16-lane group element c of the 8-byte rows that lanes
+// a, a + 4, a + 8, a + 12 of the group address.  Lane j addresses row
+// 16 g + 8 q + 4 hh + j / 4 at dims n0 + 16 (lane / 16 % 2) + 4 (j % 4), so
+// lane l receives dim n0 + l % 32 of rows 16 g + 8 q + 4 hh + 0..3 in read
+// q: element e of the fragment is row 16 g + 8 (e / 4) + 4 hh + e % 4, the
+// row that C-register 8 g + e of lane half hh holds (the A or B fragment
+// built from those registers on the other side of the product matches).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int g, int n0, int lane) {
+  using T = Bwd<D>;
+  const int j = lane & 15, hh = lane >> 5;
+  const int d = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  v4i16 x[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * g + 8 * q + 4 * hh + (j >> 2);
+    const char* a = tile + r * T::ROW + (((d >> 3) ^ T::swz(r)) << 4) + (d & 7) * 2;
+    x[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
+  }
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 y = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, y);
+}
 
 // Split walks.  A dK/dV work-group walks the 32-query steps from its
 // diagonal to the end (key block kt: n_t - 4 kt steps), a dQ work-group the
@@ -92,7 +118,7 @@ struct BwdPlan {
   int64_t n_t128;
   int64_t mp;        // rows padded to n_t32 * 32
   Split kv, q;       // chunking of the dK/dV and dQ walks
-  size_t qimg, doimg, kimg, ld, colsum, dkp, dvp, dgp, qdot, dqp, total;
+  size_t ld, colsum, dkp, dvp, dgp, qdot, dqp, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -110,12 +136,8 @@ BwdPlan bwd_plan(int64_t n, int hq, int hkv, int d) {
   }
   p.kv = choose_split(t_real, kv_steps * hq);
   p.q = choose_split(t_real, q_steps * hq);
-  const size_t img = static_cast<size_t>(d) * (kRows * 2 + 16);
   const size_t nkv = static_cast<size_t>(p.kv.nc), nq = static_cast<size_t>(p.q.nc);
   size_t o = 0;
-  p.qimg = o;   o = align256(o + static_cast<size_t>(hq) * p.n_t32 * img);
-  p.doimg = o;  o = align256(o + static_cast<size_t>(hq) * p.n_t32 * img);
-  p.kimg = o;   o = align256(o + static_cast<size_t>(hkv) * p.n_t32 * img);
   p.ld = o;     o = align256(o + static_cast<size_t>(hq) * p.n_t32 * 64 * 4);
   p.colsum = o; o = align256(o + nkv * hq * p.mp * 4);
   p.dkp = o;    o = align256(o + nkv * hq * p.mp * d * 4);
@@ -163,67 +185,21 @@ __device__ __forceinline__ float add_halves(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile images.  Row (query or key) 16 g + 8 b + 4 h' + i of a 32-row tile sits
-// at position 16 g + 8 h' + 4 b + i of every image row d, so that MFMA k-step
-// g, lane half h', element e = 4 b + i reads row 16 g + 8 (e / 4) + 4 h' + e % 4:
-// the row a C-layout register 8 g + e of lane half h' holds.  Task (kg, dc)
-// moves rows 4 kg .. 4 kg + 3, dims 8 dc .. 8 dc + 7 (D tasks per tile).
+// bwd_pack: per (query head, 32-row tile) the rows' -lse / c_h (-inf past n)
+// and -D, D_i = dO_i . O_i by eight lanes per row and a fixed butterfly.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void transpose_tile(__amdgpu_buffer_rsrc_t r, uint32_t row_stride,
-                                               uint32_t row0, char* __restrict__ img, int task) {
-  using T = Bwd<D>;
-  const int kg = task & 7, dc = task >> 3;
-  u32x4 x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = bload16(r, (row0 + 4 * kg + i) * row_stride + 16 * dc);
-  const int p = 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint2 lo, hi;   // dim 2w: low halves; dim 2w+1: high halves
-    lo.x = (x[0][w] & 0xFFFFu) | (x[1][w] << 16);
-    lo.y = (x[2][w] & 0xFFFFu) | (x[3][w] << 16);
-    hi.x = (x[0][w] >> 16) | (x[1][w] & 0xFFFF0000u);
-    hi.y = (x[2][w] >> 16) | (x[3][w] & 0xFFFF0000u);
-    const int d0 = 8 * dc + 2 * w;
-    *reinterpret_cast<uint2*>(img + d0 * T::IMG_ROW + 2 * p) = lo;
-    *reinterpret_cast<uint2*>(img + (d0 + 1) * T::IMG_ROW + 2 * p) = hi;
-  }
-}
-
-// Blocks [0, Hq * n_t32): query head h, tile t -> Q^T, dO^T images and the
-// rows' (-lse / c_h, -D); blocks after that: KV head, tile -> K^T image.
-template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pack_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ out,
-    const float* __restrict__ lse, const bf16* __restrict__ dout, const float* __restrict__ tau,
-    int M, int Hq, int Hkv, int n_t32, char* __restrict__ qimg, char* __restrict__ doimg,
-    char* __restrict__ kimg, float* __restrict__ ld) {
-  using T = Bwd<D>;
+    const bf16* __restrict__ out, const float* __restrict__ lse, const bf16* __restrict__ dout,
+    const float* __restrict__ tau, int M, int Hq, int n_t32, float* __restrict__ ld) {
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  if (b >= Hq * n_t32) {
-    const int kvh = (b - Hq * n_t32) / n_t32, t = (b - Hq * n_t32) % n_t32;
-    const uint32_t stride = static_cast<uint32_t>(Hkv) * D * 2;
-    if (tid < D) {
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + static_cast<size_t>(kvh) * D, stride * static_cast<uint32_t>(M));
-      transpose_tile<D>(rk, stride, static_cast<uint32_t>(t) * kRows,
-                        kimg + (static_cast<size_t>(kvh) * n_t32 + t) * T::IMG, tid);
-    }
-    return;
-  }
-  const int h = b / n_t32, t = b % n_t32;
+  const int h = blockIdx.x / n_t32, t = blockIdx.x % n_t32;
   const uint32_t stride = static_cast<uint32_t>(Hq) * D * 2;
   const uint32_t range = stride * static_cast<uint32_t>(M);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(h) * D, range);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + static_cast<size_t>(h) * D, range);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + static_cast<size_t>(h) * D, range);
   const size_t tile = static_cast<size_t>(h) * n_t32 + t;
   const uint32_t row0 = static_cast<uint32_t>(t) * kRows;
-  if (tid < D) transpose_tile<D>(rq, stride, row0, qimg + tile * T::IMG, tid);
-  else if (tid < 2 * D) transpose_tile<D>(rd, stride, row0, doimg + tile * T::IMG, tid - D);
-  // D_i = dO_i . O_i: eight lanes per row, D / 8 dims each, combined in a
-  // fixed butterfly.
   const int qi = tid >> 3, part = tid & 7;
   constexpr int PER = D / 8;        // dims per lane: 16 or 8
   float acc = 0.f;
@@ -259,20 +235,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
-    int n_t32, int mp, int clen, int nc, const char* __restrict__ qimg,
-    const char* __restrict__ doimg, const float* __restrict__ ld, float* __restrict__ colsum,
+    int n_t32, int mp, int clen, int nc, const float* __restrict__ ld, float* __restrict__ colsum,
     float* __restrict__ dkp, float* __restrict__ dvp, float* __restrict__ dgp) {
   using T = Bwd<D>;
   constexpr int KS = T::KS, DT = T::DT;
   constexpr int NW = kThreads / 64;
   constexpr int NJR = T::N_ROW_DMA / NW;                     // row-tile DMA chunks per wave
-  constexpr int NJI = (T::N_IMG_DMA + NW - 1) / NW;          // image chunks per wave (last partial)
   static_assert(T::N_ROW_DMA % NW == 0, "row tiles split evenly over the waves");
 
   __shared__ __align__(16) char lds_qr[2][T::ROWS_TILE];
   __shared__ __align__(16) char lds_dr[2][T::ROWS_TILE];
-  __shared__ __align__(16) char lds_qi[2][T::IMG];
-  __shared__ __align__(16) char lds_di[2][T::IMG];
   __shared__ __align__(16) float lds_ld[2][64];
   __shared__ float lds_red[kThreads / 64];
 
@@ -319,10 +291,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const uint32_t q_row = static_cast<uint32_t>(Hq) * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + static_cast<size_t>(head) * D, q_row * static_cast<uint32_t>(M));
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + static_cast<size_t>(head) * D, q_row * static_cast<uint32_t>(M));
-  const size_t img_head = static_cast<size_t>(head) * n_t32 * T::IMG;
-  const uint32_t img_bytes = static_cast<uint32_t>(n_t32) * T::IMG;
-  const __amdgpu_buffer_rsrc_t rqi = make_rsrc(qimg + img_head, img_bytes);
-  const __amdgpu_buffer_rsrc_t rdi = make_rsrc(doimg + img_head, img_bytes);
   const __amdgpu_buffer_rsrc_t rld = make_rsrc(ld + static_cast<size_t>(head) * n_t32 * 64,
                                                static_cast<uint32_t>(n_t32) * 256);
   const int lane16 = 16 * lane;
@@ -338,7 +306,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   typedef __attribute__((address_space(3))) void* lds_ptr;
   auto dma = [&](int buf, int t) __attribute__((always_inline)) {
     const uint32_t row_off = static_cast<uint32_t>(t) * kRows * q_row;
-    const int img_off = t * T::IMG;
 #pragma unroll
     for (int jj = 0; jj < NJR; ++jj) {
       const int c = wave_s + NW * jj;
@@ -346,16 +313,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
                                                static_cast<int>(row_off + roff[jj]), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)(&lds_dr[buf][0] + 1024 * c), 16,
                                                static_cast<int>(row_off + roff[jj]), 0, 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < NJI; ++jj) {
-      const int c = wave_s + NW * jj;
-      if (c < T::N_IMG_DMA) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rqi, (lds_ptr)(&lds_qi[buf][0] + 1024 * c), 16, lane16,
-                                                 img_off + 1024 * c, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rdi, (lds_ptr)(&lds_di[buf][0] + 1024 * c), 16, lane16,
-                                                 img_off + 1024 * c, 0, 0);
-      }
     }
     if (wave_s == NW - 1 && lane < 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_ptr)(&lds_ld[buf][0]), 16, lane16, t * 256, 0, 0);
@@ -404,18 +361,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
       dsk[2 * jg] = pack_bf16(dsj[0], dsj[1]);
       dsk[2 * jg + 1] = pack_bf16(dsj[2], dsj[3]);
     }
-    // dV += P^T dO, dK += dS^T Q: k-step ks2 takes registers 8 ks2 .. 8 ks2 + 7
-    const char* qi = &lds_qi[buf][0];
-    const char* di = &lds_di[buf][0];
+    // dV += P^T dO, dK += dS^T Q: k-step ks2 takes registers 8 ks2 .. 8 ks2 + 7;
+    // the dO and Q fragments are read transposed out of the row tiles
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       const u32x4 pa = {pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2], pk[4 * ks2 + 3]};
       const u32x4 da = {dsk[4 * ks2], dsk[4 * ks2 + 1], dsk[4 * ks2 + 2], dsk[4 * ks2 + 3]};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int off = (32 * dt + l32) * T::IMG_ROW + 32 * ks2 + 16 * hh;
-        dv[dt] = mfma_32x32x16(as_bf16x8(pa), *reinterpret_cast<const bf16x8*>(di + off), dv[dt]);
-        dk[dt] = mfma_32x32x16(as_bf16x8(da), *reinterpret_cast<const bf16x8*>(qi + off), dk[dt]);
+        dv[dt] = mfma_32x32x16(as_bf16x8(pa), tr_frag<D>(dr, ks2, 32 * dt, lane), dv[dt]);
+        dk[dt] = mfma_32x32x16(as_bf16x8(da), tr_frag<D>(qr, ks2, 32 * dt, lane), dk[dt]);
       }
     }
   };
@@ -468,19 +423,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
-    int n_t32, int n_t128, int mp, int clen, int nc, const char* __restrict__ kimg,
-    const float* __restrict__ ld, bf16* __restrict__ dq, float* __restrict__ dqp,
+    int n_t32, int n_t128, int mp, int clen, int nc, const float* __restrict__ ld,
+    bf16* __restrict__ dq, float* __restrict__ dqp,
     float* __restrict__ qdot) {
   using T = Bwd<D>;
   constexpr int KS = T::KS, DT = T::DT;
   constexpr int NW = kThreads / 64;
   constexpr int NJR = T::N_ROW_DMA / NW;
-  constexpr int NJI = (T::N_IMG_DMA + NW - 1) / NW;
   static_assert(T::N_ROW_DMA % NW == 0, "row tiles split evenly over the waves");
 
   __shared__ __align__(16) char lds_kr[2][T::ROWS_TILE];
   __shared__ __align__(16) char lds_vr[2][T::ROWS_TILE];
-  __shared__ __align__(16) char lds_ki[2][T::IMG];
   __shared__ __align__(16) float lds_s[2][32];
   __shared__ float lds_red[kThreads / 64];
 
@@ -522,8 +475,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   const uint32_t kv_row = static_cast<uint32_t>(Hkv) * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + static_cast<size_t>(kvh) * D, kv_row * static_cast<uint32_t>(M));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + static_cast<size_t>(kvh) * D, kv_row * static_cast<uint32_t>(M));
-  const __amdgpu_buffer_rsrc_t rki = make_rsrc(kimg + static_cast<size_t>(kvh) * n_t32 * T::IMG,
-                                               static_cast<uint32_t>(n_t32) * T::IMG);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(key_score, static_cast<uint32_t>(M) * 4);
   const int lane16 = 16 * lane;
   uint32_t roff[NJR];   // as in bwd_dkdv: K and V rows share the stride
@@ -536,7 +487,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   typedef __attribute__((address_space(3))) void* lds_ptr;
   auto dma = [&](int buf, int u) __attribute__((always_inline)) {
     const uint32_t row_off = static_cast<uint32_t>(u) * kRows * kv_row;
-    const int img_off = u * T::IMG;
 #pragma unroll
     for (int jj = 0; jj < NJR; ++jj) {
       const int c = wave_s + NW * jj;
@@ -544,13 +494,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                                                static_cast<int>(row_off + roff[jj]), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr)(&lds_vr[buf][0] + 1024 * c), 16,
                                                static_cast<int>(row_off + roff[jj]), 0, 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < NJI; ++jj) {
-      const int c = wave_s + NW * jj;
-      if (c < T::N_IMG_DMA)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rki, (lds_ptr)(&lds_ki[buf][0] + 1024 * c), 16, lane16,
-                                                 img_off + 1024 * c, 0, 0);
     }
     if (wave_s == NW - 1 && lane < 8)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(&lds_s[buf][0]), 16, lane16, u * 128, 0, 0);
@@ -586,16 +529,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
       dsk[2 * jg] = pack_bf16(dsj[0], dsj[1]);
       dsk[2 * jg + 1] = pack_bf16(dsj[2], dsj[3]);
     }
-    // dQ^T += K^T dS^T
-    const char* ki = &lds_ki[buf][0];
+    // dQ^T += K^T dS^T, the K^T fragments read transposed out of the K rows tile
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       const u32x4 b = {dsk[4 * ks2], dsk[4 * ks2 + 1], dsk[4 * ks2 + 2], dsk[4 * ks2 + 3]};
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int off = (32 * dt + l32) * T::IMG_ROW + 32 * ks2 + 16 * hh;
-        acc[dt] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ki + off), as_bf16x8(b), acc[dt]);
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = mfma_32x32x16(tr_frag<D>(kr, ks2, 32 * dt, lane), as_bf16x8(b), acc[dt]);
     }
   };
 
@@ -779,15 +719,15 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   float* dgp = reinterpret_cast<float*>(ws + p.dgp);
   float* qdot = reinterpret_cast<float*>(ws + p.qdot);
   float* dqp = reinterpret_cast<float*>(ws + p.dqp);
-  hipLaunchKernelGGL((bwd_pack_kernel<D>), dim3(static_cast<unsigned>((Hq + Hkv) * n_t32)),
-                     dim3(kThreads), 0, stream, bq, bk, reinterpret_cast<const bf16*>(out), lse, bd,
-                     t, M, Hq, Hkv, n_t32, ws + p.qimg, ws + p.doimg, ws + p.kimg, ld);
+  hipLaunchKernelGGL((bwd_pack_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t32)),
+                     dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(out), lse, bd, t, M,
+                     Hq, n_t32, ld);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.kv.nc)),
                      dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, mp,
-                     p.kv.len, p.kv.nc, ws + p.qimg, ws + p.doimg, ld, colsum, dkp, dvp, dgp);
+                     p.kv.len, p.kv.nc, ld, colsum, dkp, dvp, dgp);
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.q.nc)),
                      dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, n_t128,
-                     mp, p.q.len, p.q.nc, ws + p.kimg, ld, reinterpret_cast<bf16*>(dq), dqp, qdot);
+                     mp, p.q.len, p.q.nc, ld, reinterpret_cast<bf16*>(dq), dqp, qdot);
   const int64_t groups = static_cast<int64_t>(M) * Hkv * (D / 4);
   hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3(static_cast<unsigned>((groups + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, stream, dkp, dvp, colsum, g, M, Hq, Hkv, mp, p.kv.len,
@@ -809,11 +749,6 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
 size_t attn_bwd_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_dim) {
   if (n <= 0) return 0;
   return bwd_plan(n, n_q_heads, n_kv_heads, head_dim).total;
-}
-
-size_t attn_bwd_image_bytes_per_head(int64_t n, int head_dim) {
-  const BwdPlan p = bwd_plan(n, 1, 1, head_dim);
-  return static_cast<size_t>(p.n_t32) * head_dim * (kRows * 2 + 16);
 }
 
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,

@@ -36,13 +36,10 @@ hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const float* gain, const float* tau, uint16_t* out, float* lse,
                            void* workspace, hipStream_t stream);
 
-// Bytes of workspace the attention backward needs: Q^T, dO^T and K^T tile
-// images, per-row (lse, D), per-head key column sums of dS, fp32 per-head dK
-// and dV partials, per-work-group q.dq sums.
+// Bytes of workspace the attention backward needs: per-row (lse, D), per-head
+// key column sums of dS, fp32 per-head dK and dV partials (per split chunk),
+// per-work-group gain and q.dq sums, fp32 dQ partials when dQ walks split.
 size_t attn_bwd_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_dim);
-
-// Bytes of one head's tile images (addressed with 32-bit offsets).
-size_t attn_bwd_image_bytes_per_head(int64_t n, int head_dim);
 
 // Gradients of the token-gated attention given its output, its natural-log
 // lse and dout.  `workspace` holds attn_bwd_workspace_bytes(...) bytes.

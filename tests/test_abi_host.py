@@ -301,8 +301,7 @@ def _bwd_split(longest, total):
 
 def _bwd_ws(n, hq, hkv, d):
     """The backward workspace restated: rows padded to whole 128-row blocks;
-    q^T, dout^T (per query head) and k^T (per KV head) images of 32-row tiles,
-    d rows of 80 bytes each; (lse, D) as 64 floats per query head and tile;
+    (lse, D) as 64 floats per query head and 32-row tile;
     per dK/dV chunk, query head and padded row one column-sum float and d fp32
     each of the dk and dv partials; per dK/dV chunk, query head and 128-row
     block one float (gain partial); per dQ chunk the same for q.dq; fp32 dq
@@ -312,9 +311,8 @@ def _bwd_ws(n, hq, hkv, d):
     t_real = -(-n // 32)
     _, nkv = _bwd_split(t_real, hq * sum(t_real - 4 * b for b in range(t128)))
     _, nq = _bwd_split(t_real, hq * sum(min(4 * b + 4, t_real) for b in range(t128)))
-    img = d * 80
     o = 0
-    for size in (hq * t32 * img, hq * t32 * img, hkv * t32 * img, hq * t32 * 256,
+    for size in (hq * t32 * 256,
                  nkv * hq * mp * 4, nkv * hq * mp * d * 4, nkv * hq * mp * d * 4,
                  nkv * hq * t128 * 4, nq * hq * t128 * 4, nq * mp * hq * d * 4 if nq > 1 else 0):
         o = -(-(o + size) // 256) * 256
