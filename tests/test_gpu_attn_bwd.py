@@ -93,7 +93,8 @@ def _compare(got, ref, what):
 
 @pytest.mark.parametrize("n,hq,hkv,d", [
     (2, 2, 1, 128), (3, 4, 2, 64), (31, 4, 4, 64), (33, 2, 1, 128), (129, 4, 2, 128),
-    (300, 16, 8, 128), (700, 8, 2, 64), (1000, 16, 4, 128), (2304, 16, 8, 128)])
+    (300, 16, 8, 128), (700, 8, 2, 64), (1000, 16, 4, 128), (2304, 16, 8, 128),
+    (600, 16, 2, 64), (4352, 16, 8, 128)])
 def test_attn_bwd_vs_oracle(n, hq, hkv, d):
     rng = np.random.default_rng(1000 + n + hq + d)
     q, k, v, dout, s, gain, tau = _case(rng, n, hq, hkv, d)
