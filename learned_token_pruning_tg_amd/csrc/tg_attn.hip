@@ -65,7 +65,6 @@
 //    the whole split saves.
 #include <algorithm>
 #include <cmath>
-#include <functional>
 #include <type_traits>
 #include <vector>
 
@@ -148,21 +147,33 @@ int base_h(int n_qt, int Hq) {
 // Makespan of the launch in key-tile steps: work-groups in launch order (the
 // kernel's: longest query tiles first, last chunk first, heads interleaved)
 // onto kSlots resident slots, each busy for its key tiles plus two (three
-// when it writes a split partial).
-double simulate_split(int64_t M, int n_qt, int h, int Hq) {
-  std::vector<double> slot(kSlots, 0.0);   // min-heap of the slots' free times
-  double end = 0.0;
+// when it writes a split partial).  Durations are whole steps and a greedy
+// list schedule never starts a work-group earlier than the one before it, so
+// the slots are counted per free time and a pointer walks forward.
+int simulate_split(int64_t M, int n_qt, int h, int Hq) {
+  auto walk = [&](int qt) {
+    return static_cast<int>((std::min<int64_t>(static_cast<int64_t>(kBM) * (qt + 1), M) + kBN - 1) / kBN);
+  };
+  int64_t total = 0;
+  int longest = 0;
+  for (int qt = 0; qt < n_qt; ++qt) {
+    const int nch = (qt + h) / h;
+    total += static_cast<int64_t>(walk(qt) + (2 + (nch > 1 ? 1 : 0)) * nch) * Hq;
+    longest = std::max(longest, std::min(kTilesPerQt * h, walk(qt)) + 3);
+  }
+  // list scheduling ends by total / slots + the longest work-group
+  std::vector<int> free_at(static_cast<size_t>(total / kSlots + longest + 2), 0);
+  free_at[0] = kSlots;
+  int t = 0, end = 0;
   for (int qt = n_qt - 1; qt >= 0; --qt) {
-    const int walk = static_cast<int>((std::min<int64_t>(static_cast<int64_t>(kBM) * (qt + 1), M) + kBN - 1) / kBN);
     const int nch = (qt + h) / h;
     for (int c = nch - 1; c >= 0; --c) {
-      const int len = std::min(kTilesPerQt * h, walk - kTilesPerQt * h * c);
-      const double d = len + 2.0 + (nch > 1 ? 1.0 : 0.0);
+      const int d = std::min(kTilesPerQt * h, walk(qt) - kTilesPerQt * h * c) + 2 + (nch > 1 ? 1 : 0);
       for (int head = 0; head < Hq; ++head) {
-        std::pop_heap(slot.begin(), slot.end(), std::greater<double>());
-        slot.back() += d;
-        end = std::max(end, slot.back());
-        std::push_heap(slot.begin(), slot.end(), std::greater<double>());
+        while (free_at[t] == 0) ++t;
+        --free_at[t];
+        ++free_at[t + d];
+        end = std::max(end, t + d);
       }
     }
   }
@@ -176,19 +187,12 @@ double simulate_split(int64_t M, int n_qt, int h, int Hq) {
 // at 16 heads (base -> chosen h): 2000 rows 43.4 -> 38.5 us, 2304 rows 45.1 ->
 // 43.5 us, 2600 rows 52.9 -> 51.6 us, 3000 rows 63.0 -> 61.1 us; at 1800 and
 // 3500-7000 rows, where the simulation keeps base_h, the shorter chunk
-// measured 0-12 % slower.  The last choice is cached (the layers of one
-// model call this with the same shape).
+// measured 0-12 % slower.
 int choose_h(int64_t M, int n_qt, int Hq) {
-  thread_local int64_t c_m = -1;
-  thread_local int c_hq = -1, c_h = 0;
-  if (M == c_m && Hq == c_hq) return c_h;
   int h = base_h(n_qt, Hq);
   if (h > kMinChunk && h < n_qt &&
       simulate_split(M, n_qt, h - 1, Hq) < 0.94 * simulate_split(M, n_qt, h, Hq))
     h -= 1;
-  c_m = M;
-  c_hq = Hq;
-  c_h = h;
   return h;
 }
 
