@@ -249,6 +249,10 @@ def main():
         stage += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
     stage /= args.steps
     attn_ms_launch = stage[3] / w.n_layers
+    tensor_bytes = lambda *ts: int(sum(t.numel() * t.element_size() for t in ts))
+    # buffers the gated step writes (scores, indices, compacted rows, two
+    # layer outputs, workspaces) and the kept rows' q/k/v of one layer
+    gated_buffers = tensor_bytes(scores, idx, h_kept, s_kept, *outs, ws, tws) + tensor_bytes(*kept_qkv[0])
 
     # The key bias's own cost: the same 27 calls over the same kept rows as
     # plain causal attention (gain 0, tau 1), timed like the gated loop.
@@ -416,6 +420,7 @@ def main():
             # both sides also pay the gate layer's own attention over all N rows
             "speedup_incl_gate_layer": round((f_ms + f_launch) / (ms_step + f_launch), 2),
             "steps": fsteps,
+            "step_buffers_bytes": tensor_bytes(fout, fws) + tensor_bytes(*full_qkv[0]),
         }
         del fout, fws
 
@@ -456,6 +461,19 @@ def main():
                        "bias_cost_ratio": round(attn_ms_launch / plain_ms_launch, 3)},
     }
 
+    # KV cache the method keeps: the gate layer over all N rows plus the upper
+    # layers over the M kept rows, against every attention layer over N rows
+    kv_row = 2 * w.n_kv_heads * w.head_dim * 2
+    memory = {
+        "kv_cache_bytes_pruned": (w.n + w.n_layers * m) * kv_row,
+        "kv_cache_bytes_unpruned": (1 + w.n_layers) * w.n * kv_row,
+        "kv_cache_ratio": round((1 + w.n_layers) * w.n / (w.n + w.n_layers * m), 2),
+        "gated_step_buffers_bytes": gated_buffers,
+        "full_step_buffers_bytes": full["step_buffers_bytes"] if full else None,
+        # whole process, including the full-N synthetic q/k/v templates
+        "max_memory_allocated_bytes": int(torch.cuda.max_memory_allocated()),
+    }
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, g, gain, tau, args.cpu_seconds)
@@ -485,6 +503,7 @@ def main():
                      "flops_per_launch": fl, "avg_launch_ms": round(attn_ms_launch, 5)},
         "stages": stages,
         "full_prefill_baseline": full,
+        "memory": memory,
         "first_decode_step": decode,
         "upper_layer_qk_prologue": prologue_stats,
         "upper_layer_backward": bwd_stats,
