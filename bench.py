@@ -244,6 +244,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    per_step = sorted(e[0].elapsed_time(e[4]) for e in evs)
+    ms_step_median = per_step[len(per_step) // 2]
+    ms_step_min = per_step[0]
     stage = np.zeros(4)
     for e in evs:
         stage += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
@@ -486,6 +489,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(ms_step_median, 4),
+        "ms_per_step_min": round(ms_step_min, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -558,7 +563,30 @@ def cpu_baseline(w, g, gain, tau, budget_s):
                    f"{len(layer_t)} of {w.n_layers} gated-attention layers measured "
                    f"(mean {np.mean(layer_t):.2f} s/layer, scaled to {w.n_layers})"),
         "seconds_measured": round(time.perf_counter() - t0, 2),
+        "cpu_model": cpu_model(),
+        "blas": blas_name(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_name() -> str:
+    try:
+        import threadpoolctl
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpoolctl.threadpool_info()
+                if i.get("user_api") == "blas"]
+        return ", ".join(libs) or "unknown"
+    except Exception:  # pragma: no cover
+        return "unknown"
 
 
 if __name__ == "__main__":
