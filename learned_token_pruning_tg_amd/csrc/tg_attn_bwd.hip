@@ -30,9 +30,9 @@
 //    to the diagonal: S^T = K Q^T, dP^T = V dO^T (lane = query), dS^T, then
 //    dQ^T += K^T dS^T with the K^T A fragments read transposed out of the K
 //    rows tile.  Writes dQ (bf16) and per work-group sum_i q_i.dq_i.
-// 4. bwd_reduce: dK, dV = sum over the heads of each KV group (bf16) and the
-//    score gradient ds_j = sum_h g_h colsum_hj; bwd_dq_reduce when the dQ
-//    walks are split.  5. bwd_head: dg_h, dtau_h.
+// 4. bwd_finish: dK, dV = sum over the heads of each KV group (bf16) and the
+//    score gradient ds_j = sum_h g_h colsum_hj; split dQ partials summed; the
+//    gain and temperature gradients dg_h, dtau_h.
 // Short kept prefixes leave too few long walks to fill the chip; then walks
 // are cut into chunks whose fp32 partials the reduce launches add in order.
 #include <algorithm>
@@ -604,12 +604,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // chunks, of the fp32 partials (bf16 out); the threads of (key, KV head 0,
 // dims 0..3) also form the score gradient ds_j = sum_h g_h sum_c colsum_chj.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(
-    const float* __restrict__ dkp, const float* __restrict__ dvp,
+__device__ __forceinline__ void reduce_dkdv_block(
+    int blk, const float* __restrict__ dkp, const float* __restrict__ dvp,
     const float* __restrict__ colsum, const float* __restrict__ gain, int M, int Hq, int Hkv,
     int mp, int clen, int nc, bf16* __restrict__ dk, bf16* __restrict__ dv,
     float* __restrict__ dscore) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // one 4-dim group
+  const int64_t e = static_cast<int64_t>(blk) * kThreads + threadIdx.x;  // one 4-dim group
   const int64_t per_row = static_cast<int64_t>(Hkv) * (D / 4);
   if (e >= static_cast<int64_t>(M) * per_row) return;
   const int64_t key = e / per_row;
@@ -647,10 +647,10 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(
 // dq [row][h][d] = sum over the query block's chunks of the fp32 partials
 // (only launched when the dQ walks are split).
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_reduce_kernel(const float* __restrict__ dqp,
-                                                                 int M, int Hq, int mp, int clen,
-                                                                 int nc, bf16* __restrict__ dq) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+__device__ __forceinline__ void reduce_dq_block(int blk, const float* __restrict__ dqp, int M,
+                                                int Hq, int mp, int clen, int nc,
+                                                bf16* __restrict__ dq) {
+  const int64_t e = static_cast<int64_t>(blk) * kThreads + threadIdx.x;
   const int64_t per_row = static_cast<int64_t>(Hq) * (D / 4);
   if (e >= static_cast<int64_t>(M) * per_row) return;
   const int64_t row = e / per_row;
@@ -668,12 +668,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_reduce_kernel(const float* __
 // work-groups' sum_j s_j colsum_j; dtau_h = -(1 / tau_h) sum of q.dq over
 // query blocks and chunks.  Thread i takes blocks i, i + 256, ..., then a
 // fixed tree (deterministic).
-__global__ __launch_bounds__(kThreads) void bwd_head_kernel(
-    const float* __restrict__ dgp, const float* __restrict__ qdot, const float* __restrict__ tau,
-    int M, int Hq, int n_t128, int kv_len, int kv_nc, int q_len, int q_nc,
-    float* __restrict__ dgain, float* __restrict__ dtau) {
+__device__ __forceinline__ void head_block(
+    int h, const float* __restrict__ dgp, const float* __restrict__ qdot,
+    const float* __restrict__ tau, int M, int Hq, int n_t128, int kv_len, int kv_nc, int q_len,
+    int q_nc, float* __restrict__ dgain, float* __restrict__ dtau) {
   __shared__ float red_g[kThreads], red_t[kThreads];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int t_real = (M + kRows - 1) / kRows;
   float g = 0.f, t = 0.f;
   for (int b = tid; b < n_t128; b += kThreads) {
@@ -696,6 +696,28 @@ __global__ __launch_bounds__(kThreads) void bwd_head_kernel(
     dgain[h] = red_g[0];
     dtau[h] = -red_t[0] / tau[h];
   }
+}
+
+// The launch after dQ: blocks [0, n_kv) reduce dK/dV (and form the score
+// gradient), the next n_q reduce split dQ partials, the last Hq form the gain
+// and temperature gradients: independent work, one launch.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_finish_kernel(
+    const float* __restrict__ dkp, const float* __restrict__ dvp,
+    const float* __restrict__ colsum, const float* __restrict__ gain,
+    const float* __restrict__ dqp, const float* __restrict__ dgp, const float* __restrict__ qdot,
+    const float* __restrict__ tau, int M, int Hq, int Hkv, int mp, int n_t128, int kv_len,
+    int kv_nc, int q_len, int q_nc, int n_kv, int n_q, bf16* __restrict__ dk,
+    bf16* __restrict__ dv, bf16* __restrict__ dq, float* __restrict__ dscore,
+    float* __restrict__ dgain, float* __restrict__ dtau) {
+  const int b = blockIdx.x;   // block-uniform branches
+  if (b < n_kv)
+    reduce_dkdv_block<D>(b, dkp, dvp, colsum, gain, M, Hq, Hkv, mp, kv_len, kv_nc, dk, dv, dscore);
+  else if (b < n_kv + n_q)
+    reduce_dq_block<D>(b - n_kv, dqp, M, Hq, mp, q_len, q_nc, dq);
+  else
+    head_block(b - n_kv - n_q, dgp, qdot, tau, M, Hq, n_t128, kv_len, kv_nc, q_len, q_nc, dgain,
+               dtau);
 }
 
 template <int D>
@@ -729,18 +751,14 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
                      dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, n_t128,
                      mp, p.q.len, p.q.nc, ld, reinterpret_cast<bf16*>(dq), dqp, qdot);
   const int64_t groups = static_cast<int64_t>(M) * Hkv * (D / 4);
-  hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3(static_cast<unsigned>((groups + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, dkp, dvp, colsum, g, M, Hq, Hkv, mp, p.kv.len,
-                     p.kv.nc, reinterpret_cast<bf16*>(dk), reinterpret_cast<bf16*>(dv), dscore);
-  if (p.q.nc > 1) {
-    const int64_t qgroups = static_cast<int64_t>(M) * Hq * (D / 4);
-    hipLaunchKernelGGL((bwd_dq_reduce_kernel<D>),
-                       dim3(static_cast<unsigned>((qgroups + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, dqp, M, Hq, mp, p.q.len, p.q.nc,
-                       reinterpret_cast<bf16*>(dq));
-  }
-  hipLaunchKernelGGL(bwd_head_kernel, dim3(static_cast<unsigned>(Hq)), dim3(kThreads), 0, stream,
-                     dgp, qdot, t, M, Hq, n_t128, p.kv.len, p.kv.nc, p.q.len, p.q.nc, dgain, dtau);
+  const int n_kv = static_cast<int>((groups + kThreads - 1) / kThreads);
+  const int64_t qgroups = static_cast<int64_t>(M) * Hq * (D / 4);
+  const int n_q = p.q.nc > 1 ? static_cast<int>((qgroups + kThreads - 1) / kThreads) : 0;
+  hipLaunchKernelGGL((bwd_finish_kernel<D>), dim3(static_cast<unsigned>(n_kv + n_q + Hq)),
+                     dim3(kThreads), 0, stream, dkp, dvp, colsum, g, dqp, dgp, qdot, t, M, Hq, Hkv,
+                     mp, n_t128, p.kv.len, p.kv.nc, p.q.len, p.q.nc, n_kv, n_q,
+                     reinterpret_cast<bf16*>(dk), reinterpret_cast<bf16*>(dv),
+                     reinterpret_cast<bf16*>(dq), dscore, dgain, dtau);
   return hipGetLastError();
 }
 
