@@ -13,13 +13,13 @@
 // histograms; the ordered output is one pass of block-wide scans.  Bit-exact
 // and deterministic by construction on both paths below.
 //  * Short inputs: one 1024-thread work-group does all of it (no global
-//    atomics, no inter-block ordering).  Scores are read 16 bytes per lane
-//    (buffer loads: reads past n return zeros and are ignored); each pair of
-//    waves counts into its own copy of the histogram (scores bunch into a few
-//    top digits, so one shared histogram serialises on LDS atomics); the
-//    output pass works on 16-row-per-thread chunks laid out so that wave-wide
-//    loads and stores are contiguous, and loads the next chunk before
-//    scanning this one.
+//    atomics, no inter-block ordering).  Every score is read once, into
+//    registers as its key (up to 2 x 16 rows per thread, laid out so that
+//    wave-wide loads and output stores are contiguous; buffer loads past n
+//    return zeros and are ignored), and the three digit passes and the
+//    ordered output pass work from those registers; each pair of waves counts
+//    into its own copy of the histogram (scores bunch into a few top digits,
+//    so one shared histogram serialises on LDS atomics).
 //  * Long inputs: the same passes spread over up to 1024 work-groups with
 //    global histograms and per-range counts in the caller's workspace (see
 //    the multi-work-group section).
@@ -39,6 +39,7 @@ constexpr int kChunk = kThreads * kPerThread;      // block counts stay below 2^
 // path's six dependent launches cost more than they save (measured: 20 vs
 // 23 us at 16k rows, 33 vs 23 us at 32k, 108 vs 24 us at 128k).
 constexpr int64_t kSingleGroupMax = 24576;
+constexpr int kMaxChunks = static_cast<int>((kSingleGroupMax + kChunk - 1) / kChunk);   // 2
 
 // Monotone 32-bit key of a float32 score.
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -74,6 +75,8 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* t
   return wave_base + inc - x;
 }
 
+// NC: chunks of kChunk rows held in registers (n <= NC * kChunk).
+template <int NC>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ scores,
                                                                int n, int db, int de, int k,
                                                                int m_total,
@@ -88,6 +91,18 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   uint32_t* my_hist = hist[(tid >> 6) % kCopies];
   uint32_t thresh;   // keys > thresh are kept
   uint32_t ties;     // number of keys == thresh kept, lowest index first
+
+  // Every score this thread handles is read once, as its key: row
+  // kChunk * c + kThreads * r + tid (the output pass's layout, so wave-wide
+  // loads are contiguous); rows past n read as zeros and are never used.
+  uint32_t key[NC][kPerThread];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int r = 0; r < kPerThread; ++r)
+      key[c][r] = score_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rs, static_cast<int>((kChunk * c + kThreads * r + tid) * 4), 0, 0)));
+  }
 
   if (k <= 0) {
     thresh = 0xFFFFFFFFu;  // no key exceeds it and none equals it (max key is +inf's)
@@ -105,14 +120,13 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       const uint32_t dmask = (1u << widths[pass]) - 1u;
       for (int b = tid; b < kCopies * kBins; b += kThreads) (&hist[0][0])[b] = 0;
       __syncthreads();
-#pragma unroll 4
-      for (int j = (db & ~3) + 4 * tid; j < de; j += 4 * kThreads) {
-        const u32x4 x = bload16(rs, static_cast<uint32_t>(j) * 4u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = score_key(__uint_as_float(x[e]));
-          if (j + e >= db && j + e < de && (key & pmask) == prefix)
-            atomicAdd(&my_hist[(key >> shift) & dmask], 1u);
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int r = 0; r < kPerThread; ++r) {
+          const int i = kChunk * c + kThreads * r + tid;
+          if (i >= db && i < de && (key[c][r] & pmask) == prefix)
+            atomicAdd(&my_hist[(key[c][r] >> shift) & dmask], 1u);
         }
       }
       __syncthreads();
@@ -153,16 +167,10 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   __shared__ uint32_t cnt[kPerThread * kWaves];   // packed: sure | eq << 16
   const int lane = tid & 63, wave = tid >> 6;
   uint32_t out_base = 0, eq_base = 0;
-  uint32_t cur[kPerThread];
 #pragma unroll
-  for (int r = 0; r < kPerThread; ++r)
-    cur[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>((kThreads * r + tid) * 4), 0, 0);
-  for (int c0 = 0; c0 < n; c0 += kChunk) {
-    uint32_t nxt[kPerThread];
-#pragma unroll
-    for (int r = 0; r < kPerThread; ++r)   // zeros past n
-      nxt[r] = __builtin_amdgcn_raw_buffer_load_b32(
-          rs, static_cast<int>(static_cast<uint32_t>(c0 + kChunk + kThreads * r + tid) * 4u), 0, 0);
+  for (int ci = 0; ci < NC; ++ci) {
+    const int c0 = kChunk * ci;
+    if (c0 >= n) break;   // uniform
     uint64_t b_sure[kPerThread], b_eq[kPerThread];
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
@@ -172,9 +180,8 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
         if (i < db || i >= de) {
           sure = true;
         } else {
-          const uint32_t key = score_key(__uint_as_float(cur[r]));
-          sure = key > thresh;
-          eq = key == thresh;
+          sure = key[ci][r] > thresh;
+          eq = key[ci][r] == thresh;
         }
       }
       b_sure[r] = __ballot(sure);
@@ -225,7 +232,6 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       // from ever writing past the caller's buffer.
       if ((is_sure || (is_eq && eq_pre < ties_left_chunk)) && pos < static_cast<uint32_t>(m_total))
         out[pos] = c0 + kThreads * r + tid;
-      cur[r] = nxt[r];
     }
     const uint32_t taken_chunk = eq_tot < ties_left_chunk ? eq_tot : ties_left_chunk;
     out_base += sure_tot + taken_chunk;
@@ -504,8 +510,12 @@ hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin,
   const int m_total = static_cast<int>(k + (n - n_doc));
   const int ni = static_cast<int>(n), db = static_cast<int>(doc_begin), de = static_cast<int>(doc_end);
   if (n <= kSingleGroupMax) {
-    hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, stream, scores, ni, db, de,
-                       k, m_total, kept_idx);
+    if (n <= kChunk)
+      hipLaunchKernelGGL(topk_select_kernel<1>, dim3(1), dim3(kThreads), 0, stream, scores, ni, db,
+                         de, k, m_total, kept_idx);
+    else
+      hipLaunchKernelGGL(topk_select_kernel<kMaxChunks>, dim3(1), dim3(kThreads), 0, stream, scores,
+                         ni, db, de, k, m_total, kept_idx);
     return hipGetLastError();
   }
   uint32_t* ws = static_cast<uint32_t*>(workspace);

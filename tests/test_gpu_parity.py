@@ -111,6 +111,8 @@ def test_topk_special_values_and_ties(seed):
 @pytest.mark.parametrize("n,db,de,k", [(131072, 0, 130816, 8192), (131072, 1000, 130000, 8192),
                                        (65536, 0, 65280, 1024), (65536, 0, 65280, 16384),
                                        (16384, 0, 16128, 2048), (70001, 3, 69999, 33333),
+                                       (16385, 1, 16384, 8000), (24576, 0, 24320, 4096),
+                                       (20000, 100, 19900, 1),
                                        (2 * 1024 * 2048 + 4099, 517, 2 * 1024 * 2048, 300007)])
 def test_topk_large_quantised(n, db, de, k):
     rng = np.random.default_rng(n + k)
@@ -136,6 +138,18 @@ def test_topk_long_special_values_and_shared_workspace():
             out = tg.topk_select(sd, db, de, k, workspace=ws)
             torch.cuda.synchronize()
             assert np.array_equal(out.cpu().numpy(), O.topk_select(s32, db, de, k)), (n, db, de, k)
+
+
+def test_topk_special_values_two_register_chunks():
+    # One work-group holding two 16384-row chunks of keys (16384 < n <= 24576).
+    rng = np.random.default_rng(11)
+    pool = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, 1e-45, -1e-45, 0.5, -2.0, 3.0],
+                    dtype=np.float32)
+    s32 = rng.choice(pool, size=24000).astype(np.float32)
+    for db, de in ((0, 24000), (16000, 17000), (300, 23999)):
+        for k in (0, 1, 2399, 2400, de - db - 1, de - db):
+            assert np.array_equal(_topk_gpu(s32, db, de, k), O.topk_select(s32, db, de, k)), \
+                (db, de, k)
 
 
 def test_topk_all_equal():
