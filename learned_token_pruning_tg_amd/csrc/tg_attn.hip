@@ -39,9 +39,12 @@
 //      * The softmax runs on fp32 logits in log2 units: the logit scale is
 //        folded into the exponent's FMA, and the row sum adds the fp16 P
 //        values that the P.V product uses (v_dot2_f32_f16 against (1, 1)).
-//      * Software-pipelined steps: step t issues the QK MFMAs of tile t + 1
-//        before the exponentials of tile t (independent work for the MFMA
-//        pipe while the VALU runs the softmax).
+//      * Software-pipelined steps: step t runs the QK MFMAs of tile t + 1
+//        with the exponentials of tile t placed between them, half after
+//        the k-steps of the QK product and half after the first P.V
+//        MFMAs, in an order fixed in the source (independent work for the
+//        MFMA pipe while the VALU runs the softmax, within one wave as well
+//        as across the two work-groups of a CU).
 //      * Tiles arrive by buffer-to-LDS DMA (buffer_load_dwordx4 ... lds): K
 //        straight from k (and the tile's bias values), two tiles ahead, V^T
 //        images one tile ahead, each in its own double-buffered LDS ring; no
@@ -525,12 +528,11 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
   };
 
   // ---- online softmax of one set's tile, in two parts so that the next
-  // tile's QK MFMAs can go between them: (1) causal mask (compile-time MASK,
-  // diagonal tile only) and running max, raising it lazily (only when a tile
-  // exceeds it by more than 2^8, which also rescales O and l); (2) P =
-  // exp2(S * alpha - m) as fp16 pairs [32-key half][pair], the logit scale
-  // folded into the exponent's FMA.  The row sum adds the fp16 P values that
-  // the P.V product uses (v_dot2_f32_f16 against (1, 1)).
+  // tile's QK MFMAs can go between them: (1) here, causal mask (compile-time
+  // MASK, diagonal tile only) and running max, raising it lazily (only when a
+  // tile exceeds it by more than 2^8, which also rescales O and l); (2) in
+  // the step below, P = exp2(S * alpha - m) as fp16 pairs [32-key
+  // half][pair], the logit scale folded into the exponent's FMA.
   auto softmax_max = [&](auto mask_c, int r, floatx16 (&s)[2], int kb)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
@@ -565,60 +567,86 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
       }
     }
   };
-  auto softmax_exp = [&](int r, floatx16 (&s)[2], uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
-    const float nm = -m_run[r];
-    const f16x2 ones = {static_cast<__fp16>(1.f), static_cast<__fp16>(1.f)};
-    float rs = 0.f;
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[t2][j], alpha, nm));
-        const float p1 = fast_exp2(__builtin_fmaf(s[t2][j + 1], alpha, nm));
-        const f16x2 h = __builtin_amdgcn_cvt_pkrtz(p0, p1);
-        rs = __builtin_amdgcn_fdot2(h, ones, rs, false);
-        pk[t2][j >> 1] = __builtin_bit_cast(uint32_t, h);
-      }
-    }
-    l_run[r] += rs;
-  };
-
-  // ---- O^T += V^T P^T for every set: each V^T fragment read feeds kSets MFMAs
-  auto pv = [&](const char* vimg, uint32_t (&pk)[kSets][2][8]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
-      f16x8 b[kSets];
-#pragma unroll
-      for (int r = 0; r < kSets; ++r) {
-        const uint32_t* src = &pk[r][ps >> 1][4 * (ps & 1)];
-        const u32x4 pv4 = {src[0], src[1], src[2], src[3]};
-        b[r] = __builtin_bit_cast(f16x8, pv4);
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(
-            vimg + (32 * dt + l32) * T::V_ROW + (16 * ps + 8 * hh) * 2);
-#pragma unroll
-        for (int r = 0; r < kSets; ++r) o[r][dt] = mfma_f16(a, b[r], o[r][dt]);
-      }
-    }
-  };
-
-  // ---- one pipelined step: S(t+1) = K~(t+1) Q~^T goes to the MFMA pipe
-  // first (it does not depend on this tile's softmax), then softmax(S(t)) and
-  // O += V(t) P(t).  sc holds S(t), sn receives S(t+1); past the last tile
-  // the extra QK reads stale LDS and its result is never used.
+  // ---- one pipelined step, written out in issue order (sched_barrier fences
+  // keep the compiler from regrouping it): S(t+1) = K~(t+1) Q~^T, one k-step
+  // at a time with the next k-step's K fragments already in flight, each
+  // k-step followed by exponentials of S(t)'s first 32 keys; then O += V(t)
+  // P(t), 32 dims of V^T per fragment read, the first two of its four 16-key
+  // steps followed by the exponentials of the last 32 keys (which the last two
+  // steps consume).  The row sum adds the fp16 P values that the P.V product
+  // uses (v_dot2_f32_f16 against (1, 1)), in key order.  sc holds S(t), sn
+  // receives S(t+1); past the last tile the extra QK reads stale LDS and its
+  // result is never used.
   auto step = [&](auto mask_c, floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2], int t, int j)
       __attribute__((always_inline)) {
+    static_assert(kSets == 1, "the interleaved step is written for one query set");
+    softmax_max(mask_c, 0, sc[0], t * kBN);
+    const char* kimg = &lds_k[(j + 1) & 1][0];
+    const char* simg = &lds_s[(j + 1) & 1][0];
+    const char* vimg = &lds_v[j & 1][0];
 #pragma unroll
-    for (int r = 0; r < kSets; ++r) softmax_max(mask_c, r, sc[r], t * kBN);
-    // one basic block from here: the QK MFMAs of the next tile interleave
-    // with this tile's exponentials, then the P.V MFMAs with the V^T reads
-    qk(&lds_k[(j + 1) & 1][0], &lds_s[(j + 1) & 1][0], sn);
-    uint32_t pk[kSets][2][8];
+    for (int t2 = 0; t2 < 2; ++t2) {
+      if (kBias) {
 #pragma unroll
-    for (int r = 0; r < kSets; ++r) softmax_exp(r, sc[r], pk[r]);
-    pv(&lds_v[j & 1][0], pk);
+        for (int jg = 0; jg < 4; ++jg) {
+          const float4 b = *reinterpret_cast<const float4*>(simg + 4 * (32 * t2 + 8 * jg + 4 * hh));
+          sn[0][t2][4 * jg] = b.x; sn[0][t2][4 * jg + 1] = b.y;
+          sn[0][t2][4 * jg + 2] = b.z; sn[0][t2][4 * jg + 3] = b.w;
+        }
+      } else {
+        sn[0][t2] = zero16();
+      }
+    }
+    const float nm = -m_run[0];
+    const f16x2 ones = {static_cast<__fp16>(1.f), static_cast<__fp16>(1.f)};
+    float rs = 0.f;
+    uint32_t pk[2][8];
+    auto exp_pair = [&](int t2, int jj) __attribute__((always_inline)) {
+      const float p0 = fast_exp2(__builtin_fmaf(sc[0][t2][jj], alpha, nm));
+      const float p1 = fast_exp2(__builtin_fmaf(sc[0][t2][jj + 1], alpha, nm));
+      const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+      rs = __builtin_amdgcn_fdot2(hv, ones, rs, false);
+      pk[t2][jj >> 1] = __builtin_bit_cast(uint32_t, hv);
+    };
+    bf16x8 ka[2][2];
+    auto kread = [&](int ks, bf16x8 (&dst)[2]) __attribute__((always_inline)) {
+      const uint32_t off = k_base ^ static_cast<uint32_t>(32 * ks);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+        dst[t2] = *reinterpret_cast<const bf16x8*>(kimg + off + 32 * t2 * T::K_ROW);
+    };
+    f16x8 va[2][DT];
+    auto vread = [&](int ps, f16x8 (&dst)[DT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dst[dt] = *reinterpret_cast<const f16x8*>(vimg + (32 * dt + l32) * T::V_ROW + (16 * ps + 8 * hh) * 2);
+    };
+    kread(0, ka[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) kread(ks + 1, ka[(ks + 1) & 1]);
+      else vread(0, va[0]);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) sn[0][t2] = mfma_32x32x16(ka[ks & 1][t2], qf[0][ks], sn[0][t2]);
+#pragma unroll
+      for (int e = 0; e < 8 / KS; ++e) exp_pair(0, 2 * ((8 / KS) * ks + e));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+      if (ps + 1 < 4) vread(ps + 1, va[(ps + 1) & 1]);
+      const uint32_t* src = &pk[ps >> 1][4 * (ps & 1)];
+      const u32x4 pv4 = {src[0], src[1], src[2], src[3]};
+      const f16x8 b = __builtin_bit_cast(f16x8, pv4);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[0][dt] = mfma_f16(va[ps & 1][dt], b, o[0][dt]);
+      if (ps < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) exp_pair(1, 8 * ps + 2 * e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run[0] += rs;
   };
 
   // ---- main loop, one barrier per tile.  At the barrier of step j the DMA of
