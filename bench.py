@@ -553,6 +553,22 @@ def cpu_baseline(w, g, gain, tau, budget_s):
         if (time.perf_counter() - t0) + np.mean(layer_t) > budget_s or len(layer_t) >= w.n_layers:
             break
     step_s = (t1 - t0) + (t2 - t1) + (t3 - t2) + w.n_layers * float(np.mean(layer_t))
+    # The unpruned baseline on the CPU, row-sampled: 256 query rows of full-N
+    # causal attention (the first and last rows, both sides of the
+    # document/question boundary, the rest drawn with the workload's seed) for
+    # two layers (two q/k/v templates).  Reported as measured seconds for those
+    # rows, not scaled to a whole layer.
+    rng = np.random.default_rng(w.seed)
+    fixed = np.unique([0, w.n - 1, max(w.doc_end - 1, 0), min(w.doc_end, w.n - 1)])
+    others = np.setdiff1d(np.arange(w.n), fixed)
+    rest = rng.choice(others, size=min(256 - fixed.size, others.size), replace=False)
+    rows = np.union1d(fixed, rest)
+    full_t = []
+    for t in range(2):
+        qf, kf, vf = (q, k, v) if t == 0 else inputs.qkv_template(w, t)
+        a = time.perf_counter()
+        O.full_attention(qf, kf, vf, rows=rows)
+        full_t.append(time.perf_counter() - a)
     return {
         "value": round(w.n / step_s, 2),
         "unit": "tokens/s",
@@ -562,6 +578,10 @@ def cpu_baseline(w, g, gain, tau, budget_s):
                    f"({t1 - t0:.2f} s), top-K ({t2 - t1:.3f} s), compaction ({t3 - t2:.3f} s), "
                    f"{len(layer_t)} of {w.n_layers} gated-attention layers measured "
                    f"(mean {np.mean(layer_t):.2f} s/layer, scaled to {w.n_layers})"),
+        "full_n_sample": {"rows_per_layer": int(rows.size), "layers": 2,
+                          "seconds": [round(x, 3) for x in full_t],
+                          "note": "full-N causal attention oracle on sampled query rows; "
+                                  "seconds for those rows, not extrapolated"},
         "seconds_measured": round(time.perf_counter() - t0, 2),
         "cpu_model": cpu_model(),
         "blas": blas_name(),
