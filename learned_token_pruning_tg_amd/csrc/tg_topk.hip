@@ -14,12 +14,12 @@
 // and deterministic by construction on both paths below.
 //  * Short inputs: one 1024-thread work-group does all of it (no global
 //    atomics, no inter-block ordering).  Every score is read once, into
-//    registers as its key (up to 2 x 16 rows per thread, laid out so that
-//    wave-wide loads and output stores are contiguous; buffer loads past n
-//    return zeros and are ignored), and the three digit passes and the
-//    ordered output pass work from those registers; each pair of waves counts
-//    into its own copy of the histogram (scores bunch into a few top digits,
-//    so one shared histogram serialises on LDS atomics).
+//    registers as its key (16 rows per thread, laid out so that wave-wide
+//    loads and output stores are contiguous; buffer loads past n return zeros
+//    and are ignored), and the three digit passes and the ordered output pass
+//    work from those registers; each pair of waves counts into its own copy
+//    of the histogram (scores bunch into a few top digits, so one shared
+//    histogram serialises on LDS atomics).
 //  * Long inputs: the same passes spread over up to 1024 work-groups with
 //    global histograms and per-range counts in the caller's workspace (see
 //    the multi-work-group section).
@@ -33,13 +33,12 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kCopies = 8;                         // histogram copies (two waves each)
-constexpr int kPerThread = 16;                     // rows per thread per output chunk
-constexpr int kChunk = kThreads * kPerThread;      // block counts stay below 2^16
-// Rows up to which one work-group does it all: below this the multi-group
-// path's six dependent launches cost more than they save (measured: 20 vs
-// 23 us at 16k rows, 33 vs 23 us at 32k, 108 vs 24 us at 128k).
-constexpr int64_t kSingleGroupMax = 24576;
-constexpr int kMaxChunks = static_cast<int>((kSingleGroupMax + kChunk - 1) / kChunk);   // 2
+constexpr int kPerThread = 16;                     // rows per thread
+// Rows up to which one work-group does it all (each thread holding 16 keys):
+// up to here the multi-group path's six dependent launches cost more than
+// they save, above it less (measured: 16.8 vs 21 us at 16384 rows; 25.6 vs
+// 21.9 us at 16400, 26.9 vs 22.6 us at 24576, 108 vs 24 us at 128k).
+constexpr int64_t kSingleGroupMax = static_cast<int64_t>(kThreads) * kPerThread;   // 16384
 
 // Monotone 32-bit key of a float32 score.
 __device__ __forceinline__ uint32_t score_key(float x) {
@@ -75,8 +74,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* t
   return wave_base + inc - x;
 }
 
-// NC: chunks of kChunk rows held in registers (n <= NC * kChunk).
-template <int NC>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ scores,
                                                                int n, int db, int de, int k,
                                                                int m_total,
@@ -93,16 +90,13 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
   uint32_t ties;     // number of keys == thresh kept, lowest index first
 
   // Every score this thread handles is read once, as its key: row
-  // kChunk * c + kThreads * r + tid (the output pass's layout, so wave-wide
-  // loads are contiguous); rows past n read as zeros and are never used.
-  uint32_t key[NC][kPerThread];
+  // kThreads * r + tid (the output pass's layout, so wave-wide loads are
+  // contiguous); rows past n read as zeros and are never used.
+  uint32_t key[kPerThread];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-#pragma unroll
-    for (int r = 0; r < kPerThread; ++r)
-      key[c][r] = score_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-          rs, static_cast<int>((kChunk * c + kThreads * r + tid) * 4), 0, 0)));
-  }
+  for (int r = 0; r < kPerThread; ++r)
+    key[r] = score_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        rs, static_cast<int>((kThreads * r + tid) * 4), 0, 0)));
 
   if (k <= 0) {
     thresh = 0xFFFFFFFFu;  // no key exceeds it and none equals it (max key is +inf's)
@@ -121,13 +115,10 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
       for (int b = tid; b < kCopies * kBins; b += kThreads) (&hist[0][0])[b] = 0;
       __syncthreads();
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-#pragma unroll
-        for (int r = 0; r < kPerThread; ++r) {
-          const int i = kChunk * c + kThreads * r + tid;
-          if (i >= db && i < de && (key[c][r] & pmask) == prefix)
-            atomicAdd(&my_hist[(key[c][r] >> shift) & dmask], 1u);
-        }
+      for (int r = 0; r < kPerThread; ++r) {
+        const int i = kThreads * r + tid;
+        if (i >= db && i < de && (key[r] & pmask) == prefix)
+          atomicAdd(&my_hist[(key[r] >> shift) & dmask], 1u);
       }
       __syncthreads();
       // Thread t owns bins (2047 - 2t) and (2046 - 2t): thread order is
@@ -158,85 +149,69 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     ties = remaining;
   }
 
-  // Ordered output over all rows, in chunks of kChunk rows: thread t takes
-  // rows c0 + kThreads * r + t (r < kPerThread), so every wave-wide load and
-  // store touches consecutive rows / positions.  Per (r, wave): ballots of
-  // the rows kept for sure and of the document rows equal to the threshold;
-  // their counts are scanned in row order (r-major, wave-minor) by one wave,
-  // and a lane's position adds the set bits of the ballots below it.
+  // Ordered output over all rows: thread t holds rows kThreads * r + t
+  // (r < kPerThread), so every wave-wide store touches consecutive
+  // positions.  Per (r, wave): ballots of the rows kept for sure and of the
+  // document rows equal to the threshold; their counts (below 2^16 each) are
+  // scanned in row order (r-major, wave-minor) by one wave, and a lane's
+  // position adds the set bits of the ballots below it.
   __shared__ uint32_t cnt[kPerThread * kWaves];   // packed: sure | eq << 16
   const int lane = tid & 63, wave = tid >> 6;
-  uint32_t out_base = 0, eq_base = 0;
+  uint64_t b_sure[kPerThread], b_eq[kPerThread];
 #pragma unroll
-  for (int ci = 0; ci < NC; ++ci) {
-    const int c0 = kChunk * ci;
-    if (c0 >= n) break;   // uniform
-    uint64_t b_sure[kPerThread], b_eq[kPerThread];
-#pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-      const int i = c0 + kThreads * r + tid;
-      bool sure = false, eq = false;
-      if (i < n) {
-        if (i < db || i >= de) {
-          sure = true;
-        } else {
-          sure = key[ci][r] > thresh;
-          eq = key[ci][r] == thresh;
-        }
+  for (int r = 0; r < kPerThread; ++r) {
+    const int i = kThreads * r + tid;
+    bool sure = false, eq = false;
+    if (i < n) {
+      if (i < db || i >= de) {
+        sure = true;
+      } else {
+        sure = key[r] > thresh;
+        eq = key[r] == thresh;
       }
-      b_sure[r] = __ballot(sure);
-      b_eq[r] = __ballot(eq);
-      if (lane == 0)
-        cnt[r * kWaves + wave] = static_cast<uint32_t>(__popcll(b_sure[r])) |
-                                 (static_cast<uint32_t>(__popcll(b_eq[r])) << 16);
     }
-    __syncthreads();
-    uint32_t tot = 0;
-    if (wave == 0) {
-      // exclusive scan of the kPerThread * kWaves packed counts, 4 per lane
-      constexpr int PL = kPerThread * kWaves / 64;
-      uint32_t v[PL], run = 0;
+    b_sure[r] = __ballot(sure);
+    b_eq[r] = __ballot(eq);
+    if (lane == 0)
+      cnt[r * kWaves + wave] = static_cast<uint32_t>(__popcll(b_sure[r])) |
+                               (static_cast<uint32_t>(__popcll(b_eq[r])) << 16);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scan of the kPerThread * kWaves packed counts, 4 per lane
+    constexpr int PL = kPerThread * kWaves / 64;
+    uint32_t v[PL], run = 0;
 #pragma unroll
-      for (int e = 0; e < PL; ++e) {
-        v[e] = cnt[lane * PL + e];
-        run += v[e];
-      }
-      uint32_t inc = run;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-      }
-      uint32_t pre = inc - run;
-#pragma unroll
-      for (int e = 0; e < PL; ++e) {
-        cnt[lane * PL + e] = pre;
-        pre += v[e];
-      }
-      if (lane == 63) scan_tmp[0] = inc;
+    for (int e = 0; e < PL; ++e) {
+      v[e] = cnt[lane * PL + e];
+      run += v[e];
     }
-    __syncthreads();
-    tot = scan_tmp[0];
-    const uint32_t sure_tot = tot & 0xFFFFu, eq_tot = tot >> 16;
-    // ties still available when this chunk starts
-    const uint32_t ties_left_chunk = ties > eq_base ? ties - eq_base : 0u;
+    uint32_t inc = run;
 #pragma unroll
-    for (int r = 0; r < kPerThread; ++r) {
-      const uint32_t base = cnt[r * kWaves + wave];
-      const uint64_t below = (1ull << lane) - 1ull;
-      const uint32_t sure_pre = (base & 0xFFFFu) + static_cast<uint32_t>(__popcll(b_sure[r] & below));
-      const uint32_t eq_pre = (base >> 16) + static_cast<uint32_t>(__popcll(b_eq[r] & below));
-      const bool is_sure = (b_sure[r] >> lane) & 1ull, is_eq = (b_eq[r] >> lane) & 1ull;
-      const uint32_t pos = out_base + sure_pre + (eq_pre < ties_left_chunk ? eq_pre : ties_left_chunk);
-      // pos < m_total holds by construction; the guard keeps a logic error
-      // from ever writing past the caller's buffer.
-      if ((is_sure || (is_eq && eq_pre < ties_left_chunk)) && pos < static_cast<uint32_t>(m_total))
-        out[pos] = c0 + kThreads * r + tid;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
     }
-    const uint32_t taken_chunk = eq_tot < ties_left_chunk ? eq_tot : ties_left_chunk;
-    out_base += sure_tot + taken_chunk;
-    eq_base += eq_tot;
-    __syncthreads();   // cnt and scan_tmp are rewritten by the next chunk
+    uint32_t pre = inc - run;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) {
+      cnt[lane * PL + e] = pre;
+      pre += v[e];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kPerThread; ++r) {
+    const uint32_t base = cnt[r * kWaves + wave];
+    const uint64_t below = (1ull << lane) - 1ull;
+    const uint32_t sure_pre = (base & 0xFFFFu) + static_cast<uint32_t>(__popcll(b_sure[r] & below));
+    const uint32_t eq_pre = (base >> 16) + static_cast<uint32_t>(__popcll(b_eq[r] & below));
+    const bool is_sure = (b_sure[r] >> lane) & 1ull, is_eq = (b_eq[r] >> lane) & 1ull;
+    const uint32_t pos = sure_pre + (eq_pre < ties ? eq_pre : ties);
+    // pos < m_total holds by construction; the guard keeps a logic error
+    // from ever writing past the caller's buffer.
+    if ((is_sure || (is_eq && eq_pre < ties)) && pos < static_cast<uint32_t>(m_total))
+      out[pos] = kThreads * r + tid;
   }
 }
 
@@ -510,12 +485,8 @@ hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin,
   const int m_total = static_cast<int>(k + (n - n_doc));
   const int ni = static_cast<int>(n), db = static_cast<int>(doc_begin), de = static_cast<int>(doc_end);
   if (n <= kSingleGroupMax) {
-    if (n <= kChunk)
-      hipLaunchKernelGGL(topk_select_kernel<1>, dim3(1), dim3(kThreads), 0, stream, scores, ni, db,
-                         de, k, m_total, kept_idx);
-    else
-      hipLaunchKernelGGL(topk_select_kernel<kMaxChunks>, dim3(1), dim3(kThreads), 0, stream, scores,
-                         ni, db, de, k, m_total, kept_idx);
+    hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, stream, scores, ni, db, de,
+                       k, m_total, kept_idx);
     return hipGetLastError();
   }
   uint32_t* ws = static_cast<uint32_t*>(workspace);

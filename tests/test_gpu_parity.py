@@ -140,8 +140,9 @@ def test_topk_long_special_values_and_shared_workspace():
             assert np.array_equal(out.cpu().numpy(), O.topk_select(s32, db, de, k)), (n, db, de, k)
 
 
-def test_topk_special_values_two_register_chunks():
-    # One work-group holding two 16384-row chunks of keys (16384 < n <= 24576).
+def test_topk_special_values_above_single_group_limit():
+    # Just above the one-work-group limit (16384 rows): the multi-work-group
+    # path with few row ranges, on NaN/inf/signed-zero/tie-heavy scores.
     rng = np.random.default_rng(11)
     pool = np.array([np.nan, -np.inf, np.inf, -0.0, 0.0, 1e-45, -1e-45, 0.5, -2.0, 3.0],
                     dtype=np.float32)
