@@ -318,9 +318,11 @@ def test_tiny_workload_chain_all_layers():
 
 # --------------------------------------------------------------------------- full-size chains
 
-def _chain(w, layers, n_rows=48, full_rows=32):
-    """Gate -> top-K -> compaction -> gated attention at full size, checked on
-    sampled rows (gate, attention) and in full (indices, compacted bytes)."""
+def _chain(w, layers, n_rows=None, full_rows=32):
+    """Gate -> top-K -> compaction -> gated attention at full size, checked in
+    full (indices, compacted bytes; every gated-attention output and LSE when
+    n_rows is None) or on sampled rows (gate scores; attention when n_rows is
+    given; the full-N baseline)."""
     rng = np.random.default_rng(w.seed)
     g = inputs.gate_inputs(w)
     gain, tau = inputs.layer_params(w)
@@ -350,7 +352,11 @@ def _chain(w, layers, n_rows=48, full_rows=32):
         out, lse = tg.gated_attn_fwd(qk, kk, vk, s_kept, dev_f32(gain[li]), dev_f32(tau[li]),
                                      want_lse=True)
         torch.cuda.synchronize()
-        r = _sample_rows(w.kept, rng, extra=(kept_doc - 1, kept_doc, kept_doc + 1), n_random=n_rows)
+        if n_rows is None:
+            r = np.arange(w.kept)
+        else:
+            r = _sample_rows(w.kept, rng, extra=(kept_doc - 1, kept_doc, kept_doc + 1),
+                             n_random=n_rows)
         ref, ref_lse = O.gated_attention(q[idx], k[idx], v[idx], s32[idx], gain[li], tau[li],
                                          rows=r, return_lse=True)
         check_attn(host_bf16(out)[r], ref, f"{w.name} layer {li}")
@@ -370,11 +376,11 @@ def test_chain_qwen_16k():
 
 
 def test_chain_qwen_32k():
-    _chain(W["qwen3-1.7b-32k"], layers=[1])
+    _chain(W["qwen3-1.7b-32k"], layers=[0, 26])
 
 
 def test_chain_qwen_128k():
-    _chain(W["qwen3-1.7b-128k"], layers=[2], n_rows=32, full_rows=16)
+    _chain(W["qwen3-1.7b-128k"], layers=[0, 26], full_rows=16)
 
 
 @pytest.mark.parametrize("k_doc", inputs.SWEEP_BUDGETS)
