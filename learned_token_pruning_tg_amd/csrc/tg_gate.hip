@@ -58,10 +58,13 @@ __device__ __forceinline__ float gelu_erf(float z) {
 
 // BM tokens per work-group (BM / 64 row groups x CW column waves); the
 // work-group covers 128 * CT gate units, each wave UT = 4 CT / CW tiles of 32.
-// KC: K chunk (32 or 64).  LDS rows of a 32-wide chunk are padded to 80 B;
-// rows of a 64-wide chunk are 128 B with 16-byte piece j of row r stored at
-// slot j ^ ((r / 2) % 8).  Either way the 16 lanes that one pass of a 16-byte
-// LDS read serves (64 banks of 4 bytes) hit 16 different bank groups.
+// KC: K chunk (32 or 64).  LDS rows are unpadded and XOR-swizzled: rows of a
+// 32-wide chunk are 64 B with 16-byte piece j of row r at slot j ^ ((r / 4)
+// % 4), rows of a 64-wide chunk 128 B with piece j at slot j ^ ((r / 2) % 8).
+// Either way the 16 lanes that one pass of a 16-byte LDS read serves (one
+// piece of 16 consecutive rows; 64 banks of 4 bytes) hit 16 different bank
+// groups, and so do those of a staging write (all pieces of 4 or 2
+// consecutive rows: 256 contiguous bytes).
 template <int BM, int CT, int CW, int KC>
 __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
     const bf16* __restrict__ h, int64_t n, int64_t ld_h, int H, const bf16* __restrict__ w1,
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
   constexpr int UT = 4 * CT / CW;               // 32-unit tiles per wave
   static_assert(KC == 32 || KC == 64, "K chunk");
   constexpr int P = KC / 8;                     // 16-byte pieces per row of a chunk
-  constexpr int LD = KC == 32 ? 40 : 64;        // LDS row, bf16 elements
+  constexpr int LD = KC;                        // LDS row, bf16 elements
   constexpr int W_PIECES = HGP * P;             // 16-byte pieces of a W1 chunk
   constexpr int H_PIECES = BM * P;              // ... of an h chunk
   constexpr int W_PER_T = (W_PIECES + NT - 1) / NT;
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(BM / 64 * CW * 64) void gate_score_kernel(
   __shared__ __align__(16) bf16 w_lds[2][HGP * LD];
   __shared__ __align__(16) bf16 h_lds[2][BM * LD];
   auto lds_at = [](int row, int piece) {
-    return row * LD + 8 * (KC == 64 ? piece ^ ((row >> 1) & 7) : piece);
+    return row * LD + 8 * (KC == 64 ? piece ^ ((row >> 1) & 7) : piece ^ ((row >> 2) & 3));
   };
   __shared__ float red[CW][BM];
 
