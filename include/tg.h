@@ -15,8 +15,8 @@
  *     in the prompt and the caller passes a budget of kept prefill tokens.
  *   - fugumt.com, "論文の概要: TokenGate: Adapting LLMs for Fast and
  *     Memory-Efficient Prefill with Learned Token Pruning", English abstract:
- *     token-gated attention re-weights attention logits with token
- *     importance scores.
+ *     in the layers above the gate, the kept tokens' importance scores act on
+ *     the attention logits.
  *
  * Readings fixed here where the pages are silent:
  *   - logit_ij = q_i.k_j / (sqrt(d) * tau_h) + gain_h * s_j (s_j raw score);
@@ -158,8 +158,8 @@ size_t tg_attn_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads,
  * Token-gated causal GQA attention over the n kept rows (lucasainews.com
  * article, "작동 방식": each kept token's score is added to the attention
  * logits above the gate, scaled by a per-head learned gain, with a per-head
- * temperature; fugumt.com abstract: attention logits re-weighted by token
- * importance scores):
+ * temperature; fugumt.com abstract: the importance scores act on the
+ * attention logits):
  *     logit_ij = q_i,h . k_j,g / (sqrt(head_dim) * tau[h]) + gain[h] * key_score[j]
  *     out_i,h  = sum_{j <= i} softmax_j(logit_i,h) v_j,g,   g = h / (n_q_heads / n_kv_heads)
  * Causality is by row order (kept rows are in original order).
@@ -187,6 +187,21 @@ tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
                             const float* key_score, const float* gain, const float* tau,
                             tg_bf16* out, float* lse, void* workspace, size_t workspace_bytes,
                             tg_stream_t stream);
+
+/*
+ * tg_gated_attn_fwd for a training step (lucasainews.com article, "작동 방식":
+ * the gate is trained through the score bias above it): the same
+ * computation, layouts, limits and workspace, and in addition
+ *   lse     [n_q_heads, n] fp32 (required here)
+ *   out_f32 [n, n_q_heads, head_dim] fp32, 16-byte aligned: the output before
+ *           its bf16 rounding, which tg_gated_attn_bwd takes (output)
+ * NULL lse or out_f32 -> TG_E_INVALID.  n == 0 is a no-op.
+ */
+tg_status tg_gated_attn_fwd_train(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  const float* key_score, const float* gain, const float* tau,
+                                  tg_bf16* out, float* lse, float* out_f32, void* workspace,
+                                  size_t workspace_bytes, tg_stream_t stream);
 
 /*
  * Unpruned causal GQA attention over all n rows, softmax(q.k / sqrt(d)) v:
@@ -225,8 +240,11 @@ size_t tg_attn_bwd_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_he
  *     dv_j = sum_h sum_i P_ij dout_i      dscore_j = sum_h gain[h] sum_i dS_ij
  *     dgain[h] = sum_ij dS_ij key_score[j]
  *     dtau[h]  = -(1 / tau[h]) sum_i q_i.dq_i     (sums over i, j within head h)
- *   q, k, v, key_score, gain, tau  as given to tg_gated_attn_fwd
- *   out   [n, n_q_heads, head_dim] bf16: that call's output
+ *   q, k, v, key_score, gain, tau  as given to tg_gated_attn_fwd_train
+ *   out_f32 [n, n_q_heads, head_dim] fp32: that call's output before rounding
+ *         (D_i = dout_i.out_i is formed from it: from the bf16 output, rows
+ *         with few keys, whose dS terms nearly cancel against D, would lose
+ *         most of their precision)
  *   lse   [n_q_heads, n] fp32: that call's natural-log log-sum-exp
  *   dout  [n, n_q_heads, head_dim] bf16: gradient of the loss w.r.t. out
  *   dq    [n, n_q_heads, head_dim], dk, dv [n, n_kv_heads, head_dim] bf16
@@ -243,7 +261,7 @@ size_t tg_attn_bwd_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_he
 tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                             const float* key_score, const float* gain, const float* tau,
-                            const tg_bf16* out, const float* lse, const tg_bf16* dout,
+                            const float* out_f32, const float* lse, const tg_bf16* dout,
                             tg_bf16* dq, tg_bf16* dk, tg_bf16* dv, float* dscore, float* dgain,
                             float* dtau, void* workspace, size_t workspace_bytes,
                             tg_stream_t stream);

@@ -160,8 +160,25 @@ tg_status tg_gated_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
   if (st != TG_OK || n == 0) return st;
   if (!key_score || !gain || !tau) return fail(TG_E_INVALID, "%s: null key_score/gain/tau", fn);
   return hip_status(tg::launch_attn_fwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, key_score,
-                                        gain, tau, out, lse, workspace, as_hip(stream)),
+                                        gain, tau, out, lse, nullptr, workspace, as_hip(stream)),
                     "tg_gated_attn_fwd launch");
+}
+
+tg_status tg_gated_attn_fwd_train(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
+                                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  const float* key_score, const float* gain, const float* tau,
+                                  tg_bf16* out, float* lse, float* out_f32, void* workspace,
+                                  size_t workspace_bytes, tg_stream_t stream) {
+  const char* fn = "tg_gated_attn_fwd_train";
+  const tg_status st = check_attn(fn, q, k, v, n, n_q_heads, n_kv_heads, head_dim, out,
+                                  workspace, workspace_bytes, true);
+  if (st != TG_OK || n == 0) return st;
+  if (!key_score || !gain || !tau) return fail(TG_E_INVALID, "%s: null key_score/gain/tau", fn);
+  if (!lse || !out_f32) return fail(TG_E_INVALID, "%s: null lse/out_f32", fn);
+  if (!aligned16(out_f32)) return fail(TG_E_INVALID, "%s: out_f32 must be 16-byte aligned", fn);
+  return hip_status(tg::launch_attn_fwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, key_score,
+                                        gain, tau, out, lse, out_f32, workspace, as_hip(stream)),
+                    "tg_gated_attn_fwd_train launch");
 }
 
 tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
@@ -172,7 +189,8 @@ tg_status tg_full_attn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v,
                                   out, workspace, workspace_bytes, false);
   if (st != TG_OK || n == 0) return st;
   return hip_status(tg::launch_attn_fwd(q, k, v, n, n_q_heads, n_kv_heads, head_dim, nullptr,
-                                        nullptr, nullptr, out, lse, workspace, as_hip(stream)),
+                                        nullptr, nullptr, out, lse, nullptr, workspace,
+                                        as_hip(stream)),
                     "tg_full_attn_fwd launch");
 }
 
@@ -187,11 +205,12 @@ size_t tg_attn_bwd_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_he
 tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, int64_t n,
                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                             const float* key_score, const float* gain, const float* tau,
-                            const tg_bf16* out, const float* lse, const tg_bf16* dout,
+                            const float* out_f32, const float* lse, const tg_bf16* dout,
                             tg_bf16* dq, tg_bf16* dk, tg_bf16* dv, float* dscore, float* dgain,
                             float* dtau, void* workspace, size_t workspace_bytes,
                             tg_stream_t stream) {
   const char* fn = "tg_gated_attn_bwd";
+  const float* out = out_f32;
   if (n < 0 || n >= (int64_t(1) << 31)) return fail(TG_E_INVALID, "%s: n=%lld out of range", fn, (long long)n);
   if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0)
     return fail(TG_E_INVALID, "%s: n_q_heads=%d, n_kv_heads=%d", fn, n_q_heads, n_kv_heads);
@@ -207,7 +226,7 @@ tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
     return fail(TG_E_INVALID, "%s: null key_score/gain/tau/lse/dscore/dgain/dtau", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return fail(TG_E_INVALID, "%s: q/k/v/out/dout/dq/dk/dv must be 16-byte aligned", fn);
+    return fail(TG_E_INVALID, "%s: q/k/v/out_f32/dout/dq/dk/dv must be 16-byte aligned", fn);
   const size_t need = tg::attn_bwd_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(TG_E_WORKSPACE, "%s: workspace %p of %zu bytes (need %zu, 16-byte aligned)", fn,

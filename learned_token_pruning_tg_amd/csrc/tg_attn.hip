@@ -310,22 +310,29 @@ __device__ __forceinline__ int64_t split_slot0(int head, int qt, int h, int unit
 }
 
 // Normalise O^T (lane = query column my_q, registers = its D/2 dims of this
-// lane half) and write the bf16 output row slice and the natural-log LSE.
+// lane half) and write the bf16 output row slice, the natural-log LSE and,
+// for a training forward, the fp32 output before rounding (out32).
 template <int D>
 __device__ __forceinline__ void store_out(const floatx16 (&o)[D / 32], float m, float l, int my_q,
                                           int M, int Hq, int head, int hh, bf16* __restrict__ out,
-                                          float* __restrict__ lse) {
+                                          float* __restrict__ lse, float* __restrict__ out32) {
   if (my_q >= M) return;
   const float inv = 1.f / l;
-  bf16* orow = out + static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
+  const size_t row = static_cast<size_t>(my_q) * Hq * D + static_cast<size_t>(head) * D;
+  bf16* orow = out + row;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       bf16 pkk[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pkk[r] = static_cast<bf16>(o[dt][4 * jj + r] * inv);
+      float4 f;
+      f.x = o[dt][4 * jj] * inv; f.y = o[dt][4 * jj + 1] * inv;
+      f.z = o[dt][4 * jj + 2] * inv; f.w = o[dt][4 * jj + 3] * inv;
+      pkk[0] = static_cast<bf16>(f.x); pkk[1] = static_cast<bf16>(f.y);
+      pkk[2] = static_cast<bf16>(f.z); pkk[3] = static_cast<bf16>(f.w);
       *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * jj + 4 * hh) = __builtin_bit_cast(uint2, pkk);
+      if (out32 != nullptr)
+        *reinterpret_cast<float4*>(out32 + row + 32 * dt + 8 * jj + 4 * hh) = f;
     }
   }
   if (lse != nullptr && hh == 0)
@@ -339,8 +346,8 @@ template <int D, bool kBias>
 __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const char* __restrict__ ws,
     const char* __restrict__ bias_frag, int M, int Hq, int Hkv, const float* __restrict__ gain,
-    const float* __restrict__ tau, bf16* __restrict__ out, float* __restrict__ lse, int h,
-    int units, char* __restrict__ part) {
+    const float* __restrict__ tau, bf16* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ out32, int h, int units, char* __restrict__ part) {
   using T = Tile<D, kBias>;
   constexpr int KS = T::KS;
   constexpr int DT = D / 32;                 // 32-row tiles of O^T
@@ -696,7 +703,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
       __builtin_nontemporal_store(m, reinterpret_cast<float*>(pw + T::PART_O + lane * 8));
       __builtin_nontemporal_store(l, reinterpret_cast<float*>(pw + T::PART_O + lane * 8 + 4));
     } else {
-      store_out<D>(o[r], m, l, my_q[r], M, Hq, head, hh, out, lse);
+      store_out<D>(o[r], m, l, my_q[r], M, Hq, head, hh, out, lse, out32);
     }
   }
 }
@@ -711,7 +718,8 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const char* __restrict__ part, int M,
                                                         int Hq, int h, int units, int n_split,
                                                         bf16* __restrict__ out,
-                                                        float* __restrict__ lse) {
+                                                        float* __restrict__ lse,
+                                                        float* __restrict__ out32) {
   using T = Tile<D, false>;   // partial layout does not depend on the bias
   constexpr int DT = D / 32;
   constexpr int NV = DT * 2;
@@ -775,14 +783,14 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const char* __restrict__
         }
       }
     }
-    store_out<D>(o, m, l, my_q, M, Hq, head, hh, out, lse);
+    store_out<D>(o, m, l, my_q, M, Hq, head, hh, out, lse, out32);
   }
 }
 
 template <int D, bool kBias>
 hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M, int Hq, int Hkv,
                   const float* s, const float* g, const float* t, uint16_t* out, float* lse,
-                  void* ws, hipStream_t stream) {
+                  float* out32, void* ws, hipStream_t stream) {
   const Plan p = make_plan<D, kBias>(M, Hq, Hkv);
   char* img = static_cast<char*>(ws);
   char* sc = img + p.sc_off;
@@ -793,13 +801,13 @@ hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M
   const dim3 grid(static_cast<unsigned>(p.units * Hq));
   hipLaunchKernelGGL((attn_fwd_kernel<D, kBias>), grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k), img, sc, M,
-                     Hq, Hkv, g, t, reinterpret_cast<bf16*>(out), lse, p.h,
+                     Hq, Hkv, g, t, reinterpret_cast<bf16*>(out), lse, out32, p.h,
                      static_cast<int>(p.units), part);
   if (p.n_split > 0)
     hipLaunchKernelGGL((attn_merge_kernel<D>),
                        dim3(static_cast<unsigned>(Hq * p.n_split * (kThreads / 64))), dim3(64), 0,
                        stream, part, M, Hq, p.h, static_cast<int>(p.units),
-                       static_cast<int>(p.n_split), reinterpret_cast<bf16*>(out), lse);
+                       static_cast<int>(p.n_split), reinterpret_cast<bf16*>(out), lse, out32);
   return hipGetLastError();
 }
 
@@ -825,19 +833,19 @@ size_t attn_image_bytes_per_kv_head(int64_t n, int head_dim, bool gated) {
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
                            int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
                            const float* gain, const float* tau, uint16_t* out, float* lse,
-                           void* workspace, hipStream_t stream) {
+                           float* out32, void* workspace, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int M = static_cast<int>(n);
   const bool bias = gain != nullptr;
   if (head_dim == 128)
     return bias ? launch<128, true>(q, k, v, M, n_q_heads, n_kv_heads, key_score, gain, tau, out,
-                                    lse, workspace, stream)
+                                    lse, out32, workspace, stream)
                 : launch<128, false>(q, k, v, M, n_q_heads, n_kv_heads, nullptr, nullptr,
-                                     nullptr, out, lse, workspace, stream);
+                                     nullptr, out, lse, out32, workspace, stream);
   return bias ? launch<64, true>(q, k, v, M, n_q_heads, n_kv_heads, key_score, gain, tau, out,
-                                 lse, workspace, stream)
+                                 lse, out32, workspace, stream)
               : launch<64, false>(q, k, v, M, n_q_heads, n_kv_heads, nullptr, nullptr, nullptr,
-                                  out, lse, workspace, stream);
+                                  out, lse, out32, workspace, stream);
 }
 
 }  // namespace tg

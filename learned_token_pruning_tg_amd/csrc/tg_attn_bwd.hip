@@ -186,18 +186,21 @@ __device__ __forceinline__ float add_halves(float x) {
 
 // ---------------------------------------------------------------------------
 // bwd_pack: per (query head, 32-row tile) the rows' -lse / c_h (-inf past n)
-// and -D, D_i = dO_i . O_i by eight lanes per row and a fixed butterfly.
+// and -D, D_i = dO_i . O_i by eight lanes per row and a fixed butterfly.  O is
+// the forward's fp32 output before its bf16 rounding: D then carries the
+// forward's own arithmetic error only (with the rounded output, short rows,
+// whose dS terms nearly cancel against D, lose most of their precision).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pack_kernel(
-    const bf16* __restrict__ out, const float* __restrict__ lse, const bf16* __restrict__ dout,
+    const float* __restrict__ out, const float* __restrict__ lse, const bf16* __restrict__ dout,
     const float* __restrict__ tau, int M, int Hq, int n_t32, float* __restrict__ ld) {
   const int tid = threadIdx.x;
   const int h = blockIdx.x / n_t32, t = blockIdx.x % n_t32;
-  const uint32_t stride = static_cast<uint32_t>(Hq) * D * 2;
+  const uint32_t stride = static_cast<uint32_t>(Hq) * D * 2;      // dout row bytes
   const uint32_t range = stride * static_cast<uint32_t>(M);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + static_cast<size_t>(h) * D, range);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + static_cast<size_t>(h) * D, range);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + static_cast<size_t>(h) * D, 2 * range);
   const size_t tile = static_cast<size_t>(h) * n_t32 + t;
   const uint32_t row0 = static_cast<uint32_t>(t) * kRows;
   const int qi = tid >> 3, part = tid & 7;
@@ -206,11 +209,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pack_kernel(
 #pragma unroll
   for (int c = 0; c < PER / 8; ++c) {
     const uint32_t off = (row0 + qi) * stride + (part * PER + 8 * c) * 2;
-    const u32x4 a = bload16(rd, off), o = bload16(ro, off);
+    const u32x4 a = bload16(rd, off);
+    const u32x4 o0 = bload16(ro, 2 * off), o1 = bload16(ro, 2 * off + 16);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(o[w] << 16), acc);
-      acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(o[w] & 0xFFFF0000u), acc);
+      const u32x4& o = w < 2 ? o0 : o1;
+      acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(o[2 * (w & 1)]), acc);
+      acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(o[2 * (w & 1) + 1]), acc);
     }
   }
   acc += __shfl_xor(acc, 1);
@@ -722,7 +727,7 @@ __global__ __launch_bounds__(kThreads) void bwd_finish_kernel(
 
 template <int D>
 hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int M, int Hq,
-                    int Hkv, const float* s, const float* g, const float* t, const uint16_t* out,
+                    int Hkv, const float* s, const float* g, const float* t, const float* out,
                     const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
                     uint16_t* dv, float* dscore, float* dgain, float* dtau, void* workspace,
                     hipStream_t stream) {
@@ -742,8 +747,7 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   float* qdot = reinterpret_cast<float*>(ws + p.qdot);
   float* dqp = reinterpret_cast<float*>(ws + p.dqp);
   hipLaunchKernelGGL((bwd_pack_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t32)),
-                     dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(out), lse, bd, t, M,
-                     Hq, n_t32, ld);
+                     dim3(kThreads), 0, stream, out, lse, bd, t, M, Hq, n_t32, ld);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.kv.nc)),
                      dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, mp,
                      p.kv.len, p.kv.nc, ld, colsum, dkp, dvp, dgp);
@@ -771,7 +775,7 @@ size_t attn_bwd_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int he
 
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
                            int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
-                           const float* gain, const float* tau, const uint16_t* out,
+                           const float* gain, const float* tau, const float* out,
                            const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
                            uint16_t* dv, float* dscore, float* dgain, float* dtau,
                            void* workspace, hipStream_t stream) {

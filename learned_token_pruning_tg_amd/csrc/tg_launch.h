@@ -30,22 +30,23 @@ size_t attn_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_d
 size_t attn_image_bytes_per_kv_head(int64_t n, int head_dim, bool gated);
 
 // gain == nullptr selects the unbiased (full-prefill) kernel with tau = 1.
+// out32 (nullable) also receives the fp32 output before its bf16 rounding.
 // `workspace` holds attn_workspace_bytes(n, n_q_heads, n_kv_heads, head_dim, gated) bytes.
 hipError_t launch_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
                            int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
                            const float* gain, const float* tau, uint16_t* out, float* lse,
-                           void* workspace, hipStream_t stream);
+                           float* out32, void* workspace, hipStream_t stream);
 
 // Bytes of workspace the attention backward needs: per-row (lse, D), per-head
 // key column sums of dS, fp32 per-head dK and dV partials (per split chunk),
 // per-work-group gain and q.dq sums, fp32 dQ partials when dQ walks split.
 size_t attn_bwd_workspace_bytes(int64_t n, int n_q_heads, int n_kv_heads, int head_dim);
 
-// Gradients of the token-gated attention given its output, its natural-log
-// lse and dout.  `workspace` holds attn_bwd_workspace_bytes(...) bytes.
+// Gradients of the token-gated attention given its fp32 output, its
+// natural-log lse and dout.  `workspace` holds attn_bwd_workspace_bytes(...) bytes.
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t n,
                            int n_q_heads, int n_kv_heads, int head_dim, const float* key_score,
-                           const float* gain, const float* tau, const uint16_t* out,
+                           const float* gain, const float* tau, const float* out,
                            const float* lse, const uint16_t* dout, uint16_t* dq, uint16_t* dk,
                            uint16_t* dv, float* dscore, float* dgain, float* dtau,
                            void* workspace, hipStream_t stream);

@@ -33,6 +33,8 @@ _SIGNATURES = {
     "tg_attn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
     "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                          _P, ctypes.c_size_t, _P]),
+    "tg_gated_attn_fwd_train": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P,
+                                               _P, _P, _P, ctypes.c_size_t, _P]),
     "tg_full_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
                                         ctypes.c_size_t, _P]),
     "tg_attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
@@ -247,6 +249,37 @@ def gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score:
     return (out, lse) if lse is not None else out
 
 
+def gated_attn_fwd_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         key_score: torch.Tensor, gain: torch.Tensor, tau: torch.Tensor,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         out_f32: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """gated_attn_fwd for a training step: also returns lse [Hq, M] and the
+    fp32 output before rounding (what gated_attn_bwd takes).
+    Returns (out, lse, out_f32)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    _need(key_score, "key_score", torch.float32); _need(gain, "gain", torch.float32)
+    _need(tau, "tau", torch.float32)
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (n, hkv, d) or v.shape != k.shape or key_score.shape != (n,) \
+            or gain.shape != (hq,) or tau.shape != (hq,):
+        raise ValueError("attention operand shapes do not match")
+    out, lse = _attn_out(q, out, lse, True)
+    if out_f32 is None:
+        out_f32 = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _need(out_f32, "out_f32", torch.float32)
+    if out_f32.shape != q.shape:
+        raise ValueError("out_f32 must be shaped like q")
+    ws, ws_bytes = _workspace(workspace, n, hq, hkv, d, q.device)
+    _check(lib().tg_gated_attn_fwd_train(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d,
+                                         _ptr(key_score), _ptr(gain), _ptr(tau), _ptr(out),
+                                         _ptr(lse), _ptr(out_f32), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
+    return out, lse, out_f32
+
+
 def full_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                   want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
@@ -276,15 +309,18 @@ def attn_bwd_workspace(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
 
 
 def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score: torch.Tensor,
-                   gain: torch.Tensor, tau: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
-                   dout: torch.Tensor, grads: Optional[dict] = None,
+                   gain: torch.Tensor, tau: torch.Tensor, out_f32: torch.Tensor,
+                   lse: torch.Tensor, dout: torch.Tensor, grads: Optional[dict] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """Gradients of gated_attn_fwd given its out, its lse [Hq, M] and dout.
+    """Gradients of the gated attention given gated_attn_fwd_train's fp32
+    output, its lse [Hq, M] and dout.
     Returns dict(dq, dk, dv (bf16, shaped like q, k, v), dscore [M], dgain [Hq],
     dtau [Hq] (fp32)); ``grads`` may hold preallocated tensors under those names."""
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+    out = out_f32
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, nm, torch.bfloat16)
-    for t, nm in ((key_score, "key_score"), (gain, "gain"), (tau, "tau"), (lse, "lse")):
+    for t, nm in ((key_score, "key_score"), (gain, "gain"), (tau, "tau"), (lse, "lse"),
+                  (out, "out_f32")):
         _need(t, nm, torch.float32)
     n, hq, d = q.shape
     hkv = k.shape[1]

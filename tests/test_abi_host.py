@@ -40,7 +40,7 @@ def test_header_declares_the_five_entry_points():
     for fn in ("tg_gate_score", "tg_topk_select", "tg_topk_workspace_bytes", "tg_compact",
                "tg_gated_attn_fwd", "tg_full_attn_fwd", "tg_attn_workspace_bytes",
                "tg_gated_decode_fwd", "tg_decode_workspace_bytes", "tg_qk_norm_rope",
-               "tg_gated_attn_bwd", "tg_attn_bwd_workspace_bytes",
+               "tg_gated_attn_bwd", "tg_attn_bwd_workspace_bytes", "tg_gated_attn_fwd_train",
                "tg_kept_count", "tg_status_str", "tg_last_error"):
         assert fn in names
 
@@ -159,6 +159,21 @@ def test_attention_validation(L):
     assert L.tg_attn_workspace_bytes(0, 16, 8, 128) == 0
     assert L.tg_attn_workspace_bytes(100, 16, 6, 128) == 0
     assert L.tg_attn_workspace_bytes(100, 16, 8, 96) == 0
+
+
+def test_training_forward_validation(L):
+    t = L.tg_gated_attn_fwd_train
+    W = 1 << 30
+    #        q  k  v  n   hq hkv d    s  g  tau out lse out32 ws wsb
+    assert t(A, A, A, 10, 16, 8, 96, A, A, A, A, A, A, A, W, 0) == UNSUPPORTED
+    assert t(A, A, A, 10, 16, 8, 128, A, A, A, A, None, A, A, W, 0) == INVALID    # lse required
+    assert "lse" in tg.last_error()
+    assert t(A, A, A, 10, 16, 8, 128, A, A, A, A, A, None, A, W, 0) == INVALID    # out_f32 required
+    assert t(A, A, A, 10, 16, 8, 128, A, A, A, A, A, A + 4, A, W, 0) == INVALID   # alignment
+    assert t(A, A, A, 10, 16, 8, 128, None, A, A, A, A, A, A, W, 0) == INVALID    # key_score
+    need = L.tg_attn_workspace_bytes(100, 16, 8, 128)
+    assert t(A, A, A, 100, 16, 8, 128, A, A, A, A, A, A, A, need - 1, 0) == WORKSPACE
+    assert t(None, None, None, 0, 16, 8, 128, None, None, None, None, None, None, None, 0, 0) == OK
 
 
 def _simulated_makespan(n, n_qt, h, hq):
@@ -333,7 +348,7 @@ def test_attn_bwd_workspace_bytes(L, n, hq, hkv, d):
 def test_attn_bwd_validation(L):
     f = L.tg_gated_attn_bwd
     W = 1 << 34
-    P = [A] * 13   # key_score, gain, tau, out, lse, dout, dq, dk, dv, dscore, dgain, dtau
+    P = [A] * 13   # key_score, gain, tau, out_f32, lse, dout, dq, dk, dv, dscore, dgain, dtau
     def call(n=10, hq=16, hkv=8, d=128, q=A, ptrs=None, ws=A, wsb=W):
         p = list(P[:12] if ptrs is None else ptrs)
         return f(q, A, A, n, hq, hkv, d, *p, ws, wsb, 0)

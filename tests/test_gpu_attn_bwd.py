@@ -1,25 +1,26 @@
 """GPU parity of the token-gated attention backward (tg_gated_attn_bwd) against
 the float64 oracle, through the C ABI.
 
-The backward consumes the GPU forward's own output and log-sum-exp, as a
-training step would.  Bars, from the arithmetic: every gradient is a sum of
-products whose operands were rounded to bf16 (relative error <= 2^-9 each: q,
-k, v, dout are bf16 inputs; P and dS enter the dv, dk and dq products as bf16;
-D = dout.out uses the bf16 forward output), accumulated in fp32, and dq, dk,
-dv are rounded to bf16 once more.  With random signs the errors add in
+The backward consumes the GPU training forward's own fp32 output and
+log-sum-exp, as a training step would.  Bars, from the arithmetic: every
+gradient is a sum of products whose operands were rounded to bf16 (relative
+error <= 2^-9 each: q, k, v, dout are bf16 inputs; P and dS enter the dv, dk
+and dq products as bf16), accumulated in fp32, and dq, dk, dv are rounded to
+bf16 once more; D = dout.out is formed from the forward's fp32 output.  With random signs the errors add in
 quadrature, so a gradient tensor's relative L2 error is a few times 2^-9
-(~2e-3); the bar is 1e-2, and every element must lie within 2^-5 of the
-tensor's largest magnitude.
+(~2e-3); the bar is the attention outputs' relative L2 of 5e-3, and every
+element must lie within 2^-5 of the tensor's largest magnitude.
 
 The score, gain and temperature gradients are fp32 sums of fp32 dS terms, and
 they cancel (each softmax row of dS sums to zero), so a relative bar does not
 fit them.  Their terms' errors come from D = dout.out formed from the forward's
-output, which differs from the exact output by at most ~2^-8 relative per
-element (bf16 rounding plus the forward's fp16 P): |dD_i| <= 2^-8 A_i with
+output, which differs from the exact output by well under 2^-8 relative per
+element (the forward's fp16 P): |dD_i| <= 2^-8 A_i with
 A_i = sum_f |dout_if out_if|, hence |d dS_ij| <= 2^-8 p_ij A_i, and the
-summation bound gives |error| <= 2^-8 * the oracle's term-magnitude sum
-(p_ij (|dp_ij - D_i| + A_i) in place of dS_ij).  The bar is 2^-7 times that
-sum, per element.
+summation bound gives |error| <= 2^-8 * the term-magnitude sum
+(p_ij (|dp_ij - D_i| + A_i) in place of dS_ij; tests/bwd_bounds.py).  The bar
+is 2^-7 times that sum, per element.  The score gradient, the one that reaches
+the gate, is also held to relative L2 5e-3 as a whole vector.
 """
 
 import numpy as np
@@ -29,11 +30,12 @@ import torch
 from learned_token_pruning_tg_amd import inputs, tg
 from oracle import tokengate as O
 
+from bwd_bounds import term_magnitude_sums
 from gpu_util import dev_bf16, dev_f32, host_bf16, say
 
 pytestmark = pytest.mark.gpu
 
-REL_L2 = 1e-2
+REL_L2 = 5e-3
 MAX_FRAC = 2.0 ** -5
 
 
@@ -64,10 +66,10 @@ def _case(rng, n, hq, hkv, d):
 def _gpu_bwd(q, k, v, dout, s, gain, tau, workspace=None):
     qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
     sd, gd, td = dev_f32(s), dev_f32(gain), dev_f32(tau)
-    out, lse = tg.gated_attn_fwd(qd, kd, vd, sd, gd, td, want_lse=True)
-    g = tg.gated_attn_bwd(qd, kd, vd, sd, gd, td, out, lse, dev_bf16(dout), workspace=workspace)
+    _, lse, out32 = tg.gated_attn_fwd_train(qd, kd, vd, sd, gd, td)
+    g = tg.gated_attn_bwd(qd, kd, vd, sd, gd, td, out32, lse, dev_bf16(dout), workspace=workspace)
     torch.cuda.synchronize()
-    return g, (qd, kd, vd, sd, gd, td, out, lse)
+    return g, (qd, kd, vd, sd, gd, td, out32, lse)
 
 
 def _host(g):
@@ -76,19 +78,29 @@ def _host(g):
                 dtau=g["dtau"].cpu().numpy())
 
 
-def check_sum(got, ref, scale, what):
+def check_sum(got, ref, scale, what, rel_l2=None):
     got = np.asarray(got, dtype=np.float64)
     assert got.shape == ref.shape and np.all(np.isfinite(got)), what
     ratio = np.abs(got - ref) / np.maximum(scale, 1e-30)
-    print(f"  {what}: max |err| / term-magnitude sum {ratio.max():.2e}", flush=True)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    print(f"  {what}: max |err| / term-magnitude sum {ratio.max():.2e}, rel-L2 {rel:.2e}",
+          flush=True)
     assert ratio.max() <= 2.0 ** -7, f"{what}: error {ratio.max():.3e} of its term-magnitude sum"
+    if rel_l2 is not None:
+        assert rel <= rel_l2, f"{what}: rel-L2 {rel:.3e}"
 
 
-def _compare(got, ref, what):
+def _compare(got, ref, bounds, what):
     for name in ("dq", "dk", "dv"):
         check_grad(got[name], ref[name], f"{what} {name}")
     for name in ("dscore", "dgain", "dtau"):
-        check_sum(got[name], ref[name], ref[name + "_scale"], f"{what} {name}")
+        check_sum(got[name], ref[name], bounds[name], f"{what} {name}",
+                  rel_l2=REL_L2 if name == "dscore" else None)
+
+
+def _oracle(q, k, v, s, gain, tau, dout):
+    return (O.gated_attention_bwd(q, k, v, s, gain, tau, dout),
+            term_magnitude_sums(q, k, v, s, gain, tau, dout))
 
 
 @pytest.mark.parametrize("n,hq,hkv,d", [
@@ -100,8 +112,7 @@ def test_attn_bwd_vs_oracle(n, hq, hkv, d):
     q, k, v, dout, s, gain, tau = _case(rng, n, hq, hkv, d)
     say(f"attn bwd n={n} hq={hq} hkv={hkv} d={d}")
     g, _ = _gpu_bwd(q, k, v, dout, s, gain, tau)
-    ref = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, return_scales=True)
-    _compare(_host(g), ref, f"n={n}")
+    _compare(_host(g), *_oracle(q, k, v, s, gain, tau, dout), f"n={n}")
 
 
 def test_attn_bwd_deterministic_and_shared_workspace():
@@ -117,7 +128,7 @@ def test_attn_bwd_deterministic_and_shared_workspace():
         for name in g1:
             assert torch.equal(g1[name], g2[name]), name
         if n == 517:
-            _compare(_host(g2), O.gated_attention_bwd(q, k, v, s, gain, tau, dout, return_scales=True), "n=517 reused ws")
+            _compare(_host(g2), *_oracle(q, k, v, s, gain, tau, dout), "n=517 reused ws")
 
 
 def test_attn_bwd_full_size_one_kv_group():
@@ -135,11 +146,10 @@ def test_attn_bwd_full_size_one_kv_group():
     got = _host(_gpu_bwd(q, k, v, dout, s, gain, tau)[0])
     for name in got:
         assert np.all(np.isfinite(got[name])), name
-    ref = O.gated_attention_bwd(q[:, :2], k[:, :1], v[:, :1], s, gain[:2], tau[:2], dout[:, :2],
-                                 return_scales=True)
+    ref = _oracle(q[:, :2], k[:, :1], v[:, :1], s, gain[:2], tau[:2], dout[:, :2])
     sub = dict(dq=got["dq"][:, :2], dk=got["dk"][:, :1], dv=got["dv"][:, :1],
                dscore=got["dscore"], dgain=got["dgain"][:2], dtau=got["dtau"][:2])
-    _compare(sub, ref, "n=8448 group 0")
+    _compare(sub, *ref, "n=8448 group 0")
 
 
 def test_attn_bwd_single_row():

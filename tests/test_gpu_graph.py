@@ -62,17 +62,15 @@ def test_graph_replays_of_the_backward_match_eager():
     q, k, v, do = r(m, hq, d), r(m, hkv, d), r(m, hkv, d), r(m, hq, d)
     s, gain, tau = dev_f32(rng.standard_normal(m)), dev_f32(rng.uniform(0.5, 1.5, hq)), \
         dev_f32(rng.uniform(0.8, 1.2, hq))
-    out = torch.empty_like(q)
-    lse = torch.empty((hq, m), dtype=torch.float32, device="cuda")
     ws = tg.attn_workspace(m, hq, hkv, d)
     bws = tg.attn_bwd_workspace(m, hq, hkv, d)
-    grads = tg.gated_attn_bwd(q, k, v, s, gain, tau, *tg.gated_attn_fwd(q, k, v, s, gain, tau,
-                                                                           want_lse=True), do,
-                              workspace=bws)
+    out, lse, out32 = tg.gated_attn_fwd_train(q, k, v, s, gain, tau, workspace=ws)
+    grads = tg.gated_attn_bwd(q, k, v, s, gain, tau, out32, lse, do, workspace=bws)
 
     def work():
-        tg.gated_attn_fwd(q, k, v, s, gain, tau, out=out, lse=lse, workspace=ws)
-        tg.gated_attn_bwd(q, k, v, s, gain, tau, out, lse, do, grads=grads, workspace=bws)
+        tg.gated_attn_fwd_train(q, k, v, s, gain, tau, out=out, lse=lse, out_f32=out32,
+                                workspace=ws)
+        tg.gated_attn_bwd(q, k, v, s, gain, tau, out32, lse, do, grads=grads, workspace=bws)
 
     say("graph capture: gated attention forward + backward")
     work()

@@ -70,9 +70,10 @@ def test_gate_qwen_shapes_and_determinism(n):
     torch.cuda.synchronize()
     a, b = s1.cpu().numpy(), s2.cpu().numpy()
     assert a.tobytes() == b.tobytes()                     # deterministic
-    rows = _sample_rows(n, np.random.default_rng(n), n_random=2000)
-    ref = O.gate_scores(g["h"][rows], g["w1"], g["b1"], g["w2"], g["b2"])
-    check_scores(a[rows], ref, f"gate qwen n={n}")
+    # every row: work-groups start their K loops at staggered offsets, so each
+    # row's sum order depends on its work-group
+    ref = O.gate_scores(g["h"], g["w1"], g["b1"], g["w2"], g["b2"])
+    check_scores(a, ref, f"gate qwen n={n}")
 
 
 # --------------------------------------------------------------------------- top-K
@@ -320,9 +321,9 @@ def test_tiny_workload_chain_all_layers():
 
 def _chain(w, layers, n_rows=None, full_rows=32):
     """Gate -> top-K -> compaction -> gated attention at full size, checked in
-    full (indices, compacted bytes; every gated-attention output and LSE when
-    n_rows is None) or on sampled rows (gate scores; attention when n_rows is
-    given; the full-N baseline)."""
+    full (every gate score, indices, compacted bytes; every gated-attention
+    output and LSE when n_rows is None) or on sampled rows (attention when
+    n_rows is given; the full-N baseline)."""
     rng = np.random.default_rng(w.seed)
     g = inputs.gate_inputs(w)
     gain, tau = inputs.layer_params(w)
@@ -334,8 +335,7 @@ def _chain(w, layers, n_rows=None, full_rows=32):
     s_kept = tg.compact(idx_d, s_d)
     torch.cuda.synchronize()
     s32 = s_d.cpu().numpy(); idx = idx_d.cpu().numpy()
-    rows = _sample_rows(w.n, rng, n_random=1000)
-    check_scores(s32[rows], O.gate_scores(g["h"][rows], g["w1"], g["b1"], g["w2"], g["b2"]),
+    check_scores(s32, O.gate_scores(g["h"], g["w1"], g["b1"], g["w2"], g["b2"]),
                  f"{w.name} scores")
     assert idx.size == w.kept
     assert np.array_equal(idx, O.topk_select(s32, w.doc_begin, w.doc_end, w.k_doc))

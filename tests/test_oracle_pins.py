@@ -298,15 +298,50 @@ def test_attention_bwd_score_gradient_sums_to_zero():
     assert np.max(np.abs(flat["dgain"])) < 1e-10
 
 
-def test_attention_bwd_scales_bound_their_gradients():
-    """The term-magnitude sums dominate the gradients they describe
-    (|sum dS x| <= sum |dS| |x| and |dS_ij| <= p_ij |dp_ij - D_i|)."""
-    q, k, v, s, gain, tau, dout = _bwd_case(14, 50, 4, 2, 8)
-    got = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, row_block=16, return_scales=True)
-    plain = O.gated_attention_bwd(q, k, v, s, gain, tau, dout, row_block=16)
+def _term_sums_by_loops(q, k, v, s, gain, tau, dout):
+    """The GPU bars' term-magnitude sums written as plain loops over every
+    (head, query row, key): softmax p_ij from its definition, dp_ij = dout_i.v_j,
+    D_i = sum_j p_ij dp_ij, A_i = sum_f |dout_if out_if| with out_i = sum_j p_ij v_j,
+    mag_ij = p_ij (|dp_ij - D_i| + A_i)."""
+    m, hq, d = q.shape
+    group = hq // k.shape[1]
+    sc = np.zeros(m); sg = np.zeros(hq); st = np.zeros(hq)
+    for h in range(hq):
+        g = h // group
+        c = 1.0 / (math.sqrt(d) * tau[h])
+        for i in range(m):
+            lg = [sum(q[i, h, f] * k[j, g, f] for f in range(d)) * c + gain[h] * s[j]
+                  for j in range(i + 1)]
+            top = max(lg)
+            e = [math.exp(x - top) for x in lg]
+            p = [x / sum(e) for x in e]
+            dp = [sum(dout[i, h, f] * v[j, g, f] for f in range(d)) for j in range(i + 1)]
+            dsum = sum(p[j] * dp[j] for j in range(i + 1))
+            out = [sum(p[j] * v[j, g, f] for j in range(i + 1)) for f in range(d)]
+            a = sum(abs(dout[i, h, f] * out[f]) for f in range(d))
+            for j in range(i + 1):
+                mag = p[j] * (abs(dp[j] - dsum) + a)
+                qk = sum(q[i, h, f] * k[j, g, f] for f in range(d))
+                sc[j] += abs(gain[h]) * mag
+                sg[h] += mag * abs(s[j])
+                st[h] += mag * abs(qk) / (math.sqrt(d) * tau[h] ** 2)
+    return dict(dscore=sc, dgain=sg, dtau=st)
+
+
+@pytest.mark.parametrize("row_block", [1, 3, 256])
+def test_bwd_bound_sums_match_plain_loops(row_block):
+    """tests/bwd_bounds.py (the GPU bars of the score, gain and temperature
+    gradients) against plain loops; and the sums dominate the oracle's
+    gradients they describe (|sum dS x| <= sum |dS| |x| with |dS_ij| <=
+    p_ij |dp_ij - D_i|)."""
+    from bwd_bounds import term_magnitude_sums
+    q, k, v, s, gain, tau, dout = _bwd_case(14, 7, 4, 2, 5)
+    got = term_magnitude_sums(q, k, v, s, gain, tau, dout, row_block=row_block)
+    ref = _term_sums_by_loops(q, k, v, s, gain, tau, dout)
+    grads = O.gated_attention_bwd(q, k, v, s, gain, tau, dout)
     for name in ("dscore", "dgain", "dtau"):
-        assert np.all(got[name + "_scale"] >= np.abs(got[name])), name
-        assert np.array_equal(got[name], plain[name])
+        assert np.allclose(got[name], ref[name], rtol=1e-12, atol=0), name
+        assert np.all(got[name] >= np.abs(grads[name])), name
 
 
 def test_attention_two_key_closed_form_and_first_row():
