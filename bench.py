@@ -8,6 +8,10 @@ is timed beside it.  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line (rank 0).  Usage:
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-other-configs]
+The default workload is 131072 tokens with 8192 document tokens kept; with it
+the line also carries compact records of the 32768-token workload and of the
+65536-token budget sweep (K = 1024, 4096, 16384, N).
 """
 
 from __future__ import annotations
@@ -22,6 +26,9 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# The headline: 131072 tokens, 8192 document tokens kept (8448 kept rows).
+DEFAULT_WORKLOAD = "qwen3-1.7b-128k"
+OTHER_WORKLOADS = ("qwen3-1.7b-32k", "qwen3-1.7b-64k-sweep")
 
 
 def _parse():
@@ -29,10 +36,13 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="qwen3-1.7b-16k")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--k-doc", type=int, default=None, help="override the document budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-full-baseline", action="store_true")
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the compact records of the 32k config and the 64k budget sweep "
+                        "(measured only with the default workload)")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--step-only", action="store_true",
@@ -151,6 +161,209 @@ def attn_flops(m: int, hq: int, d: int) -> float:
     return 2.0 * hq * d * m * (m + 1)
 
 
+class HostInputs:
+    """The workload's seeded host arrays, built once (templates on a few
+    threads: numpy releases the GIL in its generators and ufuncs) and shared
+    by the GPU upload and the CPU oracle leg."""
+
+    def __init__(self, w):
+        import concurrent.futures
+
+        from learned_token_pruning_tg_amd import inputs
+
+        self.w = w
+        self.n_t = min(w.n_templates, w.n_layers)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=1 + self.n_t) as ex:
+            fg = ex.submit(inputs.gate_inputs, w)
+            ft = [ex.submit(inputs.qkv_template, w, t) for t in range(self.n_t)]
+            self.gate = fg.result()
+            self.templates = [f.result() for f in ft]
+        self.gain, self.tau = inputs.layer_params(w)
+
+
+def _timer_pair():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+class GatedStep:
+    """Device buffers and the launch sequence of one gated-prefill step:
+    gate (all N rows) -> top-K -> compaction of h and s -> 27 gated layers."""
+
+    def __init__(self, w, host, dev, full_qkv=None):
+        import torch
+
+        from learned_token_pruning_tg_amd import inputs, tg
+
+        self.w, self.dev = w, dev
+        g = host.gate
+        self.b2 = g["b2"]
+        self.h = _bf16_dev(g["h"], dev)
+        self.w1, self.b1, self.w2 = _bf16_dev(g["w1"], dev), _f32_dev(g["b1"], dev), _f32_dev(g["w2"], dev)
+        self.gain_d = [_f32_dev(host.gain[l], dev) for l in range(w.n_layers)]
+        self.tau_d = [_f32_dev(host.tau[l], dev) for l in range(w.n_layers)]
+        self.n_t = host.n_t
+        self.full_qkv = full_qkv if full_qkv is not None else [
+            tuple(_bf16_dev(x, dev) for x in host.templates[t]) for t in range(self.n_t)]
+        m = w.kept
+        self.scores = torch.empty(w.n, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(m, dtype=torch.int32, device=dev)
+        self.h_kept = torch.empty((m, w.hidden), dtype=torch.bfloat16, device=dev)
+        self.s_kept = torch.empty(m, dtype=torch.float32, device=dev)
+        self.outs = [torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+                     for _ in range(2)]
+        self.ws = tg.attn_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
+        self.tws = tg.topk_workspace(w.n, dev)
+        # The upper layers' q/k/v of the kept rows stand for what the layers'
+        # projections would produce from the kept residual; they are gathered
+        # once from the full-N templates with the selection of this very input.
+        tg.gate_score(self.h, self.w1, self.b1, self.w2, self.b2, out=self.scores)
+        tg.topk_select(self.scores, w.doc_begin, w.doc_end, w.k_doc, out=self.idx, workspace=self.tws)
+        self.kept_qkv = [tuple(tg.compact(self.idx, x) for x in self.full_qkv[t])
+                         for t in range(self.n_t)]
+        self.template_of_layer = lambda l: inputs.template_of_layer(w, l)
+        torch.cuda.synchronize()
+
+    def run(self, stream, ev=None):
+        from learned_token_pruning_tg_amd import tg
+
+        w = self.w
+        if ev is not None:
+            ev[0].record(stream)
+        tg.gate_score(self.h, self.w1, self.b1, self.w2, self.b2, out=self.scores)
+        if ev is not None:
+            ev[1].record(stream)
+        tg.topk_select(self.scores, w.doc_begin, w.doc_end, w.k_doc, out=self.idx, workspace=self.tws)
+        if ev is not None:
+            ev[2].record(stream)
+        tg.compact(self.idx, self.h, out=self.h_kept)
+        tg.compact(self.idx, self.scores, out=self.s_kept)
+        if ev is not None:
+            ev[3].record(stream)
+        for l in range(w.n_layers):
+            q, k, v = self.kept_qkv[self.template_of_layer(l)]
+            tg.gated_attn_fwd(q, k, v, self.s_kept, self.gain_d[l], self.tau_d[l],
+                              out=self.outs[l & 1], workspace=self.ws)
+        if ev is not None:
+            ev[4].record(stream)
+
+    def time(self, stream, steps, warmup):
+        """Mean ms per step over `steps` timed steps (HIP events on the launch
+        stream around the whole loop), per-step median and minimum, and the
+        mean ms of each stage (gate, top-K, compaction, the 27 layers)."""
+        import torch
+
+        for _ in range(warmup):
+            self.run(stream)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        t_start, t_end = _timer_pair()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for i in range(steps):
+            self.run(stream, evs[i])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per_step = sorted(e[0].elapsed_time(e[4]) for e in evs)
+        stage = np.zeros(4)
+        for e in evs:
+            stage += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
+        return dict(ms=t_start.elapsed_time(t_end) / steps, median=per_step[len(per_step) // 2],
+                     min=per_step[0], stage=stage / steps, wall=wall)
+
+
+def _bf16_dev(x, dev):
+    import torch
+
+    from learned_token_pruning_tg_amd import inputs
+    bits = inputs.bf16_bits(inputs.round_bf16(x))
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _f32_dev(x, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+
+def full_baseline(w, full_qkv, stream, steps, warmup, dev):
+    """27 causal attention calls over all N rows (the unpruned prefill's
+    attention), timed like the gated step.  Returns (ms per step, ms per layer,
+    bytes of the buffers it writes)."""
+    import torch
+
+    from learned_token_pruning_tg_amd import inputs, tg
+
+    fout = torch.empty((w.n, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    fws = tg.attn_workspace(w.n, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
+
+    def full_step():
+        for l in range(w.n_layers):
+            q, k, v = full_qkv[inputs.template_of_layer(w, l)]
+            tg.full_attn_fwd(q, k, v, out=fout, workspace=fws)
+
+    for _ in range(warmup):
+        full_step()
+    a, b = _timer_pair()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        full_step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    f_ms = a.elapsed_time(b) / steps
+    nbytes = sum(t.numel() * t.element_size() for t in (fout, fws, *full_qkv[0]))
+    del fout, fws
+    return f_ms, f_ms / w.n_layers, int(nbytes)
+
+
+def other_configs(names, steps, warmup, dev, stream):
+    """Compact records of the other workloads at their full sizes: the 32k
+    config, and the 64k budget sweep (one gate serving every budget: the same
+    weights, residual and scores; top-K, compaction and the 27 layers per
+    budget).  Per budget: step time and tokens/s, the gated attention's
+    TFLOP/s and fraction of bf16 peak, and the speed-up over the full-N
+    baseline measured on the same workload."""
+    import torch
+
+    from learned_token_pruning_tg_amd import inputs
+
+    recs = []
+    for name in names:
+        base = inputs.WORKLOADS[name]
+        budgets = inputs.SWEEP_BUDGETS if name.endswith("sweep") else (base.k_doc,)
+        host = HostInputs(base)
+        full_qkv = [tuple(_bf16_dev(x, dev) for x in host.templates[t]) for t in range(host.n_t)]
+        f_ms, f_layer, _ = full_baseline(base, full_qkv, stream, max(1, steps), min(warmup, 1), dev)
+        for k_doc in budgets:
+            w = base if k_doc == base.k_doc and len(budgets) == 1 else base.with_budget(k_doc)
+            st = GatedStep(w, host, dev, full_qkv=full_qkv)
+            t = st.time(stream, steps, warmup)
+            m = w.kept
+            attn_ms = t["stage"][3] / w.n_layers
+            tf = attn_flops(m, w.n_q_heads, w.head_dim) / (attn_ms / 1e3) / 1e12
+            recs.append({
+                "workload": name, "n_tokens": w.n, "k_doc": k_doc, "kept_rows": m,
+                "steps": steps, "ms_per_step": round(t["ms"], 4),
+                "tokens_per_s": round(w.n / (t["ms"] / 1e3), 1),
+                "gate_ms": round(t["stage"][0], 5), "topk_ms": round(t["stage"][1], 5),
+                "compact_ms": round(t["stage"][2], 5),
+                "attn_ms_per_layer": round(attn_ms, 5), "attn_tflops": round(tf, 1),
+                "attn_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "full_n_ms_per_step": round(f_ms, 4),
+                "full_n_attn_frac_bf16_peak": round(attn_flops(w.n, w.n_q_heads, w.head_dim) /
+                                                    (f_layer / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "speedup_gated_vs_full": round(f_ms / t["ms"], 2),
+                "speedup_incl_gate_layer": round((f_ms + f_layer) / (t["ms"] + f_layer), 2),
+            })
+            del st
+            torch.cuda.synchronize()
+        del full_qkv, host
+        torch.cuda.empty_cache()
+    return recs
+
+
 def main():
     args = _parse()
     if args.summarize_pmc:
@@ -172,90 +385,22 @@ def main():
     torch.cuda.set_device(dev)
     tg.lib()  # fail loudly before any work if the library is missing
 
-    def bf16_dev(x):
-        bits = inputs.bf16_bits(inputs.round_bf16(x))
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    def f32_dev(x):
-        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
-
     # ---------------------------------------------------------------- inputs (untimed)
-    g = inputs.gate_inputs(w)
-    gain, tau = inputs.layer_params(w)
-    h = bf16_dev(g["h"])
-    w1, b1, w2 = bf16_dev(g["w1"]), f32_dev(g["b1"]), f32_dev(g["w2"])
-    gain_d = [f32_dev(gain[l]) for l in range(w.n_layers)]
-    tau_d = [f32_dev(tau[l]) for l in range(w.n_layers)]
-    n_t = min(w.n_templates, w.n_layers)
-    full_qkv = []
-    for t in range(n_t):
-        full_qkv.append(tuple(bf16_dev(x) for x in inputs.qkv_template(w, t)))
+    host = HostInputs(w)
+    st = GatedStep(w, host, dev)
     m = w.kept
-    scores = torch.empty(w.n, dtype=torch.float32, device=dev)
-    idx = torch.empty(m, dtype=torch.int32, device=dev)
-    h_kept = torch.empty((m, w.hidden), dtype=torch.bfloat16, device=dev)
-    s_kept = torch.empty(m, dtype=torch.float32, device=dev)
-    outs = [torch.empty((m, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-            for _ in range(2)]
-    ws = tg.attn_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
-    tws = tg.topk_workspace(w.n, dev)
-    # The upper layers' q/k/v of the kept rows stand for what the layers'
-    # projections would produce from the kept residual; they are gathered
-    # once from the full-N templates with the selection of this very input.
-    tg.gate_score(h, w1, b1, w2, g["b2"], out=scores)
-    tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx, workspace=tws)
-    kept_qkv = [tuple(tg.compact(idx, x) for x in full_qkv[t]) for t in range(n_t)]
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    n_ev = 5
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        tg.gate_score(h, w1, b1, w2, g["b2"], out=scores)
-        if ev is not None:
-            ev[1].record(stream)
-        tg.topk_select(scores, w.doc_begin, w.doc_end, w.k_doc, out=idx, workspace=tws)
-        if ev is not None:
-            ev[2].record(stream)
-        tg.compact(idx, h, out=h_kept)
-        tg.compact(idx, scores, out=s_kept)
-        if ev is not None:
-            ev[3].record(stream)
-        for l in range(w.n_layers):
-            q, k, v = kept_qkv[inputs.template_of_layer(w, l)]
-            tg.gated_attn_fwd(q, k, v, s_kept, gain_d[l], tau_d[l], out=outs[l & 1], workspace=ws)
-        if ev is not None:
-            ev[4].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    per_step = sorted(e[0].elapsed_time(e[4]) for e in evs)
-    ms_step_median = per_step[len(per_step) // 2]
-    ms_step_min = per_step[0]
-    stage = np.zeros(4)
-    for e in evs:
-        stage += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
-    stage /= args.steps
+    t = st.time(stream, args.steps, args.warmup)
+    ms_step, stage = t["ms"], t["stage"]
     attn_ms_launch = stage[3] / w.n_layers
+    full_qkv, kept_qkv, s_kept, idx = st.full_qkv, st.kept_qkv, st.s_kept, st.idx
+    gain_d, tau_d, outs, ws = st.gain_d, st.tau_d, st.outs, st.ws
+    n_t = st.n_t
     tensor_bytes = lambda *ts: int(sum(t.numel() * t.element_size() for t in ts))
     # buffers the gated step writes (scores, indices, compacted rows, two
     # layer outputs, workspaces) and the kept rows' q/k/v of one layer
-    gated_buffers = tensor_bytes(scores, idx, h_kept, s_kept, *outs, ws, tws) + tensor_bytes(*kept_qkv[0])
+    gated_buffers = tensor_bytes(st.scores, idx, st.h_kept, s_kept, *outs, ws, st.tws) + \
+        tensor_bytes(*kept_qkv[0])
 
     # The key bias's own cost: the same 27 calls over the same kept rows as
     # plain causal attention (gain 0, tau 1), timed like the gated loop.
@@ -265,8 +410,7 @@ def main():
             tg.full_attn_fwd(q, k, v, out=outs[l & 1], workspace=ws)
 
     plain_layers()
-    pa = torch.cuda.Event(enable_timing=True)
-    pb = torch.cuda.Event(enable_timing=True)
+    pa, pb = _timer_pair()
     torch.cuda.synchronize()
     pa.record(stream)
     for _ in range(max(1, min(args.steps, 5))):
@@ -313,8 +457,7 @@ def main():
 
         def time_calls(fn, reps):
             fn()
-            ea = torch.cuda.Event(enable_timing=True)
-            eb = torch.cuda.Event(enable_timing=True)
+            ea, eb = _timer_pair()
             torch.cuda.synchronize()
             ea.record(stream)
             for _ in range(reps):
@@ -370,8 +513,8 @@ def main():
         # dK, dQ over the causal pairs; the deterministic kernels execute seven
         # (S and dP are formed again for dQ).
         q0, k0, v0 = kept_qkv[0]
-        fo, flse = tg.gated_attn_fwd(q0, k0, v0, s_kept, gain_d[0], tau_d[0], want_lse=True,
-                                     workspace=ws)
+        _, flse, fo = tg.gated_attn_fwd_train(q0, k0, v0, s_kept, gain_d[0], tau_d[0],
+                                              workspace=ws)
         gen = torch.Generator(device=dev).manual_seed(2024)
         dout_b = (torch.randn(fo.shape, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
         bws = tg.attn_bwd_workspace(m, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
@@ -391,27 +534,8 @@ def main():
     # ---------------------------------------------------------------- full-N baseline
     full = None
     if not args.no_full_baseline:
-        fout = torch.empty((w.n, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
-        fws = tg.attn_workspace(w.n, w.n_q_heads, w.n_kv_heads, w.head_dim, dev)
-
-        def full_step():
-            for l in range(w.n_layers):
-                q, k, v = full_qkv[inputs.template_of_layer(w, l)]
-                tg.full_attn_fwd(q, k, v, out=fout, workspace=fws)
-
         fsteps = max(1, min(args.steps, 5))
-        for _ in range(min(args.warmup, 1)):
-            full_step()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(fsteps):
-            full_step()
-        b.record(stream)
-        torch.cuda.synchronize()
-        f_ms = a.elapsed_time(b) / fsteps
-        f_launch = f_ms / w.n_layers
+        f_ms, f_launch, f_bytes = full_baseline(w, full_qkv, stream, fsteps, min(args.warmup, 1), dev)
         f_fl = attn_flops(w.n, w.n_q_heads, w.head_dim)
         full = {
             "ms_per_step": round(f_ms, 4),
@@ -423,9 +547,8 @@ def main():
             # both sides also pay the gate layer's own attention over all N rows
             "speedup_incl_gate_layer": round((f_ms + f_launch) / (ms_step + f_launch), 2),
             "steps": fsteps,
-            "step_buffers_bytes": tensor_bytes(fout, fws) + tensor_bytes(*full_qkv[0]),
+            "step_buffers_bytes": f_bytes,
         }
-        del fout, fws
 
     if args.copy_calibration:
         # A cold copy: the source is filled, then an equally large buffer is
@@ -476,10 +599,17 @@ def main():
         # whole process, including the full-N synthetic q/k/v templates
         "max_memory_allocated_bytes": int(torch.cuda.max_memory_allocated()),
     }
+    del st, full_qkv, kept_qkv, outs, ws
+    torch.cuda.empty_cache()
+
+    others = None
+    if not args.no_other_configs and args.k_doc is None and args.workload == DEFAULT_WORKLOAD:
+        others = other_configs(OTHER_WORKLOADS, max(1, min(args.steps, 5)), min(args.warmup, 1),
+                               dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, g, gain, tau, args.cpu_seconds)
+        cpu = cpu_baseline(w, host, args.cpu_seconds)
 
     line = {
         "metric": "gated-prefill tokens/s + attn TFLOP/s (% bf16 MFMA peak) vs full-N prefill",
@@ -489,8 +619,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "ms_per_step_median": round(ms_step_median, 4),
-        "ms_per_step_min": round(ms_step_min, 4),
+        "ms_per_step_median": round(t["median"], 4),
+        "ms_per_step_min": round(t["min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -512,22 +642,22 @@ def main():
         "first_decode_step": decode,
         "upper_layer_qk_prologue": prologue_stats,
         "upper_layer_backward": bwd_stats,
+        "other_configs": others,
         "cpu_baseline": cpu,
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": round(t["wall"], 3),
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, g, gain, tau, budget_s):
+def cpu_baseline(w, host, budget_s):
     """The CPU oracle on a bounded sample of the same workload: the gate on all
     N rows, the top-K, the compaction, and as many upper layers of gated
     attention as fit the time budget; the per-step time is the measured stages
     plus the mean measured layer time times the number of layers."""
-    from learned_token_pruning_tg_amd import inputs
-
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from oracle import tokengate as O
 
+    g, gain, tau = host.gate, host.gain, host.tau
     try:
         import threadpoolctl
         threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()),
@@ -543,7 +673,7 @@ def cpu_baseline(w, g, gain, tau, budget_s):
     _ = O.compact_rows(idx, g["h"])
     s_kept = O.compact_rows(idx, s32)
     t3 = time.perf_counter()
-    q, k, v = inputs.qkv_template(w, 0)
+    q, k, v = host.templates[0]
     qk, kk, vk = q[idx], k[idx], v[idx]
     layer_t = []
     while True:
@@ -564,8 +694,8 @@ def cpu_baseline(w, g, gain, tau, budget_s):
     rest = rng.choice(others, size=min(256 - fixed.size, others.size), replace=False)
     rows = np.union1d(fixed, rest)
     full_t = []
-    for t in range(2):
-        qf, kf, vf = (q, k, v) if t == 0 else inputs.qkv_template(w, t)
+    for t in range(min(2, len(host.templates))):
+        qf, kf, vf = host.templates[t]
         a = time.perf_counter()
         O.full_attention(qf, kf, vf, rows=rows)
         full_t.append(time.perf_counter() - a)
@@ -578,7 +708,7 @@ def cpu_baseline(w, g, gain, tau, budget_s):
                    f"({t1 - t0:.2f} s), top-K ({t2 - t1:.3f} s), compaction ({t3 - t2:.3f} s), "
                    f"{len(layer_t)} of {w.n_layers} gated-attention layers measured "
                    f"(mean {np.mean(layer_t):.2f} s/layer, scaled to {w.n_layers})"),
-        "full_n_sample": {"rows_per_layer": int(rows.size), "layers": 2,
+        "full_n_sample": {"rows_per_layer": int(rows.size), "layers": len(full_t),
                           "seconds": [round(x, 3) for x in full_t],
                           "note": "full-N causal attention oracle on sampled query rows; "
                                   "seconds for those rows, not extrapolated"},

@@ -107,10 +107,18 @@ def _rng(seed: int, slot: int) -> np.random.Generator:
 def round_bf16(x) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); returns float32."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
-    return np.where(np.isnan(x), x, out).reshape(x.shape)
+    u = x.view(np.uint32)
+    # uint32 arithmetic wraps only for bit patterns >= 0xFFFF8001, which are
+    # NaNs; every NaN is restored from x below.
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r &= np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = x[nan]
+    return out.reshape(x.shape)
 
 
 def bf16_bits(x_rounded) -> np.ndarray:
@@ -141,9 +149,20 @@ def apply_rope(x: np.ndarray, positions: np.ndarray, base: float = 1.0e6) -> np.
     ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
     cos = np.cos(ang).astype(np.float32)[:, None, :]
     sin = np.sin(ang).astype(np.float32)[:, None, :]
+    x = np.asarray(x, dtype=np.float32)
     x1 = x[..., :half]
     x2 = x[..., half:]
-    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1).astype(np.float32)
+    out = np.empty(x.shape, dtype=np.float32)
+    lo, hi = out[..., :half], out[..., half:]
+    tmp = np.empty(x1.shape, dtype=np.float32)
+    # float32 products, each rounded, then one rounded add (no fused ops)
+    np.multiply(x1, cos, out=lo)
+    np.multiply(x2, sin, out=tmp)
+    lo -= tmp
+    np.multiply(x2, cos, out=hi)
+    np.multiply(x1, sin, out=tmp)
+    hi += tmp
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -16,9 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_cpu_baseline_tiny_shape():
     w = inputs.WORKLOADS["tiny"]
-    g = inputs.gate_inputs(w)
-    gain, tau = inputs.layer_params(w)
-    r = bench.cpu_baseline(w, g, gain, tau, 5.0)
+    r = bench.cpu_baseline(w, bench.HostInputs(w), 5.0)
     assert r["kind"] == "oracle" and r["unit"] == "tokens/s"
     assert r["value"] > 0 and r["cores"] >= 1
     assert f"{w.n_layers} of {w.n_layers} gated-attention layers measured" in r["sample"]
@@ -32,6 +30,23 @@ def test_attention_flops_count_causal_pairs():
     m, hq, d = 5, 3, 8
     pairs = sum(i + 1 for i in range(m))
     assert bench.attn_flops(m, hq, d) == 4.0 * d * hq * pairs
+
+
+def test_host_inputs_are_the_generators_arrays():
+    w = inputs.WORKLOADS["tiny"]
+    host = bench.HostInputs(w)
+    g = inputs.gate_inputs(w)
+    assert np.array_equal(host.gate["h"], g["h"]) and np.array_equal(host.gate["w1"], g["w1"])
+    for t in range(host.n_t):
+        for a, b in zip(host.templates[t], inputs.qkv_template(w, t)):
+            assert np.array_equal(a, b)
+
+
+def test_default_workload_is_the_long_context_target():
+    w = inputs.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    assert (w.n, w.k_doc, w.kept) == (131072, 8192, 8448)
+    for name in bench.OTHER_WORKLOADS:
+        assert name in inputs.WORKLOADS
 
 
 def test_more_than_one_gpu_is_refused():
