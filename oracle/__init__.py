@@ -22,8 +22,8 @@ Sources cited in this package (the method's coverage pages; there is no code):
         artificiale documenti lunghi fino a 11 volte più velocemente…";
         section "Come funziona".
 
-Pin status of every function is listed in the module docstring of
-``oracle.tokengate``.
+Pin status of every function is listed in the module docstrings of
+``oracle.tokengate`` and ``oracle.gated_deltanet``.
 """
 
 from .tokengate import (  # noqa: F401
@@ -40,3 +40,4 @@ from .tokengate import (  # noqa: F401
     qk_norm_rope,
     gated_prefill,
 )
+from .gated_deltanet import gated_delta_rule  # noqa: F401
