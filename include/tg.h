@@ -124,6 +124,22 @@ tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int6
                          size_t workspace_bytes, tg_stream_t stream);
 
 /*
+ * tg_topk_select for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same selection, arguments and result, with no workspace argument.
+ * Its scratch is a static device array of 32 KiB inside the library, one per
+ * GPU, held until the process ends; it covers every n < 2^30 (a larger need
+ * would return TG_E_UNSUPPORTED).  The call allocates and frees nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or threads without ordering) race and give
+ * undefined results.  The calling thread's current device must be the one
+ * `stream` belongs to.  Errors as tg_topk_select (no TG_E_WORKSPACE).
+ */
+tg_status tg_topk_select_noalloc(const float* scores, int64_t n, int64_t doc_begin,
+                                 int64_t doc_end, int64_t k_doc, int32_t* kept_idx,
+                                 tg_stream_t stream);
+
+/*
  * Row compaction (lucasainews.com article, "작동 방식": only kept rows go
  * up; nothing is built for the dropped ones):
  *     dst[i, :] = src[kept_idx[i], :]   for i < n_kept, bytewise

@@ -122,6 +122,25 @@ tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int6
                     "tg_topk_select launch");
 }
 
+tg_status tg_topk_select_noalloc(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
+                                 int64_t k_doc, int32_t* kept_idx, tg_stream_t stream) {
+  const char* fn = "tg_topk_select_noalloc";
+  if (n < 0 || n >= (int64_t(1) << 30))
+    return fail(TG_E_INVALID, "%s: n=%lld out of range (n < 2^30)", fn, (long long)n);
+  if (tg_kept_count(n, doc_begin, doc_end, k_doc) < 0)
+    return fail(TG_E_INVALID, "%s: need 0 <= doc_begin=%lld <= doc_end=%lld <= n=%lld, k_doc=%lld >= 0",
+                fn, (long long)doc_begin, (long long)doc_end, (long long)n, (long long)k_doc);
+  const size_t need = tg::topk_workspace_bytes(n);
+  if (need > tg::kTopkScratchBytes)
+    return fail(TG_E_UNSUPPORTED, "%s: n=%lld needs %zu scratch bytes, above the static %zu",
+                fn, (long long)n, need, tg::kTopkScratchBytes);
+  if (n == 0 || tg_kept_count(n, doc_begin, doc_end, k_doc) == 0) return TG_OK;  // nothing kept
+  if (!scores || !kept_idx) return fail(TG_E_INVALID, "%s: null pointer", fn);
+  return hip_status(tg::launch_topk_select_noalloc(scores, n, doc_begin, doc_end, k_doc, kept_idx,
+                                                   as_hip(stream)),
+                    "tg_topk_select_noalloc launch");
+}
+
 tg_status tg_compact(const int32_t* kept_idx, int64_t n_kept, const void* src, int64_t src_rows,
                      int64_t src_stride_bytes, int64_t row_bytes, void* dst,
                      int64_t dst_stride_bytes, tg_stream_t stream) {

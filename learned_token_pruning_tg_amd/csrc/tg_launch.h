@@ -18,6 +18,12 @@ hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin,
                               int64_t k_doc, int32_t* kept_idx, void* workspace,
                               hipStream_t stream);
 
+// The top-K with the library's own per-device static scratch (no allocation).
+constexpr size_t kTopkScratchBytes = 32768;
+hipError_t launch_topk_select_noalloc(const float* scores, int64_t n, int64_t doc_begin,
+                                      int64_t doc_end, int64_t k_doc, int32_t* kept_idx,
+                                      hipStream_t stream);
+
 hipError_t launch_compact(const int32_t* kept_idx, int64_t n_kept, const void* src,
                           int64_t src_rows, int64_t src_stride, int64_t row_bytes, void* dst,
                           int64_t dst_stride, hipStream_t stream);

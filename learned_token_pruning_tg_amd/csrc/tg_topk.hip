@@ -23,6 +23,8 @@
 //  * Long inputs: the same passes spread over up to 1024 work-groups with
 //    global histograms and per-range counts in the caller's workspace (see
 //    the multi-work-group section).
+#include <mutex>
+
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -511,6 +513,52 @@ hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin,
   hipLaunchKernelGGL(topk_write_kernel, grid, block, 0, stream, scores, ni, db, de,
                      p.rows_per_group, m_total, ws, kept_idx);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The same selection for callers that cannot allocate: its scratch is a
+// file-scope device array of kTopkScratchBytes, one per GPU, held until the
+// process ends.  In host code `topk_scratch` names a host-side stand-in, not
+// a device address: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in topk_scratch_dev.
+// Every call on a GPU shares that GPU's array (calls that overlap on one GPU
+// race); the clear kernel zeroes the histograms at the start of each call and
+// every other word is written before it is read within the call.
+// ---------------------------------------------------------------------------
+namespace {
+static __device__ __align__(256) char topk_scratch[kTopkScratchBytes];
+static_assert((kWsCounts + 2 * kMaxGroups) * 4 <= kTopkScratchBytes, "scratch too small");
+constexpr int kMaxDevices = 64;
+std::mutex topk_scratch_mu;
+void* topk_scratch_dev[kMaxDevices] = {};
+
+hipError_t topk_scratch_ptr(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(topk_scratch_mu);
+  if (topk_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(topk_scratch));
+    if (e != hipSuccess) return e;
+    topk_scratch_dev[dev] = p;
+  }
+  *ptr = topk_scratch_dev[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_topk_select_noalloc(const float* scores, int64_t n, int64_t doc_begin,
+                                      int64_t doc_end, int64_t k_doc, int32_t* kept_idx,
+                                      hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  void* ws = nullptr;
+  if (n > kSingleGroupMax) {          // the one-work-group path uses no scratch
+    const hipError_t e = topk_scratch_ptr(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return launch_topk_select(scores, n, doc_begin, doc_end, k_doc, kept_idx, ws, stream);
 }
 
 }  // namespace tg

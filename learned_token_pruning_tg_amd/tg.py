@@ -29,6 +29,7 @@ _SIGNATURES = {
     "tg_gate_score": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, ctypes.c_float, _I32, _P, _P]),
     "tg_topk_workspace_bytes": (ctypes.c_size_t, [_I64]),
     "tg_topk_select": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "tg_topk_select_noalloc": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
     "tg_compact": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "tg_attn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
     "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
@@ -164,6 +165,26 @@ def topk_select(scores: torch.Tensor, doc_begin: int, doc_end: int, k_doc: int,
     _check(lib().tg_topk_select(_ptr(scores), n, doc_begin, doc_end, k_doc, _ptr(out),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 _stream(stream)))
+    return out
+
+
+def topk_select_noalloc(scores: torch.Tensor, doc_begin: int, doc_end: int, k_doc: int,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """topk_select with the library's static per-GPU scratch instead of a
+    workspace (no device allocation inside the call; calls that overlap on
+    one GPU race).  Returns the kept indices [M] int32, ascending."""
+    _need(scores, "scores", torch.float32)
+    n = scores.shape[0]
+    m = kept_count(n, doc_begin, doc_end, k_doc)
+    if m < 0:
+        raise ValueError("invalid document range or budget")
+    if out is None:
+        out = torch.empty(m, dtype=torch.int32, device=scores.device)
+    _need(out, "out", torch.int32)
+    if out.shape != (m,):
+        raise ValueError(f"out must hold {m} indices")
+    _check(lib().tg_topk_select_noalloc(_ptr(scores), n, doc_begin, doc_end, k_doc, _ptr(out),
+                                        _stream(stream)))
     return out
 
 
