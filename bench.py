@@ -125,6 +125,23 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
                         "bytes_per_launch": total * 1024.0 * scale if scale and total else None}
     f, w_ = out["FETCH_SIZE"]["bytes_per_launch"], out["WRITE_SIZE"]["bytes_per_launch"]
     out["traffic_bytes_per_launch"] = f + w_ if f is not None and w_ is not None else None
+    # The other step kernels (gate, top-K, compaction), per dispatch, scaled
+    # the same way; compact_wide excludes the calibration copy itself.
+    step_kernels = ("gate_score_kernel", "topk_select_kernel", "topk_clear_kernel",
+                    "topk_hist_kernel", "topk_count_kernel", "topk_write_kernel",
+                    "compact_wide_kernel", "compact_narrow_kernel")
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = load(d, counter)
+        scale = out[counter]["scale"]
+        copy_kib = out[counter]["copy_kib"]
+        for name in step_kernels:
+            vals = [float(r["Counter_Value"]) for r in rows if name in r["Kernel_Name"]
+                    and not (name == "compact_wide_kernel" and float(r["Counter_Value"]) == copy_kib)]
+            if vals and scale:
+                per.setdefault(name, {})[counter] = round(sum(vals) / len(vals) * 1024.0 * scale)
+                per[name]["dispatches"] = len(vals)
+    out["step_kernels_bytes_per_dispatch"] = per
     path = traffic_path(workload)
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -140,6 +157,12 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
                      f"{r['merge_kib']} | {r['bytes_per_launch']} |\n")
         fh.write(f"\nTotal HBM bytes per launch: {out['traffic_bytes_per_launch']}\n")
         fh.write(f"Kernel source sha256[:16]: {out['kernel_source_sha256_16']}\n")
+        fh.write("\nThe step's other kernels, HBM bytes per dispatch (scaled as above; the "
+                 "compaction kernels include the bench's q/k/v gathers):\n\n")
+        fh.write("| kernel | dispatches | FETCH bytes | WRITE bytes |\n|---|---|---|---|\n")
+        for name, r in per.items():
+            fh.write(f"| {name} | {r.get('dispatches')} | {r.get('FETCH_SIZE')} | "
+                     f"{r.get('WRITE_SIZE')} |\n")
     print(json.dumps(out))
 
 
@@ -531,6 +554,51 @@ def main():
                      "bwd_over_fwd": round(bwd_ms / attn_ms_launch, 2)}
         del bws, grads, fo, flse, dout_b
 
+    # ---------------------------------------------------------------- hybrid-model layer
+    # One Gated DeltaNet layer of a hybrid model (16 q/k and 32 value heads of
+    # 128, a stand-in shape) above the gate: its recurrence over the M kept
+    # rows (gathered with the step's own selection) against the same layer
+    # over all N rows, which is what a method that cannot prune it pays.
+    gdn_stats = None
+    if not args.step_only:
+        gx = inputs.gdn_inputs(w.seed, w.n)
+        gd = {key: (_bf16_dev(val, dev) if key in "qkv" else _f32_dev(val, dev))
+              for key, val in gx.items()}
+        del gx
+        gk = {key: tg.compact(idx, val) for key, val in gd.items()}
+        hk, hv, dd = inputs.GDN_QK_HEADS, inputs.GDN_V_HEADS, inputs.GDN_HEAD_DIM
+        gws = tg.gdn_workspace(w.n, hk, hv, dd, dev)
+        g_out = torch.empty((w.n, hv, dd), dtype=torch.bfloat16, device=dev)
+
+        def gdn(src, rows):
+            tg.gdn_fwd(src["q"], src["k"], src["v"], src["g"], src["beta"], out=g_out[:rows],
+                       workspace=gws)
+
+        def time_gdn(src, rows, reps):
+            gdn(src, rows)
+            ea, eb = _timer_pair()
+            torch.cuda.synchronize()
+            ea.record(stream)
+            for _ in range(reps):
+                gdn(src, rows)
+            eb.record(stream)
+            torch.cuda.synchronize()
+            return ea.elapsed_time(eb) / reps
+
+        gk_ms = time_gdn(gk, m, max(3, min(args.steps, 10)))
+        gf_ms = time_gdn(gd, w.n, 2)
+        row_flop = 6.0 * hv * dd * dd       # S k, the rank-one write, S q: 2 flop per element
+        row_bytes = 2.0 * 2 * hk * dd + 2.0 * hv * dd + 8.0 * hv + 2.0 * hv * dd
+        gdn_stats = {
+            "shape": {"qk_heads": hk, "v_heads": hv, "head_dim": dd, "chunk": 64},
+            "kept_rows": m, "ms_per_layer_kept": round(gk_ms, 5),
+            "ms_per_layer_all_rows": round(gf_ms, 5), "speedup": round(gf_ms / gk_ms, 2),
+            "tflops_kept": round(row_flop * m / (gk_ms / 1e3) / 1e12, 2),
+            "gb_s_kept": round(row_bytes * m / (gk_ms / 1e3) / 1e9, 1),
+            "frac_hbm_peak_kept": round(row_bytes * m / (gk_ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        }
+        del gd, gk, gws, g_out
+
     # ---------------------------------------------------------------- full-N baseline
     full = None
     if not args.no_full_baseline:
@@ -642,6 +710,7 @@ def main():
         "first_decode_step": decode,
         "upper_layer_qk_prologue": prologue_stats,
         "upper_layer_backward": bwd_stats,
+        "hybrid_gdn_layer": gdn_stats,
         "other_configs": others,
         "cpu_baseline": cpu,
         "wall_s_timed": round(t["wall"], 3),

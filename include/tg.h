@@ -283,6 +283,46 @@ tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
                             tg_stream_t stream);
 
 /*
+ * Bytes of device workspace tg_gdn_fwd needs for n rows: per 64-row chunk and
+ * value head 56.25 KiB (the recurrence's operands as fp16 MFMA fragments and
+ * the chunk's cumulative decays), per chunk and q/k head 16 KiB (q
+ * fragments).  Host-only arithmetic; 0 for n <= 0 or unsupported shapes.
+ */
+size_t tg_gdn_workspace_bytes(int64_t n, int32_t n_qk_heads, int32_t n_v_heads, int32_t head_dim);
+
+/*
+ * A Gated DeltaNet layer's recurrence over the n kept rows (lucasainews.com
+ * article, "성능 결과": on a hybrid model with Gated DeltaNet layers between
+ * full-attention layers, TokenGate prunes the recurrent layers too, so above
+ * the gate they run over the kept tokens only, in original order; the
+ * recurrence is the gated delta rule of Gated DeltaNet, Yang, Kautz and
+ * Hatamizadeh, ICLR 2025).  Per value head h, with q/k head h / (n_v_heads /
+ * n_qk_heads) and state S [head_dim (v), head_dim (k)]:
+ *     S <- exp(g[t,h]) S
+ *     S <- S + beta[t,h] (v_t,h - S k_t) k_t^T
+ *     out_t,h = scale * S q_t
+ *   q, k  [n, n_qk_heads, head_dim] bf16, contiguous, 16-byte aligned; the
+ *         layer's L2-normalised queries and keys
+ *   v     [n, n_v_heads, head_dim] bf16, contiguous, 16-byte aligned
+ *   g     [n, n_v_heads] fp32 log decay (exp(g) <= 1 expected; g <= 0)
+ *   beta  [n, n_v_heads] fp32 write strength in [0, 1]
+ *   scale the read-out scale (1/sqrt(head_dim) in the usual layer); finite
+ *   initial_state [n_v_heads, head_dim, head_dim] fp32 or NULL (zeros)
+ *   final_state   [n_v_heads, head_dim, head_dim] fp32 or NULL (output)
+ *   out   [n, n_v_heads, head_dim] bf16 (output, round-to-nearest-even)
+ *   workspace  device scratch of at least tg_gdn_workspace_bytes(...) bytes,
+ *         16-byte aligned, caller-owned, overwritten.
+ * Supported: head_dim 128, n_v_heads % n_qk_heads == 0, n < 2^31.
+ * Numerics: chunks of 64 rows; the within-chunk solve, decays, state and sums
+ * in fp32, the MFMA operands in fp16.  n == 0 is a no-op (final_state not
+ * written).
+ */
+tg_status tg_gdn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* g,
+                     const float* beta, int64_t n, int32_t n_qk_heads, int32_t n_v_heads,
+                     int32_t head_dim, float scale, const float* initial_state, float* final_state,
+                     tg_bf16* out, void* workspace, size_t workspace_bytes, tg_stream_t stream);
+
+/*
  * Bytes of device workspace tg_gated_decode_fwd needs for n cached rows:
  * per KV head and chunk of 64-256 keys, a (max, sum, head_dim outputs) fp32
  * state for each of its query heads.  Host-only arithmetic; 0 for arguments

@@ -257,6 +257,45 @@ tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
 }
 
 namespace {
+bool gdn_shape_ok(int64_t n, int32_t hk, int32_t hv, int32_t d) {
+  return n >= 0 && n < (int64_t(1) << 31) && hk > 0 && hv > 0 && hv % hk == 0 && d == 128;
+}
+}  // namespace
+
+size_t tg_gdn_workspace_bytes(int64_t n, int32_t n_qk_heads, int32_t n_v_heads, int32_t head_dim) {
+  if (n <= 0 || !gdn_shape_ok(n, n_qk_heads, n_v_heads, head_dim)) return 0;
+  return tg::gdn_workspace_bytes(n, n_qk_heads, n_v_heads);
+}
+
+tg_status tg_gdn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const float* g,
+                     const float* beta, int64_t n, int32_t n_qk_heads, int32_t n_v_heads,
+                     int32_t head_dim, float scale, const float* initial_state, float* final_state,
+                     tg_bf16* out, void* workspace, size_t workspace_bytes, tg_stream_t stream) {
+  const char* fn = "tg_gdn_fwd";
+  if (n < 0 || n >= (int64_t(1) << 31)) return fail(TG_E_INVALID, "%s: n=%lld out of range", fn, (long long)n);
+  if (n_qk_heads <= 0 || n_v_heads <= 0 || n_v_heads % n_qk_heads != 0)
+    return fail(TG_E_INVALID, "%s: n_qk_heads=%d, n_v_heads=%d (need a positive multiple)", fn,
+                n_qk_heads, n_v_heads);
+  if (head_dim != 128) return fail(TG_E_UNSUPPORTED, "%s: head_dim=%d (supported: 128)", fn, head_dim);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(TG_E_INVALID, "%s: scale must be finite", fn);
+  if (n == 0) return TG_OK;
+  if (!q || !k || !v || !g || !beta || !out) return fail(TG_E_INVALID, "%s: null tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+    return fail(TG_E_INVALID, "%s: q/k/v/out/states must be 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(g) & 3u) || (reinterpret_cast<uintptr_t>(beta) & 3u))
+    return fail(TG_E_INVALID, "%s: g/beta must be 4-byte aligned", fn);
+  const size_t need = tg::gdn_workspace_bytes(n, n_qk_heads, n_v_heads);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(TG_E_WORKSPACE, "%s: workspace %p of %zu bytes (need %zu, 16-byte aligned)", fn,
+                workspace, workspace_bytes, need);
+  return hip_status(tg::launch_gdn_fwd(q, k, v, g, beta, n, n_qk_heads, n_v_heads, scale,
+                                       initial_state, final_state, out, workspace, as_hip(stream)),
+                    "tg_gdn_fwd launch");
+}
+
+namespace {
 bool decode_shape_ok(int64_t n, int32_t hq, int32_t hkv, int32_t d) {
   if (n <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;
   const int32_t g = hq / hkv;

@@ -1,0 +1,436 @@
+// Gated DeltaNet recurrence over the kept rows, for gfx950.
+//
+// The coverage pages (lucasainews.com TokenGate article, "성능 결과";
+// miraibroadcast.com, "Resultados em modelos maiores"; heraldofai.com,
+// "Vantaggi in velocità e memoria") report TokenGate on a hybrid model whose
+// Gated DeltaNet layers sit between full-attention layers, and that it prunes
+// those recurrent layers as well.  Above the gate such a layer runs its
+// recurrence over the kept rows only, in original order.  The recurrence is
+// the gated delta rule of Gated DeltaNet (Yang, Kautz, Hatamizadeh, ICLR 2025),
+// per value head h with state S [dv, dk]:
+//     S <- exp(g_t) S;   S <- S + beta_t (v_t - S k_t) k_t^T;   o_t = scale S q_t.
+//
+// Chunked form used here (chunks of C = 64 rows; within a chunk c_i is the
+// cumulative log decay up to row i, Gam_i = exp(c_i), S the chunk's start
+// state):
+//   A_ij = beta_i exp(c_i - c_j) k_i.k_j (j < i),  (I + A) [W | U'] =
+//          [diag(beta Gam) K | diag(beta) V]   (solved in fp32)
+//   U    = U' - W S^T                           (the rows' written deltas)
+//   O    = scale (diag(Gam) Q S^T + P U),  P_ij = exp(c_i - c_j) q_i.k_j (j <= i)
+//   S    <- Gam_last S + U^T Kt,            Kt_j = exp(c_last - c_j) k_j
+//
+// Two launches:
+// 1. gdn_prep: one work-group per (chunk, value head), chunks in parallel.
+//    Forms K K^T and Q K^T on bf16 MFMA (exact products, fp32 sums), A and P
+//    with their decays, solves (I + A) X = R by forward substitution in fp32
+//    (a thread per right-hand-side column), and writes every operand the
+//    chain needs as fp16 MFMA fragments: -W, U', P, Kt^T, Q and the c_i.
+// 2. gdn_state: one single-wave work-group per (value head, 32 value rows)
+//    walks the chunks in order.  Its fp32 state slice S^T [128 dk x 32 dv]
+//    lives in MFMA accumulators; per chunk: U = U' - W S^T and O = Q S^T
+//    (16 + 16 fp16 MFMAs), O = Gam O + P U (8), S^T = Gam_last S^T + Kt^T U
+//    (16).  The state's accumulator layout is used directly as the B operand:
+//    the contraction index k of every product (dk for W S^T and Q S^T, the
+//    chunk row for P U and Kt^T U) is permuted within each 16-wide k-step to
+//    the order in which the accumulators hold it, and the prep pass writes
+//    the A operands in that same order.  Rows of the value dimension evolve
+//    independently, which is what lets the chain split over 32-row blocks.
+//
+// Numerics: bf16 inputs; decays, the solve, the state and every sum in fp32;
+// the MFMA operands (W, U', P, Kt, q and the fp32 state and deltas) rounded
+// to fp16 (11-bit mantissa; q and k are unit vectors, values of v above 65504
+// would saturate); output rounded to bf16.
+#include <cmath>
+
+#include "tg_device.h"
+#include "tg_launch.h"
+
+namespace tg {
+namespace {
+
+constexpr int kD = 128;      // dk = dv
+constexpr int kC = 64;       // chunk rows
+constexpr int kBV = 32;      // value rows per chain
+constexpr int kXS = 2 * kD + 8;   // LDS row of the solve's result (fp16, padded)
+
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+// Per (chunk, value head) workspace record, then per (chunk, q/k head) the q
+// fragments.
+constexpr int kOffW = 0;                        // -W fragments: [s 8][r 2][lane][8 fp16]
+constexpr int kOffU = kOffW + kC * kD * 2;      // U' accumulator images: [b 4][r 2][lane][16 fp16]
+constexpr int kOffP = kOffU + kC * kD * 2;      // P fragments: [s 4][r 2][lane][8 fp16]
+constexpr int kOffK = kOffP + kC * kC * 2;      // Kt^T fragments: [s 4][t 4][lane][8 fp16]
+constexpr int kOffG = kOffK + kD * kC * 2;      // c_i [64] fp32
+constexpr int kRec = kOffG + kC * 4;
+constexpr int kQRec = kC * kD * 2;              // q fragments: [s 8][r 2][lane][8 fp16]
+
+// Index held by (k-step s, lane half hh, element e) of a fragment: the order
+// of the rows an MFMA accumulator holds in its registers 8 (s % 2) .. + 7.
+__device__ __forceinline__ int kperm(int s, int hh, int e) {
+  return 16 * s + 8 * (e >> 2) + 4 * hh + (e & 3);
+}
+// Row (within a 32-row tile) of accumulator register j in lane half hh.
+__device__ __forceinline__ int crow(int j, int hh) { return 8 * (j >> 2) + 4 * hh + (j & 3); }
+
+__device__ __forceinline__ floatx16 mfma_f16(f16x8 a, f16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Row r of a 64 x 128 bf16 tile in LDS: 16-byte chunk cc at slot cc ^ (r & 15)
+// (16 consecutive rows read the same chunk from 16 different slots).
+__device__ __forceinline__ int tile_off(int r, int cc) { return r * 256 + ((cc ^ (r & 15)) << 4); }
+__device__ __forceinline__ float tile_at(const char* t, int r, int col) {
+  return bf2f(*reinterpret_cast<const uint16_t*>(t + tile_off(r, col >> 3) + 2 * (col & 7)));
+}
+
+// ---------------------------------------------------------------------------
+// gdn_prep
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gdn_prep_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, int n, int Hk, int Hv,
+    char* __restrict__ rec_base, char* __restrict__ qrec_base) {
+  __shared__ __align__(16) char lds_k[kC * kD * 2];
+  __shared__ __align__(16) char lds_q[kC * kD * 2];
+  __shared__ __align__(16) float lds_a[kC][kC];
+  __shared__ __align__(16) float lds_p[kC][kC];
+  __shared__ __align__(16) _Float16 lds_x[kC][kXS];
+  __shared__ float lds_c[kC], lds_b[kC], lds_gam[kC];
+
+  const int c = blockIdx.x / Hv, h = blockIdx.x % Hv;
+  const int kh = h / (Hv / Hk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, m = lane & 31;
+  const int row0 = c * kC;
+  char* rec = rec_base + (static_cast<size_t>(c) * Hv + h) * kRec;
+
+  // K and Q rows of the chunk (rows past n read as zero)
+  for (int i = tid; i < kC * 16; i += 256) {
+    const int r = i >> 4, cc = i & 15;
+    u32x4 kv = zero_u32x4(), qv = zero_u32x4();
+    if (row0 + r < n) {
+      const size_t off = (static_cast<size_t>(row0 + r) * Hk + kh) * kD + 8 * cc;
+      kv = ld16(k + off);
+      qv = ld16(q + off);
+    }
+    st16(lds_k + tile_off(r, cc), kv);
+    st16(lds_q + tile_off(r, cc), qv);
+  }
+  // cumulative log decay c_i (inclusive, fixed order), beta, exp(c_i)
+  if (wave == 0) {
+    float gv = 0.f, bv = 0.f;
+    if (row0 + lane < n) {
+      gv = g[static_cast<size_t>(row0 + lane) * Hv + h];
+      bv = beta[static_cast<size_t>(row0 + lane) * Hv + h];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(gv, o);
+      if (lane >= o) gv += t;
+    }
+    lds_c[lane] = gv;
+    lds_b[lane] = bv;
+    lds_gam[lane] = __expf(gv);
+    reinterpret_cast<float*>(rec + kOffG)[lane] = gv;
+  }
+  __syncthreads();
+
+  // K K^T -> A and Q K^T -> P, lower-triangle 32 x 32 tiles (0,0), (1,0), (1,1)
+  for (int ti = wave; ti < 6; ti += 4) {
+    const bool is_p = ti >= 3;
+    const int I = (ti % 3) == 0 ? 0 : 1, J = (ti % 3) == 2 ? 1 : 0;
+    const char* src = is_p ? lds_q : lds_k;
+    const int ra = 32 * I + m, rb = 32 * J + m;
+    floatx16 acc = zero16();
+#pragma unroll
+    for (int s = 0; s < kD / 16; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(src + tile_off(ra, 2 * s + hh));
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(lds_k + tile_off(rb, 2 * s + hh));
+      acc = mfma_32x32x16(a, b, acc);
+    }
+    const int j = rb;
+    const float cj = lds_c[j];
+#pragma unroll
+    for (int jr = 0; jr < 16; ++jr) {
+      const int i = 32 * I + crow(jr, hh);
+      const float dec = j <= i ? __expf(lds_c[i] - cj) : 0.f;
+      if (is_p) lds_p[i][j] = dec * acc[jr];
+      else lds_a[i][j] = j < i ? lds_b[i] * dec * acc[jr] : 0.f;
+    }
+  }
+
+  // q fragments (once per q/k head: from the first value head of its group)
+  if (h % (Hv / Hk) == 0) {
+    char* qrec = qrec_base + (static_cast<size_t>(c) * Hk + kh) * kQRec;
+    for (int u = tid; u < 8 * 2 * 64; u += 256) {
+      const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
+      const int mm = ln & 31, h2 = ln >> 5;
+      f16x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = static_cast<_Float16>(tile_at(lds_q, 32 * r + mm, kperm(s, h2, e)));
+      *reinterpret_cast<f16x8*>(qrec + static_cast<size_t>(u) * 16) = x;
+    }
+  }
+  // Kt^T fragments: exp(c_last - c_j) k_j, A operand [dk][row]
+  {
+    const float c_last = lds_c[kC - 1];
+    for (int u = tid; u < 4 * 4 * 64; u += 256) {
+      const int ln = u & 63, t = (u >> 6) & 3, s = u >> 8;
+      const int mm = ln & 31, h2 = ln >> 5;
+      f16x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int rr = kperm(s, h2, e);
+        x[e] = static_cast<_Float16>(__expf(c_last - lds_c[rr]) * tile_at(lds_k, rr, 32 * t + mm));
+      }
+      *reinterpret_cast<f16x8*>(rec + kOffK + static_cast<size_t>(u) * 16) = x;
+    }
+  }
+  __syncthreads();
+
+  // (I + A) X = R, one right-hand-side column per thread: columns 0..127 are
+  // beta_i Gam_i k_i (-> W), 128..255 are beta_i v_i (-> U').  Forward
+  // substitution in fp32, row by row.
+  {
+    const int col = tid;
+    float x[kC];
+    if (col < kD) {
+#pragma unroll
+      for (int i = 0; i < kC; ++i) x[i] = lds_b[i] * lds_gam[i] * tile_at(lds_k, i, col);
+    } else {
+      const uint16_t* vp = reinterpret_cast<const uint16_t*>(v) + static_cast<size_t>(h) * kD + (col - kD);
+#pragma unroll
+      for (int i = 0; i < kC; ++i)
+        x[i] = row0 + i < n ? lds_b[i] * bf2f(vp[static_cast<size_t>(row0 + i) * Hv * kD]) : 0.f;
+    }
+#pragma unroll
+    for (int i = 1; i < kC; ++i) {
+      float acc = x[i];
+#pragma unroll
+      for (int j4 = 0; j4 < i; j4 += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(&lds_a[i][j4]);
+        acc = __builtin_fmaf(-a.x, x[j4], acc);
+        if (j4 + 1 < i) acc = __builtin_fmaf(-a.y, x[j4 + 1], acc);
+        if (j4 + 2 < i) acc = __builtin_fmaf(-a.z, x[j4 + 2], acc);
+        if (j4 + 3 < i) acc = __builtin_fmaf(-a.w, x[j4 + 3], acc);
+      }
+      x[i] = acc;
+    }
+#pragma unroll
+    for (int i = 0; i < kC; ++i) lds_x[i][col] = static_cast<_Float16>(col < kD ? -x[i] : x[i]);
+  }
+  __syncthreads();
+
+  // -W fragments (A operand [row][dk])
+  for (int u = tid; u < 8 * 2 * 64; u += 256) {
+    const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
+    const int mm = ln & 31, h2 = ln >> 5;
+    f16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = lds_x[32 * r + mm][kperm(s, h2, e)];
+    *reinterpret_cast<f16x8*>(rec + kOffW + static_cast<size_t>(u) * 16) = x;
+  }
+  // U' accumulator images per 32-row value block: lane (dv column mm, half
+  // h2), register jr = row 32 r + crow(jr, h2)
+  for (int u = tid; u < 4 * 2 * 64; u += 256) {
+    const int ln = u & 63, r = (u >> 6) & 1, b = u >> 7;
+    const int mm = ln & 31, h2 = ln >> 5;
+    f16x8 x0, x1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x0[e] = lds_x[32 * r + crow(e, h2)][kD + kBV * b + mm];
+      x1[e] = lds_x[32 * r + crow(8 + e, h2)][kD + kBV * b + mm];
+    }
+    f16x8* dst = reinterpret_cast<f16x8*>(rec + kOffU + static_cast<size_t>(u) * 32);
+    dst[0] = x0;
+    dst[1] = x1;
+  }
+  // P fragments (A operand [row i][row j], zero above the diagonal)
+  for (int u = tid; u < 4 * 2 * 64; u += 256) {
+    const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
+    const int mm = ln & 31, h2 = ln >> 5;
+    const int i = 32 * r + mm;
+    f16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = kperm(s, h2, e);
+      x[e] = static_cast<_Float16>(j <= i ? lds_p[i][j] : 0.f);
+    }
+    *reinterpret_cast<f16x8*>(rec + kOffP + static_cast<size_t>(u) * 16) = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gdn_state
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f16x8 to_f16x8(const floatx16& a, int half) {
+  f16x8 x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(a[8 * half + e]);
+  return x;
+}
+
+__global__ __launch_bounds__(64) void gdn_state_kernel(const char* __restrict__ rec_base,
+                                                       const char* __restrict__ qrec_base, int n,
+                                                       int Hk, int Hv, float scale,
+                                                       const float* __restrict__ s_init,
+                                                       float* __restrict__ s_final,
+                                                       bf16* __restrict__ out) {
+  const int h = blockIdx.x / (kD / kBV), b = blockIdx.x % (kD / kBV);
+  const int kh = h / (Hv / Hk);
+  const int lane = threadIdx.x, m = lane & 31, hh = lane >> 5;
+  const int nc = (n + kC - 1) / kC;
+  const int dv = kBV * b + m;   // this lane's value row
+
+  // S^T slice: tile t = dk rows 32 t .., register jr = dk row 32 t + crow(jr, hh)
+  floatx16 st[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int jr = 0; jr < 16; ++jr)
+      st[t][jr] = s_init != nullptr
+                      ? s_init[(static_cast<size_t>(h) * kD + dv) * kD + 32 * t + crow(jr, hh)]
+                      : 0.f;
+  }
+
+  for (int c = 0; c < nc; ++c) {
+    const char* rec = rec_base + (static_cast<size_t>(c) * Hv + h) * kRec;
+    const char* qrec = qrec_base + (static_cast<size_t>(c) * Hk + kh) * kQRec;
+    f16x8 wf[2][8], qf[2][8], pf[2][4], kf[4][4];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        wf[r][s] = *reinterpret_cast<const f16x8*>(rec + kOffW + ((s * 2 + r) * 64 + lane) * 16);
+        qf[r][s] = *reinterpret_cast<const f16x8*>(qrec + ((s * 2 + r) * 64 + lane) * 16);
+      }
+    }
+    f16x8 up[2][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const f16x8* src = reinterpret_cast<const f16x8*>(rec + kOffU + ((b * 2 + r) * 64 + lane) * 32);
+      up[r][0] = src[0];
+      up[r][1] = src[1];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        pf[r][s] = *reinterpret_cast<const f16x8*>(rec + kOffP + ((s * 2 + r) * 64 + lane) * 16);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        kf[t][s] = *reinterpret_cast<const f16x8*>(rec + kOffK + ((s * 4 + t) * 64 + lane) * 16);
+    }
+    const float* cg = reinterpret_cast<const float*>(rec + kOffG);
+    float4 cr[2][4];   // c_i of this lane's rows: 32 r + 8 q + 4 hh + 0..3
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) cr[r][qq] = *reinterpret_cast<const float4*>(cg + 32 * r + 8 * qq + 4 * hh);
+    }
+    const float c_last = cg[kC - 1];
+
+    // B operand of the state: k-step s = registers 8 (s % 2) .. + 7 of tile s / 2
+    f16x8 bs[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bs[s] = to_f16x8(st[s >> 1], s & 1);
+
+    floatx16 u[2], o[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u[r][e] = static_cast<float>(up[r][0][e]);
+        u[r][8 + e] = static_cast<float>(up[r][1][e]);
+      }
+      o[r] = zero16();
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        u[r] = mfma_f16(wf[r][s], bs[s], u[r]);
+        o[r] = mfma_f16(qf[r][s], bs[s], o[r]);
+      }
+    }
+    // the rows' own decay from the chunk start
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        o[r][4 * qq + 0] *= __expf(cr[r][qq].x);
+        o[r][4 * qq + 1] *= __expf(cr[r][qq].y);
+        o[r][4 * qq + 2] *= __expf(cr[r][qq].z);
+        o[r][4 * qq + 3] *= __expf(cr[r][qq].w);
+      }
+    }
+    f16x8 bu[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bu[s] = to_f16x8(u[s >> 1], s & 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) o[r] = mfma_f16(pf[r][s], bu[s], o[r]);
+    }
+    const float gl = __expf(c_last);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int jr = 0; jr < 16; ++jr) st[t][jr] *= gl;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) st[t] = mfma_f16(kf[t][s], bu[s], st[t]);
+    }
+    // outputs: lane (value row dv, half hh), register jr = row 32 r + crow(jr, hh)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int jr = 0; jr < 16; ++jr) {
+        const int row = c * kC + 32 * r + crow(jr, hh);
+        if (row < n)
+          out[(static_cast<size_t>(row) * Hv + h) * kD + dv] = static_cast<bf16>(scale * o[r][jr]);
+      }
+    }
+  }
+  if (s_final != nullptr) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int jr = 0; jr < 16; ++jr)
+        s_final[(static_cast<size_t>(h) * kD + dv) * kD + 32 * t + crow(jr, hh)] = st[t][jr];
+    }
+  }
+}
+
+}  // namespace
+
+size_t gdn_workspace_bytes(int64_t n, int n_qk_heads, int n_v_heads) {
+  if (n <= 0) return 0;
+  const size_t nc = static_cast<size_t>((n + kC - 1) / kC);
+  return nc * (static_cast<size_t>(n_v_heads) * kRec + static_cast<size_t>(n_qk_heads) * kQRec);
+}
+
+hipError_t launch_gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                          const float* beta, int64_t n, int n_qk_heads, int n_v_heads, float scale,
+                          const float* initial_state, float* final_state, uint16_t* out,
+                          void* workspace, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int nc = static_cast<int>((n + kC - 1) / kC);
+  char* rec = static_cast<char*>(workspace);
+  char* qrec = rec + static_cast<size_t>(nc) * n_v_heads * kRec;
+  const int ni = static_cast<int>(n);
+  hipLaunchKernelGGL(gdn_prep_kernel, dim3(static_cast<unsigned>(nc) * n_v_heads), dim3(256), 0,
+                     stream, reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
+                     reinterpret_cast<const bf16*>(v), g, beta, ni, n_qk_heads, n_v_heads, rec, qrec);
+  hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(n_v_heads) * (kD / kBV)), dim3(64),
+                     0, stream, rec, qrec, ni, n_qk_heads, n_v_heads, scale, initial_state,
+                     final_state, reinterpret_cast<bf16*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace tg

@@ -72,4 +72,16 @@ hipError_t launch_qk_norm_rope(const uint16_t* src, int64_t src_rows, const int3
                                const float* norm_weight, float eps, double theta, uint16_t* dst,
                                hipStream_t stream);
 
+// Bytes of workspace the Gated DeltaNet launch needs for n rows (head_dim 128):
+// per 64-row chunk and value head the prep pass's fp16 operand fragments and
+// cumulative decays, per chunk and q/k head the q fragments.
+size_t gdn_workspace_bytes(int64_t n, int n_qk_heads, int n_v_heads);
+
+// Gated delta rule over n rows (head_dim 128); initial_state / final_state
+// [n_v_heads, 128, 128] fp32 are optional.
+hipError_t launch_gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
+                          const float* beta, int64_t n, int n_qk_heads, int n_v_heads, float scale,
+                          const float* initial_state, float* final_state, uint16_t* out,
+                          void* workspace, hipStream_t stream);
+
 }  // namespace tg

@@ -227,3 +227,40 @@ def qkv_template(w: Workload, t: int, n: Optional[int] = None):
 
 def template_of_layer(w: Workload, layer: int) -> int:
     return layer % min(w.n_templates, w.n_layers)
+
+
+# ---------------------------------------------------------------------------
+# Hybrid-model (Gated DeltaNet) layer inputs
+# ---------------------------------------------------------------------------
+
+# The pages run TokenGate on a hybrid Qwen3.5-2B (Gated DeltaNet layers between
+# full-attention layers) but give none of its shapes.  Stand-in: the
+# linear-attention layout of the Qwen3-Next family, 16 q/k heads and 32 value
+# heads of 128 (value head h reads q/k head h // 2).
+GDN_QK_HEADS = 16
+GDN_V_HEADS = 32
+GDN_HEAD_DIM = 128
+_S_GDN0 = 40
+
+
+def gdn_inputs(seed: int, n: int, n_qk_heads: int = GDN_QK_HEADS, n_v_heads: int = GDN_V_HEADS,
+               head_dim: int = GDN_HEAD_DIM, layer: int = 0) -> dict:
+    """One Gated DeltaNet layer's inputs over n rows (positions 0..n-1):
+    q, k ~ N(0, 1) L2-normalised per head (the layer's own normalisation) and
+    rounded to bf16; v ~ N(0, 1) clipped to +-3.5, bf16; per row and value
+    head a log decay g = log(a) with a ~ U(0.82, 0.999) and a write strength
+    beta = sigmoid(N(0, 1)), both float32."""
+    out = {}
+    for j, (name, heads) in enumerate((("q", n_qk_heads), ("k", n_qk_heads), ("v", n_v_heads))):
+        rng = _rng(seed, _S_GDN0 + 8 * layer + j)
+        x = rng.standard_normal((n, heads, head_dim), dtype=np.float32)
+        if name == "v":
+            np.clip(x, -3.5, 3.5, out=x)
+        else:
+            x /= np.linalg.norm(x, axis=-1, keepdims=True)
+        out[name] = round_bf16(x)
+    rng = _rng(seed, _S_GDN0 + 8 * layer + 3)
+    out["g"] = np.log(rng.uniform(0.82, 0.999, size=(n, n_v_heads))).astype(np.float32)
+    rng = _rng(seed, _S_GDN0 + 8 * layer + 4)
+    out["beta"] = (1.0 / (1.0 + np.exp(-rng.standard_normal((n, n_v_heads))))).astype(np.float32)
+    return out

@@ -42,6 +42,9 @@ _SIGNATURES = {
     "tg_gated_attn_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "tg_decode_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
+    "tg_gdn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
+    "tg_gdn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, ctypes.c_float, _P,
+                                  _P, _P, _P, ctypes.c_size_t, _P]),
     "tg_qk_norm_rope": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I32, _I32, _P, ctypes.c_float,
                                        ctypes.c_double, _P, _P]),
     "tg_gated_decode_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P,
@@ -370,6 +373,52 @@ def gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_score:
                                    _ptr(g["dgain"]), _ptr(g["dtau"]), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return g
+
+
+def gdn_workspace_bytes(n: int, n_qk_heads: int, n_v_heads: int, head_dim: int = 128) -> int:
+    return int(lib().tg_gdn_workspace_bytes(n, n_qk_heads, n_v_heads, head_dim))
+
+
+def gdn_workspace(n: int, n_qk_heads: int, n_v_heads: int, head_dim: int = 128,
+                  device="cuda") -> torch.Tensor:
+    """A device buffer large enough for one Gated DeltaNet call over n rows."""
+    return torch.empty(max(gdn_workspace_bytes(n, n_qk_heads, n_v_heads, head_dim), 16),
+                       dtype=torch.uint8, device=device)
+
+
+def gdn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+            beta: torch.Tensor, scale: Optional[float] = None,
+            initial_state: Optional[torch.Tensor] = None, want_state: bool = False,
+            out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gated delta rule over the rows of q/k [n, Hk, d], v [n, Hv, d] (bf16),
+    g/beta [n, Hv] (fp32).  Returns out [n, Hv, d] bf16 (and the final state
+    [Hv, d, d] fp32 if asked or given)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16)
+    _need(g, "g", torch.float32); _need(beta, "beta", torch.float32)
+    n, hk, d = q.shape
+    hv = v.shape[1]
+    if k.shape != q.shape or v.shape != (n, hv, d) or g.shape != (n, hv) or beta.shape != (n, hv):
+        raise ValueError("gated delta rule operand shapes do not match")
+    if out is None:
+        out = torch.empty((n, hv, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32)
+    if want_state and final_state is None:
+        final_state = torch.empty((hv, d, d), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32)
+    if workspace is None:
+        workspace = gdn_workspace(n, hk, hv, d, q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    sc = 1.0 / (d ** 0.5) if scale is None else float(scale)
+    _check(lib().tg_gdn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), n, hk, hv, d, sc,
+                            _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (out, final_state) if final_state is not None else out
 
 
 def decode_workspace_bytes(n: int, n_q_heads: int, n_kv_heads: int, head_dim: int) -> int:

@@ -41,6 +41,7 @@ def test_header_declares_the_five_entry_points():
                "tg_gated_attn_fwd", "tg_full_attn_fwd", "tg_attn_workspace_bytes",
                "tg_gated_decode_fwd", "tg_decode_workspace_bytes", "tg_qk_norm_rope",
                "tg_gated_attn_bwd", "tg_attn_bwd_workspace_bytes", "tg_gated_attn_fwd_train",
+               "tg_gdn_fwd", "tg_gdn_workspace_bytes",
                "tg_kept_count", "tg_status_str", "tg_last_error"):
         assert fn in names
 
@@ -159,6 +160,39 @@ def test_attention_validation(L):
     assert L.tg_attn_workspace_bytes(0, 16, 8, 128) == 0
     assert L.tg_attn_workspace_bytes(100, 16, 6, 128) == 0
     assert L.tg_attn_workspace_bytes(100, 16, 8, 96) == 0
+
+
+def test_gdn_workspace_bytes(L):
+    # per 64-row chunk: 56.25 KiB per value head + 16 KiB of q fragments per q/k head
+    rec = 16384 + 16384 + 8192 + 16384 + 256
+    for n, hk, hv in ((1, 1, 1), (64, 16, 32), (65, 16, 32), (8448, 16, 32)):
+        assert L.tg_gdn_workspace_bytes(n, hk, hv, 128) == -(-n // 64) * (hv * rec + hk * 16384)
+    assert L.tg_gdn_workspace_bytes(0, 16, 32, 128) == 0
+    assert L.tg_gdn_workspace_bytes(100, 16, 24, 128) == 0      # 24 % 16
+    assert L.tg_gdn_workspace_bytes(100, 16, 32, 64) == 0
+
+
+def test_gdn_validation(L):
+    f = L.tg_gdn_fwd
+    W = 1 << 34
+    #        q  k  v  g  b  n   hk hv d    scale s0 s1 out ws wsb
+    def call(n=10, hk=2, hv=4, d=128, scale=0.1, q=A, g=A, s0=None, s1=None, out=A, ws=A, wsb=W):
+        return f(q, A, A, g, A, n, hk, hv, d, ctypes.c_float(scale), s0, s1, out, ws, wsb, 0)
+    assert call(n=-1) == INVALID
+    assert call(hk=3, hv=4) == INVALID
+    assert call(hk=0) == INVALID
+    assert call(d=64) == UNSUPPORTED
+    assert call(scale=float("nan")) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(q=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(q=A + 8) == INVALID                                  # alignment
+    assert call(g=A + 2) == INVALID
+    assert call(s0=A + 4) == INVALID
+    need = L.tg_gdn_workspace_bytes(10, 2, 4, 128)
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(n=0, q=None, g=None, out=None, ws=None, wsb=0) == OK   # no-op
 
 
 def test_training_forward_validation(L):
