@@ -284,9 +284,9 @@ tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
 
 /*
  * Bytes of device workspace tg_gdn_fwd needs for n rows: per 64-row chunk and
- * value head 56.25 KiB (the recurrence's operands as fp16 MFMA fragments and
- * the chunk's cumulative decays), per chunk and q/k head 16 KiB (q
- * fragments).  Host-only arithmetic; 0 for n <= 0 or unsupported shapes.
+ * value head 72.25 KiB (the recurrence's operands as fp16 MFMA fragments and
+ * the chunk's decay).  Host-only arithmetic; 0 for n <= 0 or unsupported
+ * shapes.
  */
 size_t tg_gdn_workspace_bytes(int64_t n, int32_t n_qk_heads, int32_t n_v_heads, int32_t head_dim);
 
@@ -312,7 +312,8 @@ size_t tg_gdn_workspace_bytes(int64_t n, int32_t n_qk_heads, int32_t n_v_heads, 
  *   out   [n, n_v_heads, head_dim] bf16 (output, round-to-nearest-even)
  *   workspace  device scratch of at least tg_gdn_workspace_bytes(...) bytes,
  *         16-byte aligned, caller-owned, overwritten.
- * Supported: head_dim 128, n_v_heads % n_qk_heads == 0, n < 2^31.
+ * Supported: head_dim 128, n_v_heads % n_qk_heads == 0,
+ * n * n_v_heads * head_dim * 2 < 2^31 (else TG_E_UNSUPPORTED).
  * Numerics: chunks of 64 rows; the within-chunk solve, decays, state and sums
  * in fp32, the MFMA operands in fp16.  n == 0 is a no-op (final_state not
  * written).

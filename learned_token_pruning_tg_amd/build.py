@@ -30,9 +30,15 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-source additions.  The Gated DeltaNet chain keeps its fp32 state in MFMA
+# accumulators that the VALU also touches every chunk (decay, fp16 copies):
+# accumulators in arch VGPRs avoid an AGPR round trip per touch.
+SOURCE_FLAGS = {"tg_gdn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *DEVICE_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

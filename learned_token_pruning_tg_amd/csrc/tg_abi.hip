@@ -258,7 +258,8 @@ tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
 
 namespace {
 bool gdn_shape_ok(int64_t n, int32_t hk, int32_t hv, int32_t d) {
-  return n >= 0 && n < (int64_t(1) << 31) && hk > 0 && hv > 0 && hv % hk == 0 && d == 128;
+  return n >= 0 && n < (int64_t(1) << 31) && hk > 0 && hv > 0 && hv % hk == 0 && d == 128 &&
+         n * hv * d * 2 < (int64_t(1) << 31);
 }
 }  // namespace
 
@@ -277,6 +278,9 @@ tg_status tg_gdn_fwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v, const
     return fail(TG_E_INVALID, "%s: n_qk_heads=%d, n_v_heads=%d (need a positive multiple)", fn,
                 n_qk_heads, n_v_heads);
   if (head_dim != 128) return fail(TG_E_UNSUPPORTED, "%s: head_dim=%d (supported: 128)", fn, head_dim);
+  if (n * n_v_heads * head_dim * 2 >= (int64_t(1) << 31))
+    return fail(TG_E_UNSUPPORTED, "%s: n=%lld rows of %d value heads x %d exceed 2^31 bytes", fn,
+                (long long)n, n_v_heads, head_dim);
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(TG_E_INVALID, "%s: scale must be finite", fn);
   if (n == 0) return TG_OK;

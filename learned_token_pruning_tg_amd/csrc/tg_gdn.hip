@@ -24,12 +24,15 @@
 //    Forms K K^T and Q K^T on bf16 MFMA (exact products, fp32 sums), A and P
 //    with their decays, solves (I + A) X = R by forward substitution in fp32
 //    (a thread per right-hand-side column), and writes every operand the
-//    chain needs as fp16 MFMA fragments: -W, U', P, Kt^T, Q and the c_i.
-// 2. gdn_state: one single-wave work-group per (value head, 32 value rows)
-//    walks the chunks in order.  Its fp32 state slice S^T [128 dk x 32 dv]
-//    lives in MFMA accumulators; per chunk: U = U' - W S^T and O = Q S^T
-//    (16 + 16 fp16 MFMAs), O = Gam O + P U (8), S^T = Gam_last S^T + Kt^T U
-//    (16).  The state's accumulator layout is used directly as the B operand:
+//    chain needs as fp16 MFMA fragments: -W, U', scale P, Kt^T and the scaled
+//    queries scale Gam_i q_i, then Gam_last.
+// 2. gdn_state: one work-group per value head walks the chunks in order, a
+//    wave per 32 value rows (the rows of S evolve independently), the head's
+//    per-chunk operands DMAed once into a two-stage LDS ring for the four
+//    waves.  Each wave's fp32 state slice S^T [128 dk x 32 dv]
+//    lives in MFMA accumulators; per chunk: U = U' - W S^T and
+//    O = (scale Gam Q) S^T (16 + 16 fp16 MFMAs), O += (scale P) U (8),
+//    S^T = Gam_last S^T + Kt^T U (16).  The state's accumulator layout is used directly as the B operand:
 //    the contraction index k of every product (dk for W S^T and Q S^T, the
 //    chunk row for P U and Kt^T U) is permuted within each 16-wide k-step to
 //    the order in which the accumulators hold it, and the prep pass writes
@@ -55,15 +58,14 @@ constexpr int kXS = 2 * kD + 8;   // LDS row of the solve's result (fp16, padded
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
-// Per (chunk, value head) workspace record, then per (chunk, q/k head) the q
-// fragments.
+// Per (chunk, value head) workspace record.
 constexpr int kOffW = 0;                        // -W fragments: [s 8][r 2][lane][8 fp16]
 constexpr int kOffU = kOffW + kC * kD * 2;      // U' accumulator images: [b 4][r 2][lane][16 fp16]
 constexpr int kOffP = kOffU + kC * kD * 2;      // P fragments: [s 4][r 2][lane][8 fp16]
 constexpr int kOffK = kOffP + kC * kC * 2;      // Kt^T fragments: [s 4][t 4][lane][8 fp16]
-constexpr int kOffG = kOffK + kD * kC * 2;      // c_i [64] fp32
-constexpr int kRec = kOffG + kC * 4;
-constexpr int kQRec = kC * kD * 2;              // q fragments: [s 8][r 2][lane][8 fp16]
+constexpr int kOffQ = kOffK + kD * kC * 2;      // scaled q fragments: [s 8][r 2][lane][8 fp16]
+constexpr int kOffG = kOffQ + kC * kD * 2;      // Gam_last (fp32), then padding to 256 B
+constexpr int kRec = kOffG + 256;
 
 // Index held by (k-step s, lane half hh, element e) of a fragment: the order
 // of the rows an MFMA accumulator holds in its registers 8 (s % 2) .. + 7.
@@ -94,13 +96,19 @@ __device__ __forceinline__ float tile_at(const char* t, int r, int col) {
 __global__ __launch_bounds__(256) void gdn_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int n, int Hk, int Hv,
-    char* __restrict__ rec_base, char* __restrict__ qrec_base) {
-  __shared__ __align__(16) char lds_k[kC * kD * 2];
-  __shared__ __align__(16) char lds_q[kC * kD * 2];
+    float scale, char* __restrict__ rec_base) {
+  // The K, Q and V tiles are dead once the solve has read its right-hand
+  // sides; its result X then overlays them (74 KiB in all: two work-groups
+  // per compute unit).
+  __shared__ __align__(16) char lds_tiles[3 * kC * kD * 2];
   __shared__ __align__(16) float lds_a[kC][kC];
-  __shared__ __align__(16) float lds_p[kC][kC];
-  __shared__ __align__(16) _Float16 lds_x[kC][kXS];
+  __shared__ __align__(16) _Float16 lds_p[kC][kC];
   __shared__ float lds_c[kC], lds_b[kC], lds_gam[kC];
+  char* const lds_k = lds_tiles;
+  char* const lds_q = lds_tiles + kC * kD * 2;
+  char* const lds_v = lds_tiles + 2 * kC * kD * 2;
+  _Float16 (*const lds_x)[kXS] = reinterpret_cast<_Float16 (*)[kXS]>(lds_tiles);
+  static_assert(kC * kXS * 2 <= 3 * kC * kD * 2, "X fits over the tiles");
 
   const int c = blockIdx.x / Hv, h = blockIdx.x % Hv;
   const int kh = h / (Hv / Hk);
@@ -109,17 +117,30 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   const int row0 = c * kC;
   char* rec = rec_base + (static_cast<size_t>(c) * Hv + h) * kRec;
 
-  // K and Q rows of the chunk (rows past n read as zero)
-  for (int i = tid; i < kC * 16; i += 256) {
-    const int r = i >> 4, cc = i & 15;
-    u32x4 kv = zero_u32x4(), qv = zero_u32x4();
-    if (row0 + r < n) {
-      const size_t off = (static_cast<size_t>(row0 + r) * Hk + kh) * kD + 8 * cc;
-      kv = ld16(k + off);
-      qv = ld16(q + off);
+  // K, Q and V rows of the chunk (rows past n read as zero), every load
+  // issued before the first store
+  {
+    u32x4 kv[4], qv[4], vv[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = tid + 256 * p;
+      const int r = i >> 4, cc = i & 15;
+      kv[p] = qv[p] = vv[p] = zero_u32x4();
+      if (row0 + r < n) {
+        const size_t off = (static_cast<size_t>(row0 + r) * Hk + kh) * kD + 8 * cc;
+        kv[p] = ld16(k + off);
+        qv[p] = ld16(q + off);
+        vv[p] = ld16(v + (static_cast<size_t>(row0 + r) * Hv + h) * kD + 8 * cc);
+      }
     }
-    st16(lds_k + tile_off(r, cc), kv);
-    st16(lds_q + tile_off(r, cc), qv);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = tid + 256 * p;
+      const int r = i >> 4, cc = i & 15;
+      st16(lds_k + tile_off(r, cc), kv[p]);
+      st16(lds_q + tile_off(r, cc), qv[p]);
+      st16(lds_v + tile_off(r, cc), vv[p]);
+    }
   }
   // cumulative log decay c_i (inclusive, fixed order), beta, exp(c_i)
   if (wave == 0) {
@@ -136,7 +157,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     lds_c[lane] = gv;
     lds_b[lane] = bv;
     lds_gam[lane] = __expf(gv);
-    reinterpret_cast<float*>(rec + kOffG)[lane] = gv;
+    if (lane == kC - 1) reinterpret_cast<float*>(rec + kOffG)[0] = __expf(gv);
   }
   __syncthreads();
 
@@ -159,23 +180,22 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     for (int jr = 0; jr < 16; ++jr) {
       const int i = 32 * I + crow(jr, hh);
       const float dec = j <= i ? __expf(lds_c[i] - cj) : 0.f;
-      if (is_p) lds_p[i][j] = dec * acc[jr];
+      if (is_p) lds_p[i][j] = static_cast<_Float16>(scale * dec * acc[jr]);
       else lds_a[i][j] = j < i ? lds_b[i] * dec * acc[jr] : 0.f;
     }
   }
 
-  // q fragments (once per q/k head: from the first value head of its group)
-  if (h % (Hv / Hk) == 0) {
-    char* qrec = qrec_base + (static_cast<size_t>(c) * Hk + kh) * kQRec;
-    for (int u = tid; u < 8 * 2 * 64; u += 256) {
-      const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
-      const int mm = ln & 31, h2 = ln >> 5;
-      f16x8 x;
+  // scaled q fragments: scale * Gam_i q_i, A operand [row][dk] (the rows' own
+  // decay from the chunk start and the read-out scale, folded in here)
+  for (int u = tid; u < 8 * 2 * 64; u += 256) {
+    const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
+    const int mm = ln & 31, h2 = ln >> 5;
+    const float f = scale * lds_gam[32 * r + mm];
+    f16x8 x;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = static_cast<_Float16>(tile_at(lds_q, 32 * r + mm, kperm(s, h2, e)));
-      *reinterpret_cast<f16x8*>(qrec + static_cast<size_t>(u) * 16) = x;
-    }
+    for (int e = 0; e < 8; ++e)
+      x[e] = static_cast<_Float16>(f * tile_at(lds_q, 32 * r + mm, kperm(s, h2, e)));
+    *reinterpret_cast<f16x8*>(rec + kOffQ + static_cast<size_t>(u) * 16) = x;
   }
   // Kt^T fragments: exp(c_last - c_j) k_j, A operand [dk][row]
   {
@@ -204,11 +224,10 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 #pragma unroll
       for (int i = 0; i < kC; ++i) x[i] = lds_b[i] * lds_gam[i] * tile_at(lds_k, i, col);
     } else {
-      const uint16_t* vp = reinterpret_cast<const uint16_t*>(v) + static_cast<size_t>(h) * kD + (col - kD);
 #pragma unroll
-      for (int i = 0; i < kC; ++i)
-        x[i] = row0 + i < n ? lds_b[i] * bf2f(vp[static_cast<size_t>(row0 + i) * Hv * kD]) : 0.f;
+      for (int i = 0; i < kC; ++i) x[i] = lds_b[i] * tile_at(lds_v, i, col - kD);
     }
+    __syncthreads();   // every right-hand side read: X may overwrite the tiles
 #pragma unroll
     for (int i = 1; i < kC; ++i) {
       float acc = x[i];
@@ -260,7 +279,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = kperm(s, h2, e);
-      x[e] = static_cast<_Float16>(j <= i ? lds_p[i][j] : 0.f);
+      x[e] = j <= i ? lds_p[i][j] : static_cast<_Float16>(0.f);
     }
     *reinterpret_cast<f16x8*>(rec + kOffP + static_cast<size_t>(u) * 16) = x;
   }
@@ -276,17 +295,37 @@ __device__ __forceinline__ f16x8 to_f16x8(const floatx16& a, int half) {
   return x;
 }
 
-__global__ __launch_bounds__(64) void gdn_state_kernel(const char* __restrict__ rec_base,
-                                                       const char* __restrict__ qrec_base, int n,
-                                                       int Hk, int Hv, float scale,
-                                                       const float* __restrict__ s_init,
-                                                       float* __restrict__ s_final,
-                                                       bf16* __restrict__ out) {
-  const int h = blockIdx.x / (kD / kBV), b = blockIdx.x % (kD / kBV);
-  const int kh = h / (Hv / Hk);
-  const int lane = threadIdx.x, m = lane & 31, hh = lane >> 5;
+// One work-group of four waves per value head; wave b carries the state
+// slice of value rows 32 b .. 32 b + 31.  Each chunk's operand record (the
+// -W, U', P, Kt^T and scaled q fragments and Gam_last, as the prep pass laid
+// them out) is DMAed into a two-stage LDS ring, once for the four waves; one
+// barrier per chunk, the next chunk's DMA in flight during this chunk.
+constexpr int kRecLds = (kRec + 1023) / 1024 * 1024;   // whole 1 KiB DMA pieces
+constexpr int kStage = kRecLds;
+
+__global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__ rec_base, int n,
+                                                        int Hv, const float* __restrict__ s_init,
+                                                        float* __restrict__ s_final,
+                                                        bf16* __restrict__ out) {
+  __shared__ __align__(16) char lds[2][kStage];
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int b = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // provably wave-uniform
+  const int m = lane & 31, hh = lane >> 5;
   const int nc = (n + kC - 1) / kC;
   const int dv = kBV * b + m;   // this lane's value row
+
+  // DMA of chunk c into stage st: pieces of 1 KiB dealt round-robin over the
+  // four waves (lane i moves the 16 bytes at 16 i of its piece); bytes past
+  // the record read as zeros.
+  auto dma = [&](int st, int c) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rr =
+        make_rsrc(rec_base + (static_cast<size_t>(c) * Hv + h) * kRec, kRec);
+    for (int j = b; j < kRecLds / 1024; j += 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rr, (__attribute__((address_space(3))) void*)(&lds[st][0] + 1024 * j), 16, 16 * lane,
+          1024 * j, 0, 0);
+  };
 
   // S^T slice: tile t = dk rows 32 t .., register jr = dk row 32 t + crow(jr, hh)
   floatx16 st[4];
@@ -299,101 +338,100 @@ __global__ __launch_bounds__(64) void gdn_state_kernel(const char* __restrict__ 
                       : 0.f;
   }
 
-  for (int c = 0; c < nc; ++c) {
-    const char* rec = rec_base + (static_cast<size_t>(c) * Hv + h) * kRec;
-    const char* qrec = qrec_base + (static_cast<size_t>(c) * Hk + kh) * kQRec;
-    f16x8 wf[2][8], qf[2][8], pf[2][4], kf[4][4];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        wf[r][s] = *reinterpret_cast<const f16x8*>(rec + kOffW + ((s * 2 + r) * 64 + lane) * 16);
-        qf[r][s] = *reinterpret_cast<const f16x8*>(qrec + ((s * 2 + r) * 64 + lane) * 16);
-      }
-    }
-    f16x8 up[2][2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const f16x8* src = reinterpret_cast<const f16x8*>(rec + kOffU + ((b * 2 + r) * 64 + lane) * 32);
-      up[r][0] = src[0];
-      up[r][1] = src[1];
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        pf[r][s] = *reinterpret_cast<const f16x8*>(rec + kOffP + ((s * 2 + r) * 64 + lane) * 16);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        kf[t][s] = *reinterpret_cast<const f16x8*>(rec + kOffK + ((s * 4 + t) * 64 + lane) * 16);
-    }
-    const float* cg = reinterpret_cast<const float*>(rec + kOffG);
-    float4 cr[2][4];   // c_i of this lane's rows: 32 r + 8 q + 4 hh + 0..3
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) cr[r][qq] = *reinterpret_cast<const float4*>(cg + 32 * r + 8 * qq + 4 * hh);
-    }
-    const float c_last = cg[kC - 1];
+  // output rows of this head: byte offset row * row_bytes + (4 hh row part) +
+  // dv * 2; the range ends at row n
+  const uint32_t row_bytes = static_cast<uint32_t>(Hv) * kD * 2;   // n * row_bytes < 2^31
+  const __amdgpu_buffer_rsrc_t rout =
+      make_rsrc(reinterpret_cast<const char*>(out) + static_cast<size_t>(h) * kD * 2,
+                static_cast<uint32_t>(n) * row_bytes - static_cast<uint32_t>(h) * kD * 2);
+  const uint32_t lane_off = static_cast<uint32_t>(4 * hh) * row_bytes + 2u * dv;
 
+  if (nc > 0) dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int c = 0; c < nc; ++c) {
+    // Every wave waited for its own DMA of chunk c (and its stores of chunk
+    // c - 2) before storing chunk c - 1's outputs; the barrier makes chunk c
+    // complete for all waves and frees the stage chunk c - 1 used.
+    __syncthreads();
+    if (c + 1 < nc) dma((c + 1) & 1, c + 1);
+    const char* rec = &lds[c & 1][0];
+    auto frag = [&](const char* base, int off) __attribute__((always_inline)) {
+      return *reinterpret_cast<const f16x8*>(base + off + lane * 16);
+    };
     // B operand of the state: k-step s = registers 8 (s % 2) .. + 7 of tile s / 2
     f16x8 bs[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) bs[s] = to_f16x8(st[s >> 1], s & 1);
 
+    // U = U' - W S^T and O = Q S^T, the fragments of k-step s + 1 read while
+    // k-step s multiplies
     floatx16 u[2], o[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
+      const f16x8* src = reinterpret_cast<const f16x8*>(rec + kOffU + ((b * 2 + r) * 64 + lane) * 32);
+      const f16x8 u0 = src[0], u1 = src[1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        u[r][e] = static_cast<float>(up[r][0][e]);
-        u[r][8 + e] = static_cast<float>(up[r][1][e]);
+        u[r][e] = static_cast<float>(u0[e]);
+        u[r][8 + e] = static_cast<float>(u1[e]);
       }
       o[r] = zero16();
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    f16x8 wf[2][2], qf[2][2];
+    auto read_wq = [&](int s, int slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        u[r] = mfma_f16(wf[r][s], bs[s], u[r]);
-        o[r] = mfma_f16(qf[r][s], bs[s], o[r]);
+        wf[slot][r] = frag(rec, kOffW + (s * 2 + r) * 1024);
+        qf[slot][r] = frag(rec, kOffQ + (s * 2 + r) * 1024);
       }
-    }
-    // the rows' own decay from the chunk start
+    };
+    // the state's decay over the chunk, Gam_last S^T, applied while the U and
+    // O products run (the fp16 copies bs above are of the undecayed state)
+    const float gl = *reinterpret_cast<const float*>(rec + kOffG);
+    read_wq(0, 0);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) read_wq(s + 1, (s + 1) & 1);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        o[r][4 * qq + 0] *= __expf(cr[r][qq].x);
-        o[r][4 * qq + 1] *= __expf(cr[r][qq].y);
-        o[r][4 * qq + 2] *= __expf(cr[r][qq].z);
-        o[r][4 * qq + 3] *= __expf(cr[r][qq].w);
+      for (int r = 0; r < 2; ++r) {
+        u[r] = mfma_f16(wf[s & 1][r], bs[s], u[r]);
+        o[r] = mfma_f16(qf[s & 1][r], bs[s], o[r]);
       }
+#pragma unroll
+      for (int jr = 0; jr < 8; ++jr) st[s >> 1][8 * (s & 1) + jr] *= gl;
+      __builtin_amdgcn_sched_barrier(0);
     }
     f16x8 bu[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) bu[s] = to_f16x8(u[s >> 1], s & 1);
+    // O += P U
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) o[r] = mfma_f16(pf[r][s], bu[s], o[r]);
+      for (int r = 0; r < 2; ++r) o[r] = mfma_f16(frag(rec, kOffP + (s * 2 + r) * 1024), bu[s], o[r]);
     }
-    const float gl = __expf(c_last);
+    __builtin_amdgcn_sched_barrier(0);
+    // S^T = Gam_last S^T + Kt^T U
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int jr = 0; jr < 16; ++jr) st[t][jr] *= gl;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) st[t] = mfma_f16(kf[t][s], bu[s], st[t]);
+      for (int s = 0; s < 4; ++s) st[t] = mfma_f16(frag(rec, kOffK + (s * 4 + t) * 1024), bu[s], st[t]);
     }
-    // outputs: lane (value row dv, half hh), register jr = row 32 r + crow(jr, hh)
+    // the next chunk's DMA has landed (and this wave's stores of two chunks
+    // ago): the stores below drain during the next chunk instead of being
+    // waited for at its start
+    __builtin_amdgcn_s_waitcnt(0);
+    // outputs: lane (value row dv, half hh), register jr = row 32 r + crow(jr, hh);
+    // the whole byte offset is in the per-lane offset, so rows past n fall
+    // outside the buffer's range check and are dropped
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
 #pragma unroll
       for (int jr = 0; jr < 16; ++jr) {
-        const int row = c * kC + 32 * r + crow(jr, hh);
-        if (row < n)
-          out[(static_cast<size_t>(row) * Hv + h) * kD + dv] = static_cast<bf16>(scale * o[r][jr]);
+        const uint32_t row_u = static_cast<uint32_t>(c * kC + 32 * r + 8 * (jr >> 2) + (jr & 3));
+        const bf16 x = static_cast<bf16>(o[r][jr]);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, x), rout,
+                                              static_cast<int>(lane_off + row_u * row_bytes), 0, 0);
       }
     }
   }
@@ -412,7 +450,8 @@ __global__ __launch_bounds__(64) void gdn_state_kernel(const char* __restrict__ 
 size_t gdn_workspace_bytes(int64_t n, int n_qk_heads, int n_v_heads) {
   if (n <= 0) return 0;
   const size_t nc = static_cast<size_t>((n + kC - 1) / kC);
-  return nc * (static_cast<size_t>(n_v_heads) * kRec + static_cast<size_t>(n_qk_heads) * kQRec);
+  (void)n_qk_heads;
+  return nc * static_cast<size_t>(n_v_heads) * kRec;
 }
 
 hipError_t launch_gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
@@ -422,14 +461,12 @@ hipError_t launch_gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
   if (n == 0) return hipSuccess;
   const int nc = static_cast<int>((n + kC - 1) / kC);
   char* rec = static_cast<char*>(workspace);
-  char* qrec = rec + static_cast<size_t>(nc) * n_v_heads * kRec;
   const int ni = static_cast<int>(n);
   hipLaunchKernelGGL(gdn_prep_kernel, dim3(static_cast<unsigned>(nc) * n_v_heads), dim3(256), 0,
                      stream, reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
-                     reinterpret_cast<const bf16*>(v), g, beta, ni, n_qk_heads, n_v_heads, rec, qrec);
-  hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(n_v_heads) * (kD / kBV)), dim3(64),
-                     0, stream, rec, qrec, ni, n_qk_heads, n_v_heads, scale, initial_state,
-                     final_state, reinterpret_cast<bf16*>(out));
+                     reinterpret_cast<const bf16*>(v), g, beta, ni, n_qk_heads, n_v_heads, scale, rec);
+  hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(n_v_heads)), dim3(256), 0, stream,
+                     rec, ni, n_v_heads, initial_state, final_state, reinterpret_cast<bf16*>(out));
   return hipGetLastError();
 }
 

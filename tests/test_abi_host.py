@@ -163,10 +163,10 @@ def test_attention_validation(L):
 
 
 def test_gdn_workspace_bytes(L):
-    # per 64-row chunk: 56.25 KiB per value head + 16 KiB of q fragments per q/k head
-    rec = 16384 + 16384 + 8192 + 16384 + 256
+    # per 64-row chunk and value head 72.25 KiB: -W, U', P, Kt^T, scaled q, Gam_last
+    rec = 16384 + 16384 + 8192 + 16384 + 16384 + 256
     for n, hk, hv in ((1, 1, 1), (64, 16, 32), (65, 16, 32), (8448, 16, 32)):
-        assert L.tg_gdn_workspace_bytes(n, hk, hv, 128) == -(-n // 64) * (hv * rec + hk * 16384)
+        assert L.tg_gdn_workspace_bytes(n, hk, hv, 128) == -(-n // 64) * hv * rec
     assert L.tg_gdn_workspace_bytes(0, 16, 32, 128) == 0
     assert L.tg_gdn_workspace_bytes(100, 16, 24, 128) == 0      # 24 % 16
     assert L.tg_gdn_workspace_bytes(100, 16, 32, 64) == 0
@@ -182,6 +182,7 @@ def test_gdn_validation(L):
     assert call(hk=3, hv=4) == INVALID
     assert call(hk=0) == INVALID
     assert call(d=64) == UNSUPPORTED
+    assert call(n=1 << 20, hk=16, hv=32) == UNSUPPORTED               # 2^31-byte offsets
     assert call(scale=float("nan")) == INVALID
     assert call(scale=float("inf")) == INVALID
     assert call(q=None) == INVALID
