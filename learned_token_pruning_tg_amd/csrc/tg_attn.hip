@@ -359,9 +359,27 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
 
   // K ring (with the tile's packed scores) runs one tile ahead of the V^T
   // ring: step t reads K(t+1) and V^T(t) while K(t+2) and V^T(t+1) land.
-  __shared__ __align__(16) char lds_k[2][T::K_IMG];
-  __shared__ __align__(16) char lds_s[2][kBias ? T::S_TILE : 16];
-  __shared__ __align__(16) char lds_v[2][T::V_IMG];
+  // Each ring stage is an LDS object of its own, always named at compile
+  // time: the compiler tracks DMA into LDS per object and makes a read of an
+  // object wait for every DMA in flight into it, so two stages of one array
+  // would serialize each tile's reads behind the next tiles' DMA.
+  __shared__ __align__(16) char lds_k0[T::K_IMG];
+  __shared__ __align__(16) char lds_k1[T::K_IMG];
+  __shared__ __align__(16) char lds_s0[kBias ? T::S_TILE : 16];
+  __shared__ __align__(16) char lds_s1[kBias ? T::S_TILE : 16];
+  __shared__ __align__(16) char lds_v0[T::V_IMG];
+  __shared__ __align__(16) char lds_v1[T::V_IMG];
+  auto ring_k = [&](auto b_c) __attribute__((always_inline)) -> char* {
+    if constexpr (decltype(b_c)::value) return lds_k1; else return lds_k0;
+  };
+  auto ring_s = [&](auto b_c) __attribute__((always_inline)) -> char* {
+    if constexpr (decltype(b_c)::value) return lds_s1; else return lds_s0;
+  };
+  auto ring_v = [&](auto b_c) __attribute__((always_inline)) -> char* {
+    if constexpr (decltype(b_c)::value) return lds_v1; else return lds_v0;
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   // ---- work-group -> (head, unit); unit -> (query tile, chunk)
   const int n_qt = (M + kBM - 1) / kBM;
@@ -467,23 +485,23 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
     koff[jj] = static_cast<uint32_t>(r) * kv_row + static_cast<uint32_t>(kvh) * D * 2 +
                static_cast<uint32_t>((slot ^ T::swz(r)) * 16);
   }
-  auto dma_k = [&](int buf, int t) __attribute__((always_inline)) {
+  auto dma_k = [&](auto buf, int t) __attribute__((always_inline)) {
     const uint32_t tile_off = static_cast<uint32_t>(t) * kBN * kv_row;
 #pragma unroll
     for (int jj = 0; jj < NKJ; ++jj) {
       const int j = wave_s + NW * jj;
       if (j < N_DMA_K)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(&lds_k[buf][0] + 1024 * j), 16,
+            rk, (__attribute__((address_space(3))) void*)(ring_k(buf) + 1024 * j), 16,
             static_cast<int>(tile_off + koff[jj]), 0, 0, 0);
     }
     if (kBias && wave_s == NW - 1 && lane < T::S_TILE / 16) {
       const int s_off = t * T::S_TILE;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsc, (__attribute__((address_space(3))) void*)(&lds_s[buf][0]), 16, lane16, s_off, 0, 0);
+          rsc, (__attribute__((address_space(3))) void*)(ring_s(buf)), 16, lane16, s_off, 0, 0);
     }
   };
-  auto dma_v = [&](int buf, int t) __attribute__((always_inline)) {
+  auto dma_v = [&](auto buf, int t) __attribute__((always_inline)) {
     // (the tile offset is formed outside the loop: written inline in the
     // builtin's offset argument, the host pass drops this kernel's stub)
     const int tile_off = t * T::V_IMG;
@@ -492,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
       const int j = wave_s + NW * jj;
       if (j < N_DMA_V)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(&lds_v[buf][0] + 1024 * j), 16, lane16,
+            rv, (__attribute__((address_space(3))) void*)(ring_v(buf) + 1024 * j), 16, lane16,
             tile_off + 1024 * j, 0, 0);
     }
   };
@@ -584,13 +602,15 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
   // uses (v_dot2_f32_f16 against (1, 1)), in key order.  sc holds S(t), sn
   // receives S(t+1); past the last tile the extra QK reads stale LDS and its
   // result is never used.
-  auto step = [&](auto mask_c, floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2], int t, int j)
-      __attribute__((always_inline)) {
+  // par_c: the step's parity (K~(t+1) in stage 1 - par, V^T(t) in stage par)
+  auto step = [&](auto mask_c, auto par_c, floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2],
+                  int t) __attribute__((always_inline)) {
     static_assert(kSets == 1, "the interleaved step is written for one query set");
+    constexpr int par = decltype(par_c)::value;
     softmax_max(mask_c, 0, sc[0], t * kBN);
-    const char* kimg = &lds_k[(j + 1) & 1][0];
-    const char* simg = &lds_s[(j + 1) & 1][0];
-    const char* vimg = &lds_v[j & 1][0];
+    const char* kimg = ring_k(std::integral_constant<int, 1 - par>{});
+    const char* simg = ring_s(std::integral_constant<int, 1 - par>{});
+    const char* vimg = ring_v(par_c);
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       if (kBias) {
@@ -660,26 +680,28 @@ __global__ __launch_bounds__(kThreads, 2 / kSets) void attn_fwd_kernel(
   // K~(t+1) and V^T(t) (issued one step earlier) has landed and every wave is
   // done with K~(t) and V^T(t-1), whose buffers the new DMA refills.
   floatx16 sa[kSets][2], sb[kSets][2];
-  dma_k(0, t_begin);
-  dma_v(0, t_begin);
-  if (t_begin + 1 < t_end) dma_k(1, t_begin + 1);
+  dma_k(B0{}, t_begin);
+  dma_v(B0{}, t_begin);
+  if (t_begin + 1 < t_end) dma_k(B1{}, t_begin + 1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (t_begin < n_vis) qk(&lds_k[0][0], &lds_s[0][0], sa);
-  auto run = [&](floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2], int t) __attribute__((always_inline)) {
-    const int j = t - t_begin;
+  if (t_begin < n_vis) qk(ring_k(B0{}), ring_s(B0{}), sa);
+  // step j = t - t_begin has parity par (the loop below takes steps in pairs)
+  auto run = [&](auto par_c, floatx16 (&sc)[kSets][2], floatx16 (&sn)[kSets][2], int t)
+      __attribute__((always_inline)) {
+    constexpr int par = decltype(par_c)::value;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA has landed
     __syncthreads();                 // ... and every other wave's
-    if (t + 2 < t_end) dma_k(j & 1, t + 2);
-    if (t + 1 < t_end) dma_v((j + 1) & 1, t + 1);
+    if (t + 2 < t_end) dma_k(par_c, t + 2);
+    if (t + 1 < t_end) dma_v(std::integral_constant<int, 1 - par>{}, t + 1);
     if (t < n_vis) {
-      if (t * kBN + kBN - 1 > q0) step(std::true_type{}, sc, sn, t, j);   // the diagonal tile
-      else step(std::false_type{}, sc, sn, t, j);
+      if (t * kBN + kBN - 1 > q0) step(std::true_type{}, par_c, sc, sn, t);   // the diagonal tile
+      else step(std::false_type{}, par_c, sc, sn, t);
     }
   };
   for (int t = t_begin; t < t_end; t += 2) {
-    run(sa, sb, t);
-    if (t + 1 < t_end) run(sb, sa, t + 1);
+    run(B0{}, sa, sb, t);
+    if (t + 1 < t_end) run(B1{}, sb, sa, t + 1);
   }
 
   // ---- epilogue per set: the output, or this chunk's normalised partial

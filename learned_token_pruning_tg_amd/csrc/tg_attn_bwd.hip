@@ -248,10 +248,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   constexpr int NJR = T::N_ROW_DMA / NW;                     // row-tile DMA chunks per wave
   static_assert(T::N_ROW_DMA % NW == 0, "row tiles split evenly over the waves");
 
-  __shared__ __align__(16) char lds_qr[2][T::ROWS_TILE];
-  __shared__ __align__(16) char lds_dr[2][T::ROWS_TILE];
-  __shared__ __align__(16) float lds_ld[2][64];
-  __shared__ float lds_red[kThreads / 64];
+  // All of the kernel's LDS is one object.  The compiler tracks DMA into LDS
+  // per object once there are several, and then makes every read of an
+  // object wait for all DMA in flight into it, which would hold each step's
+  // reads behind the next step's DMA; the explicit waits below order the ring.
+  __shared__ __align__(16) char lds_all[4 * T::ROWS_TILE + 2 * 64 * 4 + kThreads / 64 * 4];
+  auto* lds_qr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all);
+  auto* lds_dr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all + 2 * T::ROWS_TILE);
+  auto* lds_ld = reinterpret_cast<float (*)[64]>(lds_all + 4 * T::ROWS_TILE);
+  float* lds_red = reinterpret_cast<float*>(lds_all + 4 * T::ROWS_TILE + 2 * 64 * 4);
 
   int head, unit;
   head_unit(blockIdx.x, Hq, head, unit);
@@ -437,10 +442,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   constexpr int NJR = T::N_ROW_DMA / NW;
   static_assert(T::N_ROW_DMA % NW == 0, "row tiles split evenly over the waves");
 
-  __shared__ __align__(16) char lds_kr[2][T::ROWS_TILE];
-  __shared__ __align__(16) char lds_vr[2][T::ROWS_TILE];
-  __shared__ __align__(16) float lds_s[2][32];
-  __shared__ float lds_red[kThreads / 64];
+  // all of the kernel's LDS is one object (as in the dK/dV kernel)
+  __shared__ __align__(16) char lds_all[4 * T::ROWS_TILE + 2 * 32 * 4 + kThreads / 64 * 4];
+  auto* lds_kr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all);
+  auto* lds_vr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all + 2 * T::ROWS_TILE);
+  auto* lds_s = reinterpret_cast<float (*)[32]>(lds_all + 4 * T::ROWS_TILE);
+  float* lds_red = reinterpret_cast<float*>(lds_all + 4 * T::ROWS_TILE + 2 * 32 * 4);
 
   int head, unit;
   head_unit(blockIdx.x, Hq, head, unit);
