@@ -124,6 +124,22 @@ tg_status tg_topk_select(const float* scores, int64_t n, int64_t doc_begin, int6
                          size_t workspace_bytes, tg_stream_t stream);
 
 /*
+ * tg_topk_select that also gathers the kept rows' scores in the same pass
+ * (lucasainews.com article, "작동 방식": the kept tokens' scores are the
+ * bias the layers above the gate take):
+ *   kept_scores [tg_kept_count(...)] fp32 (output): kept_scores[i] =
+ *               scores[kept_idx[i]], bit for bit; NULL when that count is
+ *               positive -> TG_E_INVALID
+ * Every other argument, the result in kept_idx and the errors are those of
+ * tg_topk_select.  Saves the compaction of the scores (a launch and a pass
+ * over the kept indices).
+ */
+tg_status tg_topk_select_scores(const float* scores, int64_t n, int64_t doc_begin,
+                                int64_t doc_end, int64_t k_doc, int32_t* kept_idx,
+                                float* kept_scores, void* workspace, size_t workspace_bytes,
+                                tg_stream_t stream);
+
+/*
  * tg_topk_select for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the same selection, arguments and result, with no workspace argument.

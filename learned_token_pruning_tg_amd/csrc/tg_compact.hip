@@ -6,11 +6,12 @@
 // dst[i] = src[idx[i]].
 //
 // Design: a pure HBM stream.  Wide rows (>= 1 KiB, e.g. a 4 KiB bf16
-// residual row) get one 256-thread work-group pass per row with 16-byte
-// accesses, so each row is one fully coalesced read and write; narrow rows
-// (e.g. 4-byte scores) are flattened so that consecutive lanes touch
-// consecutive elements.  The grid is sized to a few waves of work-groups per
-// compute unit and strides over the rows.
+// residual row) go in blocks of rows per 256-thread work-group, 16-byte
+// accesses, consecutive lanes on consecutive bytes of a row; every thread
+// issues all of its loads (kBatch of them) before its first store, so each
+// work-group keeps 32 KiB in flight instead of one row's read, then its
+// write.  Narrow rows (e.g. 4-byte scores) are flattened so that consecutive
+// lanes touch consecutive elements, on a grid strided over the rows.
 #include "tg_device.h"
 #include "tg_launch.h"
 
@@ -19,18 +20,41 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One work-group per row (grid-stride over rows); T is the access unit.
+// A block of rows per work-group: thread t moves units t, t + 256, ... of
+// the block's flattened (row, unit) space, all loads first.  units * rows per
+// block <= 256 * kBatch < 2^31.
+constexpr int kBatch = 8;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void compact_wide_kernel(
     const int32_t* __restrict__ idx, int64_t n_kept, const char* __restrict__ src,
-    int64_t src_rows, int64_t src_stride, int64_t units, char* __restrict__ dst,
-    int64_t dst_stride) {
-  for (int64_t r = blockIdx.x; r < n_kept; r += gridDim.x) {
-    const int64_t s = idx[r];
-    if (s < 0 || s >= src_rows) continue;
-    const T* sp = reinterpret_cast<const T*>(src + s * src_stride);
-    T* dp = reinterpret_cast<T*>(dst + r * dst_stride);
-    for (int64_t u = threadIdx.x; u < units; u += kThreads) dp[u] = sp[u];
+    int64_t src_rows, int64_t src_stride, uint32_t units, uint32_t rows_per_block,
+    char* __restrict__ dst, int64_t dst_stride) {
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+  const int64_t left = n_kept - r0;
+  const uint32_t rows = static_cast<uint32_t>(left < rows_per_block ? left : rows_per_block);
+  const uint32_t total = rows * units;
+  for (uint32_t f0 = 0; f0 < total; f0 += kThreads * kBatch) {
+    T v[kBatch];
+    int64_t d_off[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const uint32_t f = f0 + threadIdx.x + kThreads * j;
+      d_off[j] = -1;
+      if (f < total) {
+        const uint32_t rr = f / units, u = f - rr * units;
+        const int64_t r = r0 + rr;
+        const int64_t s = idx[r];
+        if (s >= 0 && s < src_rows) {
+          v[j] = reinterpret_cast<const T*>(src + s * src_stride)[u];
+          d_off[j] = r * dst_stride + static_cast<int64_t>(u) * sizeof(T);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (d_off[j] >= 0) *reinterpret_cast<T*>(dst + d_off[j]) = v[j];
+    }
   }
 }
 
@@ -59,10 +83,12 @@ hipError_t launch_t(const int32_t* idx, int64_t n_kept, const void* src, int64_t
   const char* s = static_cast<const char*>(src);
   char* d = static_cast<char*>(dst);
   constexpr int64_t kMaxBlocks = 256 * 16;
-  if (row_bytes >= 1024) {
-    const int64_t blocks = n_kept < kMaxBlocks ? n_kept : kMaxBlocks;
+  if (row_bytes >= 1024 && units <= kThreads * kBatch) {
+    const int64_t per_block = kThreads * kBatch / units;   // >= 1
+    const int64_t blocks = (n_kept + per_block - 1) / per_block;
     hipLaunchKernelGGL(compact_wide_kernel<T>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, idx, n_kept, s, src_rows, src_stride, units, d,
+                       dim3(kThreads), 0, stream, idx, n_kept, s, src_rows, src_stride,
+                       static_cast<uint32_t>(units), static_cast<uint32_t>(per_block), d,
                        dst_stride);
   } else {
     const int64_t total = n_kept * units;

@@ -14,9 +14,10 @@ hipError_t launch_gate_score(const uint16_t* h, int64_t n, int64_t ld_h, int hid
 // Bytes of workspace the top-K launch needs for n scores.
 size_t topk_workspace_bytes(int64_t n);
 
+// kept_scores may be null; else kept_scores[i] = scores[kept_idx[i]], bit for bit
 hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
-                              int64_t k_doc, int32_t* kept_idx, void* workspace,
-                              hipStream_t stream);
+                              int64_t k_doc, int32_t* kept_idx, float* kept_scores,
+                              void* workspace, hipStream_t stream);
 
 // The top-K with the library's own per-device static scratch (no allocation).
 constexpr size_t kTopkScratchBytes = 32768;

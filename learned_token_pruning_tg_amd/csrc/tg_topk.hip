@@ -79,7 +79,8 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* t
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __restrict__ scores,
                                                                int n, int db, int de, int k,
                                                                int m_total,
-                                                               int32_t* __restrict__ out) {
+                                                               int32_t* __restrict__ out,
+                                                               uint32_t* __restrict__ out_scores) {
   __shared__ uint32_t hist[kCopies][kBins];
   __shared__ uint32_t scan_tmp[kWaves];
   __shared__ uint32_t sel_digit, sel_above;
@@ -212,8 +213,14 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(const float* __re
     const uint32_t pos = sure_pre + (eq_pre < ties ? eq_pre : ties);
     // pos < m_total holds by construction; the guard keeps a logic error
     // from ever writing past the caller's buffer.
-    if ((is_sure || (is_eq && eq_pre < ties)) && pos < static_cast<uint32_t>(m_total))
+    if ((is_sure || (is_eq && eq_pre < ties)) && pos < static_cast<uint32_t>(m_total)) {
       out[pos] = kThreads * r + tid;
+      // the kept score itself, bit for bit (re-read: the key above folds -0
+      // and every NaN)
+      if (out_scores != nullptr)
+        out_scores[pos] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, static_cast<int>((kThreads * r + tid) * 4), 0, 0);
+    }
   }
 }
 
@@ -417,7 +424,8 @@ __global__ __launch_bounds__(kMThreads) void topk_write_kernel(const float* __re
                                                                int n, int db, int de,
                                                                int rows_per_group, int m_total,
                                                                const uint32_t* __restrict__ ws,
-                                                               int32_t* __restrict__ out) {
+                                                               int32_t* __restrict__ out,
+                                                               uint32_t* __restrict__ out_scores) {
   __shared__ uint32_t tmp[kMWaves];
   const int tid = threadIdx.x;
   const uint32_t T = ws[kWsSel + 6], ties = ws[kWsSel + 7];
@@ -461,7 +469,10 @@ __global__ __launch_bounds__(kMThreads) void topk_write_kernel(const float* __re
       const uint32_t pos = out_base + sp + (ep < left ? ep : left);
       // pos < m_total holds by construction; the guard keeps a logic error
       // from ever writing past the caller's buffer.
-      if ((sure || (eq && ep < left)) && pos < static_cast<uint32_t>(m_total)) out[pos] = row0 + e;
+      if ((sure || (eq && ep < left)) && pos < static_cast<uint32_t>(m_total)) {
+        out[pos] = row0 + e;
+        if (out_scores != nullptr) out_scores[pos] = e < 4 ? xa[e] : xb[e - 4];   // bit for bit
+      }
       sp += sure;
       ep += eq;
     }
@@ -479,8 +490,9 @@ size_t topk_workspace_bytes(int64_t n) {
 }
 
 hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin, int64_t doc_end,
-                              int64_t k_doc, int32_t* kept_idx, void* workspace,
-                              hipStream_t stream) {
+                              int64_t k_doc, int32_t* kept_idx, float* kept_scores,
+                              void* workspace, hipStream_t stream) {
+  uint32_t* ks = reinterpret_cast<uint32_t*>(kept_scores);
   if (n == 0) return hipSuccess;
   const int64_t n_doc = doc_end - doc_begin;
   const int k = static_cast<int>(k_doc < n_doc ? k_doc : n_doc);
@@ -488,7 +500,7 @@ hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin,
   const int ni = static_cast<int>(n), db = static_cast<int>(doc_begin), de = static_cast<int>(doc_end);
   if (n <= kSingleGroupMax) {
     hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, stream, scores, ni, db, de,
-                       k, m_total, kept_idx);
+                       k, m_total, kept_idx, ks);
     return hipGetLastError();
   }
   uint32_t* ws = static_cast<uint32_t*>(workspace);
@@ -511,7 +523,7 @@ hipError_t launch_topk_select(const float* scores, int64_t n, int64_t doc_begin,
   hipLaunchKernelGGL(topk_count_kernel, grid, block, 0, stream, scores, ni, db, de,
                      derive ? 1 : 0, t_given, ties_given, p.rows_per_group, ws);
   hipLaunchKernelGGL(topk_write_kernel, grid, block, 0, stream, scores, ni, db, de,
-                     p.rows_per_group, m_total, ws, kept_idx);
+                     p.rows_per_group, m_total, ws, kept_idx, ks);
   return hipGetLastError();
 }
 
@@ -558,7 +570,7 @@ hipError_t launch_topk_select_noalloc(const float* scores, int64_t n, int64_t do
     const hipError_t e = topk_scratch_ptr(&ws);
     if (e != hipSuccess) return e;
   }
-  return launch_topk_select(scores, n, doc_begin, doc_end, k_doc, kept_idx, ws, stream);
+  return launch_topk_select(scores, n, doc_begin, doc_end, k_doc, kept_idx, nullptr, ws, stream);
 }
 
 }  // namespace tg

@@ -30,6 +30,8 @@ _SIGNATURES = {
     "tg_topk_workspace_bytes": (ctypes.c_size_t, [_I64]),
     "tg_topk_select": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
     "tg_topk_select_noalloc": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P]),
+    "tg_topk_select_scores": (ctypes.c_int, [_P, _I64, _I64, _I64, _I64, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
     "tg_compact": (ctypes.c_int, [_P, _I64, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "tg_attn_workspace_bytes": (ctypes.c_size_t, [_I64, _I32, _I32, _I32]),
     "tg_gated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P,
@@ -149,10 +151,12 @@ def topk_workspace(n: int, device="cuda") -> torch.Tensor:
 
 def topk_select(scores: torch.Tensor, doc_begin: int, doc_end: int, k_doc: int,
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                stream=None) -> torch.Tensor:
+                stream=None, kept_scores: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Kept row indices (ascending int32) of a top-K over the document rows
     [doc_begin, doc_end) with every other row kept.
-    ``workspace``: scratch from topk_workspace() (allocated per call if None)."""
+    ``workspace``: scratch from topk_workspace() (allocated per call if None).
+    ``kept_scores``: if given ([M] fp32), also filled with scores[idx] in the
+    same pass (tg_topk_select_scores)."""
     _need(scores, "scores", torch.float32)
     n = scores.numel()
     m = kept_count(n, doc_begin, doc_end, k_doc)
@@ -165,9 +169,17 @@ def topk_select(scores: torch.Tensor, doc_begin: int, doc_end: int, k_doc: int,
         workspace = topk_workspace(n, scores.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
-    _check(lib().tg_topk_select(_ptr(scores), n, doc_begin, doc_end, k_doc, _ptr(out),
-                                _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream)))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if kept_scores is None:
+        _check(lib().tg_topk_select(_ptr(scores), n, doc_begin, doc_end, k_doc, _ptr(out),
+                                    _ptr(workspace), ws_bytes, _stream(stream)))
+    else:
+        _need(kept_scores, "kept_scores", torch.float32)
+        if kept_scores.numel() < m:
+            raise ValueError(f"kept_scores holds {kept_scores.numel()} < {m} scores")
+        _check(lib().tg_topk_select_scores(_ptr(scores), n, doc_begin, doc_end, k_doc, _ptr(out),
+                                           _ptr(kept_scores), _ptr(workspace), ws_bytes,
+                                           _stream(stream)))
     return out
 
 

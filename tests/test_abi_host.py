@@ -37,7 +37,8 @@ def L():
 
 def test_header_declares_the_five_entry_points():
     names = _declared()
-    for fn in ("tg_gate_score", "tg_topk_select", "tg_topk_workspace_bytes", "tg_compact",
+    for fn in ("tg_gate_score", "tg_topk_select", "tg_topk_select_scores",
+               "tg_topk_workspace_bytes", "tg_compact",
                "tg_gated_attn_fwd", "tg_full_attn_fwd", "tg_attn_workspace_bytes",
                "tg_gated_decode_fwd", "tg_decode_workspace_bytes", "tg_qk_norm_rope",
                "tg_gated_attn_bwd", "tg_attn_bwd_workspace_bytes", "tg_gated_attn_fwd_train",
@@ -103,6 +104,21 @@ def test_topk_validation(L):
     assert "workspace" in tg.last_error()
     assert f(None, 0, 0, 0, 3, None, None, 0, 0) == OK
     assert f(A, 10, 0, 10, 0, None, A, W, 0) == OK                       # nothing kept
+
+
+def test_topk_scores_validation(L):
+    # the same checks as tg_topk_select, plus kept_scores: required when rows
+    # are kept, may be NULL when none are
+    f = L.tg_topk_select_scores
+    W = 1 << 20
+    assert f(A, 10, 0, 11, 3, A, A, A, W, 0) == INVALID
+    assert f(A, 10, 0, 5, 3, A, None, A, W, 0) == INVALID                # kept_scores NULL
+    assert "kept_scores" in tg.last_error()
+    assert f(None, 10, 0, 5, 3, A, A, A, W, 0) == INVALID
+    assert f(A, 10, 0, 5, 3, A, A, None, W, 0) == WORKSPACE
+    assert f(None, 0, 0, 0, 3, None, None, None, 0, 0) == OK
+    assert f(A, 10, 0, 5, 0, A, None, A, W, 0) == INVALID                # 5 kept (non-document rows)
+    assert f(A, 10, 0, 10, 0, None, None, A, W, 0) == OK                 # nothing kept
 
 
 def _topk_ws(n):

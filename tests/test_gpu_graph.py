@@ -24,19 +24,20 @@ def test_graph_replays_match_eager():
     out = torch.empty_like(q)
     dout = torch.empty((hq, d), dtype=torch.bfloat16, device="cuda")
     idx = torch.empty(tg.kept_count(30000, 0, 29000, 3000), dtype=torch.int32, device="cuda")
+    s_kept = torch.empty(idx.numel(), dtype=torch.float32, device="cuda")
     ws = tg.attn_workspace(m, hq, hkv, d)
     dws = tg.decode_workspace(m, hq, hkv, d)
     tws = tg.topk_workspace(30000)
 
     def work():
-        tg.topk_select(scores, 0, 29000, 3000, out=idx, workspace=tws)
+        tg.topk_select(scores, 0, 29000, 3000, out=idx, workspace=tws, kept_scores=s_kept)
         tg.gated_attn_fwd(q, k, v, s, gain, tau, out=out, workspace=ws)
         tg.gated_decode(q[-1], k, v, s, gain, tau, out=dout, workspace=dws)
 
     say("graph capture: top-K + gated attention + decode")
     work()
     torch.cuda.synchronize()
-    ref = (idx.clone(), out.clone(), dout.clone())
+    ref = (idx.clone(), out.clone(), dout.clone(), s_kept.clone())
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -46,11 +47,12 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(graph):
         work()
     for rep in range(4):
-        idx.zero_(); out.zero_(); dout.zero_()                 # eager work between replays
+        idx.zero_(); out.zero_(); dout.zero_(); s_kept.zero_()   # eager work between replays
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(idx, ref[0]) and torch.equal(out, ref[1]) and torch.equal(dout, ref[2]), rep
+        assert torch.equal(s_kept, ref[3]) and torch.equal(s_kept, scores[idx.long()]), rep
 
 
 def test_graph_replays_of_the_backward_match_eager():

@@ -79,10 +79,20 @@ def test_gate_qwen_shapes_and_determinism(n):
 # --------------------------------------------------------------------------- top-K
 
 def _topk_gpu(s32, db, de, k):
+    """Indices from tg_topk_select, checked equal to those of
+    tg_topk_select_scores, whose gathered scores must be s32[idx] bit for bit
+    (NaN payloads and signed zeros included)."""
     say(f"topk n={s32.size} doc=[{db},{de}) k={k}")
-    out = tg.topk_select(dev_f32(s32), db, de, k)
+    sd = dev_f32(s32)
+    out = tg.topk_select(sd, db, de, k)
+    m = tg.kept_count(s32.size, db, de, k)
+    ks = torch.full((m,), float("nan"), dtype=torch.float32, device="cuda")
+    out2 = tg.topk_select(sd, db, de, k, kept_scores=ks)
     torch.cuda.synchronize()
-    return out.cpu().numpy()
+    idx = out.cpu().numpy()
+    assert np.array_equal(out2.cpu().numpy(), idx)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), s32[idx].view(np.uint32))
+    return idx
 
 
 def test_topk_tiny_on_gpu_scores():
@@ -161,9 +171,14 @@ def test_topk_all_equal():
 
 # --------------------------------------------------------------------------- compaction
 
+# rows of 4096 and 2048 B (16-byte units, blocks of 8 and 16 rows), 1204 B
+# (4-byte units, blocks of 6), 1500 B (byte units, one row per block), 40000 B
+# (past a block's 32 KiB: the flattened path) and narrow rows
 @pytest.mark.parametrize("row_shape,dtype", [((2048,), torch.bfloat16), ((), torch.float32),
                                              ((3,), torch.int16), ((3,), torch.float32),
-                                             ((8, 128), torch.bfloat16), ((5,), torch.uint8)])
+                                             ((8, 128), torch.bfloat16), ((5,), torch.uint8),
+                                             ((301,), torch.float32), ((1500,), torch.uint8),
+                                             ((20000,), torch.bfloat16)])
 def test_compact_bytewise(row_shape, dtype):
     rng = np.random.default_rng(len(row_shape))
     rows = 3000
@@ -330,9 +345,10 @@ def _chain(w, layers, n_rows=None, full_rows=32):
     say(f"chain {w.name}: gate/top-K/compact")
     hd = dev_bf16(g["h"])
     s_d = tg.gate_score(hd, dev_bf16(g["w1"]), dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
-    idx_d = tg.topk_select(s_d, w.doc_begin, w.doc_end, w.k_doc)
+    # the step's own launch sequence: top-K also gathers s', then h is compacted
+    s_kept = torch.empty(w.kept, dtype=torch.float32, device="cuda")
+    idx_d = tg.topk_select(s_d, w.doc_begin, w.doc_end, w.k_doc, kept_scores=s_kept)
     h_kept = tg.compact(idx_d, hd)
-    s_kept = tg.compact(idx_d, s_d)
     torch.cuda.synchronize()
     s32 = s_d.cpu().numpy(); idx = idx_d.cpu().numpy()
     check_scores(s32, O.gate_scores(g["h"], g["w1"], g["b1"], g["w2"], g["b2"]),
