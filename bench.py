@@ -127,7 +127,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
     out["traffic_bytes_per_launch"] = f + w_ if f is not None and w_ is not None else None
     # The other step kernels (gate, top-K, compaction), per dispatch, scaled
     # the same way; compact_wide excludes the calibration copy itself.
-    step_kernels = ("gate_score_kernel", "topk_select_kernel", "topk_clear_kernel",
+    step_kernels = ("gate_score_kernel", "gate_score_wide_kernel", "topk_select_kernel",
+                    "topk_clear_kernel",
                     "topk_hist_kernel", "topk_count_kernel", "topk_write_kernel",
                     "compact_wide_kernel", "compact_narrow_kernel")
     per = {}
