@@ -15,8 +15,8 @@
  *     in the prompt and the caller passes a budget of kept prefill tokens.
  *   - fugumt.com, "論文の概要: TokenGate: Adapting LLMs for Fast and
  *     Memory-Efficient Prefill with Learned Token Pruning", English abstract:
- *     in the layers above the gate, the kept tokens' importance scores act on
- *     the attention logits.
+ *     above the gate, each kept key's gate score enters the attention
+ *     logits as an additive bias.
  *
  * Readings fixed here where the pages are silent:
  *   - logit_ij = q_i.k_j / (sqrt(d) * tau_h) + gain_h * s_j (s_j raw score);
@@ -190,8 +190,8 @@ size_t tg_attn_workspace_bytes(int64_t n, int32_t n_q_heads, int32_t n_kv_heads,
  * Token-gated causal GQA attention over the n kept rows (lucasainews.com
  * article, "작동 방식": each kept token's score is added to the attention
  * logits above the gate, scaled by a per-head learned gain, with a per-head
- * temperature; fugumt.com abstract: the importance scores act on the
- * attention logits):
+ * temperature; fugumt.com abstract: the kept keys' gate scores bias the
+ * logits):
  *     logit_ij = q_i,h . k_j,g / (sqrt(head_dim) * tau[h]) + gain[h] * key_score[j]
  *     out_i,h  = sum_{j <= i} softmax_j(logit_i,h) v_j,g,   g = h / (n_q_heads / n_kv_heads)
  * Causality is by row order (kept rows are in original order).
