@@ -1,8 +1,9 @@
 """Gated-prefill benchmark on one MI355X.
 
 One step = one pass of the whole gated path over one synthetic prompt:
-    gate scores (all N rows) -> top-K over the document -> compaction of the
-    residual and scores -> token-gated attention in each of the 27 upper layers.
+    gate scores (all N rows) -> top-K over the document (which also gathers
+    the kept rows' scores) -> compaction of the residual -> token-gated
+    attention in each of the 27 upper layers.
 The unpruned baseline (causal attention over all N rows in the same 27 layers)
 is timed beside it.  Inputs are resident in HBM before timing starts.
 
