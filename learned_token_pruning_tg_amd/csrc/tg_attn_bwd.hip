@@ -252,11 +252,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   // per object once there are several, and then makes every read of an
   // object wait for all DMA in flight into it, which would hold each step's
   // reads behind the next step's DMA; the explicit waits below order the ring.
-  __shared__ __align__(16) char lds_all[4 * T::ROWS_TILE + 2 * 64 * 4 + kThreads / 64 * 4];
+  // The step's 64 (-lse/c_h, -D) values take 256 bytes of a 1 KiB stage: the
+  // whole wave issues their DMA (a lane-divergent DMA made the compiler wait
+  // for every DMA in flight before the step's first LDS read); lanes past 16
+  // fetch the next steps' values, or zeros past the end, into the rest.
+  __shared__ __align__(16) char lds_all[4 * T::ROWS_TILE + 2 * 1024 + kThreads / 64 * 4];
   auto* lds_qr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all);
   auto* lds_dr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all + 2 * T::ROWS_TILE);
-  auto* lds_ld = reinterpret_cast<float (*)[64]>(lds_all + 4 * T::ROWS_TILE);
-  float* lds_red = reinterpret_cast<float*>(lds_all + 4 * T::ROWS_TILE + 2 * 64 * 4);
+  auto* lds_ld = reinterpret_cast<float (*)[256]>(lds_all + 4 * T::ROWS_TILE);
+  float* lds_red = reinterpret_cast<float*>(lds_all + 4 * T::ROWS_TILE + 2 * 1024);
 
   int head, unit;
   head_unit(blockIdx.x, Hq, head, unit);
@@ -303,47 +307,58 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dout + static_cast<size_t>(head) * D, q_row * static_cast<uint32_t>(M));
   const __amdgpu_buffer_rsrc_t rld = make_rsrc(ld + static_cast<size_t>(head) * n_t32 * 64,
                                                static_cast<uint32_t>(n_t32) * 256);
-  const int lane16 = 16 * lane;
   // Row tiles: the lane filling LDS slot s of row r fetches chunk s ^ swz(r)
-  // of that row (Q and dO rows share the stride, hence these offsets).
-  uint32_t roff[NJR];
-#pragma unroll
-  for (int jj = 0; jj < NJR; ++jj) {
-    const int byte = 1024 * (wave_s + NW * jj) + lane16;
-    const int r = byte / T::ROW, slot = (byte % T::ROW) / 16;
-    roff[jj] = static_cast<uint32_t>(r) * q_row + static_cast<uint32_t>((slot ^ T::swz(r)) * 16);
-  }
+  // of that row (Q and dO rows share the stride, hence one offset for both).
+  // The offsets are formed at each DMA from a copy of the lane id the
+  // compiler cannot see through: hoisted out of the loop they are live across
+  // it, and at this register pressure they were spilled, and every reload's
+  // wait also waited for the DMA issued just before it.
+  auto fresh_lane = []() __attribute__((always_inline)) {
+    int l = static_cast<int>(threadIdx.x & 63);
+    asm volatile("" : "+v"(l));
+    return l;
+  };
   typedef __attribute__((address_space(3))) void* lds_ptr;
   auto dma = [&](int buf, int t) __attribute__((always_inline)) {
     const uint32_t row_off = static_cast<uint32_t>(t) * kRows * q_row;
+    const int ln = fresh_lane();
 #pragma unroll
     for (int jj = 0; jj < NJR; ++jj) {
       const int c = wave_s + NW * jj;
+      const int byte = 1024 * c + 16 * ln;
+      const int r = byte / T::ROW, slot = (byte % T::ROW) / 16;
+      const uint32_t roff =
+          static_cast<uint32_t>(r) * q_row + static_cast<uint32_t>((slot ^ T::swz(r)) * 16);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_ptr)(&lds_qr[buf][0] + 1024 * c), 16,
-                                               static_cast<int>(row_off + roff[jj]), 0, 0, 0);
+                                               static_cast<int>(row_off + roff), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_ptr)(&lds_dr[buf][0] + 1024 * c), 16,
-                                               static_cast<int>(row_off + roff[jj]), 0, 0, 0);
+                                               static_cast<int>(row_off + roff), 0, 0, 0);
     }
-    if (wave_s == NW - 1 && lane < 16)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_ptr)(&lds_ld[buf][0]), 16, lane16, t * 256, 0, 0);
+    if (wave_s == NW - 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_ptr)(&lds_ld[buf][0]), 16, 16 * ln, t * 256,
+                                               0, 0);
   };
 
   // ---- one step: queries 32 t .. 32 t + 31 against this wave's keys
   const uint32_t a_base = static_cast<uint32_t>(l32) * T::ROW + ((hh ^ T::swz(l32)) << 4);
-  auto step = [&](auto diag_c, int buf, int t) __attribute__((always_inline)) {
-    constexpr bool DIAG = decltype(diag_c)::value;
-    const char* qr = &lds_qr[buf][0];
-    const char* dr = &lds_dr[buf][0];
-    // S and dP start from -lse_i / c_h and -D_i of their query rows (register
-    // j holds query 8 (j/4) + 4 hh + j%4), so S = q.k - lse / c_h and dP = dO.v - D
-    floatx16 s, dp;
+  // S and dP start from -lse_i / c_h and -D_i of their query rows (register
+  // j holds query 8 (j/4) + 4 hh + j%4), so S = q.k - lse / c_h and dP = dO.v
+  // - D.  The step reads them before the next step's DMA is issued: read
+  // after it, the compiler makes the read wait for that DMA.
+  auto start_values = [&](int buf, floatx16& s, floatx16& dp) __attribute__((always_inline)) {
+    const float* ldb = &lds_ld[buf][4 * (fresh_lane() >> 5)];
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
-      const float4 l2 = *reinterpret_cast<const float4*>(&lds_ld[buf][8 * jg + 4 * hh]);
-      const float4 dd = *reinterpret_cast<const float4*>(&lds_ld[buf][32 + 8 * jg + 4 * hh]);
+      const float4 l2 = *reinterpret_cast<const float4*>(ldb + 8 * jg);
+      const float4 dd = *reinterpret_cast<const float4*>(ldb + 32 + 8 * jg);
       s[4 * jg] = l2.x; s[4 * jg + 1] = l2.y; s[4 * jg + 2] = l2.z; s[4 * jg + 3] = l2.w;
       dp[4 * jg] = dd.x; dp[4 * jg + 1] = dd.y; dp[4 * jg + 2] = dd.z; dp[4 * jg + 3] = dd.w;
     }
+  };
+  auto step = [&](auto diag_c, int buf, int t, floatx16 s, floatx16 dp) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_c)::value;
+    const char* qr = &lds_qr[buf][0];
+    const char* dr = &lds_dr[buf][0];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint32_t off = a_base ^ static_cast<uint32_t>(32 * ks);
@@ -386,15 +401,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   };
 
   // ---- main loop over this chunk's query tiles, one barrier per step
-  const int t_vis = kt * (kWgRows / kRows) + wave;   // this wave's diagonal tile
   dma(0, t_begin);
   for (int t = t_begin; t < t_stop; ++t) {
     const int buf = (t - t_begin) & 1;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA has landed
     __syncthreads();                 // ... and every other wave's; the other slot is free
+    floatx16 s0, dp0;
+    start_values(buf, s0, dp0);
     if (t + 1 < t_stop) dma(buf ^ 1, t + 1);
-    if (t == t_vis) step(std::true_type{}, buf, t);
-    else if (t > t_vis) step(std::false_type{}, buf, t);
+    // this wave's diagonal tile, formed here for the reason the DMA offsets are
+    const int t_vis = kt * (kWgRows / kRows) + (wave_s * 64 + fresh_lane()) / 64;
+    if (t == t_vis) step(std::true_type{}, buf, t, s0, dp0);
+    else if (t > t_vis) step(std::false_type{}, buf, t, s0, dp0);
   }
 
   // ---- epilogue: fp32 partials of this head and chunk (rows = keys, columns = d)
@@ -512,7 +530,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   };
 
   const uint32_t a_base = static_cast<uint32_t>(l32) * T::ROW + ((hh ^ T::swz(l32)) << 4);
-  auto step = [&](auto diag_c, int buf, int u) __attribute__((always_inline)) {
+  // The step's 16 key scores (register j: key 8 (j/4) + 4 hh + j%4), read
+  // before the next step's DMA is issued: read after it, the compiler makes
+  // the read wait for that DMA.
+  auto key_scores = [&](int buf, float (&sk)[16]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const float4 sv = *reinterpret_cast<const float4*>(&lds_s[buf][8 * jg + 4 * hh]);
+      sk[4 * jg] = sv.x; sk[4 * jg + 1] = sv.y; sk[4 * jg + 2] = sv.z; sk[4 * jg + 3] = sv.w;
+    }
+  };
+  auto step = [&](auto diag_c, int buf, int u, const float (&sk)[16]) __attribute__((always_inline)) {
     constexpr bool DIAG = decltype(diag_c)::value;
     const char* kr = &lds_kr[buf][0];
     const char* vr = &lds_vr[buf][0];
@@ -528,13 +556,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int kbase = u * kRows + 4 * hh;
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
-      const float4 sv = *reinterpret_cast<const float4*>(&lds_s[buf][8 * jg + 4 * hh]);
-      const float sk[4] = {sv.x, sv.y, sv.z, sv.w};
       float dsj[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * jg + i;
-        float p = fast_exp2(fmaf(st[j], alpha, fmaf(sk[i], gl, nlse2)));
+        float p = fast_exp2(fmaf(st[j], alpha, fmaf(sk[j], gl, nlse2)));
         if (DIAG && kbase + 8 * jg + i > my_q) p = 0.f;
         dsj[i] = p * (dpt[j] + ndd);
       }
@@ -558,9 +584,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int buf = (u - u_begin) & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    float sk[16];
+    key_scores(buf, sk);
     if (u + 1 < u_stop) dma(buf ^ 1, u + 1);
-    if (u == u_diag) step(std::true_type{}, buf, u);
-    else if (u < u_diag) step(std::false_type{}, buf, u);
+    if (u == u_diag) step(std::true_type{}, buf, u, sk);
+    else if (u < u_diag) step(std::false_type{}, buf, u, sk);
   }
 
   // ---- epilogue: dq = c_h (K^T dS^T)^T; lane = query, registers = dims
