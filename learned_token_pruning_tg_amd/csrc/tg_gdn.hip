@@ -13,19 +13,23 @@
 // Chunked form used here (chunks of C = 64 rows; within a chunk c_i is the
 // cumulative log decay up to row i, Gam_i = exp(c_i), S the chunk's start
 // state):
-//   A_ij = beta_i exp(c_i - c_j) k_i.k_j (j < i),  (I + A) [W | U'] =
-//          [diag(beta Gam) K | diag(beta) V]   (solved in fp32)
+//   A_ij = beta_i exp(c_i - c_j) k_i.k_j (j < i),  T = (I + A)^-1,
+//   W = T diag(beta Gam) K,  U' = T diag(beta) V
 //   U    = U' - W S^T                           (the rows' written deltas)
 //   O    = scale (diag(Gam) Q S^T + P U),  P_ij = exp(c_i - c_j) q_i.k_j (j <= i)
 //   S    <- Gam_last S + U^T Kt,            Kt_j = exp(c_last - c_j) k_j
 //
 // Two launches:
 // 1. gdn_prep: one work-group per (chunk, value head), chunks in parallel.
-//    Forms K K^T and Q K^T on bf16 MFMA (exact products, fp32 sums), A and P
-//    with their decays, solves (I + A) X = R by forward substitution in fp32
-//    (a thread per right-hand-side column), and writes every operand the
-//    chain needs as fp16 MFMA fragments: -W, U', scale P, Kt^T and the scaled
-//    queries scale Gam_i q_i, then Gam_last.
+//    Forms K K^T and K Q^T on bf16 MFMA (exact products, fp32 sums), A and P
+//    with their decays (P goes out straight from the accumulators), inverts
+//    the unit lower-triangular I + A in fp32 by 16 x 16 blocks (diagonal
+//    blocks by forward substitution, the blocks below by
+//    T_IJ = -T_II sum_K A_IK T_KJ), and forms W and U' as bf16 MFMA products
+//    of K and V with T's scaled columns split into bf16 high and low parts
+//    (16 mantissa bits).  Every operand the chain needs leaves as fp16 MFMA
+//    fragments: -W, U', scale P, Kt^T and the scaled queries
+//    scale Gam_i q_i, then Gam_last.
 // 2. gdn_state: one work-group per value head walks the chunks in order, a
 //    wave per 32 value rows (the rows of S evolve independently), the head's
 //    per-chunk operands DMAed once into a two-stage LDS ring for the four
@@ -39,7 +43,8 @@
 //    the A operands in that same order.  Rows of the value dimension evolve
 //    independently, which is what lets the chain split over 32-row blocks.
 //
-// Numerics: bf16 inputs; decays, the solve, the state and every sum in fp32;
+// Numerics: bf16 inputs; decays, the inverse, the state and every sum in
+// fp32 (T's scaled entries carried to 16 mantissa bits into W and U');
 // the MFMA operands (W, U', P, Kt, q and the fp32 state and deltas) rounded
 // to fp16 (11-bit mantissa; q and k are unit vectors, values of v above 65504
 // would saturate); output rounded to bf16.
@@ -54,7 +59,6 @@ namespace {
 constexpr int kD = 128;      // dk = dv
 constexpr int kC = 64;       // chunk rows
 constexpr int kBV = 32;      // value rows per chain
-constexpr int kXS = 2 * kD + 8;   // LDS row of the solve's result (fp16, padded)
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
@@ -93,22 +97,66 @@ __device__ __forceinline__ float tile_at(const char* t, int r, int col) {
 // ---------------------------------------------------------------------------
 // gdn_prep
 // ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f16x8 to_f16x8(const floatx16& a, int half) {
+  f16x8 x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(a[8 * half + e]);
+  return x;
+}
+
+// MFMA fragment with a 64 x 128 bf16 tile's rows as k and its columns as the
+// 32 lanes of m (or n), read transposed out of the swizzled row tile by two
+// ds_read_b64_tr_b16: within each 16-lane group that instruction gives lane
+// 4 a + c element c of the 8-byte rows that lanes a, a + 4, a + 8, a + 12
+// address.  Lane j (of 16) addresses row 16 g + 8 q + 4 hh + j / 4 at columns
+// n0 + 16 ((lane / 16) % 2) + 4 (j % 4), so element e of lane l's fragment is
+// row kperm(g, hh, e) at column n0 + l % 32.
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int g, int n0, int lane) {
+  const int j = lane & 15, hh = lane >> 5;
+  const int col = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  v4i16 x[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * g + 8 * q + 4 * hh + (j >> 2);
+    const char* a = tile + tile_off(r, col >> 3) + (col & 7) * 2;
+    x[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
+  }
+  const v8i16 y = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, y);
+}
+
+// A 64 x 64 bf16 matrix M[i][j] stored for fragment reads along j: row i
+// (128 bytes) holds, in 16-byte piece q = 2 g + hh, the elements
+// j = kperm(g, hh, 0..7); piece q sits at slot q ^ ((i / 2) % 8), so the 16
+// rows one read pass serves hit 16 distinct bank groups.
+__device__ __forceinline__ int tmat_off(int i, int q) { return i * 128 + ((q ^ ((i >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<bf16>(x));
+}
+
 __global__ __launch_bounds__(256) void gdn_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int n, int Hk, int Hv,
     float scale, char* __restrict__ rec_base) {
-  // The K, Q and V tiles are dead once the solve has read its right-hand
-  // sides; its result X then overlays them (74 KiB in all: two work-groups
-  // per compute unit).
+  // LDS: the K, Q and V tiles (48 KiB) and A (16 KiB).  Once P and the
+  // scaled q fragments are out, the Q tile holds T = (I + A)^-1 (fp32), then
+  // the bf16 hi/lo parts of T diag(beta); once T is formed, A's space holds
+  // those of -T diag(beta Gam).
   __shared__ __align__(16) char lds_tiles[3 * kC * kD * 2];
   __shared__ __align__(16) float lds_a[kC][kC];
-  __shared__ __align__(16) _Float16 lds_p[kC][kC];
   __shared__ float lds_c[kC], lds_b[kC], lds_gam[kC];
   char* const lds_k = lds_tiles;
   char* const lds_q = lds_tiles + kC * kD * 2;
   char* const lds_v = lds_tiles + 2 * kC * kD * 2;
-  _Float16 (*const lds_x)[kXS] = reinterpret_cast<_Float16 (*)[kXS]>(lds_tiles);
-  static_assert(kC * kXS * 2 <= 3 * kC * kD * 2, "X fits over the tiles");
+  float (*const lds_t)[kC] = reinterpret_cast<float (*)[kC]>(lds_q);
+  char* const tv_hi = lds_q;                       // T diag(beta), bf16 hi / lo
+  char* const tv_lo = lds_q + kC * kC * 2;
+  char* const tk_hi = reinterpret_cast<char*>(&lds_a[0][0]);   // -T diag(beta Gam)
+  char* const tk_lo = tk_hi + kC * kC * 2;
 
   const int c = blockIdx.x / Hv, h = blockIdx.x % Hv;
   const int kh = h / (Hv / Hk);
@@ -161,28 +209,56 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   }
   __syncthreads();
 
-  // K K^T -> A and Q K^T -> P, lower-triangle 32 x 32 tiles (0,0), (1,0), (1,1)
+  // K K^T -> A (lower-triangle 32 x 32 tiles (0,0), (1,0), (1,1): lane = j,
+  // registers = i) and K Q^T -> scale P^T (tiles with j <= i: lane = i,
+  // registers = j, which is the P fragment order: k-step s = 2 J + register
+  // half), written straight out as fragments.
   for (int ti = wave; ti < 6; ti += 4) {
     const bool is_p = ti >= 3;
-    const int I = (ti % 3) == 0 ? 0 : 1, J = (ti % 3) == 2 ? 1 : 0;
-    const char* src = is_p ? lds_q : lds_k;
-    const int ra = 32 * I + m, rb = 32 * J + m;
+    const int I = (ti % 3) == 0 ? 0 : 1, J = (ti % 3) == 2 ? 1 : 0;   // rows i of tile I, j of J
     floatx16 acc = zero16();
+    if (!is_p) {
+      const int ra = 32 * I + m, rb = 32 * J + m;
 #pragma unroll
-    for (int s = 0; s < kD / 16; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(src + tile_off(ra, 2 * s + hh));
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(lds_k + tile_off(rb, 2 * s + hh));
-      acc = mfma_32x32x16(a, b, acc);
-    }
-    const int j = rb;
-    const float cj = lds_c[j];
+      for (int s = 0; s < kD / 16; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + tile_off(ra, 2 * s + hh));
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(lds_k + tile_off(rb, 2 * s + hh));
+        acc = mfma_32x32x16(a, bb, acc);
+      }
+      const int j = rb;
+      const float cj = lds_c[j];
 #pragma unroll
-    for (int jr = 0; jr < 16; ++jr) {
-      const int i = 32 * I + crow(jr, hh);
-      const float dec = j <= i ? __expf(lds_c[i] - cj) : 0.f;
-      if (is_p) lds_p[i][j] = static_cast<_Float16>(scale * dec * acc[jr]);
-      else lds_a[i][j] = j < i ? lds_b[i] * dec * acc[jr] : 0.f;
+      for (int jr = 0; jr < 16; ++jr) {
+        const int i = 32 * I + crow(jr, hh);
+        lds_a[i][j] = j < i ? lds_b[i] * __expf(lds_c[i] - cj) * acc[jr] : 0.f;
+      }
+    } else {
+      const int rj = 32 * J + m, ri = 32 * I + m;
+#pragma unroll
+      for (int s = 0; s < kD / 16; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + tile_off(rj, 2 * s + hh));
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(lds_q + tile_off(ri, 2 * s + hh));
+        acc = mfma_32x32x16(a, bb, acc);
+      }
+      const int i = ri;
+      const float ci = lds_c[i];
+      f16x8 x[2];
+#pragma unroll
+      for (int jr = 0; jr < 16; ++jr) {
+        const int j = 32 * J + crow(jr, hh);
+        x[jr >> 3][jr & 7] = static_cast<_Float16>(j <= i ? scale * __expf(ci - lds_c[j]) * acc[jr] : 0.f);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        *reinterpret_cast<f16x8*>(rec + kOffP + ((2 * J + half) * 2 + I) * 1024 + lane * 16) = x[half];
     }
+  }
+  // the tile with j > i everywhere: zero P fragments (k-steps 2, 3 of row tile 0)
+  if (wave == 3) {
+    const f16x8 z = {};
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      *reinterpret_cast<f16x8*>(rec + kOffP + ((2 + half) * 2 + 0) * 1024 + lane * 16) = z;
   }
 
   // scaled q fragments: scale * Gam_i q_i, A operand [row][dk] (the rows' own
@@ -212,88 +288,161 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
       *reinterpret_cast<f16x8*>(rec + kOffK + static_cast<size_t>(u) * 16) = x;
     }
   }
-  __syncthreads();
+  __syncthreads();   // A complete; the Q tile is free for T
 
-  // (I + A) X = R, one right-hand-side column per thread: columns 0..127 are
-  // beta_i Gam_i k_i (-> W), 128..255 are beta_i v_i (-> U').  Forward
-  // substitution in fp32, row by row.
-  {
-    const int col = tid;
-    float x[kC];
-    if (col < kD) {
+  // T = (I + A)^-1, unit lower triangular, fp32, in 16 x 16 blocks.
+  // Diagonal blocks by forward substitution (wave 0: lane = block * 16 +
+  // column); the blocks above the diagonal are zeroed by the other waves.
+  if (wave == 0) {
+    const int I = lane >> 4, cl = lane & 15, b0 = 16 * I;
+    float t[16];
 #pragma unroll
-      for (int i = 0; i < kC; ++i) x[i] = lds_b[i] * lds_gam[i] * tile_at(lds_k, i, col);
-    } else {
+    for (int r = 0; r < 16; ++r) t[r] = r == cl ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < kC; ++i) x[i] = lds_b[i] * tile_at(lds_v, i, col - kD);
+    for (int r = 1; r < 16; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < r; ++jj) acc = __builtin_fmaf(lds_a[b0 + r][b0 + jj], t[jj], acc);
+      if (r > cl) t[r] = -acc;
     }
-    __syncthreads();   // every right-hand side read: X may overwrite the tiles
 #pragma unroll
-    for (int i = 1; i < kC; ++i) {
-      float acc = x[i];
+    for (int r = 0; r < 16; ++r) lds_t[b0 + r][b0 + cl] = t[r];
+  } else {
+    // blocks (I, J) with J > I: 6 blocks of 256 zeros, 8 per thread
+    const int u0 = (tid - 64) * 8;                 // 0 .. 1535 + 7
+    for (int u = u0; u < u0 + 8; ++u) {
+      const int blk = u >> 8, e = u & 255;
+      const int I = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+      const int J = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+      lds_t[16 * I + (e >> 4)][16 * J + (e & 15)] = 0.f;
+    }
+  }
+  __syncthreads();
+  // Block rows 1..3: wave w forms T_IJ, J = w < I:
+  //   X = sum_{K=J}^{I-1} A_IK T_KJ,  T_IJ = -T_II X.
+  // Lane: row r = lane / 4 of the block, columns 4 (lane % 4) .. + 3.  X goes
+  // through T_IJ's own slot (a wave's LDS accesses stay in order).
+  for (int I = 1; I < 4; ++I) {
+    if (wave < I) {
+      const int J = wave;
+      const int r = lane >> 2, c4 = 4 * (lane & 3);
+      float4 x = {0.f, 0.f, 0.f, 0.f};
+      for (int K = J; K < I; ++K) {
 #pragma unroll
-      for (int j4 = 0; j4 < i; j4 += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(&lds_a[i][j4]);
-        acc = __builtin_fmaf(-a.x, x[j4], acc);
-        if (j4 + 1 < i) acc = __builtin_fmaf(-a.y, x[j4 + 1], acc);
-        if (j4 + 2 < i) acc = __builtin_fmaf(-a.z, x[j4 + 2], acc);
-        if (j4 + 3 < i) acc = __builtin_fmaf(-a.w, x[j4 + 3], acc);
+        for (int mm = 0; mm < 16; ++mm) {
+          const float a = lds_a[16 * I + r][16 * K + mm];
+          const float4 tk = *reinterpret_cast<const float4*>(&lds_t[16 * K + mm][16 * J + c4]);
+          x.x = __builtin_fmaf(a, tk.x, x.x); x.y = __builtin_fmaf(a, tk.y, x.y);
+          x.z = __builtin_fmaf(a, tk.z, x.z); x.w = __builtin_fmaf(a, tk.w, x.w);
+        }
       }
-      x[i] = acc;
-    }
+      *reinterpret_cast<float4*>(&lds_t[16 * I + r][16 * J + c4]) = x;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kC; ++i) lds_x[i][col] = static_cast<_Float16>(col < kD ? -x[i] : x[i]);
+      for (int mm = 0; mm < 16; ++mm) {
+        const float tii = lds_t[16 * I + r][16 * I + mm];
+        const float4 xm = *reinterpret_cast<const float4*>(&lds_t[16 * I + mm][16 * J + c4]);
+        y.x = __builtin_fmaf(-tii, xm.x, y.x); y.y = __builtin_fmaf(-tii, xm.y, y.y);
+        y.z = __builtin_fmaf(-tii, xm.z, y.z); y.w = __builtin_fmaf(-tii, xm.w, y.w);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      *reinterpret_cast<float4*>(&lds_t[16 * I + r][16 * J + c4]) = y;
+    }
+    __syncthreads();
+  }
+
+  // T diag(beta) (for U') and -T diag(beta Gam) (for W) as bf16 hi + lo
+  // parts (hi + lo carries 16 mantissa bits), stored along j in fragment
+  // order.  Thread: row i = tid / 4, k-step block gj = tid % 4 (j = 16 gj ..).
+  {
+    const int i = tid >> 2, gj = tid & 3;
+    float tr[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 x = *reinterpret_cast<const float4*>(&lds_t[i][16 * gj + 4 * q4]);
+      tr[4 * q4] = x.x; tr[4 * q4 + 1] = x.y; tr[4 * q4 + 2] = x.z; tr[4 * q4 + 3] = x.w;
+    }
+    __syncthreads();   // all of T read: its space takes the bf16 parts
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      u32x4 vh, vl, kh4, kl4;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        uint32_t pvh = 0, pvl = 0, pkh = 0, pkl = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const int e = 2 * e2 + w2;
+          const int jl = 8 * (e >> 2) + 4 * h2 + (e & 3);      // j - 16 gj = kperm(gj, h2, e) - 16 gj
+          const int j = 16 * gj + jl;
+          const float tvv = tr[jl] * lds_b[j];
+          const float tkv = -tr[jl] * lds_b[j] * lds_gam[j];
+          const uint16_t a = bf16_rne(tvv), bb = bf16_rne(tvv - __uint_as_float(static_cast<uint32_t>(a) << 16));
+          const uint16_t cc = bf16_rne(tkv), dd = bf16_rne(tkv - __uint_as_float(static_cast<uint32_t>(cc) << 16));
+          pvh |= static_cast<uint32_t>(a) << (16 * w2);
+          pvl |= static_cast<uint32_t>(bb) << (16 * w2);
+          pkh |= static_cast<uint32_t>(cc) << (16 * w2);
+          pkl |= static_cast<uint32_t>(dd) << (16 * w2);
+        }
+        vh[e2] = pvh; vl[e2] = pvl; kh4[e2] = pkh; kl4[e2] = pkl;
+      }
+      const int off = tmat_off(i, 2 * gj + h2);
+      st16(tv_hi + off, vh);
+      st16(tv_lo + off, vl);
+      st16(tk_hi + off, kh4);
+      st16(tk_lo + off, kl4);
+    }
   }
   __syncthreads();
 
-  // -W fragments (A operand [row][dk])
-  for (int u = tid; u < 8 * 2 * 64; u += 256) {
-    const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
-    const int mm = ln & 31, h2 = ln >> 5;
-    f16x8 x;
+  // -W = (-T diag(beta Gam)) K and U' = (T diag(beta)) V on bf16 MFMA, hi and
+  // lo parts of T each a product.  Wave w: the W^T tiles of dk 32 w .. (rows
+  // of the chunk as n: their accumulators are the -W fragments of k-steps
+  // 2 w, 2 w + 1) and the U' tiles of value rows 32 w .. (accumulator images).
+  {
+    const int t = wave;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = lds_x[32 * r + mm][kperm(s, h2, e)];
-    *reinterpret_cast<f16x8*>(rec + kOffW + static_cast<size_t>(u) * 16) = x;
-  }
-  // U' accumulator images per 32-row value block: lane (dv column mm, half
-  // h2), register jr = row 32 r + crow(jr, h2)
-  for (int u = tid; u < 4 * 2 * 64; u += 256) {
-    const int ln = u & 63, r = (u >> 6) & 1, b = u >> 7;
-    const int mm = ln & 31, h2 = ln >> 5;
-    f16x8 x0, x1;
+    for (int r = 0; r < 2; ++r) {
+      floatx16 acc = zero16();
+      const int i = 32 * r + m;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x0[e] = lds_x[32 * r + crow(e, h2)][kD + kBV * b + mm];
-      x1[e] = lds_x[32 * r + crow(8 + e, h2)][kD + kBV * b + mm];
+      for (int gg = 0; gg < 4; ++gg) {
+        const bf16x8 a = tr_frag(lds_k, gg, 32 * t, lane);
+        const int off = tmat_off(i, 2 * gg + hh);
+        acc = mfma_32x32x16(a, *reinterpret_cast<const bf16x8*>(tk_hi + off), acc);
+        acc = mfma_32x32x16(a, *reinterpret_cast<const bf16x8*>(tk_lo + off), acc);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        *reinterpret_cast<f16x8*>(rec + kOffW + ((2 * t + half) * 2 + r) * 1024 + lane * 16) =
+            to_f16x8(acc, half);
     }
-    f16x8* dst = reinterpret_cast<f16x8*>(rec + kOffU + static_cast<size_t>(u) * 32);
-    dst[0] = x0;
-    dst[1] = x1;
-  }
-  // P fragments (A operand [row i][row j], zero above the diagonal)
-  for (int u = tid; u < 4 * 2 * 64; u += 256) {
-    const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
-    const int mm = ln & 31, h2 = ln >> 5;
-    const int i = 32 * r + mm;
-    f16x8 x;
+    const int bv = wave;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = kperm(s, h2, e);
-      x[e] = j <= i ? lds_p[i][j] : static_cast<_Float16>(0.f);
+    for (int r = 0; r < 2; ++r) {
+      floatx16 acc = zero16();
+      const int i = 32 * r + m;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const bf16x8 bb = tr_frag(lds_v, gg, kBV * bv, lane);
+        const int off = tmat_off(i, 2 * gg + hh);
+        acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(tv_hi + off), bb, acc);
+        acc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(tv_lo + off), bb, acc);
+      }
+      f16x8* dst = reinterpret_cast<f16x8*>(rec + kOffU + ((bv * 2 + r) * 64 + lane) * 32);
+      dst[0] = to_f16x8(acc, 0);
+      dst[1] = to_f16x8(acc, 1);
     }
-    *reinterpret_cast<f16x8*>(rec + kOffP + static_cast<size_t>(u) * 16) = x;
   }
 }
 
 // ---------------------------------------------------------------------------
 // gdn_state
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ f16x8 to_f16x8(const floatx16& a, int half) {
-  f16x8 x;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = static_cast<_Float16>(a[8 * half + e]);
-  return x;
-}
 
 // One work-group of four waves per value head; wave b carries the state
 // slice of value rows 32 b .. 32 b + 31.  Each chunk's operand record (the
