@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   // those of -T diag(beta Gam).
   __shared__ __align__(16) char lds_tiles[3 * kC * kD * 2];
   __shared__ __align__(16) float lds_a[kC][kC];
-  __shared__ float lds_c[kC], lds_b[kC], lds_gam[kC];
+  __shared__ float lds_c[kC], lds_b[kC], lds_gam[kC], lds_fk[kC];
   char* const lds_k = lds_tiles;
   char* const lds_q = lds_tiles + kC * kD * 2;
   char* const lds_v = lds_tiles + 2 * kC * kD * 2;
@@ -205,6 +205,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
     lds_c[lane] = gv;
     lds_b[lane] = bv;
     lds_gam[lane] = __expf(gv);
+    lds_fk[lane] = __expf(__shfl(gv, kC - 1) - gv);   // exp(c_last - c_j)
     if (lane == kC - 1) reinterpret_cast<float*>(rec + kOffG)[0] = __expf(gv);
   }
   __syncthreads();
@@ -262,31 +263,33 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   }
 
   // scaled q fragments: scale * Gam_i q_i, A operand [row][dk] (the rows' own
-  // decay from the chunk start and the read-out scale, folded in here)
+  // decay from the chunk start and the read-out scale, folded in here).
+  // Elements 0-3 and 4-7 of a lane are dk 16 s + 4 hh .. + 3 and 8 further:
+  // 8-byte reads of chunks 2 s and 2 s + 1 of the row.
   for (int u = tid; u < 8 * 2 * 64; u += 256) {
     const int ln = u & 63, r = (u >> 6) & 1, s = u >> 7;
-    const int mm = ln & 31, h2 = ln >> 5;
-    const float f = scale * lds_gam[32 * r + mm];
+    const int row = 32 * r + (ln & 31), h2 = ln >> 5;
+    const float f = scale * lds_gam[row];
+    const uint2 lo = *reinterpret_cast<const uint2*>(lds_q + tile_off(row, 2 * s) + 8 * h2);
+    const uint2 hi = *reinterpret_cast<const uint2*>(lds_q + tile_off(row, 2 * s + 1) + 8 * h2);
+    const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
     f16x8 x;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      x[e] = static_cast<_Float16>(f * tile_at(lds_q, 32 * r + mm, kperm(s, h2, e)));
+      x[e] = static_cast<_Float16>(f * bf2f(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)))));
     *reinterpret_cast<f16x8*>(rec + kOffQ + static_cast<size_t>(u) * 16) = x;
   }
-  // Kt^T fragments: exp(c_last - c_j) k_j, A operand [dk][row]
-  {
-    const float c_last = lds_c[kC - 1];
-    for (int u = tid; u < 4 * 4 * 64; u += 256) {
-      const int ln = u & 63, t = (u >> 6) & 3, s = u >> 8;
-      const int mm = ln & 31, h2 = ln >> 5;
-      f16x8 x;
+  // Kt^T fragments: exp(c_last - c_j) k_j, A operand [dk][row]: the transposed
+  // read of K's tile, element e of lane l being row kperm(s, hh, e), dk 32 t + l % 32
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int rr = kperm(s, h2, e);
-        x[e] = static_cast<_Float16>(__expf(c_last - lds_c[rr]) * tile_at(lds_k, rr, 32 * t + mm));
-      }
-      *reinterpret_cast<f16x8*>(rec + kOffK + static_cast<size_t>(u) * 16) = x;
-    }
+  for (int s = 0; s < 4; ++s) {
+    const int t = wave;
+    const bf16x8 kf = tr_frag(lds_k, s, 32 * t, lane);
+    f16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      x[e] = static_cast<_Float16>(lds_fk[kperm(s, hh, e)] * static_cast<float>(kf[e]));
+    *reinterpret_cast<f16x8*>(rec + kOffK + static_cast<size_t>((s * 4 + t) * 64 + lane) * 16) = x;
   }
   __syncthreads();   // A complete; the Q tile is free for T
 

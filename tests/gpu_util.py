@@ -41,6 +41,7 @@ def check_attn(got: np.ndarray, ref: np.ndarray, what: str) -> None:
     assert np.all(np.isfinite(got)), what
     err = np.abs(got - ref)
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    print(f"[attn] {what}: max-abs {err.max():.3e} rel-L2 {rel:.3e}", flush=True)
     assert err.max() <= ATTN_MAX_ABS, f"{what}: max-abs {err.max():.3e}"
     assert rel <= ATTN_REL_L2, f"{what}: rel-L2 {rel:.3e}"
 

@@ -44,7 +44,9 @@ def test_gate_tiny(random_bias):
 @pytest.mark.parametrize("n,hidden,hg,ld", [(1000, 256, 96, 264), (1, 64, 32, 64),
                                            (130, 512, 512, 520), (64, 128, 64, 128),
                                            (333, 192, 200, 200), (77, 64, 1, 64),
-                                           (300, 128, 384, 136), (66000, 64, 256, 64)])
+                                           (300, 128, 384, 136), (66000, 64, 256, 64),
+                                           (40000, 64, 300, 72), (33000, 128, 512, 128),
+                                           (33023, 192, 257, 200)])
 def test_gate_ragged_strided(n, hidden, hg, ld):
     rng = np.random.default_rng(n + hg)
     base = inputs.round_bf16(rng.standard_normal((n, ld)).astype(np.float32))
@@ -66,7 +68,9 @@ def test_gate_qwen_shapes_and_determinism(n):
     say(f"gate qwen n={n}")
     hd = dev_bf16(g["h"]); w1d = dev_bf16(g["w1"])
     s1 = tg.gate_score(hd, w1d, dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
-    s2 = tg.gate_score(hd, w1d, dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"])
+    # into a buffer that holds NaNs: every score is written afresh
+    s2 = tg.gate_score(hd, w1d, dev_f32(g["b1"]), dev_f32(g["w2"]), g["b2"],
+                       out=torch.full((n,), float("nan"), dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
     a, b = s1.cpu().numpy(), s2.cpu().numpy()
     assert a.tobytes() == b.tobytes()                     # deterministic
