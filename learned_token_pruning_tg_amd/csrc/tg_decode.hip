@@ -22,7 +22,7 @@
 // softmax in log2 units with block reductions; P.V again eight lanes per row,
 // reduced across rows by lane exchanges and a fixed-order sum over the four
 // waves.  Each chunk leaves (max, sum, unnormalised output) per head in the
-// workspace; a combine launch merges the chunks in chunk order
+// workspace; a combine launch merges the chunks in a fixed order
 // (deterministic) and writes the bf16 output and the log-sum-exp.
 // Everything after the bf16 inputs is fp32.
 #include "tg_device.h"
@@ -249,46 +249,62 @@ __global__ __launch_bounds__(kDThreads) void decode_chunk_kernel(
   }
 }
 
-// Merge the chunks of one query head: one work-group of 256 threads; the
-// global max from a strided scan of the chunk maxima, then 256 / D groups of D
-// threads (thread = output dim) each sum a fixed, strided subset of the
-// chunks, and the groups are added in group order (deterministic).
+// Merge the chunks of one query head in one pass: a work-group of 1024
+// threads in NG = 1024 / (D / 4) groups of D / 4 threads; group cg folds the
+// chunks cg, cg + NG, ... in that order into a running (max, sum, output)
+// (each thread four dims, dim + D/4 i, so every load of a group is one
+// contiguous run), then the groups' states are merged in group order
+// (deterministic).  One pass over the partials, several chunks' loads in
+// flight per thread: the merge is a few load latencies, not one per chunk.
+constexpr int kCThreads = 1024;
 template <int D>
-__global__ __launch_bounds__(kDThreads) void decode_combine_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(kCThreads) void decode_combine_kernel(const float* __restrict__ part,
                                                                   int n_chunks, int G,
                                                                   bf16* __restrict__ out,
                                                                   float* __restrict__ lse) {
-  constexpr int NG = kDThreads / D;
+  constexpr int TPR = D / 4;             // threads per chunk row
+  constexpr int NG = kCThreads / TPR;    // chunk groups
   __shared__ float so[NG][D];
-  __shared__ float sl[NG];
-  __shared__ float tmp[kDWaves];
+  __shared__ float sm[NG], sl[NG];
   const int h = blockIdx.x, kvh = h / G, g = h % G;
-  const int tid = threadIdx.x, dim = tid % D, cg = tid / D;
+  const int tid = threadIdx.x, t = tid % TPR, cg = tid / TPR;
   const size_t stride = static_cast<size_t>(G) * (D + 2);
   const float* base = part + static_cast<size_t>(kvh) * n_chunks * stride + g * (D + 2);
-  float mx = -INFINITY;
-  for (int c = tid; c < n_chunks; c += kDThreads) mx = fmaxf(mx, base[c * stride]);
-  mx = block_reduce<true>(mx, tmp);
-  float l = 0.f, o = 0.f;
-#pragma unroll 8
+  float m = -INFINITY, l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int c = cg; c < n_chunks; c += NG) {
     const float* pc = base + c * stride;
-    const float w = fast_exp2(pc[0] - mx);
-    l = fmaf(pc[1], w, l);
-    o = fmaf(pc[2 + dim], w, o);
-  }
-  so[cg][dim] = o;
-  if (dim == 0) sl[cg] = l;
-  __syncthreads();
-  if (cg == 0) {
-    float ot = so[0][dim], lt = sl[0];
+    const float mc = pc[0], lc = pc[1];   // mc is finite: every chunk holds a key below n
+    float oc[4];
 #pragma unroll
-    for (int i = 1; i < NG; ++i) {
-      ot += so[i][dim];
-      lt += sl[i];
+    for (int i = 0; i < 4; ++i) oc[i] = pc[2 + t + TPR * i];
+    const float mn = fmaxf(m, mc);
+    const float a = fast_exp2(m - mn), b = fast_exp2(mc - mn);   // a = 0 on the first chunk
+    l = fmaf(l, a, lc * b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = fmaf(o[i], a, oc[i] * b);
+    m = mn;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) so[cg][t + TPR * i] = o[i];
+  if (t == 0) {
+    sm[cg] = m;
+    sl[cg] = l;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float mx = -INFINITY;
+    for (int i = 0; i < NG; ++i) mx = fmaxf(mx, sm[i]);
+    float lt = 0.f, ot = 0.f;
+    for (int i = 0; i < NG; ++i) {
+      if (sl[i] > 0.f) {   // groups without chunks (m = -inf) contribute nothing
+        const float w = fast_exp2(sm[i] - mx);
+        lt = fmaf(sl[i], w, lt);
+        ot = fmaf(so[i][tid], w, ot);
+      }
     }
-    out[static_cast<size_t>(h) * D + dim] = static_cast<bf16>(ot / lt);
-    if (lse != nullptr && dim == 0) lse[h] = (mx + __log2f(lt)) * kLn2;
+    out[static_cast<size_t>(h) * D + tid] = static_cast<bf16>(ot / lt);
+    if (lse != nullptr && tid == 0) lse[h] = (mx + __log2f(lt)) * kLn2;
   }
 }
 
@@ -315,7 +331,7 @@ void launch_dg(const uint16_t* q, const uint16_t* k, const uint16_t* v, int n, i
     else if constexpr (G <= 2)
       launch_chunks<D, G, 256, kBias>(q, k, v, n, Hq, Hkv, s, gain, tau, p, part, stream);
   }
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(static_cast<unsigned>(Hq)), dim3(kDThreads),
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(static_cast<unsigned>(Hq)), dim3(kCThreads),
                      0, stream, part, p.n_chunks, G, reinterpret_cast<bf16*>(out), lse);
 }
 
