@@ -451,14 +451,17 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 // slice of value rows 32 b .. 32 b + 31.  Each chunk's operand record (the
 // -W, U', P, Kt^T and scaled q fragments and Gam_last, as the prep pass laid
 // them out) is DMAed into a two-stage LDS ring, once for the four waves; one
-// barrier per chunk, the next chunk's DMA in flight during this chunk.  The
-// record after that is touched into L2 meanwhile (4-byte DMAs, one per
-// 128-byte line, into a small sink), so the DMA that fills the ring reads L2,
-// not HBM.
+// barrier per chunk, the next chunk's DMA in flight during this chunk.  Each
+// wave's share of that DMA is issued a few pieces at a time between the MFMAs
+// of the chunk's first k-steps: issued all at once after the barrier, the
+// pieces (19 per wave, a 1 KiB request each) held the wave's MFMAs behind
+// them in the in-order issue.
 constexpr int kRecLds = (kRec + 1023) / 1024 * 1024;   // whole 1 KiB DMA pieces
 constexpr int kStage = kRecLds;
 constexpr int kPieces = kRecLds / 1024;
-constexpr int kTouch = (kRec / 128 + 255) / 256;       // touch loads per wave (64 lines each)
+constexpr int kPiecesPerWave = (kPieces + 3) / 4;
+constexpr int kPiecesPerStep = 3;                      // DMA pieces per k-step of U / O
+static_assert(kPiecesPerStep * 8 >= kPiecesPerWave, "the DMA fits the k-steps");
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector
 // memory operations of this wave are outstanding and leaves the other
@@ -469,12 +472,11 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__
                                                         int Hv, const float* __restrict__ s_init,
                                                         float* __restrict__ s_final,
                                                         bf16* __restrict__ out) {
-  // One LDS object (ring stages and the touch sink): with several, the
-  // compiler would make each read of the ring wait for all DMA in flight into
-  // it, the next chunk's included; the explicit waits below order the ring.
-  __shared__ __align__(16) char lds_all[2 * kStage + 4 * 256];
+  // One LDS object: with several, the compiler would make each read of the
+  // ring wait for all DMA in flight into it, the next chunk's included; the
+  // explicit waits below order the ring.
+  __shared__ __align__(16) char lds_all[2 * kStage];
   auto* lds = reinterpret_cast<char (*)[kStage]>(lds_all);
-  auto* sink = reinterpret_cast<char (*)[256]>(lds_all + 2 * kStage);
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int b = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // provably wave-uniform
@@ -486,28 +488,19 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__
   // four waves (lane i moves the 16 bytes at 16 i of its piece); bytes past
   // the record read as zeros.  The whole offset is per lane, the LDS
   // address wave-uniform.
-  auto dma = [&](int st, int c) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rr =
-        make_rsrc(rec_base + (static_cast<size_t>(c) * Hv + h) * kRec, kRec);
-#pragma unroll
-    for (int i = 0; i < (kPieces + 3) / 4; ++i) {
-      const int j = b + 4 * i;
-      if (j < kPieces)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rr, (__attribute__((address_space(3))) void*)(&lds[st][0] + 1024 * j), 16,
-            16 * lane + 1024 * j, 0, 0, 0);
+  auto dma_piece = [&](int st, int c, int i) __attribute__((always_inline)) {
+    const int j = b + 4 * i;
+    if (j < kPieces) {
+      const __amdgpu_buffer_rsrc_t rr =
+          make_rsrc(rec_base + (static_cast<size_t>(c) * Hv + h) * kRec, kRec);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rr, (__attribute__((address_space(3))) void*)(&lds[st][0] + 1024 * j), 16,
+          16 * lane + 1024 * j, 0, 0, 0);
     }
   };
-  // L2 touch of chunk c: wave b takes lines b, b + 4, ... (lines past the
-  // record are out of range and touch nothing)
-  auto touch = [&](int c) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rr =
-        make_rsrc(rec_base + (static_cast<size_t>(c) * Hv + h) * kRec, kRec);
+  auto dma = [&](int st, int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kTouch; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rr, (__attribute__((address_space(3))) void*)(&sink[b][0]), 4,
-          128 * (b + 4 * (lane + 64 * i)), 0, 0, 0);
+    for (int i = 0; i < kPiecesPerWave; ++i) dma_piece(st, c, i);
   };
 
   // S^T slice: tile t = dk rows 32 t .., register jr = dk row 32 t + crow(jr, hh)
@@ -529,33 +522,23 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__
                 static_cast<uint32_t>(n) * row_bytes - static_cast<uint32_t>(h) * kD * 2);
   const uint32_t lane_off = static_cast<uint32_t>(4 * hh) * row_bytes + 2u * dv;
 
-  // Per wave, in issue order, chunk c adds: the DMA of chunk c + 1, the
-  // touch of chunk c + 2, then chunk c's 32 output stores.  Vector memory
-  // operations retire in order, so "at most kTouch + 32 outstanding" at the
-  // top of chunk c + 1 means its DMA has landed while the touch and the
-  // stores still drain.
+  // Per wave, in issue order, chunk c adds the DMA of chunk c + 1 and then
+  // chunk c's 32 output stores.  Vector memory operations retire in order,
+  // so "at most 32 outstanding" at the top of chunk c + 1 means its DMA has
+  // landed while the stores still drain.
   __builtin_amdgcn_s_waitcnt(vm_wait(0));   // the initial state has arrived
   if (nc > 0) dma(0, 0);
-  if (nc > 1) touch(1);
   for (int c = 0; c < nc; ++c) {
-    if (c == 0) {
-      if (nc > 1) __builtin_amdgcn_s_waitcnt(vm_wait(kTouch));
-      else __builtin_amdgcn_s_waitcnt(vm_wait(0));
-    } else if (c + 1 < nc) {
-      __builtin_amdgcn_s_waitcnt(vm_wait(kTouch + 32));   // touch(c + 1) was issued
-    } else {
-      __builtin_amdgcn_s_waitcnt(vm_wait(32));
-    }
+    if (c == 0) __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    else __builtin_amdgcn_s_waitcnt(vm_wait(32));
     // every wave's DMA of chunk c has landed and every wave is done with
     // chunk c - 1, whose stage the next DMA refills.  A plain barrier: a
-    // workgroup fence would also wait for the touches (LDS DMA) and the
-    // stores still in flight; the empty asm keeps the compiler from moving
-    // LDS accesses across it.
+    // workgroup fence would also wait for the stores still in flight; the
+    // empty asm keeps the compiler from moving LDS accesses across it.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (c + 1 < nc) dma((c + 1) & 1, c + 1);
-    if (c + 2 < nc) touch(c + 2);
+    const bool more = c + 1 < nc;
     const char* rec = &lds[c & 1][0];
     auto frag = [&](const char* base, int off) __attribute__((always_inline)) {
       return *reinterpret_cast<const f16x8*>(base + off + lane * 16);
@@ -598,6 +581,12 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__
       for (int r = 0; r < 2; ++r) {
         u[r] = mfma_f16(wf[s & 1][r], bs[s], u[r]);
         o[r] = mfma_f16(qf[s & 1][r], bs[s], o[r]);
+      }
+      // this k-step's share of the DMA of chunk c + 1
+#pragma unroll
+      for (int e = 0; e < kPiecesPerStep; ++e) {
+        const int i = kPiecesPerStep * s + e;
+        if (i < kPiecesPerWave && more) dma_piece((c + 1) & 1, c + 1, i);
       }
 #pragma unroll
       for (int jr = 0; jr < 8; ++jr) st[s >> 1][8 * (s & 1) + jr] *= gl;
