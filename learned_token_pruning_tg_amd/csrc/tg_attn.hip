@@ -13,7 +13,8 @@
 // 1. v_pack: per KV head and 64-key tile, the V^T image the main kernel
 //    DMAs into LDS, in the caller's workspace: fp16 [d][key], key order
 //    permuted inside each 16-key group so that every lane's eight keys of a
-//    P.V step are one 16-byte run, rows padded; plus (gated) per query head
+//    P.V step are one 16-byte run, the runs of a row XOR-swizzled (unpadded
+//    128-byte rows, conflict-free fragment reads); plus (gated) per query head
 //    and key the bias in units of q.k, c_h s_j with c_h = gain_h sqrt(d)
 //    tau_h, in fp32.  Keys past n are zero.  K is not copied: the main kernel
 //    DMAs K tiles straight from k.
@@ -98,7 +99,8 @@ struct Tile {
   static constexpr int K_ROW = D * 2;                     // LDS bytes per key: 16-byte chunks,
                                                           //   chunk c of key r at slot c ^ swz(r)
   static constexpr int K_IMG = kBN * K_ROW;               // one K tile in LDS
-  static constexpr int V_ROW = kBN * 2 + 16;              // bytes, padded
+  static constexpr int V_ROW = kBN * 2;                   // bytes: 16-byte piece c of dim row r at
+                                                          //   slot c ^ vswz(r)
   static constexpr int V_IMG = D * V_ROW;                 // one V^T tile (workspace and LDS)
   static constexpr int S_TILE = kBN * 4;                  // one head's bias values of a tile (fp32)
   // XOR key of K row r: 16 consecutive rows hit 16 different 16-byte slots
@@ -107,6 +109,9 @@ struct Tile {
   static __host__ __device__ constexpr int swz(int r) {
     return D == 128 ? (r & 15) : ((r >> 1) & 7);
   }
+  // XOR key of V^T row r (128-byte rows): the 16 rows one pass of a fragment
+  // read serves, eight of each parity, hit 16 different 16-byte bank slots.
+  static __host__ __device__ constexpr int vswz(int r) { return (r >> 1) & 7; }
   static_assert(K_IMG % 1024 == 0 && V_IMG % 1024 == 0, "tiles must be whole 1 KiB DMA chunks");
   // One split chunk's partial state: per 32-row set (kSets per wave), the
   // lane-major fp16 output (D bytes per lane in 16-byte vectors) and a
@@ -240,7 +245,8 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // v_pack: one work-group per (tile, KV head) builds the tile's V^T image in
 // the workspace (fp16, [d][key] with the key order permuted inside each
 // 16-key group so that every lane's eight keys of a P.V step are one 16-byte
-// run; rows padded; keys past n zero).  In a gated call each work-group also
+// run; the runs of row r at slot run ^ vswz(r); keys past n zero).  In a
+// gated call each work-group also
 // stores, for the query heads of its KV group and the tile's keys, the bias
 // c_h s_j (fp32, [head][key]).  K needs no pass of its own: the attention
 // kernel DMAs its tiles straight from k.
@@ -288,11 +294,11 @@ __global__ __launch_bounds__(256) void v_pack_kernel(const bf16* __restrict__ v,
       hi.x = (x0 >> 16) | (x1 & 0xFFFF0000u);
       hi.y = (x2 >> 16) | (x3 & 0xFFFF0000u);
       const int d0 = 8 * dc + 2 * w;
-      *reinterpret_cast<uint2*>(vimg + d0 * T::V_ROW + 2 * phys) = lo;
-      *reinterpret_cast<uint2*>(vimg + (d0 + 1) * T::V_ROW + 2 * phys) = hi;
+      const int pc = phys >> 3, pb = (2 * phys) & 15;   // 16-byte piece, byte within it
+      *reinterpret_cast<uint2*>(vimg + d0 * T::V_ROW + ((pc ^ T::vswz(d0)) << 4) + pb) = lo;
+      *reinterpret_cast<uint2*>(vimg + (d0 + 1) * T::V_ROW + ((pc ^ T::vswz(d0 + 1)) << 4) + pb) = hi;
     }
   }
-  if (tid < D) st16(vimg + tid * T::V_ROW + kBN * 2, zero_u32x4());
   if (score_task) {
     // the key's bias in units of q.k for each head of this group:
     // c_h s_j with c_h = gain_h sqrt(d) tau_h
@@ -532,6 +538,12 @@ __global__ __launch_bounds__(kThreads * HG, 2 / (kSets * HG)) void attn_fwd_kern
   // MFMAs.  Lane (l32, hh) reads chunk 2 ks + hh of key 32 t2 + l32, stored at
   // slot (2 ks + hh) ^ swz(l32): the per-k-step address is one XOR.
   const uint32_t k_base = static_cast<uint32_t>(l32) * T::K_ROW + ((hh ^ T::swz(l32)) << 4);
+  // V^T fragment of P.V step ps: dim row 32 dt + l32, piece 2 ps + hh (its
+  // XOR key depends on l32 only)
+  uint32_t v_off[4];
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps)
+    v_off[ps] = static_cast<uint32_t>(l32) * T::V_ROW + (((2 * ps + hh) ^ T::vswz(l32)) << 4);
   auto qk = [&](const char* kimg, const char* simg, floatx16 (&s)[kSets][2])
       __attribute__((always_inline)) {
     // S~ starts from the keys' bias c_h s_j (register j of 32-key half t2
@@ -659,7 +671,7 @@ __global__ __launch_bounds__(kThreads * HG, 2 / (kSets * HG)) void attn_fwd_kern
     auto vread = [&](int ps, f16x8 (&dst)[DT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        dst[dt] = *reinterpret_cast<const f16x8*>(vimg + (32 * dt + l32) * T::V_ROW + (16 * ps + 8 * hh) * 2);
+        dst[dt] = *reinterpret_cast<const f16x8*>(vimg + 32 * dt * T::V_ROW + v_off[ps]);
     };
     kread(0, ka[0]);
 #pragma unroll

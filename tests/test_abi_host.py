@@ -165,7 +165,7 @@ def test_attention_validation(L):
     assert full(A, A, A, 10, 16, 8, 64 + 1, A, None, A, W, 0) == UNSUPPORTED
     assert full(A, A, A, 1 << 20, 16, 8, 128, A, None, A, W, 0) == UNSUPPORTED  # 2^31-byte offsets
     need = L.tg_attn_workspace_bytes(100, 16, 8, 128)
-    assert need == 2 * 8 * 128 * 144 + 16 * 2 * 256  # V^T images (2 tiles x 8 heads) + fp32 biases
+    assert need == 2 * 8 * 128 * 128 + 16 * 2 * 256  # V^T images (2 tiles x 8 heads) + fp32 biases
     assert g(A, A, A, 100, 16, 8, 128, A, A, A, A, None, A, need - 1, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, A, 1000, 0) == WORKSPACE
     assert full(A, A, A, 100, 16, 8, 128, A, None, None, need, 0) == WORKSPACE
@@ -263,7 +263,7 @@ def _split_layout(n, hq, hkv, d, gated=True):
     if 4 < h < n_qt and _simulated_makespan(n, n_qt, h - 1, hq) < 0.94 * _simulated_makespan(n, n_qt, h, hq):
         h -= 1
     units = sum(-(-(qt + 1) // h) for qt in range(n_qt))
-    img = d * 144                              # V^T image of one tile (fp16, padded rows)
+    img = d * 128                              # V^T image of one tile (fp16, 128-byte rows)
     sc = hq * n_tiles * 64 * 4                 # per query head and key: the fp32 bias
     n_part = units - min(h, n_qt)
     return n_tiles * hkv * img + -(-sc // 256) * 256 + hq * n_part * part, h, units
