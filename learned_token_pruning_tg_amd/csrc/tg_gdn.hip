@@ -33,7 +33,8 @@
 // 2. gdn_state: one work-group per value head walks the chunks in order, a
 //    wave per 32 value rows (the rows of S evolve independently), the head's
 //    per-chunk operands DMAed once into a two-stage LDS ring for the four
-//    waves.  Each wave's fp32 state slice S^T [128 dk x 32 dv]
+//    state waves by four waves of their own.  Each state wave's fp32 slice
+//    S^T [128 dk x 32 dv]
 //    lives in MFMA accumulators; per chunk: U = U' - W S^T and
 //    O = (scale Gam Q) S^T (16 + 16 fp16 MFMAs), O += (scale P) U (8),
 //    S^T = Gam_last S^T + Kt^T U (16).  The state's accumulator layout is used directly as the B operand:
@@ -447,28 +448,26 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
 // gdn_state
 // ---------------------------------------------------------------------------
 
-// One work-group of four waves per value head; wave b carries the state
-// slice of value rows 32 b .. 32 b + 31.  Each chunk's operand record (the
-// -W, U', P, Kt^T and scaled q fragments and Gam_last, as the prep pass laid
-// them out) is DMAed into a two-stage LDS ring, once for the four waves; one
-// barrier per chunk, the next chunk's DMA in flight during this chunk.  Each
-// wave's share of that DMA is issued a few pieces at a time between the MFMAs
-// of the chunk's first k-steps: issued all at once after the barrier, the
-// pieces (19 per wave, a 1 KiB request each) held the wave's MFMAs behind
-// them in the in-order issue.
+// One work-group of eight waves per value head.  Waves 0-3 carry the state:
+// wave b the slice of value rows 32 b .. 32 b + 31.  Waves 4-7 only move each
+// chunk's operand record (the -W, U', P, Kt^T and scaled q fragments and
+// Gam_last, as the prep pass laid them out) into a two-stage LDS ring, once
+// for the four state waves, the next chunk's DMA in flight during this chunk;
+// one barrier per chunk for all eight.  The DMA (73 pieces of 1 KiB per
+// chunk) costs its issuing waves time in proportion to their share of the
+// pieces, so it runs on waves of its own, one beside each state wave on its
+// SIMD (the kernel's 223 registers leave room for two waves per SIMD).
 constexpr int kRecLds = (kRec + 1023) / 1024 * 1024;   // whole 1 KiB DMA pieces
 constexpr int kStage = kRecLds;
 constexpr int kPieces = kRecLds / 1024;
-constexpr int kPiecesPerWave = (kPieces + 3) / 4;
-constexpr int kPiecesPerStep = 3;                      // DMA pieces per k-step of U / O
-static_assert(kPiecesPerStep * 8 >= kPiecesPerWave, "the DMA fits the k-steps");
+constexpr int kPiecesPerWave = (kPieces + 3) / 4;       // per DMA wave
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most `vm` vector
 // memory operations of this wave are outstanding and leaves the other
 // counters alone.
 constexpr int vm_wait(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-__global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__ rec_base, int n,
+__global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__ rec_base, int n,
                                                         int Hv, const float* __restrict__ s_init,
                                                         float* __restrict__ s_final,
                                                         bf16* __restrict__ out) {
@@ -488,19 +487,21 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__
   // four waves (lane i moves the 16 bytes at 16 i of its piece); bytes past
   // the record read as zeros.  The whole offset is per lane, the LDS
   // address wave-uniform.
-  auto dma_piece = [&](int st, int c, int i) __attribute__((always_inline)) {
-    const int j = b + 4 * i;
-    if (j < kPieces) {
-      const __amdgpu_buffer_rsrc_t rr =
-          make_rsrc(rec_base + (static_cast<size_t>(c) * Hv + h) * kRec, kRec);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rr, (__attribute__((address_space(3))) void*)(&lds[st][0] + 1024 * j), 16,
-          16 * lane + 1024 * j, 0, 0, 0);
-    }
-  };
+  // DMA of chunk c into stage st by DMA wave b: pieces b - 4, b, b + 4, ...
+  // of 1 KiB (lane i moves the 16 bytes at 16 i of its piece); bytes past the
+  // record read as zeros.  The whole offset is per lane, the LDS address
+  // wave-uniform.
   auto dma = [&](int st, int c) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rr =
+        make_rsrc(rec_base + (static_cast<size_t>(c) * Hv + h) * kRec, kRec);
 #pragma unroll
-    for (int i = 0; i < kPiecesPerWave; ++i) dma_piece(st, c, i);
+    for (int i = 0; i < kPiecesPerWave; ++i) {
+      const int j = (b & 3) + 4 * i;
+      if (j < kPieces)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rr, (__attribute__((address_space(3))) void*)(&lds[st][0] + 1024 * j), 16,
+            16 * lane + 1024 * j, 0, 0, 0);
+    }
   };
 
   // S^T slice: tile t = dk rows 32 t .., register jr = dk row 32 t + crow(jr, hh)
@@ -522,23 +523,27 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__
                 static_cast<uint32_t>(n) * row_bytes - static_cast<uint32_t>(h) * kD * 2);
   const uint32_t lane_off = static_cast<uint32_t>(4 * hh) * row_bytes + 2u * dv;
 
-  // Per wave, in issue order, chunk c adds the DMA of chunk c + 1 and then
-  // chunk c's 32 output stores.  Vector memory operations retire in order,
-  // so "at most 32 outstanding" at the top of chunk c + 1 means its DMA has
-  // landed while the stores still drain.
-  __builtin_amdgcn_s_waitcnt(vm_wait(0));   // the initial state has arrived
-  if (nc > 0) dma(0, 0);
+  // A DMA wave waits for its own pieces of chunk c before the barrier at the
+  // top of chunk c; the barrier then also means every state wave is done with
+  // chunk c - 1, whose stage the next DMA refills.  A plain barrier: a
+  // workgroup fence would also wait for the state waves' output stores; the
+  // empty asm keeps the compiler from moving LDS accesses across it.
+  if (b >= 4) {   // DMA waves: the ring's DMA only, one barrier per chunk like the others
+    if (nc > 0) dma(0, 0);
+    for (int c = 0; c < nc; ++c) {
+      __builtin_amdgcn_s_waitcnt(vm_wait(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (c + 1 < nc) dma((c + 1) & 1, c + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    return;
+  }
   for (int c = 0; c < nc; ++c) {
-    if (c == 0) __builtin_amdgcn_s_waitcnt(vm_wait(0));
-    else __builtin_amdgcn_s_waitcnt(vm_wait(32));
-    // every wave's DMA of chunk c has landed and every wave is done with
-    // chunk c - 1, whose stage the next DMA refills.  A plain barrier: a
-    // workgroup fence would also wait for the stores still in flight; the
-    // empty asm keeps the compiler from moving LDS accesses across it.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const bool more = c + 1 < nc;
     const char* rec = &lds[c & 1][0];
     auto frag = [&](const char* base, int off) __attribute__((always_inline)) {
       return *reinterpret_cast<const f16x8*>(base + off + lane * 16);
@@ -581,12 +586,6 @@ __global__ __launch_bounds__(256) void gdn_state_kernel(const char* __restrict__
       for (int r = 0; r < 2; ++r) {
         u[r] = mfma_f16(wf[s & 1][r], bs[s], u[r]);
         o[r] = mfma_f16(qf[s & 1][r], bs[s], o[r]);
-      }
-      // this k-step's share of the DMA of chunk c + 1
-#pragma unroll
-      for (int e = 0; e < kPiecesPerStep; ++e) {
-        const int i = kPiecesPerStep * s + e;
-        if (i < kPiecesPerWave && more) dma_piece((c + 1) & 1, c + 1, i);
       }
 #pragma unroll
       for (int jr = 0; jr < 8; ++jr) st[s >> 1][8 * (s & 1) + jr] *= gl;
@@ -652,7 +651,7 @@ hipError_t launch_gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
   hipLaunchKernelGGL(gdn_prep_kernel, dim3(static_cast<unsigned>(nc) * n_v_heads), dim3(256), 0,
                      stream, reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
                      reinterpret_cast<const bf16*>(v), g, beta, ni, n_qk_heads, n_v_heads, scale, rec);
-  hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(n_v_heads)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(n_v_heads)), dim3(512), 0, stream,
                      rec, ni, n_v_heads, initial_state, final_state, reinterpret_cast<bf16*>(out));
   return hipGetLastError();
 }
