@@ -46,7 +46,7 @@ def test_gate_tiny(random_bias):
                                            (333, 192, 200, 200), (77, 64, 1, 64),
                                            (300, 128, 384, 136), (66000, 64, 256, 64),
                                            (40000, 64, 300, 72), (33000, 128, 512, 128),
-                                           (33023, 192, 257, 200)])
+                                           (33023, 192, 257, 200), (49999, 64, 450, 72)])
 def test_gate_ragged_strided(n, hidden, hg, ld):
     rng = np.random.default_rng(n + hg)
     base = inputs.round_bf16(rng.standard_normal((n, ld)).astype(np.float32))
