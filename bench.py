@@ -211,6 +211,25 @@ def _timer_pair():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+def _steady_ms(fn, reps, stream, warm=3, batches=3):
+    """Per-call milliseconds of fn on `stream`: `warm` untimed calls, then
+    `batches` event-timed batches of `reps` calls; the median batch."""
+    import torch
+    for _ in range(warm):
+        fn()
+    per = []
+    for _ in range(batches):
+        ea, eb = _timer_pair()
+        torch.cuda.synchronize()
+        ea.record(stream)
+        for _ in range(reps):
+            fn()
+        eb.record(stream)
+        torch.cuda.synchronize()
+        per.append(ea.elapsed_time(eb) / reps)
+    return sorted(per)[len(per) // 2]
+
+
 class GatedStep:
     """Device buffers and the launch sequence of one gated-prefill step:
     gate (all N rows) -> top-K (which also gathers the kept scores s') ->
@@ -496,15 +515,7 @@ def main():
             return graph
 
         def time_calls(fn, reps):
-            fn()
-            ea, eb = _timer_pair()
-            torch.cuda.synchronize()
-            ea.record(stream)
-            for _ in range(reps):
-                fn()
-            eb.record(stream)
-            torch.cuda.synchronize()
-            return ea.elapsed_time(eb) / reps
+            return _steady_ms(fn, reps, stream)
 
         g_upper, g_gate = graphed(decode_upper), graphed(decode_gate_layer)
         dec_upper_ms = time_calls(g_upper.replay, 20) / w.n_layers
@@ -592,15 +603,7 @@ def main():
                        workspace=gws)
 
         def time_gdn(src, rows, reps):
-            gdn(src, rows)
-            ea, eb = _timer_pair()
-            torch.cuda.synchronize()
-            ea.record(stream)
-            for _ in range(reps):
-                gdn(src, rows)
-            eb.record(stream)
-            torch.cuda.synchronize()
-            return ea.elapsed_time(eb) / reps
+            return _steady_ms(lambda: gdn(src, rows), reps, stream)
 
         gk_ms = time_gdn(gk, m, max(3, min(args.steps, 10)))
         gf_ms = time_gdn(gd, w.n, 2)
