@@ -34,7 +34,7 @@ def _gpu(x, s0=None, want_state=False, ws=None):
 
 
 @pytest.mark.parametrize("n,hk,hv", [(1, 1, 1), (2, 1, 2), (63, 2, 2), (64, 1, 1), (65, 2, 4),
-                                     (130, 1, 2), (200, 4, 8), (1000, 16, 32)])
+                                     (130, 1, 2), (200, 4, 8), (1000, 16, 32), (1100, 1, 3)])
 def test_gdn_vs_oracle(n, hk, hv):
     x = inputs.gdn_inputs(2000 + n, n, hk, hv)
     say(f"gdn n={n} hk={hk} hv={hv}")
@@ -43,11 +43,13 @@ def test_gdn_vs_oracle(n, hk, hv):
     check_attn(got, ref, f"gdn n={n}")
 
 
-def test_gdn_initial_and_final_state():
-    n, hk, hv = 300, 2, 4
-    x = inputs.gdn_inputs(77, n, hk, hv)
+@pytest.mark.parametrize("n", [300, 1100, 2500])
+def test_gdn_initial_and_final_state(n):
+    """At 300, 1100 and 2500 rows (5, 18 and 40 chunks)."""
+    hk, hv = 2, 4
+    x = inputs.gdn_inputs(77 + n, n, hk, hv)
     s0 = (np.random.default_rng(78).standard_normal((hv, 128, 128)) * 0.05).astype(np.float32)
-    say("gdn with initial/final state")
+    say(f"gdn with initial/final state n={n}")
     got, st = _gpu(x, s0=s0, want_state=True)
     ref, ref_st = G.gated_delta_rule(x["q"], x["k"], x["v"], x["g"], x["beta"], initial_state=s0,
                                      return_state=True)
