@@ -120,6 +120,18 @@ def kept_count(n: int, doc_begin: int, doc_end: int, k_doc: int) -> int:
     return m
 
 
+def k_doc_for_budget(n: int, doc_begin: int, doc_end: int, max_kept_prefill_tokens: int) -> int:
+    """Document budget for a budget on all kept prefill tokens (lucasainews.com
+    article, "사용법과 비용": the caller marks the prunable document and passes a
+    kept-token budget).  Rows outside the document are always kept, so the
+    document gets what is left of the budget: max(0, B - (n - N_doc)); the
+    kept count is then B, clamped to [n - N_doc, n]."""
+    if not 0 <= doc_begin <= doc_end <= n or max_kept_prefill_tokens < 0:
+        raise ValueError(f"invalid segment/budget: n={n} doc=[{doc_begin},{doc_end}) "
+                         f"B={max_kept_prefill_tokens}")
+    return max(0, max_kept_prefill_tokens - (n - (doc_end - doc_begin)))
+
+
 def gate_score(h: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: float,
                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """scores[i] = w2 . GELU(W1 h[i] + b1) + b2.  h [n, H] bf16 (row stride may

@@ -73,6 +73,23 @@ def test_kept_count(L, args, expect):
     assert L.tg_kept_count(*args) == expect
 
 
+@pytest.mark.parametrize("n,db,de", [(512, 0, 448), (16384, 0, 16128), (1000, 100, 900),
+                                     (10, 3, 3), (64, 0, 64)])
+def test_total_budget_maps_to_a_document_budget(L, n, db, de):
+    """A budget B on all kept prefill tokens: the rows outside the document
+    are always kept, so B is met exactly when it lies between that count and
+    n, and clamped to those ends otherwise."""
+    outside = n - (de - db)
+    for b in (0, 1, outside - 1, outside, outside + 1, (outside + n) // 2, n - 1, n, n + 7):
+        if b < 0:
+            continue
+        k = tg.k_doc_for_budget(n, db, de, b)
+        assert k >= 0
+        assert L.tg_kept_count(n, db, de, k) == min(max(b, outside), n)
+    with pytest.raises(ValueError):
+        tg.k_doc_for_budget(n, db, de, -1)
+
+
 def test_gate_validation(L):
     s = 0
     f = L.tg_gate_score
