@@ -34,10 +34,10 @@
 //    wave per 32 value rows (the rows of S evolve independently), the head's
 //    per-chunk operands DMAed once into a two-stage LDS ring for the four
 //    state waves by four waves of their own.  Each state wave's fp32 slice
-//    S^T [128 dk x 32 dv]
-//    lives in MFMA accumulators; per chunk: U = U' - W S^T and
-//    O = (scale Gam Q) S^T (16 + 16 fp16 MFMAs), O += (scale P) U (8),
-//    S^T = Gam_last S^T + Kt^T U (16).  The state's accumulator layout is used directly as the B operand:
+//    S^T [128 dk x 32 dv] lives in MFMA accumulators; per chunk:
+//    U = U' - W S^T and O = (scale Gam Q) S^T (16 + 16 fp16 MFMAs),
+//    O += (scale P) U (8), S^T = Gam_last S^T + Kt^T U (16).  The state's
+//    accumulator layout is used directly as the B operand:
 //    the contraction index k of every product (dk for W S^T and Q S^T, the
 //    chunk row for P U and Kt^T U) is permuted within each 16-wide k-step to
 //    the order in which the accumulators hold it, and the prep pass writes
@@ -483,10 +483,6 @@ __global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__
   const int nc = (n + kC - 1) / kC;
   const int dv = kBV * b + m;   // this lane's value row
 
-  // DMA of chunk c into stage st: pieces of 1 KiB dealt round-robin over the
-  // four waves (lane i moves the 16 bytes at 16 i of its piece); bytes past
-  // the record read as zeros.  The whole offset is per lane, the LDS
-  // address wave-uniform.
   // DMA of chunk c into stage st by DMA wave b: pieces b - 4, b, b + 4, ...
   // of 1 KiB (lane i moves the 16 bytes at 16 i of its piece); bytes past the
   // record read as zeros.  The whole offset is per lane, the LDS address
