@@ -11,8 +11,8 @@ Prints ONE JSON line (rank 0).  Usage:
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--no-other-configs]
 The default workload is 131072 tokens with 8192 document tokens kept; with it
-the line also carries compact records of the 32768-token workload and of the
-65536-token budget sweep (K = 1024, 4096, 16384, N).
+the line also carries compact records of the 16384- and 32768-token workloads
+and of the 65536-token budget sweep (K = 1024, 4096, 16384, N).
 """
 
 from __future__ import annotations
@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # The headline: 131072 tokens, 8192 document tokens kept (8448 kept rows).
 DEFAULT_WORKLOAD = "qwen3-1.7b-128k"
-OTHER_WORKLOADS = ("qwen3-1.7b-32k", "qwen3-1.7b-64k-sweep")
+OTHER_WORKLOADS = ("qwen3-1.7b-16k", "qwen3-1.7b-32k", "qwen3-1.7b-64k-sweep")
 
 
 def _parse():
@@ -42,7 +42,7 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-full-baseline", action="store_true")
     p.add_argument("--no-other-configs", action="store_true",
-                   help="skip the compact records of the 32k config and the 64k budget sweep "
+                   help="skip the compact records of the 16k and 32k configs and the 64k budget sweep "
                         "(measured only with the default workload)")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU time of the oracle sample")
@@ -364,8 +364,8 @@ def full_baseline(w, full_qkv, stream, steps, warmup, dev):
 
 
 def other_configs(names, steps, warmup, dev, stream):
-    """Compact records of the other workloads at their full sizes: the 32k
-    config, and the 64k budget sweep (one gate serving every budget: the same
+    """Compact records of the other workloads at their full sizes: the 16k and
+    32k configs, and the 64k budget sweep (one gate serving every budget: the same
     weights, residual and scores; top-K, compaction and the 27 layers per
     budget).  Per budget: step time and tokens/s, the gated attention's
     TFLOP/s and fraction of bf16 peak, and the speed-up over the full-N
