@@ -500,17 +500,6 @@ __global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__
     }
   };
 
-  // S^T slice: tile t = dk rows 32 t .., register jr = dk row 32 t + crow(jr, hh)
-  floatx16 st[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int jr = 0; jr < 16; ++jr)
-      st[t][jr] = s_init != nullptr
-                      ? s_init[(static_cast<size_t>(h) * kD + dv) * kD + 32 * t + crow(jr, hh)]
-                      : 0.f;
-  }
-
   // output rows of this head: byte offset row * row_bytes + (4 hh row part) +
   // dv * 2; the range ends at row n
   const uint32_t row_bytes = static_cast<uint32_t>(Hv) * kD * 2;   // n * row_bytes < 2^31
@@ -535,6 +524,18 @@ __global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__
     }
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
     return;
+  }
+  // S^T slice of a state wave (value rows dv < 128; the DMA waves, whose dv
+  // would run past the head, have left): tile t = dk rows 32 t .., register
+  // jr = dk row 32 t + crow(jr, hh)
+  floatx16 st[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int jr = 0; jr < 16; ++jr)
+      st[t][jr] = s_init != nullptr
+                      ? s_init[(static_cast<size_t>(h) * kD + dv) * kD + 32 * t + crow(jr, hh)]
+                      : 0.f;
   }
   for (int c = 0; c < nc; ++c) {
     asm volatile("" ::: "memory");
