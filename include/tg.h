@@ -301,8 +301,10 @@ tg_status tg_gated_attn_bwd(const tg_bf16* q, const tg_bf16* k, const tg_bf16* v
 /*
  * Bytes of device workspace tg_gdn_fwd needs for n rows: per 64-row chunk and
  * value head 72.25 KiB (the recurrence's operands as fp16 MFMA fragments and
- * the chunk's decay).  Host-only arithmetic; 0 for n <= 0 or unsupported
- * shapes.
+ * the chunk's decay), plus 64 KiB per value head (the fp32 state handed from
+ * one piece of the recurrence to the next: the layer runs in pieces of chunks,
+ * each piece's recurrence beside the next piece's operand preparation).
+ * Host-only arithmetic; 0 for n <= 0 or unsupported shapes.
  */
 size_t tg_gdn_workspace_bytes(int64_t n, int32_t n_qk_heads, int32_t n_v_heads, int32_t head_dim);
 

@@ -49,6 +49,7 @@
 // the MFMA operands (W, U', P, Kt, q and the fp32 state and deltas) rounded
 // to fp16 (11-bit mantissa; q and k are unit vectors, values of v above 65504
 // would saturate); output rounded to bf16.
+#include <algorithm>
 #include <cmath>
 
 #include "tg_device.h"
@@ -139,17 +140,27 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<bf16>(x));
 }
 
-__global__ __launch_bounds__(256) void gdn_prep_kernel(
+// LDS of one prep item: the K, Q and V tiles (48 KiB), A (16 KiB) and the
+// per-row decays and write strengths (1 KiB)
+constexpr int kPrepLds = 3 * kC * kD * 2 + kC * kC * 4 + 4 * kC * 4;
+
+// The prep of one (chunk c, value head h) on 256 threads (tid 0..255) with
+// kPrepLds bytes of LDS at lmem.  Contains work-group barriers: every thread
+// of the work-group calls it the same way.
+__device__ __forceinline__ void gdn_prep_item(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int n, int Hk, int Hv,
-    float scale, char* __restrict__ rec_base) {
+    float scale, char* __restrict__ rec_base, int c, int h, int tid, char* lmem) {
   // LDS: the K, Q and V tiles (48 KiB) and A (16 KiB).  Once P and the
   // scaled q fragments are out, the Q tile holds T = (I + A)^-1 (fp32), then
   // the bf16 hi/lo parts of T diag(beta); once T is formed, A's space holds
   // those of -T diag(beta Gam).
-  __shared__ __align__(16) char lds_tiles[3 * kC * kD * 2];
-  __shared__ __align__(16) float lds_a[kC][kC];
-  __shared__ float lds_c[kC], lds_b[kC], lds_gam[kC], lds_fk[kC];
+  char* const lds_tiles = lmem;
+  float (*const lds_a)[kC] = reinterpret_cast<float (*)[kC]>(lmem + 3 * kC * kD * 2);
+  float* const lds_c = reinterpret_cast<float*>(lmem + 3 * kC * kD * 2 + kC * kC * 4);
+  float* const lds_b = lds_c + kC;
+  float* const lds_gam = lds_c + 2 * kC;
+  float* const lds_fk = lds_c + 3 * kC;
   char* const lds_k = lds_tiles;
   char* const lds_q = lds_tiles + kC * kD * 2;
   char* const lds_v = lds_tiles + 2 * kC * kD * 2;
@@ -159,9 +170,8 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(
   char* const tk_hi = reinterpret_cast<char*>(&lds_a[0][0]);   // -T diag(beta Gam)
   char* const tk_lo = tk_hi + kC * kC * 2;
 
-  const int c = blockIdx.x / Hv, h = blockIdx.x % Hv;
   const int kh = h / (Hv / Hk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, m = lane & 31;
   const int row0 = c * kC;
   char* rec = rec_base + (static_cast<size_t>(c) * Hv + h) * kRec;
@@ -467,20 +477,20 @@ constexpr int kPiecesPerWave = (kPieces + 3) / 4;       // per DMA wave
 // counters alone.
 constexpr int vm_wait(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-__global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__ rec_base, int n,
-                                                        int Hv, const float* __restrict__ s_init,
-                                                        float* __restrict__ s_final,
-                                                        bf16* __restrict__ out) {
-  // One LDS object: with several, the compiler would make each read of the
-  // ring wait for all DMA in flight into it, the next chunk's included; the
-  // explicit waits below order the ring.
-  __shared__ __align__(16) char lds_all[2 * kStage];
-  auto* lds = reinterpret_cast<char (*)[kStage]>(lds_all);
-  const int h = blockIdx.x;
+// The chain of value head h over chunks c0 .. c1 - 1 on 512 threads with
+// 2 kStage bytes of LDS at lmem (the caller's single LDS object: with
+// several, the compiler would make each read of the ring wait for all DMA in
+// flight into it, the next chunk's included; the explicit waits below order
+// the ring).  Stage (c - c0) & 1 holds chunk c.
+__device__ __forceinline__ void gdn_chain_head(const char* __restrict__ rec_base, int n, int Hv,
+                                               int h, int c0, int c1,
+                                               const float* __restrict__ s_init,
+                                               float* __restrict__ s_final,
+                                               bf16* __restrict__ out, char* lmem) {
+  auto* lds = reinterpret_cast<char (*)[kStage]>(lmem);
   const int lane = threadIdx.x & 63;
   const int b = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // provably wave-uniform
   const int m = lane & 31, hh = lane >> 5;
-  const int nc = (n + kC - 1) / kC;
   const int dv = kBV * b + m;   // this lane's value row
 
   // DMA of chunk c into stage st by DMA wave b: pieces b - 4, b, b + 4, ...
@@ -514,13 +524,13 @@ __global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__
   // workgroup fence would also wait for the state waves' output stores; the
   // empty asm keeps the compiler from moving LDS accesses across it.
   if (b >= 4) {   // DMA waves: the ring's DMA only, one barrier per chunk like the others
-    if (nc > 0) dma(0, 0);
-    for (int c = 0; c < nc; ++c) {
+    if (c0 < c1) dma(0, c0);
+    for (int c = c0; c < c1; ++c) {
       __builtin_amdgcn_s_waitcnt(vm_wait(0));
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (c + 1 < nc) dma((c + 1) & 1, c + 1);
+      if (c + 1 < c1) dma((c + 1 - c0) & 1, c + 1);
     }
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
     return;
@@ -537,11 +547,11 @@ __global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__
                       ? s_init[(static_cast<size_t>(h) * kD + dv) * kD + 32 * t + crow(jr, hh)]
                       : 0.f;
   }
-  for (int c = 0; c < nc; ++c) {
+  for (int c = c0; c < c1; ++c) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const char* rec = &lds[c & 1][0];
+    const char* rec = &lds[(c - c0) & 1][0];
     auto frag = [&](const char* base, int off) __attribute__((always_inline)) {
       return *reinterpret_cast<const f16x8*>(base + off + lane * 16);
     };
@@ -628,13 +638,47 @@ __global__ __launch_bounds__(512) void gdn_state_kernel(const char* __restrict__
   }
 }
 
+// One launch of the layer: work-groups 0 .. n_chain - 1 run the chain of
+// their value head over chunks c0 .. c1 - 1 (their prep done by an earlier
+// launch); the others run the prep of items p0 Hv .. (chunk p0 + item / Hv,
+// value head item % Hv), two per work-group on its two 256-thread halves
+// (an odd last item is done by both halves, which write the same bytes).
+struct GdnLaunch {
+  const bf16* q; const bf16* k; const bf16* v; const float* g; const float* beta;
+  int n, Hk, Hv;
+  float scale;
+  char* rec;
+  bf16* out;
+  int n_chain, c0, c1;            // chain work-groups (0 or Hv) and their chunks
+  const float* s_init;
+  float* s_final;
+  int p0, n_items;                // first prep chunk and (chunk, value head) items
+};
+
+constexpr int kFusedLds = 2 * kStage > 2 * kPrepLds ? 2 * kStage : 2 * kPrepLds;
+
+__global__ __launch_bounds__(512) void gdn_fused_kernel(GdnLaunch a) {
+  __shared__ __align__(16) char lds_all[kFusedLds];
+  if (static_cast<int>(blockIdx.x) < a.n_chain) {
+    gdn_chain_head(a.rec, a.n, a.Hv, blockIdx.x, a.c0, a.c1, a.s_init, a.s_final, a.out, lds_all);
+    return;
+  }
+  const int half = threadIdx.x >> 8;
+  int item = 2 * (static_cast<int>(blockIdx.x) - a.n_chain) + half;
+  if (item >= a.n_items) item = a.n_items - 1;
+  gdn_prep_item(a.q, a.k, a.v, a.g, a.beta, a.n, a.Hk, a.Hv, a.scale, a.rec, a.p0 + item / a.Hv,
+                item % a.Hv, threadIdx.x & 255, lds_all + half * kPrepLds);
+}
+
 }  // namespace
 
 size_t gdn_workspace_bytes(int64_t n, int n_qk_heads, int n_v_heads) {
   if (n <= 0) return 0;
   const size_t nc = static_cast<size_t>((n + kC - 1) / kC);
   (void)n_qk_heads;
-  return nc * static_cast<size_t>(n_v_heads) * kRec;
+  // the records, then the state handed from one piece of the chain to the next
+  return nc * static_cast<size_t>(n_v_heads) * kRec +
+         static_cast<size_t>(n_v_heads) * kD * kD * sizeof(float);
 }
 
 hipError_t launch_gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* g,
@@ -644,12 +688,35 @@ hipError_t launch_gdn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* 
   if (n == 0) return hipSuccess;
   const int nc = static_cast<int>((n + kC - 1) / kC);
   char* rec = static_cast<char*>(workspace);
+  float* state = reinterpret_cast<float*>(rec + static_cast<size_t>(nc) * n_v_heads * kRec);
   const int ni = static_cast<int>(n);
-  hipLaunchKernelGGL(gdn_prep_kernel, dim3(static_cast<unsigned>(nc) * n_v_heads), dim3(256), 0,
-                     stream, reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
-                     reinterpret_cast<const bf16*>(v), g, beta, ni, n_qk_heads, n_v_heads, scale, rec);
-  hipLaunchKernelGGL(gdn_state_kernel, dim3(static_cast<unsigned>(n_v_heads)), dim3(512), 0, stream,
-                     rec, ni, n_v_heads, initial_state, final_state, reinterpret_cast<bf16*>(out));
+  // Pieces of pc chunks: launch i runs the chain over piece i - 1 (work-groups
+  // 0 .. Hv - 1, dispatched first, one CU each) beside the prep of piece i on
+  // the other CUs.  pc ~ 2 sqrt(nc) balances the extra launches against the
+  // first piece's prep, which nothing overlaps.
+  int pc = static_cast<int>(2.0 * std::sqrt(static_cast<double>(nc)) + 0.5);
+  pc = std::max(8, std::min(pc, nc));
+  const int pieces = (nc + pc - 1) / pc;
+  for (int i = 0; i <= pieces; ++i) {
+    GdnLaunch a{};
+    a.q = reinterpret_cast<const bf16*>(q); a.k = reinterpret_cast<const bf16*>(k);
+    a.v = reinterpret_cast<const bf16*>(v); a.g = g; a.beta = beta;
+    a.n = ni; a.Hk = n_qk_heads; a.Hv = n_v_heads; a.scale = scale; a.rec = rec;
+    a.out = reinterpret_cast<bf16*>(out);
+    if (i > 0) {   // the chain over piece i - 1
+      a.n_chain = n_v_heads;
+      a.c0 = (i - 1) * pc;
+      a.c1 = std::min(nc, i * pc);
+      a.s_init = i == 1 ? initial_state : state;
+      a.s_final = i == pieces ? final_state : state;
+    }
+    if (i < pieces) {   // the prep of piece i
+      a.p0 = i * pc;
+      a.n_items = (std::min(nc, (i + 1) * pc) - a.p0) * n_v_heads;
+    }
+    const unsigned grid = static_cast<unsigned>(a.n_chain + (a.n_items + 1) / 2);
+    hipLaunchKernelGGL(gdn_fused_kernel, dim3(grid), dim3(512), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -196,10 +196,11 @@ def test_attention_validation(L):
 
 
 def test_gdn_workspace_bytes(L):
-    # per 64-row chunk and value head 72.25 KiB: -W, U', P, Kt^T, scaled q, Gam_last
+    # per 64-row chunk and value head 72.25 KiB: -W, U', P, Kt^T, scaled q, Gam_last;
+    # plus the fp32 state handed between the pieces of the recurrence
     rec = 16384 + 16384 + 8192 + 16384 + 16384 + 256
     for n, hk, hv in ((1, 1, 1), (64, 16, 32), (65, 16, 32), (8448, 16, 32)):
-        assert L.tg_gdn_workspace_bytes(n, hk, hv, 128) == -(-n // 64) * hv * rec
+        assert L.tg_gdn_workspace_bytes(n, hk, hv, 128) == -(-n // 64) * hv * rec + hv * 128 * 128 * 4
     assert L.tg_gdn_workspace_bytes(0, 16, 32, 128) == 0
     assert L.tg_gdn_workspace_bytes(100, 16, 24, 128) == 0      # 24 % 16
     assert L.tg_gdn_workspace_bytes(100, 16, 32, 64) == 0
