@@ -19,8 +19,13 @@
 //   O    = scale (diag(Gam) Q S^T + P U),  P_ij = exp(c_i - c_j) q_i.k_j (j <= i)
 //   S    <- Gam_last S + U^T Kt,            Kt_j = exp(c_last - c_j) k_j
 //
-// Two launches:
-// 1. gdn_prep: one work-group per (chunk, value head), chunks in parallel.
+// Two roles of one kernel, gdn_fused_kernel, launched once per piece of
+// about 2 sqrt(chunks) chunks (plus one): launch i runs the chain over piece
+// i - 1 on work-groups 0 .. Hv - 1 (dispatched first, one CU each) beside the
+// prep of piece i on the other work-groups, the state passing from piece to
+// piece through the workspace.  The chain occupies Hv CUs; the prep of the
+// next piece fills the rest instead of waiting for the whole chain.
+// 1. prep: one 256-thread half work-group per (chunk, value head).
 //    Forms K K^T and K Q^T on bf16 MFMA (exact products, fp32 sums), A and P
 //    with their decays (P goes out straight from the accumulators), inverts
 //    the unit lower-triangular I + A in fp32 by 16 x 16 blocks (diagonal
@@ -30,7 +35,7 @@
 //    (16 mantissa bits).  Every operand the chain needs leaves as fp16 MFMA
 //    fragments: -W, U', scale P, Kt^T and the scaled queries
 //    scale Gam_i q_i, then Gam_last.
-// 2. gdn_state: one work-group per value head walks the chunks in order, a
+// 2. chain: one work-group per value head walks the piece's chunks in order, a
 //    wave per 32 value rows (the rows of S evolve independently), the head's
 //    per-chunk operands DMAed once into a two-stage LDS ring for the four
 //    state waves by four waves of their own.  Each state wave's fp32 slice
