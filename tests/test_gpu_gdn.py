@@ -45,7 +45,8 @@ def test_gdn_vs_oracle(n, hk, hv):
 
 @pytest.mark.parametrize("n", [300, 1100, 2500])
 def test_gdn_initial_and_final_state(n):
-    """At 300, 1100 and 2500 rows (5, 18 and 40 chunks)."""
+    """At 300, 1100 and 2500 rows: one, three and four pieces of the pipelined
+    layer (the state passes from piece to piece through the workspace)."""
     hk, hv = 2, 4
     x = inputs.gdn_inputs(77 + n, n, hk, hv)
     s0 = (np.random.default_rng(78).standard_normal((hv, 128, 128)) * 0.05).astype(np.float32)
