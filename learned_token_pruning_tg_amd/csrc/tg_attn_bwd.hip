@@ -236,12 +236,13 @@ __global__ __launch_bounds__(kThreads) void bwd_pack_kernel(
 // bwd_dkdv
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
+__device__ __forceinline__ void bwd_dkdv_body(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
     int n_t32, int mp, int clen, int nc, const float* __restrict__ ld, float* __restrict__ colsum,
-    float* __restrict__ dkp, float* __restrict__ dvp, float* __restrict__ dgp) {
+    float* __restrict__ dkp, float* __restrict__ dvp, float* __restrict__ dgp, int bid,
+    char* lds_all) {
   using T = Bwd<D>;
   constexpr int KS = T::KS, DT = T::DT;
   constexpr int NW = kThreads / 64;
@@ -256,14 +257,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
   // whole wave issues their DMA (a lane-divergent DMA made the compiler wait
   // for every DMA in flight before the step's first LDS read); lanes past 16
   // fetch the next steps' values, or zeros past the end, into the rest.
-  __shared__ __align__(16) char lds_all[4 * T::ROWS_TILE + 2 * 1024 + kThreads / 64 * 4];
   auto* lds_qr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all);
   auto* lds_dr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all + 2 * T::ROWS_TILE);
   auto* lds_ld = reinterpret_cast<float (*)[256]>(lds_all + 4 * T::ROWS_TILE);
   float* lds_red = reinterpret_cast<float*>(lds_all + 4 * T::ROWS_TILE + 2 * 1024);
 
   int head, unit;
-  head_unit(blockIdx.x, Hq, head, unit);
+  head_unit(bid, Hq, head, unit);
   const int kt = unit / nc, ch = unit % nc;       // kt ascending: longest walks first
   const int t_end = (M + kRows - 1) / kRows;
   const int t_begin = kt * (kWgRows / kRows) + ch * clen;   // this chunk's query steps
@@ -447,13 +447,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(
 // bwd_dq
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
+__device__ __forceinline__ void bwd_dq_body(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
     int n_t32, int n_t128, int mp, int clen, int nc, const float* __restrict__ ld,
     bf16* __restrict__ dq, float* __restrict__ dqp,
-    float* __restrict__ qdot) {
+    float* __restrict__ qdot, int bid, char* lds_all) {
   using T = Bwd<D>;
   constexpr int KS = T::KS, DT = T::DT;
   constexpr int NW = kThreads / 64;
@@ -461,14 +461,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   static_assert(T::N_ROW_DMA % NW == 0, "row tiles split evenly over the waves");
 
   // all of the kernel's LDS is one object (as in the dK/dV kernel)
-  __shared__ __align__(16) char lds_all[4 * T::ROWS_TILE + 2 * 32 * 4 + kThreads / 64 * 4];
   auto* lds_kr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all);
   auto* lds_vr = reinterpret_cast<char (*)[T::ROWS_TILE]>(lds_all + 2 * T::ROWS_TILE);
   auto* lds_s = reinterpret_cast<float (*)[32]>(lds_all + 4 * T::ROWS_TILE);
   float* lds_red = reinterpret_cast<float*>(lds_all + 4 * T::ROWS_TILE + 2 * 32 * 4);
 
   int head, unit;
-  head_unit(blockIdx.x, Hq, head, unit);
+  head_unit(bid, Hq, head, unit);
   const int qt = n_t128 - 1 - unit / nc, ch = unit % nc;   // longest walks first
   const int u_end = q_walk(qt, M);
   const int u_begin = ch * clen;                 // this chunk's key steps
@@ -637,6 +636,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
   }
 }
 
+// One launch for both walks, which depend only on the pack pass: work-groups
+// 0 .. n_dkdv - 1 take the dK/dV walks (longest first), the rest the dQ
+// walks, so that the dQ work-groups start on the CUs the dK/dV walks leave
+// instead of behind the whole dK/dV launch.  One LDS object, sized for the
+// larger of the two.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_walks_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ key_score,
+    const float* __restrict__ gain, const float* __restrict__ tau, int M, int Hq, int Hkv,
+    int n_t32, int n_t128, int mp, int kv_len, int kv_nc, int q_len, int q_nc,
+    const float* __restrict__ ld, float* __restrict__ colsum, float* __restrict__ dkp,
+    float* __restrict__ dvp, float* __restrict__ dgp, bf16* __restrict__ dq,
+    float* __restrict__ dqp, float* __restrict__ qdot, int n_dkdv) {
+  using T = Bwd<D>;
+  constexpr int kDkdvLds = 4 * T::ROWS_TILE + 2 * 1024 + kThreads / 64 * 4;
+  constexpr int kDqLds = 4 * T::ROWS_TILE + 2 * 32 * 4 + kThreads / 64 * 4;
+  __shared__ __align__(16) char lds_all[kDkdvLds > kDqLds ? kDkdvLds : kDqLds];
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < n_dkdv)
+    bwd_dkdv_body<D>(q, k, v, dout, key_score, gain, tau, M, Hq, Hkv, n_t32, mp, kv_len, kv_nc, ld,
+                     colsum, dkp, dvp, dgp, b, lds_all);
+  else
+    bwd_dq_body<D>(q, k, v, dout, key_score, gain, tau, M, Hq, Hkv, n_t32, n_t128, mp, q_len, q_nc,
+                   ld, dq, dqp, qdot, b - n_dkdv, lds_all);
+}
+
 // ---------------------------------------------------------------------------
 // Reductions (fixed order)
 // ---------------------------------------------------------------------------
@@ -783,12 +809,11 @@ hipError_t launch_d(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
   float* dqp = reinterpret_cast<float*>(ws + p.dqp);
   hipLaunchKernelGGL((bwd_pack_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t32)),
                      dim3(kThreads), 0, stream, out, lse, bd, t, M, Hq, n_t32, ld);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.kv.nc)),
-                     dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, mp,
-                     p.kv.len, p.kv.nc, ld, colsum, dkp, dvp, dgp);
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(static_cast<unsigned>(Hq * n_t128 * p.q.nc)),
+  const int n_dkdv = Hq * n_t128 * p.kv.nc, n_dq = Hq * n_t128 * p.q.nc;
+  hipLaunchKernelGGL((bwd_walks_kernel<D>), dim3(static_cast<unsigned>(n_dkdv + n_dq)),
                      dim3(kThreads), 0, stream, bq, bk, bv, bd, s, g, t, M, Hq, Hkv, n_t32, n_t128,
-                     mp, p.q.len, p.q.nc, ld, reinterpret_cast<bf16*>(dq), dqp, qdot);
+                     mp, p.kv.len, p.kv.nc, p.q.len, p.q.nc, ld, colsum, dkp, dvp, dgp,
+                     reinterpret_cast<bf16*>(dq), dqp, qdot, n_dkdv);
   const int64_t groups = static_cast<int64_t>(M) * Hkv * (D / 4);
   const int n_kv = static_cast<int>((groups + kThreads - 1) / kThreads);
   const int64_t qgroups = static_cast<int64_t>(M) * Hq * (D / 4);
