@@ -57,6 +57,10 @@ def _parse():
                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script "
                         "into the traffic record under profiles/, then exit")
     p.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                   help="write profiles/gated_prefill.<workload>.kernel_trace.md from a rocprofv3 "
+                        "--kernel-trace output folder and the bench output of the same run")
+    p.add_argument("--trace-command", default="", help="command line recorded with --summarize-trace")
     return p.parse_args()
 
 
@@ -166,6 +170,79 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, command: str) -
             fh.write(f"| {name} | {r.get('dispatches')} | {r.get('FETCH_SIZE')} | "
                      f"{r.get('WRITE_SIZE')} |\n")
     print(json.dumps(out))
+
+
+def summarize_trace(trace_dir: str, bench_log: str, workload: str, command: str,
+                    out_path: str = "") -> None:
+    """Per (kernel, work-groups) durations from a rocprofv3 kernel trace, beside
+    the bench's own HIP-event figure for the gated-attention call of that run."""
+    import csv
+    import glob
+    import re
+
+    def demangle(name: str) -> str:
+        # this library's kernels whose names the trace leaves mangled (their
+        # bf16 parameters defeat the demangler): integer and bool template
+        # arguments only
+        m = re.match(r"_ZN2tg12_GLOBAL__N_1(\d+)", name)
+        if not m:
+            return name
+        pos = m.end()
+        kernel = name[pos:pos + int(m.group(1))]
+        rest = name[pos + int(m.group(1)):]
+        if not rest.startswith("I"):
+            return f"tg::{kernel}("
+        args = re.findall(r"L([ib])(\d+)E", rest[:rest.find("EEv")])
+        vals = [("true" if v == "1" else "false") if t == "b" else v for t, v in args]
+        return f"tg::{kernel}<{', '.join(vals)}>("
+
+    def short(name: str) -> str:
+        name = demangle(name)
+        if "tg::" not in name:
+            return "torch/other " + name[:48]
+        name = re.sub(r"^void\s+", "", name)
+        name = re.sub(r"tg::(\(anonymous namespace\)::)?", "", name)
+        depth, out = 0, []
+        for ch in name:            # drop the argument list, keep template arguments
+            if ch == "(" and depth == 0:
+                break
+            depth += ch == "<"
+            depth -= ch == ">"
+            out.append(ch)
+        return "".join(out).strip()
+
+    groups = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            wg = (int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"])
+                  * int(r["Workgroup_Size_Z"]))
+            key = (short(r["Kernel_Name"]), grid // max(wg, 1))
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            groups.setdefault(key, []).append(us)
+    total = sum(sum(v) for v in groups.values()) or 1.0
+    line = None
+    with open(bench_log) as fh:
+        for ln in fh:
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    path = out_path or os.path.join(ROOT, "profiles", f"gated_prefill.{workload}.kernel_trace.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Kernel trace: gated prefill step + decode, prologue, backward and hybrid-layer "
+                 f"stages, {workload}\n\nCommand (from the repository root, on one MI355X):\n\n"
+                 f"    {command}\n\nPer (kernel, work-groups) from the trace CSV; durations in "
+                 f"microseconds.\n\n")
+        if line and line.get("roofline"):
+            rf = line["roofline"]
+            fh.write(f"The bench's HIP-event average for one gated-attention call in the same "
+                     f"(instrumented) run: {rf['avg_launch_ms'] * 1000:.2f} us per launch "
+                     f"({rf['achieved']:.2f} TFLOP/s, frac {rf['frac']:.4f}).\n\n")
+        fh.write("| kernel | work-groups | calls | average | min | max | share |\n"
+                 "|---|---|---|---|---|---|---|\n")
+        for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            fh.write(f"| {name} | {wgs} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | "
+                     f"{max(v):.2f} | {100 * sum(v) / total:.2f}% |\n")
+    print(path)
 
 
 def load_traffic(workload: str):
@@ -411,6 +488,10 @@ def other_configs(names, steps, warmup, dev, stream):
 
 def main():
     args = _parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.workload,
+                        args.trace_command)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.pmc_command)
         return

@@ -55,3 +55,29 @@ def test_more_than_one_gpu_is_refused():
     assert p.returncode == 2
     assert "only one GPU" in p.stderr
     assert p.stdout.strip() == ""
+
+
+def test_summarize_trace_names_and_averages(tmp_path):
+    # a two-kernel trace in rocprofv3's CSV form, one name left mangled as the
+    # profiler leaves this library's bf16-parameter kernels
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    hdr = ('"Kind","Kernel_Name","Start_Timestamp","End_Timestamp","Workgroup_Size_X",'
+           '"Workgroup_Size_Y","Workgroup_Size_Z","Grid_Size_X","Grid_Size_Y","Grid_Size_Z"\n')
+    rows = [
+        ("_ZN2tg12_GLOBAL__N_113v_pack_kernelILi128ELb1EEEvPKDF16bPKfS5_S5_iiiPcS6_", 0, 9000, 256, 4224),
+        ("_ZN2tg12_GLOBAL__N_113v_pack_kernelILi128ELb1EEEvPKDF16bPKfS5_S5_iiiPcS6_", 0, 11000, 256, 4224),
+        ("void tg::(anonymous namespace)::topk_clear_kernel(unsigned int*, int)", 5, 4005, 64, 64),
+    ]
+    with open(d / "run_kernel_trace.csv", "w") as f:
+        f.write(hdr)
+        for name, t0, t1, wg, grid in rows:
+            f.write(f'"KERNEL_DISPATCH","{name}","{t0}","{t1}","{wg}","1","1","{grid}","1","1"\n')
+    log = tmp_path / "bench.log"
+    log.write_text('noise\n{"roofline": {"avg_launch_ms": 0.3, "achieved": 974.5, "frac": 0.3898}}\n')
+    out = tmp_path / "trace.md"
+    bench.summarize_trace(str(tmp_path / "trace"), str(log), "tiny", "cmd", str(out))
+    text = out.read_text()
+    assert "| v_pack_kernel<128, true> | 16 | 2 | 10.00 | 9.00 | 11.00 | 83.33% |" in text
+    assert "| topk_clear_kernel | 1 | 1 | 4.00 | 4.00 | 4.00 | 16.67% |" in text
+    assert "300.00 us per launch (974.50 TFLOP/s, frac 0.3898)" in text
