@@ -228,15 +228,18 @@ def summarize_trace(trace_dir: str, bench_log: str, workload: str, command: str,
                 line = json.loads(ln)
     path = out_path or os.path.join(ROOT, "profiles", f"gated_prefill.{workload}.kernel_trace.md")
     with open(path, "w") as fh:
-        fh.write(f"# Kernel trace: gated prefill step + decode, prologue, backward and hybrid-layer "
-                 f"stages, {workload}\n\nCommand (from the repository root, on one MI355X):\n\n"
+        fh.write(f"# Kernel trace of bench.py on {workload}\n\n"
+                 f"Command (from the repository root, on one MI355X):\n\n"
                  f"    {command}\n\nPer (kernel, work-groups) from the trace CSV; durations in "
                  f"microseconds.\n\n")
         if line and line.get("roofline"):
             rf = line["roofline"]
             fh.write(f"The bench's HIP-event average for one gated-attention call in the same "
                      f"(instrumented) run: {rf['avg_launch_ms'] * 1000:.2f} us per launch "
-                     f"({rf['achieved']:.2f} TFLOP/s, frac {rf['frac']:.4f}).\n\n")
+                     f"({rf['achieved']:.2f} TFLOP/s, frac {rf['frac']:.4f}). It spans the "
+                     f"call's launches (Vt pack, attention, and the merge where query tiles are "
+                     f"split) with any gaps between them; the table's durations are per kernel "
+                     f"and cover every call of the run, untimed ones included.\n\n")
         fh.write("| kernel | work-groups | calls | average | min | max | share |\n"
                  "|---|---|---|---|---|---|---|\n")
         for (name, wgs), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
